@@ -1,0 +1,249 @@
+"""Benchmark: NVFP4 Four-Over-Six quantization of a 32768 x 5120 bf16 prefill
+activation tensor on one MI355X.
+
+One step is one pass of the whole quantization path over the resident input:
+tensor amax -> global scale (6*256 under 4/6) -> 4/6 quantize with the MSE
+rule, writing packed E2M1 codes, E4M3 scale bytes, the per-block selection
+bitmap and the per-tensor error sum.  Throughput is counted with the
+algorithmic byte formula of the metric, 2.5625 B per element (2 B of bf16
+read, 0.5 B of codes and 0.0625 B of scales written).
+
+Before any number is reported the outputs are compared with the CPU oracle
+(bit-exact codes, scales, g and bitmap; error sum to 1e-6).  The oracle is
+timed on the host in the same run (`cpu_baseline`).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_quantize_rows_4over6_32768x5120.json")
+KERNEL_SOURCES = ["quantize_rows.hip", "nvfp4_device.h", "nvfp4_kernels.h"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "nvfp4_block_scaled_wave64_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(numel):
+    """HBM bytes per launch of the quantize kernel from the committed PMC
+    summary, or None when the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash() or t.get("numel") != numel:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the full-tensor oracle run; gate on sampled rows instead")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path's "
+              "multi-GPU sharding is described in DESIGN.md and not run here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_block_scaled_wave64_amd as nv
+    import testkit
+
+    cfg = testkit.CONFIGS[4]
+    rows, cols = cfg.rows, cfg.cols
+    numel = rows * cols
+    log(f"generating config 4 input {rows}x{cols}")
+    x = testkit.make(4)
+    checksum = testkit.fnv1a64(x)
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    pshape, sshape, nsel = nv.output_shapes(rows, cols, nv.AXIS_COLS)
+    packed = torch.empty(pshape, dtype=torch.uint8, device=dev)
+    scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+    selmap = torch.empty(nsel, dtype=torch.uint8, device=dev)
+    err = torch.empty(1, dtype=torch.float64, device=dev)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    out = {"packed": packed, "scales": scales, "selmap": selmap, "err_sum": err}
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        nv.amax(xd, out=amax)
+        nv.global_scale(amax, nv.MODE_4OVER6, out=g)
+        if ev is not None:
+            ev[0].record(stream)
+        nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, gscale=g, selmap=True,
+                    err_sum=True, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    # ---- parity gate (and the CPU baseline) ----
+    log("parity gate")
+    step()
+    torch.cuda.synchronize()
+    import oracle
+
+    g_ref = oracle.global_scale(oracle.amax(x), nv.MODE_4OVER6)
+    gpu_g = np.float32(g.item())
+    ok = gpu_g.view(np.uint32) == g_ref.view(np.uint32)
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        log("oracle on the full tensor (single-threaded C)")
+        t0 = time.perf_counter()
+        ref = oracle.quantize(x, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE)
+        t_cpu = time.perf_counter() - t0
+        ok &= np.array_equal(packed.cpu().numpy().reshape(-1), ref["packed"])
+        ok &= np.array_equal(scales.cpu().numpy().reshape(-1), ref["scales"])
+        ok &= np.array_equal(selmap.cpu().numpy(), ref["selmap"])
+        ok &= abs(err.item() - ref["err_sum"]) <= 1e-6 * abs(ref["err_sum"])
+        cpu_baseline = {
+            "value": round(numel * BYTES_PER_ELEM / t_cpu / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole {rows}x{cols} tensor, one pass (amax, global scale, 4/6 MSE "
+                      f"quantize, bitmap, error sum); {t_cpu:.1f} s single-threaded",
+            "elements_per_s": round(numel / t_cpu, 1),
+        }
+    else:
+        rng = np.random.default_rng(0)
+        pick = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 126)]))
+        ref = oracle.quantize(x[pick], nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE,
+                              gscale=g_ref, want_err=False)
+        bpr = cols // 16
+        ok &= np.array_equal(packed.cpu().numpy()[pick].reshape(-1), ref["packed"])
+        ok &= np.array_equal(scales.cpu().numpy()[pick].reshape(-1), ref["scales"])
+        bits = np.unpackbits(selmap.cpu().numpy(), bitorder="little")[: numel // 16]
+        want = np.unpackbits(ref["selmap"], bitorder="little")[: pick.size * bpr]
+        ok &= np.array_equal(bits.reshape(rows, bpr)[pick].reshape(-1), want)
+    if not ok:
+        log("PARITY FAILED: no throughput is reported")
+        sys.exit(1)
+    log("parity ok")
+
+    # ---- timed region ----
+    for _ in range(args.warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = numel * BYTES_PER_ELEM / (ms_per_step * 1e-3) / 1e9
+    k_avg_s = float(kern_ms.mean()) * 1e-3
+    achieved = numel * BYTES_PER_ELEM / k_avg_s / 1e9
+
+    # ---- secondary lines (same input, same process) ----
+    extra = {"input_fnv1a64": f"{checksum:016x}",
+             "quantize_call_us_avg": round(k_avg_s * 1e6, 2),
+             "quantize_call_us_min": round(float(kern_ms.min()) * 1e3, 2),
+             "quantize_call_gbps": round(achieved, 1),
+             "elements_per_s_step": round(numel / (ms_per_step * 1e-3), 1)}
+
+    def time_call(fn, reps=50):
+        for _ in range(5):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    t_amax = time_call(lambda: nv.amax(xd, out=amax))
+    extra["amax_gbps"] = round(numel * 2 / t_amax / 1e9, 1)
+    t_std = time_call(lambda: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_STD, nv.RULE_MSE, gscale=g,
+                                          out={"packed": packed, "scales": scales}))
+    t_46 = time_call(lambda: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE,
+                                         gscale=g, out={"packed": packed, "scales": scales}))
+    extra["std_quantize_gbps"] = round(numel * BYTES_PER_ELEM / t_std / 1e9, 1)
+    extra["4over6_quantize_gbps_no_bitmap_no_err"] = round(numel * BYTES_PER_ELEM / t_46 / 1e9, 1)
+    extra["4over6_overhead_vs_std_pct"] = round((t_46 / t_std - 1) * 100, 1)
+    t_e2e = time_call(lambda: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE,
+                                          selmap=True, err_sum=True,
+                                          out={"packed": packed, "scales": scales,
+                                               "selmap": selmap, "err_sum": err, "gscale": g}))
+    extra["e2e_quantize_ex_gbps"] = round(numel * BYTES_PER_ELEM / t_e2e / 1e9, 1)
+    deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    t_deq = time_call(lambda: nv.dequantize(packed, scales, g, rows, cols, nv.AXIS_COLS,
+                                            torch.bfloat16, out=deq))
+    extra["dequantize_bf16_gbps"] = round(numel * (0.5 + 1 / 16 + 2) / t_deq / 1e9, 1)
+
+    traffic = measured_traffic(numel)
+    line = {
+        "metric": "NVFP4 4/6 quantize GB/s (bf16 in) and % of HBM peak, 32K×5120 activations",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "4/6 NVFP4 quantize (MSE rule) of a 32768x5120 bf16 prefill activation "
+                        "tensor, 0.5*Student-t(3) with 8 outlier channels x100, plus selection "
+                        "bitmap and per-tensor MSE; step = amax + global scale + quantize",
+            "rows": rows,
+            "cols": cols,
+            "block_axis": "cols (16 contiguous elements)",
+            "mode": "4over6",
+            "rule": "mse",
+            "bytes_per_element": BYTES_PER_ELEM,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "quantize_rows_kernel (4/6, MSE, bitmap, error sum)",
+        },
+        "cpu_baseline": cpu_baseline,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

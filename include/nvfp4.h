@@ -1,0 +1,136 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 block-scaled quantization
+ * library with "Four Over Six" (4/6) adaptive block scales.
+ *
+ * The format (NVFP4): 4-bit E2M1 element codes packed two per byte, one FP8
+ * E4M3 scale per block of 16 elements, one fp32 scale per tensor.
+ *   - blocks of 16 elements: "Why Gated DeltaNet in hybrid 27B LLMs
+ *     withstands 4-bit quantization" (sns.style), "Deep analysis"; "ARCQuant"
+ *     summary (gist.science 2601.07475), "Problem definition";
+ *   - E2M1 grid {0, 0.5, 1, 1.5, 2, 3, 4, 6} and the standard max->6 block
+ *     scaling: "Technical summary: Four Over Six (4/6)" (gist.science
+ *     2512.02010), "Problem statement";
+ *   - the max->4 alternative, quantizing each block both ways and keeping the
+ *     one with lower MSE or MAE: same page, "Core mechanism" and "Adaptive
+ *     block scaling algorithm";
+ *   - E4M3 block scales and the tensor scale formed with 256 instead of 448
+ *     under 4/6: same page, "Implementation details".
+ *
+ * Arithmetic (every step one IEEE binary32 operation, round to nearest even):
+ *   g   = A / (6*M)   A = max |x|, M = 448 (standard) or 256 (4/6)
+ *   G   = 1/g, or 0 when that is not a positive finite number
+ *   per block, for c in {6} (standard) or {6, 4} (4/6):
+ *     s_c = b * (G / c)               b = max |x| over the block
+ *     S_c = E4M3(s_c)                 round to nearest even, saturating at 448
+ *     d_c = dec(S_c) * g              decode multiplier
+ *     r_c = min(G * (1/dec(S_c)), FLT_MAX), and 0 when S_c == 0
+ *     code_i = sign(x_i) | E2M1(|x_i * r_c|)   nearest even, saturating at 6
+ *     e_c = sum of (dec(code_i) * d_c - x_i)^2 (MSE) or of |.| (MAE), summed
+ *           as two sequential halves of 8 elements (fused multiply-add for the
+ *           squares) and then added
+ *   keep c = 4 iff e_4 < e_6 (ties go to 6).
+ *
+ * Conventions shared by every call:
+ *   - Every pointer is caller-owned DEVICE memory (e.g. torch tensors); the
+ *     library allocates nothing and keeps no pointer after returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued on it; no call synchronizes the host.
+ *   - Arguments are checked before any HIP call, in the order null pointers,
+ *     enums, shape, alignment.  On a failed check nothing is launched and
+ *     nothing is written.  NVFP4_ERR_HIP reports a failed launch; device
+ *     faults surface at the caller's next synchronization.
+ *   - Tensors are row-major [rows][cols] bf16 bit patterns.  Non-finite
+ *     inputs are outside the contract.
+ *   - Calls on different streams may run concurrently; they share no state.
+ *   - Alignment: bf16 inputs and dequantized outputs 16 bytes; packed codes
+ *     and the selection bitmap 4 bytes; err_sum 8 bytes; scalars 4 bytes.
+ *
+ * Layouts.  Block axis NVFP4_AXIS_COLS (=1): a block is 16 consecutive
+ * elements of one row; packed is [rows][cols/2] with element 2j in bits 0-3
+ * of byte j and element 2j+1 in bits 4-7; scales is [rows][cols/16]; block b
+ * (row-major block order) owns bit (b & 7) of byte b >> 3 of the selection
+ * bitmap (1 = the max->4 candidate was kept).  Block axis NVFP4_AXIS_ROWS
+ * (=0): a block is 16 consecutive rows of one column and every output is laid
+ * out as the NVFP4_AXIS_COLS output of the transposed tensor: packed
+ * [cols][rows/2], scales [cols][rows/16], bitmap bit c*(rows/16) + rb.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,  /* a required pointer is NULL                        */
+  NVFP4_ERR_ENUM = 2,  /* block_axis, mode, rule, out_dtype or flags invalid */
+  NVFP4_ERR_SHAPE = 3, /* non-positive extent, or block-axis extent % 16 != 0 */
+  NVFP4_ERR_ALIGN = 4, /* a pointer violates the alignment listed above      */
+  NVFP4_ERR_HIP = 5    /* a kernel launch failed                            */
+} nvfp4_status;
+
+enum { NVFP4_AXIS_ROWS = 0, NVFP4_AXIS_COLS = 1 };
+enum { NVFP4_MODE_STD = 0, NVFP4_MODE_4OVER6 = 1 };
+enum { NVFP4_RULE_MSE = 0, NVFP4_RULE_MAE = 1 }; /* ignored for NVFP4_MODE_STD */
+enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
+enum { NVFP4_FLAG_GSCALE_GIVEN = 1u }; /* use *gscale_inout as g; skip the amax pass */
+
+/* Tensor amax A = max |x| over `numel` bf16 values, written as fp32 to
+ * *amax_out (device).  numel >= 1.  The global scale of the pages is formed
+ * from it ("Technical summary: Four Over Six (4/6)", "Implementation
+ * details").  *amax_out is used as the accumulator, so it must not alias the
+ * input. */
+nvfp4_status nvfp4_amax(const uint16_t* in_bf16, int64_t numel, float* amax_out, void* stream);
+
+/* Global (per-tensor) decode scale g = A / (6*M) from a device amax, with
+ * M = 448 for NVFP4_MODE_STD and 256 for NVFP4_MODE_4OVER6 ("Technical
+ * summary: Four Over Six (4/6)", "Implementation details").  amax and
+ * gscale_out may be the same pointer. */
+nvfp4_status nvfp4_global_scale(const float* amax, int mode, float* gscale_out, void* stream);
+
+/* Quantize a [rows][cols] bf16 tensor.  Computes A and g itself and writes g
+ * to *gscale_out, then the packed codes and the E4M3 scale bytes (sizes
+ * rows*cols/2 and rows*cols/16 bytes).  mode: NVFP4_MODE_STD (every block's
+ * max mapped to 6) or NVFP4_MODE_4OVER6 (both candidates, keep the lower
+ * error under `rule`) -- "Technical summary: Four Over Six (4/6)",
+ * "Adaptive block scaling algorithm". */
+nvfp4_status nvfp4_quantize(const uint16_t* in_bf16, int64_t rows, int64_t cols, int block_axis,
+                            int mode, int rule, uint8_t* packed_out, uint8_t* scales_out,
+                            float* gscale_out, void* stream);
+
+/* As nvfp4_quantize, plus:
+ *   flags & NVFP4_FLAG_GSCALE_GIVEN: read g from *gscale_inout instead of
+ *     computing it (a calibrated or shared tensor scale); g must be finite
+ *     and in [0, 2^117].  Without the flag g is computed and written there.
+ *   selmap_out (nullable): the selection bitmap, ceil(rows*cols/128) bytes;
+ *     bits past the last block are written as 0.  All zero in standard mode.
+ *   err_sum_out (nullable): one double, zeroed by the call and then set to
+ *     the sum over blocks of the kept candidate's block error -- squared
+ *     error under NVFP4_RULE_MSE and in standard mode, absolute error under
+ *     NVFP4_RULE_MAE.  Accumulated in binary64 in an unspecified order.
+ *     Divide by rows*cols for the per-tensor MSE / MAE. */
+nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                               int block_axis, int mode, int rule, uint32_t flags,
+                               uint8_t* packed_out, uint8_t* scales_out, float* gscale_inout,
+                               uint8_t* selmap_out, double* err_sum_out, void* stream);
+
+/* Dequantize: x_hat = dec(code) * (dec(S) * g), each product one binary32
+ * rounding; the same x_hat the quantizer measured its error against.
+ * out_dtype NVFP4_OUT_F32 writes float, NVFP4_OUT_BF16 writes the bf16
+ * (round to nearest even) of it.  `out` is [rows][cols] in the caller's
+ * layout for either block axis; packed/scales are laid out as produced by
+ * nvfp4_quantize with the same block_axis. */
+nvfp4_status nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, const float* gscale,
+                              int64_t rows, int64_t cols, int block_axis, int out_dtype,
+                              void* out, void* stream);
+
+/* Static description of a status code. */
+const char* nvfp4_status_string(nvfp4_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

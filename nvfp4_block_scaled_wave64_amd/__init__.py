@@ -1,0 +1,184 @@
+"""Python binding of the NVFP4 / Four-Over-Six C ABI (include/nvfp4.h).
+
+Argument marshalling only: every step of quantization runs in the HIP
+library built from csrc/ for gfx950.  There is no fallback; if the library
+is missing or was not built, every call raises.  PyTorch supplies device
+memory and streams.
+
+Format and method: 16-element blocks with FP8 E4M3 scales, E2M1 codes and an
+fp32 tensor scale; under 4/6 each block is quantized with its max mapped to 6
+and to 4 and the one with lower MSE/MAE is kept ("Technical summary: Four
+Over Six (4/6)", gist.science 2512.02010, "Adaptive block scaling
+algorithm" and "Implementation details").
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4.so")
+
+AXIS_ROWS, AXIS_COLS = 0, 1
+MODE_STD, MODE_4OVER6 = 0, 1
+RULE_MSE, RULE_MAE = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
+FLAG_GSCALE_GIVEN = 1
+
+STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_ENUM", 3: "NVFP4_ERR_SHAPE",
+          4: "NVFP4_ERR_ALIGN", 5: "NVFP4_ERR_HIP"}
+
+# Every symbol the public headers declare, with its ctypes signature.
+_P, _I64, _I, _U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+SIGNATURES = {
+    "nvfp4_amax": ([_P, _I64, _P, _P], _I),
+    "nvfp4_global_scale": ([_P, _I, _P, _P], _I),
+    "nvfp4_quantize": ([_P, _I64, _I64, _I, _I, _I, _P, _P, _P, _P], _I),
+    "nvfp4_quantize_ex": ([_P, _I64, _I64, _I, _I, _I, _U32, _P, _P, _P, _P, _P, _P], _I),
+    "nvfp4_dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _P], _I),
+    "nvfp4_status_string": ([_I], ctypes.c_char_p),
+    "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _I, _P, _P], _I),
+    "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _I, _P, _P], _I),
+    "nvfp4v_decode_tables": ([_I, _P, _P, _P, _P], _I),
+}
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_text(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run nvfp4_block_scaled_wave64_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _status_text(status):
+    try:
+        return lib().nvfp4_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _check(status, what):
+    if status != 0:
+        raise NVFP4Error(status, what)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _bf16_input(x):
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("input must hold bf16 bit patterns (bfloat16, int16 or uint16)")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("input must be a contiguous device tensor")
+    return x
+
+
+def output_shapes(rows, cols, block_axis):
+    """Shapes of (packed, scales) and the bitmap length for a [rows][cols] tensor."""
+    n_rows, n_cols = (rows, cols) if block_axis == AXIS_COLS else (cols, rows)
+    nblocks = rows * cols // 16
+    return (n_rows, n_cols // 2), (n_rows, n_cols // 16), (nblocks + 7) // 8
+
+
+def amax(x, out=None, stream=None):
+    """A = max |x| of a bf16 tensor, as a 1-element float32 device tensor."""
+    x = _bf16_input(x)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().nvfp4_amax(_ptr(x), x.numel(), _ptr(out), _stream(stream)), "nvfp4_amax")
+    return out
+
+
+def global_scale(amax_t, mode, out=None, stream=None):
+    """g = A / (6*M) (M = 448 standard, 256 under 4/6) from a device amax."""
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=amax_t.device)
+    _check(lib().nvfp4_global_scale(_ptr(amax_t), int(mode), _ptr(out), _stream(stream)),
+           "nvfp4_global_scale")
+    return out
+
+
+def quantize(x, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE, gscale=None,
+             selmap=False, err_sum=False, out=None, stream=None):
+    """Quantize a [rows][cols] bf16 device tensor.
+
+    gscale: optional 1-element float32 device tensor holding a given g (the
+    amax pass is skipped).  Returns a dict with packed, scales, gscale and,
+    when asked for, selmap (uint8 bitmap) and err_sum (float64, 1 element).
+    `out` may supply preallocated tensors under the same keys.
+    """
+    x = _bf16_input(x)
+    if x.dim() != 2:
+        raise ValueError("input must be 2-D [rows][cols]")
+    rows, cols = x.shape
+    pshape, sshape, nsel = output_shapes(rows, cols, block_axis)
+    dev = x.device
+    out = dict(out or {})
+    packed = out.get("packed")
+    if packed is None:
+        packed = torch.empty(pshape, dtype=torch.uint8, device=dev)
+    scales = out.get("scales")
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+    flags = 0
+    if gscale is not None:
+        g = gscale
+        flags |= FLAG_GSCALE_GIVEN
+    else:
+        g = out.get("gscale")
+        if g is None:
+            g = torch.empty(1, dtype=torch.float32, device=dev)
+    sel = out.get("selmap") if selmap else None
+    if selmap and sel is None:
+        sel = torch.empty(max(nsel, 1), dtype=torch.uint8, device=dev)
+    err = out.get("err_sum") if err_sum else None
+    if err_sum and err is None:
+        err = torch.empty(1, dtype=torch.float64, device=dev)
+    st = lib().nvfp4_quantize_ex(_ptr(x), rows, cols, int(block_axis), int(mode), int(rule),
+                                 flags, _ptr(packed), _ptr(scales), _ptr(g), _ptr(sel), _ptr(err),
+                                 _stream(stream))
+    _check(st, "nvfp4_quantize_ex")
+    res = {"packed": packed, "scales": scales, "gscale": g}
+    if selmap:
+        res["selmap"] = sel
+    if err_sum:
+        res["err_sum"] = err
+    return res
+
+
+def dequantize(packed, scales, gscale, rows, cols, block_axis=AXIS_COLS, out_dtype=torch.float32,
+               out=None, stream=None):
+    """x_hat [rows][cols] (float32 or bfloat16) from packed codes and scales."""
+    code = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=packed.device)
+    st = lib().nvfp4_dequantize(_ptr(packed), _ptr(scales), _ptr(gscale), int(rows), int(cols),
+                                int(block_axis), code, _ptr(out), _stream(stream))
+    _check(st, "nvfp4_dequantize")
+    return out

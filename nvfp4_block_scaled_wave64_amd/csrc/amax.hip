@@ -1,0 +1,90 @@
+// amax.hip -- tensor amax (grid reduction), global scale and small set-up
+// kernels.
+//
+// The per-tensor scale of NVFP4 is formed from the tensor's absolute maximum
+// ("Technical summary: Four Over Six (4/6)", gist.science 2512.02010,
+// "Implementation details": 6*448 for standard NVFP4, 6*256 under 4/6).
+//
+// amax is a pure 2-byte-per-element read.  Each lane reads 16 bytes (8 bf16)
+// per step, clears the sign bits and keeps a packed pair of 16-bit maxima
+// (non-negative bf16 bit patterns order like unsigned integers, so the max of
+// the patterns is the pattern of the max).  Waves reduce with cross-lane
+// shuffles, workgroups through LDS, and each workgroup issues one atomic max
+// on the fp32 bit pattern of its result.
+#include "nvfp4_device.h"
+#include "nvfp4_kernels.h"
+
+namespace nvfp4 {
+
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
+__global__ void init_kernel(uint32_t* zero_u32, double* zero_f64, uint32_t* zero_words,
+                            int64_t nwords) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) {
+    if (zero_u32) *zero_u32 = 0u;
+    if (zero_f64) *zero_f64 = 0.0;
+  }
+  for (int64_t w = i; w < nwords; w += (int64_t)gridDim.x * blockDim.x) zero_words[w] = 0u;
+}
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  ushort2_t va = __builtin_bit_cast(ushort2_t, a), vb = __builtin_bit_cast(ushort2_t, b);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(va, vb));
+}
+
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ in, int64_t nvec,
+                                                        const uint16_t* __restrict__ tail,
+                                                        int ntail, uint32_t* __restrict__ acc) {
+  __shared__ uint32_t part[kWavesPerGroup];
+  uint32_t m = 0u;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+    const uint4 w = load_stream16(&in[i]);
+    const uint32_t a = max_u16x2(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu);
+    const uint32_t b = max_u16x2(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu);
+    m = max_u16x2(m, max_u16x2(a, b));
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max_u16x2(m, tail[threadIdx.x] & 0x7FFFu);
+  uint32_t v = max(m & 0xFFFFu, m >> 16) << 16;  // fp32 bit pattern of |x|max
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = part[0];
+    for (int k = 1; k < kWavesPerGroup; ++k) r = max(r, part[k]);
+    atomicMax(acc, r);
+  }
+}
+
+__global__ void global_scale_kernel(const float* amax, float six_m, float* gscale) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *gscale = *amax / six_m;
+}
+
+hipError_t launch_init(uint32_t* zero_u32, double* zero_f64, uint32_t* zero_words, int64_t nwords,
+                       hipStream_t s) {
+  int64_t blocks = (nwords + kThreads - 1) / kThreads;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 1024) blocks = 1024;
+  init_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(zero_u32, zero_f64, zero_words, nwords);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const uint16_t* in, int64_t numel, uint32_t* acc_bits, hipStream_t s) {
+  const int64_t nvec = numel / 8;
+  const int ntail = (int)(numel % 8);
+  int64_t want = (nvec + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)device_cu_count() * 16;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  amax_kernel<<<(unsigned)want, kThreads, 0, s>>>(reinterpret_cast<const uint4*>(in), nvec,
+                                                  in + nvec * 8, ntail, acc_bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_global_scale(const float* amax, float six_m, float* gscale, hipStream_t s) {
+  global_scale_kernel<<<1, 64, 0, s>>>(amax, six_m, gscale);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

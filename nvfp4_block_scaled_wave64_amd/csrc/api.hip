@@ -1,0 +1,148 @@
+// api.hip -- the C ABI (include/nvfp4.h): argument checks, then kernel
+// launches on the caller's stream.  No allocation, no host synchronization.
+#include <atomic>
+
+#include "../../include/nvfp4.h"
+#include "nvfp4_kernels.h"
+
+namespace nvfp4 {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace nvfp4
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+// Largest supported element count: keeps every byte offset and the bitmap
+// bit index comfortably inside int64.
+constexpr int64_t kMaxNumel = int64_t(1) << 46;
+
+nvfp4_status check_shape(int64_t rows, int64_t cols, int block_axis) {
+  if (rows <= 0 || cols <= 0) return NVFP4_ERR_SHAPE;
+  if (rows > kMaxNumel / cols) return NVFP4_ERR_SHAPE;
+  const int64_t along = block_axis == NVFP4_AXIS_COLS ? cols : rows;
+  if (along % 16 != 0) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_ENUM: return "invalid block_axis, mode, rule, out_dtype or flags";
+    case NVFP4_ERR_SHAPE: return "invalid shape (extents must be positive, block axis a multiple of 16)";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer";
+    case NVFP4_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+nvfp4_status nvfp4_amax(const uint16_t* in_bf16, int64_t numel, float* amax_out, void* stream) {
+  if (!in_bf16 || !amax_out) return NVFP4_ERR_NULL;
+  if (numel <= 0 || numel > kMaxNumel) return NVFP4_ERR_SHAPE;
+  if (!aligned(in_bf16, 16) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* acc = reinterpret_cast<uint32_t*>(amax_out);
+  hipError_t e = nvfp4::launch_init(acc, nullptr, nullptr, 0, s);
+  if (e == hipSuccess) e = nvfp4::launch_amax(in_bf16, numel, acc, s);
+  return hip_status(e);
+}
+
+nvfp4_status nvfp4_global_scale(const float* amax, int mode, float* gscale_out, void* stream) {
+  if (!amax || !gscale_out) return NVFP4_ERR_NULL;
+  if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
+  if (!aligned(amax, 4) || !aligned(gscale_out, 4)) return NVFP4_ERR_ALIGN;
+  const float six_m = mode == NVFP4_MODE_4OVER6 ? 6.0f * 256.0f : 6.0f * 448.0f;
+  return hip_status(nvfp4::launch_global_scale(amax, six_m, gscale_out,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                               int block_axis, int mode, int rule, uint32_t flags,
+                               uint8_t* packed_out, uint8_t* scales_out, float* gscale_inout,
+                               uint8_t* selmap_out, double* err_sum_out, void* stream) {
+  if (!in_bf16 || !packed_out || !scales_out || !gscale_inout) return NVFP4_ERR_NULL;
+  if (block_axis != NVFP4_AXIS_ROWS && block_axis != NVFP4_AXIS_COLS) return NVFP4_ERR_ENUM;
+  if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
+  if (rule != NVFP4_RULE_MSE && rule != NVFP4_RULE_MAE) return NVFP4_ERR_ENUM;
+  if (flags & ~uint32_t(NVFP4_FLAG_GSCALE_GIVEN)) return NVFP4_ERR_ENUM;
+  const nvfp4_status shape = check_shape(rows, cols, block_axis);
+  if (shape != NVFP4_OK) return shape;
+  if (!aligned(in_bf16, 16) || !aligned(packed_out, 4) || !aligned(gscale_inout, 4) ||
+      !aligned(selmap_out, 4) || !aligned(err_sum_out, 8))
+    return NVFP4_ERR_ALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool given = (flags & NVFP4_FLAG_GSCALE_GIVEN) != 0;
+  uint32_t variant = 0;
+  if (mode == NVFP4_MODE_4OVER6) {
+    variant |= nvfp4::kVarFourOverSix;
+    if (rule == NVFP4_RULE_MAE) variant |= nvfp4::kVarMae;
+  }
+  if (selmap_out) variant |= nvfp4::kVarSelmap;
+  if (err_sum_out) variant |= nvfp4::kVarErr;
+
+  hipError_t e = hipSuccess;
+  uint32_t* acc = reinterpret_cast<uint32_t*>(gscale_inout);
+  if (!given || err_sum_out)
+    e = nvfp4::launch_init(given ? nullptr : acc, err_sum_out, nullptr, 0, s);
+  if (e == hipSuccess && !given) {
+    e = nvfp4::launch_amax(in_bf16, rows * cols, acc, s);
+    if (e == hipSuccess) {
+      const float six_m = mode == NVFP4_MODE_4OVER6 ? 6.0f * 256.0f : 6.0f * 448.0f;
+      e = nvfp4::launch_global_scale(gscale_inout, six_m, gscale_inout, s);
+    }
+  }
+  if (e == hipSuccess) {
+    if (block_axis == NVFP4_AXIS_COLS)
+      e = nvfp4::launch_quantize_rows(in_bf16, rows * cols / 16, gscale_inout, variant,
+                                      packed_out, scales_out, selmap_out, err_sum_out, s);
+    else
+      e = nvfp4::launch_quantize_cols(in_bf16, rows, cols, gscale_inout, variant, packed_out,
+                                      scales_out, selmap_out, err_sum_out, s);
+  }
+  return hip_status(e);
+}
+
+nvfp4_status nvfp4_quantize(const uint16_t* in_bf16, int64_t rows, int64_t cols, int block_axis,
+                            int mode, int rule, uint8_t* packed_out, uint8_t* scales_out,
+                            float* gscale_out, void* stream) {
+  return nvfp4_quantize_ex(in_bf16, rows, cols, block_axis, mode, rule, 0u, packed_out,
+                           scales_out, gscale_out, nullptr, nullptr, stream);
+}
+
+nvfp4_status nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, const float* gscale,
+                              int64_t rows, int64_t cols, int block_axis, int out_dtype,
+                              void* out, void* stream) {
+  if (!packed || !scales || !gscale || !out) return NVFP4_ERR_NULL;
+  if (block_axis != NVFP4_AXIS_ROWS && block_axis != NVFP4_AXIS_COLS) return NVFP4_ERR_ENUM;
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_ENUM;
+  const nvfp4_status shape = check_shape(rows, cols, block_axis);
+  if (shape != NVFP4_OK) return shape;
+  if (!aligned(packed, 4) || !aligned(gscale, 4) || !aligned(out, 16)) return NVFP4_ERR_ALIGN;
+  return hip_status(nvfp4::launch_dequantize(packed, scales, gscale, rows, cols, block_axis,
+                                             out_dtype == NVFP4_OUT_BF16, out,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+"""The C-ABI library on the host: it loads, it exports every symbol the
+public headers declare, and it rejects bad arguments before any HIP call
+(so these run without a GPU; the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_wave64_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("nvfp4.h", "nvfp4_verify.h")]
+
+A = ctypes.c_void_p(0x10000)  # aligned dummy device address (never touched)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+MIS = ctypes.c_void_p(0x10002)
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(nvfp4v?_[a-z_0-9]+)\s*\(",
+                            text, flags=re.M)
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = nv.lib()
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(nv.SIGNATURES)
+
+
+def test_status_strings():
+    L = nv.lib()
+    for s in range(6):
+        assert L.nvfp4_status_string(s)
+    assert b"unknown" in L.nvfp4_status_string(99)
+
+
+def q(**kw):
+    args = dict(in_=A, rows=32, cols=64, axis=nv.AXIS_COLS, mode=nv.MODE_4OVER6, rule=nv.RULE_MSE,
+                flags=0, packed=B, scales=C, g=A, sel=None, err=None)
+    args.update(kw)
+    return nv.lib().nvfp4_quantize_ex(args["in_"], args["rows"], args["cols"], args["axis"],
+                                      args["mode"], args["rule"], args["flags"], args["packed"],
+                                      args["scales"], args["g"], args["sel"], args["err"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_=None), 1), (dict(packed=None), 1), (dict(scales=None), 1), (dict(g=None), 1),
+    (dict(axis=2), 2), (dict(mode=3), 2), (dict(rule=-1), 2), (dict(flags=2), 2),
+    (dict(rows=0), 3), (dict(cols=-16), 3), (dict(cols=40), 3),
+    (dict(axis=nv.AXIS_ROWS, rows=24), 3), (dict(rows=1 << 40, cols=1 << 10), 3),
+    (dict(in_=MIS), 4), (dict(sel=ctypes.c_void_p(0x10001)), 4),
+    (dict(err=ctypes.c_void_p(0x10004)), 4), (dict(packed=ctypes.c_void_p(0x10002)), 4),
+])
+def test_quantize_rejects(kw, status):
+    assert q(**kw) == status
+
+
+def test_check_order_null_before_enum_before_shape_before_align():
+    assert q(in_=None, mode=7, rows=0) == 1
+    assert q(mode=7, rows=0, in_=MIS) == 2
+    assert q(rows=0, in_=MIS) == 3
+
+
+def test_other_entry_points_reject():
+    L = nv.lib()
+    assert L.nvfp4_amax(None, 16, A, None) == 1
+    assert L.nvfp4_amax(A, 0, B, None) == 3
+    assert L.nvfp4_amax(MIS, 16, B, None) == 4
+    assert L.nvfp4_global_scale(A, 2, B, None) == 2
+    assert L.nvfp4_global_scale(None, 0, B, None) == 1
+    assert L.nvfp4_dequantize(A, B, C, 32, 64, nv.AXIS_COLS, 2, A, None) == 2
+    assert L.nvfp4_dequantize(A, B, C, 32, 8, nv.AXIS_COLS, 0, A, None) == 3
+    assert L.nvfp4_dequantize(A, B, C, 32, 64, nv.AXIS_COLS, 0, MIS, None) == 4
+    assert L.nvfp4_quantize(None, 16, 16, 1, 0, 0, A, B, C, None) == 1
+    assert L.nvfp4v_e2m1_encode_sweep(0, 16, 5, A, None) == 2
+    assert L.nvfp4v_e2m1_encode_sweep(0xFFFFFFF0, 17, 0, A, None) == 3
+    assert L.nvfp4v_e4m3_encode_sweep(0, 16, 0, None, None) == 1
+    assert L.nvfp4v_decode_tables(0, None, A, B, None) == 1
