@@ -37,9 +37,9 @@ SIGNATURES = {
     "nvfp4_quantize_ex": ([_P, _I64, _I64, _I, _I, _I, _U32, _P, _P, _P, _P, _P, _P], _I),
     "nvfp4_dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _P], _I),
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
-    "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _I, _P, _P], _I),
-    "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _I, _P, _P], _I),
-    "nvfp4v_decode_tables": ([_I, _P, _P, _P, _P], _I),
+    "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _P, _P], _I),
+    "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _P, _P], _I),
+    "nvfp4v_decode_tables": ([ctypes.c_float, _P, _P, _P, _P, _P], _I),
 }
 
 

@@ -33,13 +33,28 @@ __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(va, vb));
 }
 
+// Loads in flight per thread and step.
+constexpr int kAmaxUnroll = 4;
+
 __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ in, int64_t nvec,
                                                         const uint16_t* __restrict__ tail,
                                                         int ntail, uint32_t* __restrict__ acc) {
   __shared__ uint32_t part[kWavesPerGroup];
   uint32_t m = 0u;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kAmaxUnroll - 1) * stride < nvec; i += kAmaxUnroll * stride) {
+    uint4 w[kAmaxUnroll];
+#pragma unroll
+    for (int k = 0; k < kAmaxUnroll; ++k) w[k] = load_stream16(&in[i + k * stride]);
+#pragma unroll
+    for (int k = 0; k < kAmaxUnroll; ++k) {
+      const uint32_t a = max_u16x2(w[k].x & 0x7FFF7FFFu, w[k].y & 0x7FFF7FFFu);
+      const uint32_t b = max_u16x2(w[k].z & 0x7FFF7FFFu, w[k].w & 0x7FFF7FFFu);
+      m = max_u16x2(m, max_u16x2(a, b));
+    }
+  }
+  for (; i < nvec; i += stride) {
     const uint4 w = load_stream16(&in[i]);
     const uint32_t a = max_u16x2(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu);
     const uint32_t b = max_u16x2(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu);
@@ -73,8 +88,8 @@ hipError_t launch_init(uint32_t* zero_u32, double* zero_f64, uint32_t* zero_word
 hipError_t launch_amax(const uint16_t* in, int64_t numel, uint32_t* acc_bits, hipStream_t s) {
   const int64_t nvec = numel / 8;
   const int ntail = (int)(numel % 8);
-  int64_t want = (nvec + kThreads - 1) / kThreads;
-  const int64_t cap = (int64_t)device_cu_count() * 16;
+  int64_t want = (nvec + kThreads * kAmaxUnroll - 1) / (kThreads * kAmaxUnroll);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
   if (want > cap) want = cap;
   if (want < 1) want = 1;
   amax_kernel<<<(unsigned)want, kThreads, 0, s>>>(reinterpret_cast<const uint4*>(in), nvec,

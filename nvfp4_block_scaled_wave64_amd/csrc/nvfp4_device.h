@@ -20,6 +20,9 @@ constexpr float kFltMax = 3.40282346638528859812e+38f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Cache policy of streaming loads: non-temporal (the input is read once).
+constexpr int kStreamLoad = 2;
+
 // 16-byte streaming load (non-temporal hint: the input is read once).
 __device__ __forceinline__ uint4 load_stream16(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -41,50 +44,87 @@ __device__ __forceinline__ float e4m3_decode(uint32_t S) {
   return __uint_as_float(S << 20) * 0x1p120f;
 }
 
-// Encode s >= 0 to E4M3 with round-to-nearest-even, saturating at 448; NaN
-// and non-positive inputs give 0.  Rounding to 3 fraction bits is a single
-// add of C = 2^20 * P, where P is the power of two at or below max(s, 2^-6):
-// the ulp of C is P/8, the spacing of E4M3 in the binade of s (and 2^-9 in
-// the subnormal range).  The rounded value q times 2^-120 has the E4M3 code
-// in bits 20..26 (see e4m3_decode).
-__device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  s = fminf(fmaxf(s, 0.0f), 448.0f);
-  const float p = __uint_as_float(__float_as_uint(fmaxf(s, 0x1p-6f)) & 0x7F800000u);
-  const float t = __builtin_fmaf(p, 0x1p20f, s);
-  const float q = __builtin_fmaf(-p, 0x1p20f, t);
-  return __float_as_uint(q * 0x1p-120f) >> 20;
+// E4M3 bytes of two block scales s0, s1 (s0 in bits 0-7, s1 in bits 8-15):
+// round to nearest even, saturating at 448; NaN and non-positive inputs give
+// 0.  Clamping to [0, 448] first makes the gfx950 conversion
+// (v_cvt_pk_fp8_f32, OCP E4M3FN, round to nearest even) exact for every
+// input; the test suite checks it against the CPU reference on every fp32
+// bit pattern in [0, 464] and on the saturation range.
+// Bits 16-31 of the result are unspecified.
+__device__ __forceinline__ uint32_t e4m3_encode2(float s0, float s1) {
+  s0 = fminf(fmaxf(s0, 0.0f), 448.0f);
+  s1 = fminf(fmaxf(s1, 0.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s0, s1, (int)__builtin_bit_cast(uint32_t, s0),
+                                                   false);
 }
 
 // ---------------------------------------------------------------- E2M1 ----
 
-// Round a >= 0 (finite or +inf) to the E2M1 magnitude grid with
-// round-to-nearest-even, saturating at 6.  Same construction as e4m3_encode:
-// the grid has 1 fraction bit, spacing 0.5 below 2 (C = 2^22), 1 in [2, 4)
-// (C = 2^23) and 2 in [4, 8) (C = 2^24).  Clamping to 6 first keeps every
-// result on the grid.  Returns the grid value (0, 0.5, ..., 6).
-__device__ __forceinline__ float e2m1_round(float a) {
-  a = fminf(a, 6.0f);
-  const float p = __uint_as_float(__float_as_uint(fmaxf(a, 1.0f)) & 0x7F800000u);
-  const float t = __builtin_fmaf(p, 0x1p22f, a);
-  return __builtin_fmaf(-p, 0x1p22f, t);
+// E2M1 codes of 8 fp32 values, element i in bits 4i..4i+3: sign in bit 3,
+// magnitude rounded to nearest even on {0, 0.5, 1, 1.5, 2, 3, 4, 6},
+// saturating at 6 (infinities included).  gfx950's v_cvt_scalef32_pk_fp4_f32
+// with scale 1.0 does exactly this for every non-NaN input (checked against
+// the CPU reference on every fp32 in [0, 8] and on sampled wider and negative
+// ranges by the test suite); scaled values are never NaN here.
+__device__ __forceinline__ uint32_t e2m1_encode8(const float y[8]) {
+  // Each conversion writes one byte of w; all four bytes are written, so the
+  // starting value does not matter.
+  uint32_t w = __float_as_uint(y[0]);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+  return w;
 }
 
-// The 3-bit magnitude index of a grid value q in {0, 0.5, ..., 6}: q * 2^-126
-// is a binary32 number whose exponent and top fraction bit are exactly the
-// E2M1 exponent and mantissa (0.5 lands on the subnormal 2^-127).
-__device__ __forceinline__ uint32_t e2m1_index(float q) {
-  return __float_as_uint(q * 0x1p-126f) >> 22;
+// Values of 8 E2M1 codes (exact; code 8 decodes to -0).
+__device__ __forceinline__ void e2m1_decode8(uint32_t w, float v[8]) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+  v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
 }
 
 // ---------------------------------------------------------------- lanes ----
 
-// Value of the neighbouring lane of a lane pair (lane ^ 1) via DPP
-// quad_perm [1, 0, 3, 2].
-__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+// Lanes l and l + 32 of a wave form a pair (l < 32).  pair_values returns,
+// in both lanes of every pair, the value held by the lower lane (.x) and by
+// the upper lane (.y), using gfx950's v_permlane32_swap (one VALU op, no LDS).
+// Callers only combine .x and .y with commutative operations.
+__device__ __forceinline__ float2 pair_values(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return make_float2(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
-__device__ __forceinline__ float pair_swap(float v) {
-  return __uint_as_float(pair_swap(__float_as_uint(v)));
+
+// For per-lane partial sums a (first candidate) and b (second candidate) of
+// the two halves of a block: returns (lo_a + hi_a, lo_b + hi_b) in both lanes
+// of the pair, where lo is the lower lane's value.  One swap lets the lower
+// lane form the first sum and the upper lane the second; a second swap
+// shares both.
+__device__ __forceinline__ float2 pair_sums(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                 false);
+  // lower lane: p[0] = own a (lo_a), p[1] = partner's a (hi_a);
+  // upper lane: p[0] = partner's b (lo_b), p[1] = own b (hi_b).
+  const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  return pair_values(s);
+}
+
+// max(|a|, |b|, |c|) without canonicalising the operands (gfx950
+// v_maximum3_f32); the inputs are never NaN.
+__device__ __forceinline__ float absmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(fabsf(a), fabsf(b)),
+                                       fabsf(c));
+}
+
+// Buffer resource over `bytes` bytes at p (raw, stride 0): loads past the end
+// return 0 and stores past the end are dropped, so tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
 // Per-launch scale constants derived from g ("Implementation details": the
@@ -131,70 +171,74 @@ struct HalfBlock {
 };
 
 // One lane's half of a block held by a lane pair: wd are the lane's 8 bf16
-// values (element 2j in the low half of wd[j]); `odd` says whether this is
-// the second half.  k_mine is k6 on even lanes and k4 on odd lanes (4/6);
-// tab[S] = (d, r) for every scale byte.  Implements the block steps of the
-// method: block max, candidate scales, E2M1 rounding, reconstruction error,
+// values (element 2j in the low half of wd[j]); the pair's other lane
+// (lane ^ 32) holds the other half, the lower lane the first 8 elements.  tab[S] = (d, r) for every scale byte.
+// Implements the block steps of the method -- block max, the candidate
+// scales, E2M1 codes, reconstruction error against the original values,
 // selection ("Technical summary: Four Over Six (4/6)", "Adaptive block
-// scaling algorithm"), with the error of each half summed sequentially and
-// the two halves then added.
+// scaling algorithm") -- with each half's error summed sequentially and the
+// two halves then added, so both lanes of the pair hold the same block
+// errors and take the same decision.
 template <bool k46, bool kMae, bool kNeedErr>
-__device__ __forceinline__ HalfBlock quantize_half_block(const uint32_t wd[4], bool odd,
-                                                         float k_mine, const float2* tab) {
-  float a[8];  // |x|
+__device__ __forceinline__ HalfBlock quantize_half_block(const uint32_t wd[4], float k6, float k4,
+                                                         const float2* tab) {
+  float x[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    a[2 * j] = fabsf(bf16_lo(wd[j]));
-    a[2 * j + 1] = fabsf(bf16_hi(wd[j]));
+    x[2 * j] = bf16_lo(wd[j]);
+    x[2 * j + 1] = bf16_hi(wd[j]);
   }
-  const float m = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
-                        fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
-  const float b = fmaxf(m, pair_swap(m));
+  const float m = absmax3(absmax3(x[0], x[1], x[2]), absmax3(x[3], x[4], x[5]),
+                          __builtin_elementwise_maximum(fabsf(x[6]), fabsf(x[7])));
+  const float2 mp = pair_values(m);
+  const float b = __builtin_elementwise_maximum(mp.x, mp.y);
 
-  // Block scales: each lane encodes one candidate, the pair swaps them.
-  const uint32_t s_mine = e4m3_encode(b * k_mine);
-  uint32_t S6 = s_mine, S4 = s_mine;
-  if (k46) {
-    const uint32_t s_other = pair_swap(s_mine);
-    S6 = odd ? s_other : s_mine;
-    S4 = odd ? s_mine : s_other;
-  }
+  // Block scales of the candidates, S6 in bits 0-7 and S4 in bits 8-15.
+  const uint32_t S2 = e4m3_encode2(b * k6, k46 ? b * k4 : 0.0f);
+  const uint32_t S6 = S2 & 0xFFu, S4 = (S2 >> 8) & 0xFFu;
   const float2 t6 = tab[S6];  // (d, r)
-  const float2 t4 = k46 ? tab[S4] : t6;
 
-  // Both candidates in magnitude: x and its reconstruction share a sign, so
-  // |xhat - x| = |RN(q * d) - |x||.
-  float q6[8], q4[8];
-  float h6 = 0.0f, h4 = 0.0f;
+  HalfBlock r;
+  float y[8], v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    q6[i] = e2m1_round(a[i] * t6.y);
-    if (kNeedErr) {
-      const float d6 = q6[i] * t6.x - a[i];
-      h6 = kMae ? h6 + fabsf(d6) : __builtin_fmaf(d6, d6, h6);
-    }
-    if (k46) {
-      q4[i] = e2m1_round(a[i] * t4.y);
-      const float d4 = q4[i] * t4.x - a[i];
-      h4 = kMae ? h4 + fabsf(d4) : __builtin_fmaf(d4, d4, h4);
+  for (int i = 0; i < 8; ++i) y[i] = x[i] * t6.y;
+  const uint32_t c6 = e2m1_encode8(y);
+  float h6 = 0.0f, h4 = 0.0f;
+  if (kNeedErr) {
+    e2m1_decode8(c6, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float dl = v[i] * t6.x - x[i];
+      h6 = kMae ? h6 + fabsf(dl) : __builtin_fmaf(dl, dl, h6);
     }
   }
-  HalfBlock r;
+  uint32_t c4 = 0u;
+  if (k46) {
+    const float2 t4 = tab[S4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[i] * t4.y;
+    c4 = e2m1_encode8(y);
+    e2m1_decode8(c4, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float dl = v[i] * t4.x - x[i];
+      h4 = kMae ? h4 + fabsf(dl) : __builtin_fmaf(dl, dl, h4);
+    }
+  }
+  // Block errors lo + hi, the same sums on both lanes.
   float e6 = 0.0f, e4 = 0.0f;
-  if (kNeedErr) e6 = h6 + pair_swap(h6);  // lo + hi: the same sum on both lanes
-  if (k46) e4 = h4 + pair_swap(h4);
-  r.pick4 = k46 && (e4 < e6);             // ties and NaN keep max->6
+  if (k46) {
+    const float2 e = pair_sums(h6, h4);
+    e6 = e.x;
+    e4 = e.y;
+  } else if (kNeedErr) {
+    const float2 hp = pair_values(h6);
+    e6 = hp.x + hp.y;
+  }
+  r.pick4 = k46 && (e4 < e6);  // ties and NaN keep max->6
   r.err = r.pick4 ? e4 : e6;
   r.S = r.pick4 ? S4 : S6;
-
-  uint32_t word = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float q = (k46 && r.pick4) ? q4[i] : q6[i];
-    const uint32_t sgn = (wd[i >> 1] >> ((i & 1) ? 28 : 12)) & 8u;  // sign of x -> bit 3
-    word |= (e2m1_index(q) | sgn) << (4 * i);
-  }
-  r.word = word;
+  r.word = r.pick4 ? c4 : c6;
   return r;
 }
 

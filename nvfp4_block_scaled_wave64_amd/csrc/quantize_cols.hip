@@ -11,13 +11,13 @@
 //   2. transpose through LDS: the tile is stored column-major (tileT[col][row])
 //      with a row pitch of 72 elements; the pad keeps the 16-byte reads of
 //      step 3 aligned and spreads the columns of a wave over the banks;
-//   3. compute: a lane pair takes one block (16 rows of one column), each lane
-//      reading its 8 rows as one 16-byte LDS read, and runs the same block
-//      math as the row-wise kernel;
-//   4. store: 8 consecutive lanes cover the 4 blocks (32 bytes of codes) of
-//      one column in this tile.  Since a workgroup walks down the rows of its
-//      strip, successive tiles extend the same output rows and the partial
-//      lines merge in that XCD's L2.
+//   3. compute: a lane pair (l, l + 32) takes one block (16 rows of one
+//      column), each lane reading its 8 rows as one 16-byte LDS read, and runs
+//      the same block math as the row-wise kernel;
+//   4. store: the 4 blocks of a column in this tile are 32 contiguous bytes
+//      of codes.  Since a workgroup walks down the rows of its strip,
+//      successive tiles extend the same output rows and the partial lines
+//      merge in that XCD's L2.
 // When a selection bitmap is requested, the kernel marks the kept candidate
 // in bit 7 of the scale byte (always 0 in a non-negative E4M3 scale) and a
 // second pass turns those bits into the bitmap and clears them, which avoids
@@ -51,8 +51,6 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const bool odd = (lane & 1) != 0;
-  const float k_mine = (k46 && odd) ? ts.k4 : ts.k6;
   const int64_t c0 = (int64_t)blockIdx.x * kTileCols;
   const int64_t r_begin = (int64_t)blockIdx.y * rows_per_group;
   int64_t r_end = r_begin + rows_per_group;
@@ -89,25 +87,27 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
     }
     __syncthreads();
 
-    // 3 + 4: 256 blocks (64 columns x 4 row blocks), 512 half blocks.
+    // 3 + 4: 256 blocks (64 columns x 4 row blocks).  In pass p, wave w
+    // takes blocks (4p + w) * 32 + (lane & 31); lane l < 32 holds rows 0-7 of
+    // its block and lane l + 32 rows 8-15.
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int hbid = p * kThreads + t;
-      const int col = hbid >> 3, rb = (hbid >> 1) & 3, h = hbid & 1;
+      const int blk = (p * kWavesPerGroup + (t >> 6)) * 32 + (lane & 31);
+      const int col = blk >> 2, rb = blk & 3, h = lane >> 5;
       const uint4 w = *reinterpret_cast<const uint4*>(&tileT[col * kPitch + rb * 16 + h * 8]);
       const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-      const HalfBlock hb = quantize_half_block<k46, kMae, kNeedErr>(wd, odd, k_mine, tab);
+      const HalfBlock hb = quantize_half_block<k46, kMae, kNeedErr>(wd, ts.k6, ts.k4, tab);
       const int64_t gc = c0 + col;
       const int64_t grb = r0 / 16 + rb;  // block index along the column
       const bool valid = gc < cols && r0 + rb * 16 < r_end;
       if (valid) {
         packed[(gc * rows / 2 + grb * 8 + h * 4) / 4] = hb.word;
-        if (!odd) {
+        if (h == 0) {
           uint32_t sb = hb.S;
           if (kSel && hb.pick4) sb |= 0x80u;
           scales[gc * rb16 + grb] = (uint8_t)sb;
         }
-        if (kErr && !odd) acc += (double)hb.err;
+        if (kErr && h == 0) acc += (double)hb.err;
       }
     }
   }

@@ -11,31 +11,37 @@
 //                             errors stay in registers.
 //
 // Work layout (wave64).  The tensor is a flat sequence of 16-element blocks
-// (the packed codes, the scale bytes and the bitmap are in the same order).
-// One wave step covers a chunk of 32 blocks = 512 elements = 1 KiB of input:
-// lane l loads the 16 bytes at offset 16*l, so a lane pair (2p, 2p+1) holds
-// block p, the even lane the first 8 elements.  Loads are fully coalesced
-// 1 KiB wave accesses; each lane stores its 8 codes as one dword (256 B per
-// wave), even lanes store the block's scale byte, and the 32 selection bits
-// of a chunk are one dword of the bitmap.
+// and the packed codes, scale bytes and bitmap follow the same order.  A wave
+// step covers a chunk of 32 blocks = 512 elements = 1 KiB of input: lane l
+// (l < 32) holds the first 8 elements of block l and lane l + 32 the last 8,
+// so one 16-byte load per lane reads the whole KiB, and the 32 selection
+// bits of the chunk are the low half of one wave ballot.  The two lanes of a
+// block exchange their partial maximum and partial errors with one
+// v_permlane32_swap each.  Each lane converts both candidate scales with one
+// packed E4M3 conversion, reads their decode / encode multipliers from a
+// per-workgroup LDS table of all 128 scale bytes, and evaluates both
+// candidates on its 8 elements with packed E2M1 conversions (encode and
+// decode), keeping every intermediate in registers.
 //
-// Per block, the lane pair shares the work that is per block: each lane
-// encodes one candidate's E4M3 scale (even lane max->6, odd lane max->4) and
-// the pair swaps them with one DPP move; decode / encode multipliers of all
-// 127 scale bytes sit in a per-workgroup LDS table built at start-up.  Each
-// lane then evaluates both candidates on its 8 elements (scaled value, E2M1
-// rounding, reconstruction, error) and the pair adds its two half-block
-// errors with one more DPP move, so both lanes hold e_6 and e_4 and take the
-// same decision.
+// Memory: all global accesses are raw buffer operations with hardware range
+// checks (loads past the end read 0, stores past the end are dropped), so the
+// ragged last chunk needs no branches, and the per-lane offsets are fixed.
+// Each wave keeps the loads of its next chunks in flight while it works on
+// the current ones.  One launch covers at most 2^30 elements (buffer offsets
+// are 32-bit); the host splits larger tensors at chunk boundaries.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
 namespace nvfp4 {
 
+// Chunks in flight per wave: the next round's loads are issued before the
+// current round is processed.
+constexpr int kDepth = 2;
+
 template <uint32_t V>
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
-    const uint4* __restrict__ in, int64_t nblocks, const float* __restrict__ gscale,
-    uint32_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
+    const uint16_t* __restrict__ in, int64_t nblocks, const float* __restrict__ gscale,
+    uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
     double* __restrict__ err_sum) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr bool kMae = k46 && (V & kVarMae) != 0;
@@ -50,47 +56,60 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
   build_scale_table(tab, ts);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  const bool odd = (lane & 1) != 0;
-  const float k_mine = (k46 && odd) ? ts.k4 : ts.k6;
-  const int64_t nchunks = (nblocks + 31) / 32;
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
+  const uint32_t nb = (uint32_t)nblocks;  // <= 2^26 per launch
+  const __amdgpu_buffer_rsrc_t r_in = make_rsrc(in, nb * 32u);
+  const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed, nb * 8u);
+  const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales, nb);
+  const __amdgpu_buffer_rsrc_t r_sel = make_rsrc(selmap, (nb + 7u) / 8u);
+
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t blk_in_chunk = lane & 31u, half = lane >> 5;
+  const uint32_t off_in = blk_in_chunk * 32u + half * 16u;    // bytes within a 1 KiB chunk
+  const uint32_t off_packed = blk_in_chunk * 8u + half * 4u;  // within 256 B
+  const uint32_t off_scale = half ? 0x80000000u : blk_in_chunk;  // upper lanes: out of range
+  const uint32_t off_sel = lane < 4u ? lane : 0x80000000u;
+  const uint32_t nchunks = (nb + 31u) / 32u;
+  const uint32_t nwaves = gridDim.x * kWavesPerGroup;
+  const uint32_t first = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
   double acc = 0.0;
 
-  for (int64_t ch = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6); ch < nchunks;
-       ch += nwaves) {
-    const int64_t blk = ch * 32 + (lane >> 1);
-    const bool valid = blk < nblocks;
-    uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (valid) w = load_stream16(&in[ch * 64 + lane]);
-    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-    const HalfBlock hb = quantize_half_block<k46, kMae, kNeedErr>(wd, odd, k_mine, tab);
-    const bool pick4 = hb.pick4;
-    if (valid) {
-      packed[ch * 64 + lane] = hb.word;
-      if (!odd) scales[blk] = (uint8_t)hb.S;
-    }
-    if (kSel) {
-      // Both lanes of a pair vote the same bit; keep the even-lane bits.
-      uint64_t x = __ballot(pick4) & 0x5555555555555555ull;
-      x = (x | (x >> 1)) & 0x3333333333333333ull;
-      x = (x | (x >> 2)) & 0x0F0F0F0F0F0F0F0Full;
-      x = (x | (x >> 4)) & 0x00FF00FF00FF00FFull;
-      x = (x | (x >> 8)) & 0x0000FFFF0000FFFFull;
-      x = (x | (x >> 16)) & 0x00000000FFFFFFFFull;
-      const int64_t nvalid = nblocks - ch * 32;
-      if (nvalid >= 32) {
-        if (lane == 0) reinterpret_cast<uint32_t*>(selmap)[ch] = (uint32_t)x;
-      } else if (lane < (int)((nvalid + 7) / 8)) {
-        selmap[ch * 4 + lane] = (uint8_t)(x >> (8 * lane));
+  // Chunks past the end read as zeros (range-checked buffer load); ch stays
+  // below nchunks + kDepth * nwaves, so ch * 1024 cannot wrap.
+  auto load = [&](uint32_t ch) -> u32x4 {
+    return __builtin_amdgcn_raw_buffer_load_b128(r_in, ch * 1024u + off_in, 0, kStreamLoad);
+  };
+
+  u32x4 buf[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k) buf[k] = load(first + k * nwaves);
+
+  for (uint32_t base = first; base < nchunks; base += kDepth * nwaves) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const uint32_t ch = base + k * nwaves;
+      const u32x4 w = buf[k];
+      buf[k] = load(ch + kDepth * nwaves);
+      if (ch >= nchunks) break;  // wave-uniform
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      const HalfBlock hb = quantize_half_block<k46, kMae, kNeedErr>(wd, ts.k6, ts.k4, tab);
+      __builtin_amdgcn_raw_buffer_store_b32(hb.word, r_packed, ch * 256u + off_packed, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)hb.S, r_scales, ch * 32u + off_scale, 0, 0);
+      if (kSel) {
+        // Lane l < 32 decides block l: the low half of the ballot is the
+        // chunk's 32 selection bits; lanes 0-3 store its 4 bytes.
+        const uint32_t bits = (uint32_t)__ballot(hb.pick4);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(bits >> (8u * (lane & 3u))), r_sel,
+                                             ch * 4u + off_sel, 0, 0);
       }
+      // Both lanes of a pair hold the block error (blocks past the end
+      // contribute 0); the wave total is halved at the end.
+      if (kErr) acc += (double)hb.err;
     }
-    if (kErr && valid && !odd) acc += (double)hb.err;
   }
 
   if (kErr) {
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) wsum[threadIdx.x >> 6] = acc;
+    if (lane == 0) wsum[threadIdx.x >> 6] = 0.5 * acc;
     __syncthreads();
     if (threadIdx.x == 0) {
       double t = wsum[0];
@@ -104,14 +123,23 @@ template <uint32_t V>
 static hipError_t launch_rows_v(const uint16_t* in, int64_t nblocks, const float* gscale,
                                 uint8_t* packed, uint8_t* scales, uint8_t* selmap,
                                 double* err_sum, hipStream_t s) {
-  const int64_t nchunks = (nblocks + 31) / 32;
-  int64_t groups = (nchunks + kWavesPerGroup - 1) / kWavesPerGroup;
+  // Segments of at most 2^26 blocks (2^30 elements, 2 GiB of input) keep
+  // every buffer offset within 32 bits; a multiple of 32 blocks, so each
+  // segment's bitmap starts on a byte (indeed a dword) boundary.
+  constexpr int64_t kSeg = int64_t(1) << 26;
   const int64_t cap = (int64_t)device_cu_count() * 8;  // 8 groups (32 waves) per CU
-  if (groups > cap) groups = cap;
-  quantize_rows_kernel<V><<<(unsigned)groups, kThreads, 0, s>>>(
-      reinterpret_cast<const uint4*>(in), nblocks, gscale, reinterpret_cast<uint32_t*>(packed),
-      scales, selmap, err_sum);
-  return hipGetLastError();
+  for (int64_t b0 = 0; b0 < nblocks; b0 += kSeg) {
+    const int64_t nb = nblocks - b0 < kSeg ? nblocks - b0 : kSeg;
+    const int64_t nchunks = (nb + 31) / 32;
+    int64_t groups = (nchunks + kWavesPerGroup - 1) / kWavesPerGroup;
+    if (groups > cap) groups = cap;
+    quantize_rows_kernel<V><<<(unsigned)groups, kThreads, 0, s>>>(
+        in + b0 * 16, nb, gscale, packed + b0 * 8, scales + b0,
+        selmap ? selmap + b0 / 8 : nullptr, err_sum);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_quantize_rows(const uint16_t* in, int64_t nblocks, const float* gscale,

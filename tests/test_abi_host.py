@@ -82,7 +82,7 @@ def test_other_entry_points_reject():
     assert L.nvfp4_dequantize(A, B, C, 32, 8, nv.AXIS_COLS, 0, A, None) == 3
     assert L.nvfp4_dequantize(A, B, C, 32, 64, nv.AXIS_COLS, 0, MIS, None) == 4
     assert L.nvfp4_quantize(None, 16, 16, 1, 0, 0, A, B, C, None) == 1
-    assert L.nvfp4v_e2m1_encode_sweep(0, 16, 5, A, None) == 2
-    assert L.nvfp4v_e2m1_encode_sweep(0xFFFFFFF0, 17, 0, A, None) == 3
-    assert L.nvfp4v_e4m3_encode_sweep(0, 16, 0, None, None) == 1
-    assert L.nvfp4v_decode_tables(0, None, A, B, None) == 1
+    assert L.nvfp4v_e2m1_encode_sweep(0xFFFFFFF0, 17, A, None) == 3
+    assert L.nvfp4v_e2m1_encode_sweep(0, 0, A, None) == 3
+    assert L.nvfp4v_e4m3_encode_sweep(0, 16, None, None) == 1
+    assert L.nvfp4v_decode_tables(1.0, None, A, B, C, None) == 1
