@@ -2,9 +2,11 @@
 activation tensor on one MI355X.
 
 One step is one pass of the whole quantization path over the resident input:
-tensor amax -> global scale (6*256 under 4/6) -> 4/6 quantize with the MSE
-rule, writing packed E2M1 codes, E4M3 scale bytes, the per-block selection
-bitmap and the per-tensor error sum.  Throughput is counted with the
+zero the error accumulator -> tensor amax -> global scale (6*256 under 4/6)
+-> 4/6 quantize with the MSE rule, writing packed E2M1 codes, E4M3 scale
+bytes, the per-block selection bitmap and the per-tensor error sum.  HIP
+events on the same stream bracket the quantize kernel (one launch) in every
+step; its mean duration gives the roofline figure.  Throughput is counted with the
 algorithmic byte formula of the metric, 2.5625 B per element (2 B of bf16
 read, 0.5 B of codes and 0.0625 B of scales written).
 
@@ -96,12 +98,13 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        err.zero_()
         nv.amax(xd, out=amax)
         nv.global_scale(amax, nv.MODE_4OVER6, out=g)
         if ev is not None:
             ev[0].record(stream)
         nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, gscale=g, selmap=True,
-                    err_sum=True, out=out)
+                    err_sum=True, err_accumulate=True, out=out)
         if ev is not None:
             ev[1].record(stream)
 
@@ -200,6 +203,13 @@ def main():
                                           out={"packed": packed, "scales": scales,
                                                "selmap": selmap, "err_sum": err, "gscale": g}))
     extra["e2e_quantize_ex_gbps"] = round(numel * BYTES_PER_ELEM / t_e2e / 1e9, 1)
+    # Plain device copy of known size: the calibration kernel for the HBM
+    # byte counters, and the read+write streaming ceiling of this device.
+    csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    t_copy = time_call(lambda: cdst.copy_(csrc), reps=20)
+    extra["copy_256MiB_gbps"] = round(2 * csrc.numel() / t_copy / 1e9, 1)
+    del csrc, cdst
     deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
     t_deq = time_call(lambda: nv.dequantize(packed, scales, g, rows, cols, nv.AXIS_COLS,
                                             torch.bfloat16, out=deq))

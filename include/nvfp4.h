@@ -25,9 +25,10 @@
  *     d_c = dec(S_c) * g              decode multiplier
  *     r_c = min(G * (1/dec(S_c)), FLT_MAX), and 0 when S_c == 0
  *     code_i = sign(x_i) | E2M1(|x_i * r_c|)   nearest even, saturating at 6
- *     e_c = sum of (dec(code_i) * d_c - x_i)^2 (MSE) or of |.| (MAE), summed
- *           as two sequential halves of 8 elements (fused multiply-add for the
- *           squares) and then added
+ *     e_c = sum of delta_i^2 (MSE) or of |delta_i| (MAE), delta_i =
+ *           dec(code_i) * d_c - x_i evaluated exactly and rounded once (fused
+ *           multiply-add), summed as two sequential halves of 8 elements
+ *           (fused multiply-add for the squares) and then added
  *   keep c = 4 iff e_4 < e_6 (ties go to 6).
  *
  * Conventions shared by every call:
@@ -76,7 +77,10 @@ enum { NVFP4_AXIS_ROWS = 0, NVFP4_AXIS_COLS = 1 };
 enum { NVFP4_MODE_STD = 0, NVFP4_MODE_4OVER6 = 1 };
 enum { NVFP4_RULE_MSE = 0, NVFP4_RULE_MAE = 1 }; /* ignored for NVFP4_MODE_STD */
 enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
-enum { NVFP4_FLAG_GSCALE_GIVEN = 1u }; /* use *gscale_inout as g; skip the amax pass */
+enum {
+  NVFP4_FLAG_GSCALE_GIVEN = 1u,   /* use *gscale_inout as g; skip the amax pass          */
+  NVFP4_FLAG_ERR_ACCUMULATE = 2u  /* add the error sum to *err_sum_out, do not zero it  */
+};
 
 /* Tensor amax A = max |x| over `numel` bf16 values, written as fp32 to
  * *amax_out (device).  numel >= 1.  The global scale of the pages is formed
@@ -107,10 +111,13 @@ nvfp4_status nvfp4_quantize(const uint16_t* in_bf16, int64_t rows, int64_t cols,
  *     and in [0, 2^117].  Without the flag g is computed and written there.
  *   selmap_out (nullable): the selection bitmap, ceil(rows*cols/128) bytes;
  *     bits past the last block are written as 0.  All zero in standard mode.
- *   err_sum_out (nullable): one double, zeroed by the call and then set to
- *     the sum over blocks of the kept candidate's block error -- squared
- *     error under NVFP4_RULE_MSE and in standard mode, absolute error under
- *     NVFP4_RULE_MAE.  Accumulated in binary64 in an unspecified order.
+ *   err_sum_out (nullable): one double that receives the sum over blocks of
+ *     the kept candidate's block error -- squared error under
+ *     NVFP4_RULE_MSE and in standard mode, absolute error under
+ *     NVFP4_RULE_MAE -- accumulated in binary64 in an unspecified order.
+ *     The call zeroes it first unless flags has NVFP4_FLAG_ERR_ACCUMULATE,
+ *     in which case the sum is added to its current value (e.g. a total over
+ *     several tensors, or a value the caller zeroed on the same stream).
  *     Divide by rows*cols for the per-tensor MSE / MAE. */
 nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t cols,
                                int block_axis, int mode, int rule, uint32_t flags,
@@ -118,7 +125,8 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t co
                                uint8_t* selmap_out, double* err_sum_out, void* stream);
 
 /* Dequantize: x_hat = dec(code) * (dec(S) * g), each product one binary32
- * rounding; the same x_hat the quantizer measured its error against.
+ * rounding (x_hat is the rounding of the reconstruction dec(code) * d whose
+ * error the quantizer measured).
  * out_dtype NVFP4_OUT_F32 writes float, NVFP4_OUT_BF16 writes the bf16
  * (round to nearest even) of it.  `out` is [rows][cols] in the caller's
  * layout for either block axis; packed/scales are laid out as produced by

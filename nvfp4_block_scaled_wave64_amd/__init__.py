@@ -24,6 +24,7 @@ MODE_STD, MODE_4OVER6 = 0, 1
 RULE_MSE, RULE_MAE = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 FLAG_GSCALE_GIVEN = 1
+FLAG_ERR_ACCUMULATE = 2
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_ENUM", 3: "NVFP4_ERR_SHAPE",
           4: "NVFP4_ERR_ALIGN", 5: "NVFP4_ERR_HIP"}
@@ -125,13 +126,14 @@ def global_scale(amax_t, mode, out=None, stream=None):
 
 
 def quantize(x, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE, gscale=None,
-             selmap=False, err_sum=False, out=None, stream=None):
+             selmap=False, err_sum=False, err_accumulate=False, out=None, stream=None):
     """Quantize a [rows][cols] bf16 device tensor.
 
     gscale: optional 1-element float32 device tensor holding a given g (the
     amax pass is skipped).  Returns a dict with packed, scales, gscale and,
     when asked for, selmap (uint8 bitmap) and err_sum (float64, 1 element).
-    `out` may supply preallocated tensors under the same keys.
+    err_accumulate adds the error sum to out["err_sum"] instead of zeroing it
+    first.  `out` may supply preallocated tensors under the same keys.
     """
     x = _bf16_input(x)
     if x.dim() != 2:
@@ -159,7 +161,11 @@ def quantize(x, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE, gscale=No
         sel = torch.empty(max(nsel, 1), dtype=torch.uint8, device=dev)
     err = out.get("err_sum") if err_sum else None
     if err_sum and err is None:
+        if err_accumulate:
+            raise ValueError("err_accumulate needs out['err_sum']")
         err = torch.empty(1, dtype=torch.float64, device=dev)
+    if err_sum and err_accumulate:
+        flags |= FLAG_ERR_ACCUMULATE
     st = lib().nvfp4_quantize_ex(_ptr(x), rows, cols, int(block_axis), int(mode), int(rule),
                                  flags, _ptr(packed), _ptr(scales), _ptr(g), _ptr(sel), _ptr(err),
                                  _stream(stream))

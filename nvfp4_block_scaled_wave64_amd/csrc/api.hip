@@ -2,7 +2,7 @@
 // launches on the caller's stream.  No allocation, no host synchronization.
 #include <atomic>
 
-#include "../../include/nvfp4.h"
+#include "nvfp4.h"
 #include "nvfp4_kernels.h"
 
 namespace nvfp4 {
@@ -85,7 +85,8 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t co
   if (block_axis != NVFP4_AXIS_ROWS && block_axis != NVFP4_AXIS_COLS) return NVFP4_ERR_ENUM;
   if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
   if (rule != NVFP4_RULE_MSE && rule != NVFP4_RULE_MAE) return NVFP4_ERR_ENUM;
-  if (flags & ~uint32_t(NVFP4_FLAG_GSCALE_GIVEN)) return NVFP4_ERR_ENUM;
+  if (flags & ~uint32_t(NVFP4_FLAG_GSCALE_GIVEN | NVFP4_FLAG_ERR_ACCUMULATE))
+    return NVFP4_ERR_ENUM;
   const nvfp4_status shape = check_shape(rows, cols, block_axis);
   if (shape != NVFP4_OK) return shape;
   if (!aligned(in_bf16, 16) || !aligned(packed_out, 4) || !aligned(gscale_inout, 4) ||
@@ -94,6 +95,7 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t co
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool given = (flags & NVFP4_FLAG_GSCALE_GIVEN) != 0;
+  double* err_zero = (flags & NVFP4_FLAG_ERR_ACCUMULATE) ? nullptr : err_sum_out;
   uint32_t variant = 0;
   if (mode == NVFP4_MODE_4OVER6) {
     variant |= nvfp4::kVarFourOverSix;
@@ -104,8 +106,8 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t co
 
   hipError_t e = hipSuccess;
   uint32_t* acc = reinterpret_cast<uint32_t*>(gscale_inout);
-  if (!given || err_sum_out)
-    e = nvfp4::launch_init(given ? nullptr : acc, err_sum_out, nullptr, 0, s);
+  // One small kernel zeroes the amax accumulator and the error sum.
+  if (!given || err_zero) e = nvfp4::launch_init(given ? nullptr : acc, err_zero, nullptr, 0, s);
   if (e == hipSuccess && !given) {
     e = nvfp4::launch_amax(in_bf16, rows * cols, acc, s);
     if (e == hipSuccess) {

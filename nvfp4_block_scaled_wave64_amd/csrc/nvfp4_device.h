@@ -19,6 +19,7 @@ namespace nvfp4 {
 constexpr float kFltMax = 3.40282346638528859812e+38f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Cache policy of streaming loads: non-temporal (the input is read once).
 constexpr int kStreamLoad = 2;
@@ -147,14 +148,33 @@ __device__ __forceinline__ TensorScales tensor_scales(float g) {
   return t;
 }
 
+// Value of an E4M3 byte, for constant evaluation (exact scalings by 2).
+constexpr float e4m3_value_c(uint32_t S) {
+  const uint32_t e = (S >> 3) & 15u, m = S & 7u;
+  float v = (e == 0u) ? (float)m : (float)(8u + m);
+  int sh = (e == 0u) ? -9 : (int)e - 10;
+  for (; sh > 0; --sh) v *= 2.0f;
+  for (; sh < 0; ++sh) v *= 0.5f;
+  return v;
+}
+struct RecipTable {
+  float v[128];
+};
+// T[S] = RN(1/dec(S)) for every finite scale byte, evaluated by the compiler
+// (IEEE division, round to nearest even); T[0] = 0.
+constexpr RecipTable make_recip_table() {
+  RecipTable t{};
+  for (uint32_t S = 1; S < 127; ++S) t.v[S] = 1.0f / e4m3_value_c(S);
+  return t;
+}
+__device__ constexpr RecipTable kRecip = make_recip_table();
+
 // Decode multiplier d = dec(S) * g and encode multiplier
-// r = min(G * (1/dec(S)), FLT_MAX) (r = 0 for S = 0) of block scale S.
+// r = min(G * T[S], FLT_MAX) (r = 0 for S = 0) of block scale S.
 __device__ __forceinline__ float2 scale_pair(uint32_t S, const TensorScales& t) {
-  const float dec = e4m3_decode(S);
-  const float inv = (S == 0u) ? 0.0f : 1.0f / dec;
   float2 dr;
-  dr.x = dec * t.g;
-  dr.y = fminf(t.G * inv, kFltMax);
+  dr.x = e4m3_decode(S) * t.g;
+  dr.y = fminf(t.G * kRecip.v[S], kFltMax);
   return dr;
 }
 
@@ -208,7 +228,7 @@ __device__ __forceinline__ HalfBlock quantize_half_block(const uint32_t wd[4], f
     e2m1_decode8(c6, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float dl = v[i] * t6.x - x[i];
+      const float dl = __builtin_fmaf(v[i], t6.x, -x[i]);
       h6 = kMae ? h6 + fabsf(dl) : __builtin_fmaf(dl, dl, h6);
     }
   }
@@ -221,7 +241,7 @@ __device__ __forceinline__ HalfBlock quantize_half_block(const uint32_t wd[4], f
     e2m1_decode8(c4, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float dl = v[i] * t4.x - x[i];
+      const float dl = __builtin_fmaf(v[i], t4.x, -x[i]);
       h4 = kMae ? h4 + fabsf(dl) : __builtin_fmaf(dl, dl, h4);
     }
   }
@@ -239,6 +259,86 @@ __device__ __forceinline__ HalfBlock quantize_half_block(const uint32_t wd[4], f
   r.err = r.pick4 ? e4 : e6;
   r.S = r.pick4 ? S4 : S6;
   r.word = r.pick4 ? c4 : c6;
+  return r;
+}
+
+// Result of one whole block of 16 elements held by one lane.
+struct Block16 {
+  uint32_t lo, hi;  // codes of elements 0-7 and 8-15 (element i in bits 4i..)
+  uint32_t S;       // kept E4M3 scale byte
+  bool pick4;       // the max->4 candidate was kept
+  float err;        // kept candidate's block error
+};
+
+// Error of one candidate over 8 elements (x) given its codes (w) and decode
+// multiplier d: sequential sum of squared (or absolute) differences between
+// the candidate's reconstruction v * d and x, each difference evaluated
+// exactly and rounded once (fused multiply-add).
+template <bool kMae>
+__device__ __forceinline__ float half_error(const float* x, uint32_t w, float d) {
+  float v[8];
+  e2m1_decode8(w, v);
+  float h = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float dl = __builtin_fmaf(v[i], d, -x[i]);
+    h = kMae ? h + fabsf(dl) : __builtin_fmaf(dl, dl, h);
+  }
+  return h;
+}
+
+// One block of 16 elements in one lane: wd[0..7] are its bf16 values
+// (element 2j in the low half of wd[j]).  The same block steps as
+// quantize_half_block, with the two halves' errors summed in the same order
+// (elements 0-7 and 8-15 sequentially, then added).
+template <bool k46, bool kMae, bool kNeedErr>
+__device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float k6, float k4,
+                                                    const float2* tab) {
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[2 * j] = bf16_lo(wd[j]);
+    x[2 * j + 1] = bf16_hi(wd[j]);
+  }
+  const float b = __builtin_elementwise_maximum(
+      absmax3(absmax3(x[0], x[1], x[2]), absmax3(x[3], x[4], x[5]), absmax3(x[6], x[7], x[8])),
+      absmax3(absmax3(x[9], x[10], x[11]), absmax3(x[12], x[13], x[14]), x[15]));
+
+  const uint32_t S2 = e4m3_encode2(b * k6, k46 ? b * k4 : 0.0f);
+  const uint32_t S6 = S2 & 0xFFu, S4 = (S2 >> 8) & 0xFFu;
+  const float2 t6 = tab[S6];  // (d, r)
+
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = x[i] * t6.y;
+  const uint32_t c6lo = e2m1_encode8(y);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t6.y;
+  const uint32_t c6hi = e2m1_encode8(y);
+  float e6 = 0.0f;
+  if (kNeedErr) e6 = half_error<kMae>(x, c6lo, t6.x) + half_error<kMae>(x + 8, c6hi, t6.x);
+
+  Block16 r;
+  r.lo = c6lo;
+  r.hi = c6hi;
+  r.S = S6;
+  r.pick4 = false;
+  r.err = e6;
+  if (k46) {
+    const float2 t4 = tab[S4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[i] * t4.y;
+    const uint32_t c4lo = e2m1_encode8(y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t4.y;
+    const uint32_t c4hi = e2m1_encode8(y);
+    const float e4 = half_error<kMae>(x, c4lo, t4.x) + half_error<kMae>(x + 8, c4hi, t4.x);
+    r.pick4 = e4 < e6;  // ties and NaN keep max->6
+    r.lo = r.pick4 ? c4lo : c6lo;
+    r.hi = r.pick4 ? c4hi : c6hi;
+    r.S = r.pick4 ? S4 : S6;
+    r.err = r.pick4 ? e4 : e6;
+  }
   return r;
 }
 

@@ -12,34 +12,58 @@
 //
 // Work layout (wave64).  The tensor is a flat sequence of 16-element blocks
 // and the packed codes, scale bytes and bitmap follow the same order.  A wave
-// step covers a chunk of 32 blocks = 512 elements = 1 KiB of input: lane l
-// (l < 32) holds the first 8 elements of block l and lane l + 32 the last 8,
-// so one 16-byte load per lane reads the whole KiB, and the 32 selection
-// bits of the chunk are the low half of one wave ballot.  The two lanes of a
-// block exchange their partial maximum and partial errors with one
-// v_permlane32_swap each.  Each lane converts both candidate scales with one
-// packed E4M3 conversion, reads their decode / encode multipliers from a
-// per-workgroup LDS table of all 128 scale bytes, and evaluates both
-// candidates on its 8 elements with packed E2M1 conversions (encode and
-// decode), keeping every intermediate in registers.
+// step covers a chunk of 64 blocks = 1024 elements = 2 KiB of input, read as
+// two fully coalesced 1 KiB loads in which lane l (l < 32) holds the first
+// half of block l of that KiB and lane l + 32 its second half.  Four
+// v_permlane32_swap moves (one per dword) then leave every lane with one
+// whole block: lane l owns block l of the chunk.  Per-block work (max, the
+// two E4M3 scales, the selection) is thus done once per 16 elements, the 64
+// selection bits of a chunk are one wave ballot, and each lane stores its 16
+// codes as one 8-byte write (512 contiguous bytes per wave) and its scale
+// byte (64 contiguous bytes).  Both candidates are evaluated in registers
+// with packed E2M1 conversions (encode and decode); decode / encode
+// multipliers of all 128 scale bytes come from a per-workgroup LDS table.
 //
 // Memory: all global accesses are raw buffer operations with hardware range
 // checks (loads past the end read 0, stores past the end are dropped), so the
-// ragged last chunk needs no branches, and the per-lane offsets are fixed.
-// Each wave keeps the loads of its next chunks in flight while it works on
-// the current ones.  One launch covers at most 2^30 elements (buffer offsets
-// are 32-bit); the host splits larger tensors at chunk boundaries.
+// ragged last chunk needs no branches.  Loads and the code stores are
+// non-temporal (nothing is re-read); the small scale and bitmap stores go
+// through the L2 so that partial lines merge before they reach HBM.  Each wave keeps the loads of its next chunk in
+// flight while it works on the current one.  One launch covers at most 2^30
+// elements (buffer offsets are 32-bit); the host splits larger tensors at
+// chunk boundaries.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
 namespace nvfp4 {
 
-// Chunks in flight per wave: the next round's loads are issued before the
-// current round is processed.
-constexpr int kDepth = 2;
+// Chunks whose loads are in flight ahead of the one being processed, and
+// workgroups per compute unit.
+#ifndef NVFP4_ROWS_DEPTH
+#define NVFP4_ROWS_DEPTH 1
+#endif
+#ifndef NVFP4_ROWS_WAVES_PER_CU
+#define NVFP4_ROWS_WAVES_PER_CU 16
+#endif
+#ifndef NVFP4_ROWS_THREADS
+#define NVFP4_ROWS_THREADS 1024
+#endif
+constexpr int kDepth = NVFP4_ROWS_DEPTH;
+// One workgroup of 16 waves per compute unit: the 16 consecutive chunks a
+// workgroup handles in one round write whole 128-byte lines of the bitmap
+// (16 x 8 bytes) and of the scales from one XCD, and the error sum takes one
+// atomic per compute unit.
+constexpr int kRowsThreads = NVFP4_ROWS_THREADS;
+constexpr int kRowsWaves = kRowsThreads / 64;
+constexpr int kGroupsPerCu = NVFP4_ROWS_WAVES_PER_CU / kRowsWaves;
+// Non-temporal stores for the codes (512 contiguous bytes per wave step);
+// the scale bytes and bitmap bytes of neighbouring chunks fill their cache
+// lines piecewise, so they are written through the L2, which merges them.
+constexpr int kStreamStore = 2;
+constexpr int kMergedStore = 0;
 
 template <uint32_t V>
-__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
+__global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
     const uint16_t* __restrict__ in, int64_t nblocks, const float* __restrict__ gscale,
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
     double* __restrict__ err_sum) {
@@ -50,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
   constexpr bool kNeedErr = k46 || kErr;
 
   __shared__ float2 tab[128];
-  __shared__ double wsum[kWavesPerGroup];
+  __shared__ double wsum[kRowsWaves];
 
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
@@ -63,57 +87,85 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
   const __amdgpu_buffer_rsrc_t r_sel = make_rsrc(selmap, (nb + 7u) / 8u);
 
   const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t blk_in_chunk = lane & 31u, half = lane >> 5;
-  const uint32_t off_in = blk_in_chunk * 32u + half * 16u;    // bytes within a 1 KiB chunk
-  const uint32_t off_packed = blk_in_chunk * 8u + half * 4u;  // within 256 B
-  const uint32_t off_scale = half ? 0x80000000u : blk_in_chunk;  // upper lanes: out of range
-  const uint32_t off_sel = lane < 4u ? lane : 0x80000000u;
-  const uint32_t nchunks = (nb + 31u) / 32u;
-  const uint32_t nwaves = gridDim.x * kWavesPerGroup;
-  const uint32_t first = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const uint32_t off_in = (lane & 31u) * 32u + (lane >> 5) * 16u;  // within a 1 KiB half
+  const uint32_t off_sel = lane < 8u ? lane : 0x80000000u;
+  const uint32_t nchunks = (nb + 63u) / 64u;
+  const uint32_t nwaves = gridDim.x * kRowsWaves;
+  const uint32_t first = blockIdx.x * kRowsWaves + (threadIdx.x >> 6);
   double acc = 0.0;
 
-  // Chunks past the end read as zeros (range-checked buffer load); ch stays
-  // below nchunks + kDepth * nwaves, so ch * 1024 cannot wrap.
-  auto load = [&](uint32_t ch) -> u32x4 {
-    return __builtin_amdgcn_raw_buffer_load_b128(r_in, ch * 1024u + off_in, 0, kStreamLoad);
+  // Chunks past the end read as zeros (range-checked buffer loads); ch stays
+  // below nchunks + (kDepth + 1) * nwaves, so ch * 2048 cannot wrap.
+  struct Two {
+    u32x4 a, b;
+  };
+  auto load = [&](uint32_t ch) -> Two {
+    Two t;
+    t.a = __builtin_amdgcn_raw_buffer_load_b128(r_in, ch * 2048u + off_in, 0, kStreamLoad);
+    t.b = __builtin_amdgcn_raw_buffer_load_b128(r_in, ch * 2048u + 1024u + off_in, 0, kStreamLoad);
+    return t;
   };
 
-  u32x4 buf[kDepth];
+  auto process = [&](uint32_t ch, const Two& w) {
+    // Lane l < 32 keeps its half of block l and takes the other half from
+    // lane l + 32; lane l >= 32 takes block l (second KiB) the same way.
+    uint32_t wd[8];
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k) buf[k] = load(first + k * nwaves);
+    for (int j = 0; j < 4; ++j) {
+      const auto p = __builtin_amdgcn_permlane32_swap(w.a[j], w.b[j], false, false);
+      wd[j] = p[0];
+      wd[4 + j] = p[1];
+    }
+    const Block16 q = quantize_block16<k46, kMae, kNeedErr>(wd, ts.k6, ts.k4, tab);
+    u32x2 codes;
+    codes.x = q.lo;
+    codes.y = q.hi;
+    __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, ch * 512u + lane * 8u, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q.S, r_scales, ch * 64u + lane, 0, kMergedStore);
+    if (kSel) {
+      // Lane l decides block l: the ballot is the chunk's 64 selection bits;
+      // lanes 0-7 store its 8 bytes.
+      const uint64_t bits = __ballot(q.pick4);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(bits >> (8u * (lane & 7u))), r_sel,
+                                           ch * 8u + off_sel, 0, kMergedStore);
+    }
+    if (kErr) acc += (double)q.err;  // blocks past the end contribute 0
+  };
 
-  for (uint32_t base = first; base < nchunks; base += kDepth * nwaves) {
+  // The next chunk's loads are issued at raised wave priority so that they
+  // leave as soon as the wave is scheduled, ahead of other waves' arithmetic.
+  auto prefetch = [&](uint32_t ch) -> Two {
+    __builtin_amdgcn_s_setprio(3);
+    const Two t = load(ch);
+    __builtin_amdgcn_s_setprio(0);
+    return t;
+  };
+
+  if constexpr (kDepth == 0) {
+    for (uint32_t ch = first; ch < nchunks; ch += nwaves) process(ch, load(ch));
+  } else {
+    Two buf[kDepth > 0 ? kDepth : 1];
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) {
-      const uint32_t ch = base + k * nwaves;
-      const u32x4 w = buf[k];
-      buf[k] = load(ch + kDepth * nwaves);
-      if (ch >= nchunks) break;  // wave-uniform
-      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-      const HalfBlock hb = quantize_half_block<k46, kMae, kNeedErr>(wd, ts.k6, ts.k4, tab);
-      __builtin_amdgcn_raw_buffer_store_b32(hb.word, r_packed, ch * 256u + off_packed, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)hb.S, r_scales, ch * 32u + off_scale, 0, 0);
-      if (kSel) {
-        // Lane l < 32 decides block l: the low half of the ballot is the
-        // chunk's 32 selection bits; lanes 0-3 store its 4 bytes.
-        const uint32_t bits = (uint32_t)__ballot(hb.pick4);
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(bits >> (8u * (lane & 3u))), r_sel,
-                                             ch * 4u + off_sel, 0, 0);
+    for (int k = 0; k < kDepth; ++k) buf[k] = load(first + k * nwaves);
+    for (uint32_t base = first; base < nchunks; base += kDepth * nwaves) {
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) {
+        const uint32_t ch = base + k * nwaves;
+        const Two w = buf[k];
+        buf[k] = prefetch(ch + kDepth * nwaves);
+        if (ch >= nchunks) break;  // wave-uniform
+        process(ch, w);
       }
-      // Both lanes of a pair hold the block error (blocks past the end
-      // contribute 0); the wave total is halved at the end.
-      if (kErr) acc += (double)hb.err;
     }
   }
 
   if (kErr) {
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) wsum[threadIdx.x >> 6] = 0.5 * acc;
+    if (lane == 0) wsum[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
       double t = wsum[0];
-      for (int k = 1; k < kWavesPerGroup; ++k) t += wsum[k];
+      for (int k = 1; k < kRowsWaves; ++k) t += wsum[k];
       unsafeAtomicAdd(err_sum, t);
     }
   }
@@ -124,16 +176,17 @@ static hipError_t launch_rows_v(const uint16_t* in, int64_t nblocks, const float
                                 uint8_t* packed, uint8_t* scales, uint8_t* selmap,
                                 double* err_sum, hipStream_t s) {
   // Segments of at most 2^26 blocks (2^30 elements, 2 GiB of input) keep
-  // every buffer offset within 32 bits; a multiple of 32 blocks, so each
-  // segment's bitmap starts on a byte (indeed a dword) boundary.
+  // every buffer offset within 32 bits; a multiple of 64 blocks, so each
+  // segment's bitmap starts on a byte boundary.
   constexpr int64_t kSeg = int64_t(1) << 26;
-  const int64_t cap = (int64_t)device_cu_count() * 8;  // 8 groups (32 waves) per CU
+  const int64_t cap = (int64_t)device_cu_count() * (kGroupsPerCu > 0 ? kGroupsPerCu : 1);
   for (int64_t b0 = 0; b0 < nblocks; b0 += kSeg) {
     const int64_t nb = nblocks - b0 < kSeg ? nblocks - b0 : kSeg;
-    const int64_t nchunks = (nb + 31) / 32;
-    int64_t groups = (nchunks + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t nchunks = (nb + 63) / 64;
+    int64_t groups = (nchunks + kRowsWaves - 1) / kRowsWaves;
     if (groups > cap) groups = cap;
-    quantize_rows_kernel<V><<<(unsigned)groups, kThreads, 0, s>>>(
+    if (groups < 1) groups = 1;
+    quantize_rows_kernel<V><<<(unsigned)groups, kRowsThreads, 0, s>>>(
         in + b0 * 16, nb, gscale, packed + b0 * 8, scales + b0,
         selmap ? selmap + b0 / 8 : nullptr, err_sum);
     const hipError_t e = hipGetLastError();

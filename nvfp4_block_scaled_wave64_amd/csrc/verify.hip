@@ -6,8 +6,8 @@
 // every input.  They are not part of the quantization path.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
-#include "../../include/nvfp4.h"
-#include "../../include/nvfp4_verify.h"
+#include "nvfp4.h"
+#include "nvfp4_verify.h"
 
 namespace nvfp4 {
 

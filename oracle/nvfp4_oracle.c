@@ -33,7 +33,8 @@
  *              with T[S] = RN(1/dec(S)) and T[0] = 0
  *   per element: y = RN(x * r_c);  m = E2M1 index of |y| (RNE, saturating)
  *                code = sign(x) << 3 | m;  xhat = RN(+-VAL[m] * d_c)
- *                delta = RN(xhat - x)
+ *                delta = fma(+-VAL[m], d_c, -x)   (the error of the candidate's
+ *                reconstruction against the original value, rounded once)
  *   block error: two sequential halves of 8 elements (lo, hi), e = RN(lo + hi)
  *                MSE: h = fma(delta, delta, h)      MAE: h = RN(h + |delta|)
  *   selection:   c* = 4 iff e_4 < e_6 (ties and NaN go to 6)
@@ -45,7 +46,8 @@
  * of the block pipeline (G, k_c, r_c, y, xhat, delta, the error sums) is a
  * reading of the pages, not something the pages print: it is pinned only by
  * invariants and bounds, and is "parity unpinned" at the level of the
- * individual rounding choices.
+ * individual rounding choices.  The dequantized value is RN(v * d); the error
+ * is taken against the unrounded v * d (one rounding of v * d - x).
  *
  * Build: gcc -std=c99 -O2 -ffp-contract=off -fno-fast-math (SSE binary32,
  * FLT_EVAL_METHOD == 0).  Single-threaded, no SIMD intrinsics, no tables
@@ -235,7 +237,9 @@ void nvfp4o_quantize_block(const float x[16], float g, int mode, int rule,
       const uint8_t code = (uint8_t)((neg << 3) | m);
       const float v = neg ? -E2M1_VAL[m] : E2M1_VAL[m];
       const float xhat = v * d;
-      const float delta = xhat - x[i];
+      /* Error against the original value ([FOS, "Adaptive block scaling
+       * algorithm"]): the exact difference v*d - x, rounded once. */
+      const float delta = fmaf(v, d, -x[i]);
       out->y[c][i] = y;
       out->code[c][i] = code;
       out->xhat[c][i] = xhat;

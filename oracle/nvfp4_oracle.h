@@ -36,8 +36,8 @@ typedef struct {
   float r[2];        /* encode multiplier min(RN(G * T[S]), FLT_MAX) */
   float y[2][16];    /* scaled values RN(x * r) */
   uint8_t code[2][16];
-  float xhat[2][16]; /* reconstructed values */
-  float delta[2][16];
+  float xhat[2][16]; /* reconstructed values RN(v * d) */
+  float delta[2][16]; /* fma(v, d, -x) */
   float err[2];      /* block error (SSE, or SAE under the MAE rule) */
   int chosen;        /* 0 -> max mapped to 6, 1 -> max mapped to 4 */
 } nvfp4o_block_t;

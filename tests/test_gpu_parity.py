@@ -177,6 +177,22 @@ def test_deterministic_rerun():
     assert a["err_sum"] == pytest.approx(b["err_sum"], rel=1e-12)
 
 
+def test_error_sum_accumulates_on_request():
+    banner("err accumulate")
+    x = testkit.make(2, rows=128)
+    xd = to_device(x)
+    ref = oracle.quantize(x, AXIS_COLS, F46, MSE)
+    err = torch.full((1,), 5.0, dtype=torch.float64, device="cuda")
+    r = nv.quantize(xd, AXIS_COLS, F46, MSE, err_sum=True, err_accumulate=True,
+                    out={"err_sum": err})
+    r = nv.quantize(xd, AXIS_COLS, F46, MSE, gscale=r["gscale"], err_sum=True,
+                    err_accumulate=True, out={"err_sum": err})
+    assert err.item() == pytest.approx(5.0 + 2 * ref["err_sum"], rel=1e-6)
+    r = nv.quantize(xd, AXIS_COLS, F46, MSE, gscale=r["gscale"], err_sum=True,
+                    out={"err_sum": err})  # without the flag the sum starts from zero
+    assert err.item() == pytest.approx(ref["err_sum"], rel=1e-6)
+
+
 def test_non_default_stream():
     banner("side stream")
     x = testkit.make(2, rows=256)

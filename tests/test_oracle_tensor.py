@@ -129,8 +129,9 @@ def test_tie_goes_to_scale6():
     x = np.zeros(16, np.float32)  # both candidates have zero error
     q = oracle.quantize_block(x, 1.0, MODE_4OVER6, RULE_MSE)
     assert q.err[0] == q.err[1] == 0 and q.chosen == 0
-    x[0] = 1.0  # exact on both candidates (g = 1/6 maps 1 to 6, and to 4)
-    q = oracle.quantize_block(x, 1.0 / 6, MODE_4OVER6, RULE_MSE)
+    x[0] = 6.0  # exact on both candidates: scales 1.0 and 1.5 (g = 1), codes 6 and 4
+    q = oracle.quantize_block(x, 1.0, MODE_4OVER6, RULE_MSE)
+    assert list(q.S) == [0x38, 0x3C]
     assert q.err[0] == q.err[1] == 0 and q.chosen == 0
 
 
