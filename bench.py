@@ -1,20 +1,23 @@
 """Benchmark: NVFP4 Four-Over-Six quantization of a 32768 x 5120 bf16 prefill
 activation tensor on one MI355X.
 
-One step is one pass of the whole quantization path over the resident input:
-zero the error accumulator -> tensor amax -> global scale (6*256 under 4/6)
--> 4/6 quantize with the MSE rule, writing packed E2M1 codes, E4M3 scale
-bytes, the per-block selection bitmap and the per-tensor error sum.  HIP
-events on the same stream bracket the quantize kernel (one launch) in every
-step; its mean duration gives the roofline figure.  Throughput is counted with the
-algorithmic byte formula of the metric, 2.5625 B per element (2 B of bf16
-read, 0.5 B of codes and 0.0625 B of scales written).
+One step is one call of the whole quantization path on the resident input:
+nvfp4_quantize_ex computes the tensor amax and the global scale (6*256 under
+4/6) and then runs the 4/6 quantizer with the MSE rule, writing packed E2M1
+codes, E4M3 scale bytes, the per-block selection bitmap and the per-tensor
+error sum.  `value` is the step throughput.  Every step also binds a pair of
+HIP events to the quantize kernel itself (nvfp4_quantize_ex_timed, on the
+stream the kernel runs on); their mean is the kernel duration behind the
+roofline figure.  Bytes are counted with the metric's algorithmic formula,
+2.5625 B per element (2 B of bf16 read, 0.5 B of codes and 0.0625 B of scales
+written).
 
 Before any number is reported the outputs are compared with the CPU oracle
 (bit-exact codes, scales, g and bitmap; error sum to 1e-6).  The oracle is
 timed on the host in the same run (`cpu_baseline`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--no-extra]
 """
 import argparse
 import hashlib
@@ -30,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_quantize_rows_4over6_32768x5120.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_quantize_rows_4over6_mse_32768x5120.txt")
 KERNEL_SOURCES = ["quantize_rows.hip", "nvfp4_device.h", "nvfp4_kernels.h"]
 
 
@@ -47,16 +50,111 @@ def kernel_source_hash():
 
 
 def measured_traffic(numel):
-    """HBM bytes per launch of the quantize kernel from the committed PMC
-    summary, or None when the kernel source changed since it was taken."""
+    """HBM bytes per launch of the quantize kernel from the committed counter
+    summary ("key: value" lines), or None when the kernel sources changed
+    since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash() or t.get("numel") != numel:
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    if kv.get("numel") != str(numel) or "bytes_per_launch" not in kv:
+        return None
+    return int(kv["bytes_per_launch"])
+
+
+def kernel_times(fn, torch, reps, between=None):
+    """Per-launch kernel times (s) from events bound to the kernel itself."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for _ in range(3):
+        fn(None)
+    for e in evs:
+        if between is not None:
+            between()
+        fn(e)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e-3 for a, b in evs])
+
+
+def call_time(fn, torch, stream, reps=50):
+    """Mean time (s) of back-to-back calls between one pair of stream events."""
+    for _ in range(5):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / reps
+
+
+def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
+    """Side measurements on the same input: other modes, the amax call, the
+    same-pattern streaming ceiling, a cold-cache repeat, dequantize and the
+    quantize kernel on the other workloads (kernel-bound events throughout,
+    except where a whole call is timed)."""
+    numel = rows * cols
+    dev = xd.device
+    gb = lambda t, bpe=BYTES_PER_ELEM, n=numel: round(n * bpe / t / 1e9, 1)  # noqa: E731
+    res = {}
+    packed, scales = out["packed"], out["scales"]
+    po = {"packed": packed, "scales": scales}
+
+    def q(mode, rule=nv.RULE_MSE, **kw):
+        return lambda e: nv.quantize(xd, nv.AXIS_COLS, mode, rule, gscale=g, out=po, events=e,
+                                     **kw)
+
+    t_std = np.median(kernel_times(q(nv.MODE_STD), torch, 50))
+    t_46 = np.median(kernel_times(q(nv.MODE_4OVER6), torch, 50))
+    t_mae = np.median(kernel_times(q(nv.MODE_4OVER6, nv.RULE_MAE), torch, 50))
+    res["std_quantize_gbps"] = gb(t_std)
+    res["4over6_mse_quantize_gbps_no_bitmap_no_err"] = gb(t_46)
+    res["4over6_mae_quantize_gbps_no_bitmap_no_err"] = gb(t_mae)
+    res["4over6_overhead_vs_std_pct"] = round((t_46 / t_std - 1) * 100, 1)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    res["amax_call_gbps"] = gb(call_time(lambda: nv.amax(xd, out=amax), torch, stream), 2.0)
+    res["e2e_call_gbps"] = gb(call_time(
+        lambda: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, selmap=True,
+                            err_sum=True, out=dict(out)), torch, stream))
+    # Same bytes, no arithmetic: the attainable ceiling for this pattern.
+    res["stream_pattern_gbps"] = gb(call_time(
+        lambda: nv.stream_pattern(xd, packed, scales), torch, stream))
+    # Cold repeat: 512 MiB written between launches evicts the 256 MB MALL.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    full = lambda e: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, gscale=g,  # noqa
+                                 selmap=True, err_sum=True, out=dict(out), events=e)
+    t_cold = kernel_times(full, torch, 30, between=lambda: flush.fill_(0))
+    res["quantize_kernel_cold_us_median"] = round(float(np.median(t_cold)) * 1e6, 2)
+    del flush
+    deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    t_deq = call_time(lambda: nv.dequantize(packed, scales, g, rows, cols, nv.AXIS_COLS,
+                                            torch.bfloat16, out=deq), torch, stream)
+    res["dequantize_bf16_gbps"] = gb(t_deq, 0.5 + 1 / 16 + 2)
+    del deq
+    # The quantize kernel on the other workloads' shapes and modes.
+    for cid in (2, 3, 5):
+        cfg = testkit.CONFIGS[cid]
+        xc = torch.from_numpy(testkit.make(cid).view(np.int16)).to(dev).view(torch.bfloat16)
+        oc = nv.quantize(xc, cfg.block_axis, cfg.mode, cfg.rule)
+        gc = oc["gscale"]
+        t = kernel_times(lambda e: nv.quantize(xc, cfg.block_axis, cfg.mode, cfg.rule, gscale=gc,
+                                               out=oc, events=e), torch, 30)
+        tm = float(np.median(t))
+        res[f"workload{cid}_{cfg.rows}x{cfg.cols}_kernel_us_median"] = round(tm * 1e6, 2)
+        res[f"workload{cid}_gbps"] = gb(tm, n=cfg.rows * cfg.cols)
+        del xc, oc
+    # Plain device copy of known size (the torch copy kernel).
+    csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    res["copy_256MiB_gbps"] = round(2 * csrc.numel() / call_time(lambda: cdst.copy_(csrc), torch,
+                                                                 stream, 20) / 1e9, 1)
+    return res
 
 
 def main():
@@ -66,6 +164,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the full-tensor oracle run; gate on sampled rows instead")
+    ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path's "
@@ -92,21 +191,13 @@ def main():
     scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
     selmap = torch.empty(nsel, dtype=torch.uint8, device=dev)
     err = torch.empty(1, dtype=torch.float64, device=dev)
-    amax = torch.empty(1, dtype=torch.float32, device=dev)
     g = torch.empty(1, dtype=torch.float32, device=dev)
-    out = {"packed": packed, "scales": scales, "selmap": selmap, "err_sum": err}
+    out = {"packed": packed, "scales": scales, "selmap": selmap, "err_sum": err, "gscale": g}
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        err.zero_()
-        nv.amax(xd, out=amax)
-        nv.global_scale(amax, nv.MODE_4OVER6, out=g)
-        if ev is not None:
-            ev[0].record(stream)
-        nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, gscale=g, selmap=True,
-                    err_sum=True, err_accumulate=True, out=out)
-        if ev is not None:
-            ev[1].record(stream)
+        nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, selmap=True, err_sum=True,
+                    out=out, events=ev)
 
     # ---- parity gate (and the CPU baseline) ----
     log("parity gate")
@@ -157,6 +248,9 @@ def main():
         step()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    for a, b in evs:  # create the events before the clock starts
+        a.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -170,50 +264,15 @@ def main():
     k_avg_s = float(kern_ms.mean()) * 1e-3
     achieved = numel * BYTES_PER_ELEM / k_avg_s / 1e9
 
-    # ---- secondary lines (same input, same process) ----
     extra = {"input_fnv1a64": f"{checksum:016x}",
-             "quantize_call_us_avg": round(k_avg_s * 1e6, 2),
-             "quantize_call_us_min": round(float(kern_ms.min()) * 1e3, 2),
-             "quantize_call_gbps": round(achieved, 1),
-             "elements_per_s_step": round(numel / (ms_per_step * 1e-3), 1)}
-
-    def time_call(fn, reps=50):
-        for _ in range(5):
-            fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e-3 / reps
-
-    t_amax = time_call(lambda: nv.amax(xd, out=amax))
-    extra["amax_gbps"] = round(numel * 2 / t_amax / 1e9, 1)
-    t_std = time_call(lambda: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_STD, nv.RULE_MSE, gscale=g,
-                                          out={"packed": packed, "scales": scales}))
-    t_46 = time_call(lambda: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE,
-                                         gscale=g, out={"packed": packed, "scales": scales}))
-    extra["std_quantize_gbps"] = round(numel * BYTES_PER_ELEM / t_std / 1e9, 1)
-    extra["4over6_quantize_gbps_no_bitmap_no_err"] = round(numel * BYTES_PER_ELEM / t_46 / 1e9, 1)
-    extra["4over6_overhead_vs_std_pct"] = round((t_46 / t_std - 1) * 100, 1)
-    t_e2e = time_call(lambda: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE,
-                                          selmap=True, err_sum=True,
-                                          out={"packed": packed, "scales": scales,
-                                               "selmap": selmap, "err_sum": err, "gscale": g}))
-    extra["e2e_quantize_ex_gbps"] = round(numel * BYTES_PER_ELEM / t_e2e / 1e9, 1)
-    # Plain device copy of known size: the calibration kernel for the HBM
-    # byte counters, and the read+write streaming ceiling of this device.
-    csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
-    cdst = torch.empty_like(csrc)
-    t_copy = time_call(lambda: cdst.copy_(csrc), reps=20)
-    extra["copy_256MiB_gbps"] = round(2 * csrc.numel() / t_copy / 1e9, 1)
-    del csrc, cdst
-    deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-    t_deq = time_call(lambda: nv.dequantize(packed, scales, g, rows, cols, nv.AXIS_COLS,
-                                            torch.bfloat16, out=deq))
-    extra["dequantize_bf16_gbps"] = round(numel * (0.5 + 1 / 16 + 2) / t_deq / 1e9, 1)
+             "quantize_kernel_us_avg": round(k_avg_s * 1e6, 2),
+             "quantize_kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 2),
+             "quantize_kernel_us_min": round(float(kern_ms.min()) * 1e3, 2),
+             "quantize_kernel_us_p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 2),
+             "elements_per_s_step": round(numel / (ms_per_step * 1e-3), 1),
+             "elements_per_s_kernel": round(numel / k_avg_s, 1)}
+    if not args.no_extra:
+        extra.update(secondary(nv, torch, testkit, xd, g, out, stream, rows, cols))
 
     traffic = measured_traffic(numel)
     line = {
@@ -232,7 +291,8 @@ def main():
         "config": {
             "workload": "4/6 NVFP4 quantize (MSE rule) of a 32768x5120 bf16 prefill activation "
                         "tensor, 0.5*Student-t(3) with 8 outlier channels x100, plus selection "
-                        "bitmap and per-tensor MSE; step = amax + global scale + quantize",
+                        "bitmap and per-tensor MSE; step = one nvfp4_quantize_ex call (amax pass "
+                        "forming the global scale, then the quantize kernel)",
             "rows": rows,
             "cols": cols,
             "block_axis": "cols (16 contiguous elements)",

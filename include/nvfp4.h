@@ -124,6 +124,22 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t co
                                uint8_t* packed_out, uint8_t* scales_out, float* gscale_inout,
                                uint8_t* selmap_out, double* err_sum_out, void* stream);
 
+/* As nvfp4_quantize_ex, and in addition binds two events to the
+ * quantization kernels of the call: start_event takes the start timestamp of
+ * the first one and stop_event the end timestamp of the last one (hipEvent_t
+ * handles passed as void*, created with timing enabled; either may be NULL).
+ * hipEventElapsedTime over the pair is then the execution time of the
+ * quantization kernels alone -- the zeroing and amax kernels and the dispatch
+ * gaps around them fall outside -- i.e. the figure a kernel profiler reports.
+ * Argument checks and errors as nvfp4_quantize_ex; on an error the events
+ * are not recorded. */
+nvfp4_status nvfp4_quantize_ex_timed(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                     int block_axis, int mode, int rule, uint32_t flags,
+                                     uint8_t* packed_out, uint8_t* scales_out,
+                                     float* gscale_inout, uint8_t* selmap_out,
+                                     double* err_sum_out, void* start_event, void* stop_event,
+                                     void* stream);
+
 /* Dequantize: x_hat = dec(code) * (dec(S) * g), each product one binary32
  * rounding (x_hat is the rounding of the reconstruction dec(code) * d whose
  * error the quantizer measured).

@@ -42,6 +42,18 @@ nvfp4_status nvfp4v_e4m3_encode_sweep(uint32_t first_bits, int64_t count, uint8_
 nvfp4_status nvfp4v_decode_tables(float g, float* e2m1_out, float* e4m3_out, float* d_out,
                                   float* r_out, void* stream);
 
+/* The row-wise quantizer's memory traffic with none of its arithmetic, as
+ * the attainable-bandwidth reference for that kernel: over nblocks blocks of
+ * 16 bf16 values (in_bf16, 32 bytes each) it writes 8 bytes of packed_out
+ * and 1 byte of scales_out per block, with the same launch shape, access
+ * order and cache policies as nvfp4_quantize_ex with NVFP4_AXIS_COLS.  The
+ * bytes are a fold of the input, not NVFP4 codes: for block b with 32-bit
+ * words w0..w7, packed_out[8b..8b+7] = (w0^w1^w2^w3, w4^w5^w6^w7) as two
+ * little-endian words, and scales_out[b] = the low byte of their XOR.
+ * in_bf16 16-byte and packed_out 8-byte aligned; nblocks in [1, 2^42]. */
+nvfp4_status nvfp4v_stream_pattern(const uint16_t* in_bf16, int64_t nblocks, uint8_t* packed_out,
+                                   uint8_t* scales_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,11 +36,14 @@ SIGNATURES = {
     "nvfp4_global_scale": ([_P, _I, _P, _P], _I),
     "nvfp4_quantize": ([_P, _I64, _I64, _I, _I, _I, _P, _P, _P, _P], _I),
     "nvfp4_quantize_ex": ([_P, _I64, _I64, _I, _I, _I, _U32, _P, _P, _P, _P, _P, _P], _I),
+    "nvfp4_quantize_ex_timed": ([_P, _I64, _I64, _I, _I, _I, _U32, _P, _P, _P, _P, _P, _P, _P,
+                                 _P], _I),
     "nvfp4_dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _P], _I),
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
     "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _P, _P], _I),
     "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _P, _P], _I),
     "nvfp4v_decode_tables": ([ctypes.c_float, _P, _P, _P, _P, _P], _I),
+    "nvfp4v_stream_pattern": ([_P, _I64, _P, _P, _P], _I),
 }
 
 
@@ -125,8 +128,19 @@ def global_scale(amax_t, mode, out=None, stream=None):
     return out
 
 
+def _event_handle(ev, stream):
+    """Raw hipEvent_t of a timing torch.cuda.Event (created on first use by
+    recording it once on `stream`), or an integer handle as given."""
+    if isinstance(ev, torch.cuda.Event):
+        if not ev.cuda_event:
+            ev.record(stream)
+        return ctypes.c_void_p(ev.cuda_event)
+    return ctypes.c_void_p(int(ev)) if ev else None
+
+
 def quantize(x, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE, gscale=None,
-             selmap=False, err_sum=False, err_accumulate=False, out=None, stream=None):
+             selmap=False, err_sum=False, err_accumulate=False, out=None, stream=None,
+             events=None):
     """Quantize a [rows][cols] bf16 device tensor.
 
     gscale: optional 1-element float32 device tensor holding a given g (the
@@ -134,6 +148,10 @@ def quantize(x, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE, gscale=No
     when asked for, selmap (uint8 bitmap) and err_sum (float64, 1 element).
     err_accumulate adds the error sum to out["err_sum"] instead of zeroing it
     first.  `out` may supply preallocated tensors under the same keys.
+    events: optional (start, stop) pair of timing torch.cuda.Event objects
+    (or raw hipEvent_t handles) bound to the quantization kernels themselves
+    (nvfp4_quantize_ex_timed): start.elapsed_time(stop) is their execution
+    time without the amax pass or dispatch gaps.
     """
     x = _bf16_input(x)
     if x.dim() != 2:
@@ -166,10 +184,15 @@ def quantize(x, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE, gscale=No
         err = torch.empty(1, dtype=torch.float64, device=dev)
     if err_sum and err_accumulate:
         flags |= FLAG_ERR_ACCUMULATE
-    st = lib().nvfp4_quantize_ex(_ptr(x), rows, cols, int(block_axis), int(mode), int(rule),
-                                 flags, _ptr(packed), _ptr(scales), _ptr(g), _ptr(sel), _ptr(err),
-                                 _stream(stream))
-    _check(st, "nvfp4_quantize_ex")
+    args = (_ptr(x), rows, cols, int(block_axis), int(mode), int(rule), flags, _ptr(packed),
+            _ptr(scales), _ptr(g), _ptr(sel), _ptr(err))
+    if events is None:
+        _check(lib().nvfp4_quantize_ex(*args, _stream(stream)), "nvfp4_quantize_ex")
+    else:
+        st = stream if stream is not None else torch.cuda.current_stream()
+        ev0, ev1 = (_event_handle(e, st) for e in events)
+        _check(lib().nvfp4_quantize_ex_timed(*args, ev0, ev1, _stream(stream)),
+               "nvfp4_quantize_ex_timed")
     res = {"packed": packed, "scales": scales, "gscale": g}
     if selmap:
         res["selmap"] = sel
@@ -188,3 +211,15 @@ def dequantize(packed, scales, gscale, rows, cols, block_axis=AXIS_COLS, out_dty
                                 int(block_axis), code, _ptr(out), _stream(stream))
     _check(st, "nvfp4_dequantize")
     return out
+
+
+def stream_pattern(x, packed, scales, stream=None):
+    """The row quantizer's memory traffic without its arithmetic
+    (nvfp4v_stream_pattern): reads x, writes packed and scales with the same
+    sizes, launch shape and access order.  Measurement only; the bytes
+    written are not NVFP4 codes."""
+    x = _bf16_input(x)
+    if packed.numel() * 2 != x.numel() or scales.numel() * 16 != x.numel():
+        raise ValueError("packed / scales sizes do not match the input")
+    _check(lib().nvfp4v_stream_pattern(_ptr(x), x.numel() // 16, _ptr(packed), _ptr(scales),
+                                       _stream(stream)), "nvfp4v_stream_pattern")

@@ -33,23 +33,36 @@ __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(va, vb));
 }
 
-// amax reads with one 16-byte non-temporal buffer load per lane and step
-// (grid-stride, 32 waves per compute unit): measured on MI355X, a single
-// outstanding load per wave at this occupancy streams faster than deeper
-// unrolling, which only adds scattered DRAM pages in flight.
+// amax reads with 16-byte non-temporal buffer loads, kAmaxUnroll of them in
+// flight per lane (grid-stride), from kAmaxGroupsPerCu workgroups of 4 waves
+// per compute unit.  Measured on MI355X (32768 x 5120 bf16): 4 waves per CU
+// with 8 loads each stream at about 7.3 TB/s, 8 waves with 4 loads at 7.1,
+// while 32 waves with one load each reach about 5.4 TB/s -- fewer, deeper
+// streams keep fewer DRAM pages open at once.  Loads past the end read 0
+// (range-checked), which leaves the maximum unchanged.
+constexpr int kAmaxUnroll = 8;
+constexpr int kAmaxGroupsPerCu = 1;
+
 __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restrict__ in,
                                                         uint32_t nvec,
                                                         const uint16_t* __restrict__ tail,
-                                                        int ntail, uint32_t* __restrict__ acc) {
+                                                        int ntail, float six_m,
+                                                        uint32_t* __restrict__ acc) {
   __shared__ uint32_t part[kWavesPerGroup];
   const __amdgpu_buffer_rsrc_t r = make_rsrc(in, nvec * 16u);
   uint32_t m = 0u;
   const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, i * 16u, 0, kStreamLoad);
-    const uint32_t a = max_u16x2(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu);
-    const uint32_t b = max_u16x2(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu);
-    m = max_u16x2(m, max_u16x2(a, b));
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < nvec; i += kAmaxUnroll * stride) {
+    u32x4 w[kAmaxUnroll];
+#pragma unroll
+    for (int k = 0; k < kAmaxUnroll; ++k)
+      w[k] = __builtin_amdgcn_raw_buffer_load_b128(r, (i + k * stride) * 16u, 0, kStreamLoad);
+#pragma unroll
+    for (int k = 0; k < kAmaxUnroll; ++k) {
+      const uint32_t a = max_u16x2(w[k].x & 0x7FFF7FFFu, w[k].y & 0x7FFF7FFFu);
+      const uint32_t b = max_u16x2(w[k].z & 0x7FFF7FFFu, w[k].w & 0x7FFF7FFFu);
+      m = max_u16x2(m, max_u16x2(a, b));
+    }
   }
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max_u16x2(m, tail[threadIdx.x] & 0x7FFFu);
   uint32_t v = max(m & 0xFFFFu, m >> 16) << 16;  // fp32 bit pattern of |x|max
@@ -59,6 +72,9 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restri
   if (threadIdx.x == 0) {
     uint32_t rr = part[0];
     for (int k = 1; k < kWavesPerGroup; ++k) rr = max(rr, part[k]);
+    // Non-negative fp32 values order like their bit patterns, and so do
+    // their quotients by six_m > 0 (one rounded division, monotone in A).
+    if (six_m > 0.0f) rr = __float_as_uint(__uint_as_float(rr) / six_m);
     atomicMax(acc, rr);
   }
 }
@@ -76,13 +92,15 @@ hipError_t launch_init(uint32_t* zero_u32, double* zero_f64, uint32_t* zero_word
   return hipGetLastError();
 }
 
-hipError_t launch_amax(const uint16_t* in, int64_t numel, uint32_t* acc_bits, hipStream_t s) {
-  // Segments of at most 2^27 vectors (2 GiB) keep buffer offsets in 32 bits;
+hipError_t launch_amax(const uint16_t* in, int64_t numel, float six_m, uint32_t* acc_bits,
+                       hipStream_t s) {
+  // Segments of at most 2^27 vectors (2 GiB) keep buffer offsets in 32 bits
+  // (the furthest offset is below 2^31 + kAmaxUnroll * grid * 16 bytes);
   // every segment folds into the same accumulator.
   constexpr int64_t kSegVec = int64_t(1) << 27;
   const int64_t nvec = numel / 8;
   const int ntail = (int)(numel % 8);
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t cap = (int64_t)device_cu_count() * kAmaxGroupsPerCu;
   int64_t v0 = 0;
   do {
     const int64_t nv = nvec - v0 < kSegVec ? nvec - v0 : kSegVec;
@@ -91,7 +109,7 @@ hipError_t launch_amax(const uint16_t* in, int64_t numel, uint32_t* acc_bits, hi
     if (groups > cap) groups = cap;
     if (groups < 1) groups = 1;
     amax_kernel<<<(unsigned)groups, kThreads, 0, s>>>(in + v0 * 8, (uint32_t)nv, in + nvec * 8,
-                                                      last ? ntail : 0, acc_bits);
+                                                      last ? ntail : 0, six_m, acc_bits);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     v0 += nv;

@@ -64,7 +64,7 @@ nvfp4_status nvfp4_amax(const uint16_t* in_bf16, int64_t numel, float* amax_out,
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* acc = reinterpret_cast<uint32_t*>(amax_out);
   hipError_t e = nvfp4::launch_init(acc, nullptr, nullptr, 0, s);
-  if (e == hipSuccess) e = nvfp4::launch_amax(in_bf16, numel, acc, s);
+  if (e == hipSuccess) e = nvfp4::launch_amax(in_bf16, numel, 0.0f, acc, s);
   return hip_status(e);
 }
 
@@ -77,10 +77,14 @@ nvfp4_status nvfp4_global_scale(const float* amax, int mode, float* gscale_out, 
                                                static_cast<hipStream_t>(stream)));
 }
 
-nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t cols,
-                               int block_axis, int mode, int rule, uint32_t flags,
-                               uint8_t* packed_out, uint8_t* scales_out, float* gscale_inout,
-                               uint8_t* selmap_out, double* err_sum_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+nvfp4_status quantize_impl(const uint16_t* in_bf16, int64_t rows, int64_t cols, int block_axis,
+                           int mode, int rule, uint32_t flags, uint8_t* packed_out,
+                           uint8_t* scales_out, float* gscale_inout, uint8_t* selmap_out,
+                           double* err_sum_out, nvfp4::Events ev, void* stream) {
   if (!in_bf16 || !packed_out || !scales_out || !gscale_inout) return NVFP4_ERR_NULL;
   if (block_axis != NVFP4_AXIS_ROWS && block_axis != NVFP4_AXIS_COLS) return NVFP4_ERR_ENUM;
   if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
@@ -106,24 +110,48 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t co
 
   hipError_t e = hipSuccess;
   uint32_t* acc = reinterpret_cast<uint32_t*>(gscale_inout);
-  // One small kernel zeroes the amax accumulator and the error sum.
+  // One small kernel zeroes the scale accumulator and the error sum; the
+  // amax pass then leaves g itself in *gscale_inout.
   if (!given || err_zero) e = nvfp4::launch_init(given ? nullptr : acc, err_zero, nullptr, 0, s);
   if (e == hipSuccess && !given) {
-    e = nvfp4::launch_amax(in_bf16, rows * cols, acc, s);
-    if (e == hipSuccess) {
-      const float six_m = mode == NVFP4_MODE_4OVER6 ? 6.0f * 256.0f : 6.0f * 448.0f;
-      e = nvfp4::launch_global_scale(gscale_inout, six_m, gscale_inout, s);
-    }
+    const float six_m = mode == NVFP4_MODE_4OVER6 ? 6.0f * 256.0f : 6.0f * 448.0f;
+    e = nvfp4::launch_amax(in_bf16, rows * cols, six_m, acc, s);
   }
   if (e == hipSuccess) {
     if (block_axis == NVFP4_AXIS_COLS)
       e = nvfp4::launch_quantize_rows(in_bf16, rows * cols / 16, gscale_inout, variant,
-                                      packed_out, scales_out, selmap_out, err_sum_out, s);
+                                      packed_out, scales_out, selmap_out, err_sum_out, s, ev);
     else
       e = nvfp4::launch_quantize_cols(in_bf16, rows, cols, gscale_inout, variant, packed_out,
-                                      scales_out, selmap_out, err_sum_out, s);
+                                      scales_out, selmap_out, err_sum_out, s, ev);
   }
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                               int block_axis, int mode, int rule, uint32_t flags,
+                               uint8_t* packed_out, uint8_t* scales_out, float* gscale_inout,
+                               uint8_t* selmap_out, double* err_sum_out, void* stream) {
+  return quantize_impl(in_bf16, rows, cols, block_axis, mode, rule, flags, packed_out,
+                       scales_out, gscale_inout, selmap_out, err_sum_out, nvfp4::Events{},
+                       stream);
+}
+
+nvfp4_status nvfp4_quantize_ex_timed(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                     int block_axis, int mode, int rule, uint32_t flags,
+                                     uint8_t* packed_out, uint8_t* scales_out,
+                                     float* gscale_inout, uint8_t* selmap_out,
+                                     double* err_sum_out, void* start_event, void* stop_event,
+                                     void* stream) {
+  return quantize_impl(in_bf16, rows, cols, block_axis, mode, rule, flags, packed_out,
+                       scales_out, gscale_inout, selmap_out, err_sum_out,
+                       nvfp4::Events{static_cast<hipEvent_t>(start_event),
+                                     static_cast<hipEvent_t>(stop_event)},
+                       stream);
 }
 
 nvfp4_status nvfp4_quantize(const uint16_t* in_bf16, int64_t rows, int64_t cols, int block_axis,

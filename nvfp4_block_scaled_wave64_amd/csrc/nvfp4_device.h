@@ -23,12 +23,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Cache policy of streaming loads: non-temporal (the input is read once).
 constexpr int kStreamLoad = 2;
-
-// 16-byte streaming load (non-temporal hint: the input is read once).
-__device__ __forceinline__ uint4 load_stream16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
+// Non-temporal stores for the codes (512 contiguous bytes per wave step);
+// the scale bytes and bitmap bytes of neighbouring chunks fill their cache
+// lines piecewise, so they are written through the L2, which merges them.
+constexpr int kStreamStore = 2;
+constexpr int kMergedStore = 0;
 
 // Two bf16 values packed in one dword (element 2j in the low half) widened
 // exactly to fp32: bf16 is the upper half of a binary32 word.
@@ -86,32 +85,6 @@ __device__ __forceinline__ void e2m1_decode8(uint32_t w, float v[8]) {
   const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
   v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
   v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
-}
-
-// ---------------------------------------------------------------- lanes ----
-
-// Lanes l and l + 32 of a wave form a pair (l < 32).  pair_values returns,
-// in both lanes of every pair, the value held by the lower lane (.x) and by
-// the upper lane (.y), using gfx950's v_permlane32_swap (one VALU op, no LDS).
-// Callers only combine .x and .y with commutative operations.
-__device__ __forceinline__ float2 pair_values(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return make_float2(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-
-// For per-lane partial sums a (first candidate) and b (second candidate) of
-// the two halves of a block: returns (lo_a + hi_a, lo_b + hi_b) in both lanes
-// of the pair, where lo is the lower lane's value.  One swap lets the lower
-// lane form the first sum and the upper lane the second; a second swap
-// shares both.
-__device__ __forceinline__ float2 pair_sums(float a, float b) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
-                                                 false);
-  // lower lane: p[0] = own a (lo_a), p[1] = partner's a (hi_a);
-  // upper lane: p[0] = partner's b (lo_b), p[1] = own b (hi_b).
-  const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  return pair_values(s);
 }
 
 // max(|a|, |b|, |c|) without canonicalising the operands (gfx950
@@ -182,86 +155,6 @@ __device__ __forceinline__ float2 scale_pair(uint32_t S, const TensorScales& t) 
 
 namespace nvfp4 {
 
-// Result of one half block (8 elements) after the pair's joint decision.
-struct HalfBlock {
-  uint32_t word;  // 8 codes, element i in bits 4i..4i+3
-  uint32_t S;     // kept E4M3 scale byte (same in both lanes of the pair)
-  bool pick4;     // the max->4 candidate was kept
-  float err;      // kept candidate's block error (same in both lanes)
-};
-
-// One lane's half of a block held by a lane pair: wd are the lane's 8 bf16
-// values (element 2j in the low half of wd[j]); the pair's other lane
-// (lane ^ 32) holds the other half, the lower lane the first 8 elements.  tab[S] = (d, r) for every scale byte.
-// Implements the block steps of the method -- block max, the candidate
-// scales, E2M1 codes, reconstruction error against the original values,
-// selection ("Technical summary: Four Over Six (4/6)", "Adaptive block
-// scaling algorithm") -- with each half's error summed sequentially and the
-// two halves then added, so both lanes of the pair hold the same block
-// errors and take the same decision.
-template <bool k46, bool kMae, bool kNeedErr>
-__device__ __forceinline__ HalfBlock quantize_half_block(const uint32_t wd[4], float k6, float k4,
-                                                         const float2* tab) {
-  float x[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    x[2 * j] = bf16_lo(wd[j]);
-    x[2 * j + 1] = bf16_hi(wd[j]);
-  }
-  const float m = absmax3(absmax3(x[0], x[1], x[2]), absmax3(x[3], x[4], x[5]),
-                          __builtin_elementwise_maximum(fabsf(x[6]), fabsf(x[7])));
-  const float2 mp = pair_values(m);
-  const float b = __builtin_elementwise_maximum(mp.x, mp.y);
-
-  // Block scales of the candidates, S6 in bits 0-7 and S4 in bits 8-15.
-  const uint32_t S2 = e4m3_encode2(b * k6, k46 ? b * k4 : 0.0f);
-  const uint32_t S6 = S2 & 0xFFu, S4 = (S2 >> 8) & 0xFFu;
-  const float2 t6 = tab[S6];  // (d, r)
-
-  HalfBlock r;
-  float y[8], v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = x[i] * t6.y;
-  const uint32_t c6 = e2m1_encode8(y);
-  float h6 = 0.0f, h4 = 0.0f;
-  if (kNeedErr) {
-    e2m1_decode8(c6, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float dl = __builtin_fmaf(v[i], t6.x, -x[i]);
-      h6 = kMae ? h6 + fabsf(dl) : __builtin_fmaf(dl, dl, h6);
-    }
-  }
-  uint32_t c4 = 0u;
-  if (k46) {
-    const float2 t4 = tab[S4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = x[i] * t4.y;
-    c4 = e2m1_encode8(y);
-    e2m1_decode8(c4, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float dl = __builtin_fmaf(v[i], t4.x, -x[i]);
-      h4 = kMae ? h4 + fabsf(dl) : __builtin_fmaf(dl, dl, h4);
-    }
-  }
-  // Block errors lo + hi, the same sums on both lanes.
-  float e6 = 0.0f, e4 = 0.0f;
-  if (k46) {
-    const float2 e = pair_sums(h6, h4);
-    e6 = e.x;
-    e4 = e.y;
-  } else if (kNeedErr) {
-    const float2 hp = pair_values(h6);
-    e6 = hp.x + hp.y;
-  }
-  r.pick4 = k46 && (e4 < e6);  // ties and NaN keep max->6
-  r.err = r.pick4 ? e4 : e6;
-  r.S = r.pick4 ? S4 : S6;
-  r.word = r.pick4 ? c4 : c6;
-  return r;
-}
-
 // Result of one whole block of 16 elements held by one lane.
 struct Block16 {
   uint32_t lo, hi;  // codes of elements 0-7 and 8-15 (element i in bits 4i..)
@@ -288,9 +181,12 @@ __device__ __forceinline__ float half_error(const float* x, uint32_t w, float d)
 }
 
 // One block of 16 elements in one lane: wd[0..7] are its bf16 values
-// (element 2j in the low half of wd[j]).  The same block steps as
-// quantize_half_block, with the two halves' errors summed in the same order
-// (elements 0-7 and 8-15 sequentially, then added).
+// (element 2j in the low half of wd[j]).  Implements the block steps of the
+// method -- block max, the candidate scales, E2M1 codes, reconstruction
+// error against the original values, selection ("Technical summary: Four
+// Over Six (4/6)", "Adaptive block scaling algorithm") -- with each
+// candidate's error summed over elements 0-7 and 8-15 sequentially and the
+// two partial sums then added.
 template <bool k46, bool kMae, bool kNeedErr>
 __device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float k6, float k4,
                                                     const float2* tab) {

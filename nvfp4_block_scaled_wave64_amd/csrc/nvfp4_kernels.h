@@ -2,14 +2,62 @@
 // host-side ABI (api.hip) and the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace nvfp4 {
+
+// Optional events bound to a launch: `start` takes the kernel's start
+// timestamp and `stop` its end timestamp (hipExtLaunchKernel), so their
+// elapsed time is the kernel's execution time alone.
+struct Events {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// Launches `kernel` on stream s, binding ev.start / ev.stop (either may be
+// null) to it; the arguments are converted to the kernel's parameter types.
+template <typename... P, typename... A>
+hipError_t launch_with_events(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s,
+                              Events ev, A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count");
+  std::tuple<P...> vals(args...);
+  void* ptrs[sizeof...(P)];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, s,
+                            ev.start, ev.stop, 0);
+}
 
 // Threads per workgroup of the streaming kernels (4 waves of 64).
 constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / 64;
+
+// Launch shape of the row-wise quantizer (quantize_rows.hip): chunks whose
+// loads are in flight ahead of the one being processed, waves per compute
+// unit and threads per workgroup.
+#ifndef NVFP4_ROWS_DEPTH
+#define NVFP4_ROWS_DEPTH 1
+#endif
+#ifndef NVFP4_ROWS_WAVES_PER_CU
+#define NVFP4_ROWS_WAVES_PER_CU 16
+#endif
+#ifndef NVFP4_ROWS_THREADS
+#define NVFP4_ROWS_THREADS 1024
+#endif
+constexpr int kRowsDepth = NVFP4_ROWS_DEPTH;
+// One workgroup of 16 waves per compute unit: the 16 consecutive chunks a
+// workgroup handles in one round write whole 128-byte lines of the bitmap
+// (16 x 8 bytes) and of the scales from one XCD, and the error sum takes one
+// atomic per compute unit.
+constexpr int kRowsThreads = NVFP4_ROWS_THREADS;
+constexpr int kRowsWaves = kRowsThreads / 64;
+constexpr int kGroupsPerCu = NVFP4_ROWS_WAVES_PER_CU / kRowsWaves;
 
 // Bits of the kernel variant selector.
 enum : uint32_t {
@@ -22,23 +70,33 @@ enum : uint32_t {
 // ---- amax.hip ----
 hipError_t launch_init(uint32_t* zero_u32, double* zero_f64, uint32_t* zero_words,
                        int64_t nwords, hipStream_t s);
-hipError_t launch_amax(const uint16_t* in, int64_t numel, uint32_t* acc_bits, hipStream_t s);
+// Atomic max of A = max |x| into *acc_bits (fp32 bit pattern, zeroed by the
+// caller), or of g = A / six_m when six_m > 0: division by a positive
+// constant rounds monotonically, so the max over workgroups of A_wg / six_m
+// is the rounded quotient of the tensor's A.
+hipError_t launch_amax(const uint16_t* in, int64_t numel, float six_m, uint32_t* acc_bits,
+                       hipStream_t s);
 hipError_t launch_global_scale(const float* amax, float six_m, float* gscale, hipStream_t s);
 
 // ---- quantize_rows.hip: blocks of 16 contiguous elements ----
 hipError_t launch_quantize_rows(const uint16_t* in, int64_t nblocks, const float* gscale,
                                 uint32_t variant, uint8_t* packed, uint8_t* scales,
-                                uint8_t* selmap, double* err_sum, hipStream_t s);
+                                uint8_t* selmap, double* err_sum, hipStream_t s, Events ev);
 
 // ---- quantize_cols.hip: blocks of 16 rows within a column ----
 hipError_t launch_quantize_cols(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint32_t variant, uint8_t* packed,
-                                uint8_t* scales, uint8_t* selmap, double* err_sum, hipStream_t s);
+                                uint8_t* scales, uint8_t* selmap, double* err_sum, hipStream_t s,
+                                Events ev);
 
 // ---- dequantize.hip ----
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, const float* gscale,
                              int64_t rows, int64_t cols, int block_axis, int out_bf16, void* out,
                              hipStream_t s);
+
+// ---- verify.hip: the row quantizer's memory traffic without its arithmetic ----
+hipError_t launch_stream_pattern(const uint16_t* in, int64_t nblocks, uint8_t* packed,
+                                 uint8_t* scales, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

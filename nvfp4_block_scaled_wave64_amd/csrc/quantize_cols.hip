@@ -2,39 +2,57 @@
 // consecutive rows of one column (e.g. gradients quantized along the token
 // axis; "Technical summary: Four Over Six (4/6)", "Key contributions",
 // applies the method to activations, weights and gradients).  The outputs
-// are laid out as the row-blocked outputs of the transposed tensor.
+// are laid out as the row-blocked outputs of the transposed tensor: codes
+// [cols][rows/2], scales [cols][rows/16], bitmap bit c*(rows/16) + rb.
 //
-// A workgroup owns a strip of 64 columns and a range of rows, and walks it
-// in tiles of 64 rows x 64 columns:
-//   1. load: each row segment of the tile is 128 contiguous bytes; a thread
-//      reads 16 bytes (8 columns of one row) per load;
-//   2. transpose through LDS: the tile is stored column-major (tileT[col][row])
-//      with a row pitch of 72 elements; the pad keeps the 16-byte reads of
-//      step 3 aligned and spreads the columns of a wave over the banks;
-//   3. compute: a lane pair (l, l + 32) takes one block (16 rows of one
-//      column), each lane reading its 8 rows as one 16-byte LDS read, and runs
-//      the same block math as the row-wise kernel;
-//   4. store: the 4 blocks of a column in this tile are 32 contiguous bytes
-//      of codes.  Since a workgroup walks down the rows of its strip,
-//      successive tiles extend the same output rows and the partial lines
-//      merge in that XCD's L2.
-// When a selection bitmap is requested, the kernel marks the kept candidate
-// in bit 7 of the scale byte (always 0 in a non-negative E4M3 scale) and a
-// second pass turns those bits into the bitmap and clears them, which avoids
-// sub-byte write races between workgroups.
+// Tiles of 256 rows x 64 columns.  Per tile a workgroup of 4 waves
+//   1. has the tile's 256 row segments of 128 contiguous bytes in registers
+//      (8 x 16-byte loads per lane, issued kColsDepth tiles ahead so they
+//      are in flight while earlier tiles are computed) and writes them row-major
+//      into LDS with 16-byte writes (row pitch 144 bytes, 16-byte aligned);
+//   2. lets every lane read a column pair over 16 rows (16 x 4-byte LDS
+//      reads, consecutive banks across each half-wave), which are two whole
+//      blocks; the lane repacks them and runs the same whole-block quantizer
+//      as the row-wise kernel on each;
+//   3. stages the codes (8 bytes per block), the scale bytes and the
+//      selection flags per column in LDS, so that each column's 128 bytes of
+//      codes and 16 scale bytes leave as 16-byte stores (whole 128-byte
+//      lines of codes per column and tile).
+// The grid is persistent (a few workgroups per compute unit) and walks the
+// tiles row-tile-major within each 64-column strip.  Workgroups are
+// renumbered so that consecutive tiles run on one XCD: the 8 row tiles that
+// share a 128-byte line of a column's scale bytes are then written through
+// the same L2, which merges them.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
 namespace nvfp4 {
 
-constexpr int kTileRows = 64;
+#ifndef NVFP4_COLS_GROUPS_PER_CU
+#define NVFP4_COLS_GROUPS_PER_CU 2
+#endif
+#ifndef NVFP4_COLS_DEPTH
+#define NVFP4_COLS_DEPTH 1
+#endif
+constexpr int kColsGroupsPerCu = NVFP4_COLS_GROUPS_PER_CU;
+// Tiles whose loads are in flight (in registers) ahead of the one computed.
+constexpr int kColsDepth = NVFP4_COLS_DEPTH;
+#ifndef NVFP4_COLS_ORDER
+#define NVFP4_COLS_ORDER 0
+#endif
+// Tile walk: 0 = row tiles fastest within a strip, 1 = strips fastest.
+constexpr int kColsOrder = NVFP4_COLS_ORDER;
+constexpr int kTileRows = 256;
 constexpr int kTileCols = 64;
-constexpr int kPitch = kTileRows + 8;  // bf16 elements per LDS column
+constexpr int kRowBlocks = kTileRows / 16;  // 16 row blocks per tile
+constexpr int kInPitch = 144;               // LDS bytes per tile row (128 + 16)
+constexpr int kCodePitch = 144;             // LDS bytes per column of codes (128 + 16)
+constexpr int kLoadsPerLane = kTileRows * kTileCols * 2 / (kThreads * 16);  // 8
 
 template <uint32_t V>
 __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
-    const uint16_t* __restrict__ in, int64_t rows, int64_t cols, int64_t rows_per_group,
-    const float* __restrict__ gscale, uint32_t* __restrict__ packed, uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ in, int64_t rows, int64_t cols, const float* __restrict__ gscale,
+    uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
     double* __restrict__ err_sum) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr bool kMae = k46 && (V & kVarMae) != 0;
@@ -43,78 +61,192 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
   constexpr bool kNeedErr = k46 || kErr;
 
   __shared__ float2 tab[128];
-  __shared__ __attribute__((aligned(16))) uint16_t tileT[kTileCols * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileRows * kInPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t codes[kTileCols * kCodePitch];
+  __shared__ __attribute__((aligned(16))) uint8_t sbytes[kTileCols * kRowBlocks];
   __shared__ double wsum[kWavesPerGroup];
 
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
 
   const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int64_t c0 = (int64_t)blockIdx.x * kTileCols;
-  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_group;
-  int64_t r_end = r_begin + rows_per_group;
-  if (r_end > rows) r_end = rows;
+  const int lane = t & 63, wave = t >> 6;
+  const int64_t nstrips = (cols + kTileCols - 1) / kTileCols;
+  const int64_t nrt = (rows + kTileRows - 1) / kTileRows;
+  const int64_t ntiles = nstrips * nrt;
+  const int64_t rb_col = rows / 16;  // blocks per column = scale bytes per output row
+  // Bitmap bytes are written directly when every column's bits start on a
+  // byte boundary; otherwise bit 7 of the scale byte carries the flag to a
+  // second pass.
+  const bool sel_direct = (rb_col % 8) == 0;
   const bool vec_ok = (cols % 8) == 0;
-  const int64_t rb16 = rows / 16;  // blocks per output row (per column of x)
-  double acc = 0.0;
+  // 16-byte stores only where every column's run is 16-byte aligned; the
+  // ABI guarantees 4-byte alignment of packed and none for scales.
+  const bool codes16 = (reinterpret_cast<uintptr_t>(packed) % 16 == 0) && ((rows / 2) % 16 == 0);
+  const bool scales16 = (reinterpret_cast<uintptr_t>(scales) % 16 == 0) && (rb_col % 16 == 0);
 
-  for (int64_t r0 = r_begin; r0 < r_end; r0 += kTileRows) {
-    __syncthreads();  // previous tile fully consumed (and the table built)
-    // 1 + 2: load 64 x 64 and store transposed.  512 segments of 8 columns.
+  // Consecutive logical ids on one XCD (workgroups are dispatched round-robin
+  // over the 8 XCDs).
+  const uint32_t nwg = gridDim.x;
+  const uint32_t wg =
+      (nwg % 8u == 0u) ? (blockIdx.x % 8u) * (nwg / 8u) + blockIdx.x / 8u : blockIdx.x;
+
+  // Load k of lane t covers tile row k*32 + t/8, columns (t%8)*8 .. +7.
+  const int lrow = t >> 3, lseg = t & 7;
+  auto tile_of = [&](int64_t tt, int64_t& strip, int64_t& rt) {
+    if (kColsOrder == 0) {
+      strip = tt / nrt;
+      rt = tt % nrt;
+    } else {
+      rt = tt / nstrips;
+      strip = tt % nstrips;
+    }
+  };
+  auto load_tile = [&](int64_t tt, u32x4* w) {
+    int64_t strip, rt;
+    tile_of(tt, strip, rt);
+    const int64_t r0 = rt * kTileRows, c = strip * kTileCols + lseg * 8;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int seg = t + k * kThreads;
-      const int row = seg >> 3, cseg = (seg & 7) * 8;
-      const int64_t gr = r0 + row, gc = c0 + cseg;
-      uint32_t wd[4] = {0u, 0u, 0u, 0u};
-      if (gr < r_end) {
-        const uint16_t* src = in + gr * cols + gc;
+    for (int k = 0; k < kLoadsPerLane; ++k) {
+      const int64_t r = r0 + k * 32 + lrow;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (tt < ntiles && r < rows) {
+        const uint16_t* src = in + r * cols + c;
         if (vec_ok) {
-          if (gc < cols) {
-            const uint4 w = load_stream16(src);
-            wd[0] = w.x; wd[1] = w.y; wd[2] = w.z; wd[3] = w.w;
-          }
+          if (c < cols) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            if (gc + j < cols) wd[j >> 1] |= (uint32_t)src[j] << ((j & 1) * 16);
+            if (c + j < cols) v[j >> 1] |= (uint32_t)src[j] << ((j & 1) * 16);
         }
       }
+      w[k] = v;
+    }
+  };
+
+  double acc = 0.0;
+  // Quantizes tile tt from the registers w, then refills w with tile
+  // tt + kColsDepth * nwg.
+  auto process = [&](int64_t tt, u32x4* w) {
+    int64_t strip, rt;
+    tile_of(tt, strip, rt);
+    const int64_t r0 = rt * kTileRows, c0 = strip * kTileCols;
+    const int nrb = (int)((rows - r0) / 16 < kRowBlocks ? (rows - r0) / 16 : kRowBlocks);
+    const int ncol = (int)(cols - c0 < kTileCols ? cols - c0 : kTileCols);
+
+    __syncthreads();  // the previous tile's staging has been stored (and tab built)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        tileT[(cseg + j) * kPitch + row] = (uint16_t)(wd[j >> 1] >> ((j & 1) * 16));
+    for (int k = 0; k < kLoadsPerLane; ++k)
+      *reinterpret_cast<u32x4*>(&tile[(k * 32 + lrow) * kInPitch + lseg * 16]) = w[k];
+    __syncthreads();
+    load_tile(tt + kColsDepth * nwg, w);  // in flight during the next tiles' compute
+
+    // 16 row blocks x 32 column pairs = 512 lane tasks, two per lane: in pass
+    // p, wave w takes row block p*8 + w*2 + lane/32 and column pair lane%32.
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int rb = p * 8 + wave * 2 + (lane >> 5);
+      const int cp = lane & 31;
+      uint32_t v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = *reinterpret_cast<const uint32_t*>(&tile[(rb * 16 + i) * kInPitch + cp * 4]);
+      uint32_t wa[8], wb[8];  // columns 2cp and 2cp+1: rows 2j (low half), 2j+1
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        wa[j] = (v[2 * j] & 0xFFFFu) | (v[2 * j + 1] << 16);
+        wb[j] = (v[2 * j] >> 16) | (v[2 * j + 1] & 0xFFFF0000u);
+      }
+      const Block16 qa = quantize_block16<k46, kMae, kNeedErr>(wa, ts.k6, ts.k4, tab);
+      const Block16 qb = quantize_block16<k46, kMae, kNeedErr>(wb, ts.k6, ts.k4, tab);
+      const int ca = 2 * cp, cb = 2 * cp + 1;
+      u32x2 pa, pb;
+      pa.x = qa.lo;
+      pa.y = qa.hi;
+      pb.x = qb.lo;
+      pb.y = qb.hi;
+      *reinterpret_cast<u32x2*>(&codes[ca * kCodePitch + rb * 8]) = pa;
+      *reinterpret_cast<u32x2*>(&codes[cb * kCodePitch + rb * 8]) = pb;
+      sbytes[ca * kRowBlocks + rb] = (uint8_t)(qa.S | (kSel && qa.pick4 ? 0x80u : 0u));
+      sbytes[cb * kRowBlocks + rb] = (uint8_t)(qb.S | (kSel && qb.pick4 ? 0x80u : 0u));
+      if (kErr && rb < nrb) {
+        if (ca < ncol) acc += (double)qa.err;
+        if (cb < ncol) acc += (double)qb.err;
+      }
     }
     __syncthreads();
 
-    // 3 + 4: 256 blocks (64 columns x 4 row blocks).  In pass p, wave w
-    // takes blocks (4p + w) * 32 + (lane & 31); lane l < 32 holds rows 0-7 of
-    // its block and lane l + 32 rows 8-15.
+    // Codes: column c's nrb * 8 bytes go to packed[c][r0/2 ..]; in each of
+    // two passes lane t stores 16 bytes (two row blocks) of column t/8.
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int blk = (p * kWavesPerGroup + (t >> 6)) * 32 + (lane & 31);
-      const int col = blk >> 2, rb = blk & 3, h = lane >> 5;
-      const uint4 w = *reinterpret_cast<const uint4*>(&tileT[col * kPitch + rb * 16 + h * 8]);
-      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-      const HalfBlock hb = quantize_half_block<k46, kMae, kNeedErr>(wd, ts.k6, ts.k4, tab);
-      const int64_t gc = c0 + col;
-      const int64_t grb = r0 / 16 + rb;  // block index along the column
-      const bool valid = gc < cols && r0 + rb * 16 < r_end;
-      if (valid) {
-        packed[(gc * rows / 2 + grb * 8 + h * 4) / 4] = hb.word;
-        if (h == 0) {
-          uint32_t sb = hb.S;
-          if (kSel && hb.pick4) sb |= 0x80u;
-          scales[gc * rb16 + grb] = (uint8_t)sb;
+      const int c = p * 32 + (t >> 3), seg = t & 7;
+      if (c < ncol && 2 * seg < nrb) {
+        const u32x4 cw = *reinterpret_cast<const u32x4*>(&codes[c * kCodePitch + seg * 16]);
+        uint8_t* dst = packed + (c0 + c) * (rows / 2) + r0 / 2 + seg * 16;
+        const bool both = 2 * seg + 1 < nrb;
+        if (codes16 && both) {
+          __builtin_nontemporal_store(cw, reinterpret_cast<u32x4*>(dst));
+        } else {
+          uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);  // 4-byte aligned
+          d32[0] = cw.x;
+          d32[1] = cw.y;
+          if (both) {
+            d32[2] = cw.z;
+            d32[3] = cw.w;
+          }
         }
-        if (kErr && h == 0) acc += (double)hb.err;
       }
+    }
+    // Scale bytes (and bitmap bytes): lane t < 64 handles column t.
+    if (t < ncol) {
+      const u32x4 sw = *reinterpret_cast<const u32x4*>(&sbytes[t * kRowBlocks]);
+      uint32_t s[4] = {sw.x, sw.y, sw.z, sw.w};
+      uint32_t bits = 0u;
+      if (kSel && sel_direct) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // bit 7 of each byte -> bits 4k .. 4k+3 of the tile's 16 flags
+          const uint32_t f = (s[k] >> 7) & 0x01010101u;
+          bits |= ((f | (f >> 7) | (f >> 14) | (f >> 21)) & 15u) << (4 * k);
+          s[k] &= 0x7F7F7F7Fu;
+        }
+      }
+      uint8_t* dst = scales + (c0 + t) * rb_col + r0 / 16;
+      if (scales16 && nrb == kRowBlocks) {
+        u32x4 o;
+        o.x = s[0];
+        o.y = s[1];
+        o.z = s[2];
+        o.w = s[3];
+        *reinterpret_cast<u32x4*>(dst) = o;
+      } else {
+        for (int k = 0; k < nrb; ++k) dst[k] = (uint8_t)(s[k >> 2] >> (8 * (k & 3)));
+      }
+      if (kSel && sel_direct) {
+        // nrb is a multiple of 8 here: one or two whole bitmap bytes.
+        uint8_t* bd = selmap + ((c0 + t) * rb_col + r0 / 16) / 8;
+        bd[0] = (uint8_t)bits;
+        if (nrb > 8) bd[1] = (uint8_t)(bits >> 8);
+      }
+    }
+  };
+
+  u32x4 w0[kLoadsPerLane], w1[kLoadsPerLane];
+  load_tile(wg, w0);
+  if (kColsDepth == 1) {
+    for (int64_t tt = wg; tt < ntiles; tt += nwg) process(tt, w0);
+  } else {
+    load_tile(wg + nwg, w1);
+    for (int64_t tt = wg; tt < ntiles; tt += 2 * nwg) {
+      process(tt, w0);
+      if (tt + nwg < ntiles) process(tt + nwg, w1);  // uniform per workgroup
     }
   }
 
   if (kErr) {
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) wsum[t >> 6] = acc;
+    if (lane == 0) wsum[wave] = acc;
     __syncthreads();
     if (t == 0) {
       double s = wsum[0];
@@ -124,7 +256,8 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
   }
 }
 
-// Bitmap pass: byte j of the bitmap collects bit 7 of scale bytes 8j..8j+7,
+// Bitmap pass for shapes whose columns' bits do not start on byte
+// boundaries: byte j of the bitmap collects bit 7 of scale bytes 8j..8j+7,
 // which are then cleared.
 __global__ __launch_bounds__(kThreads) void selmap_from_scales_kernel(uint8_t* __restrict__ scales,
                                                                      int64_t nblocks,
@@ -148,37 +281,35 @@ __global__ __launch_bounds__(kThreads) void selmap_from_scales_kernel(uint8_t* _
 template <uint32_t V>
 static hipError_t launch_cols_v(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint8_t* packed, uint8_t* scales,
-                                uint8_t* selmap, double* err_sum, hipStream_t s) {
-  const int64_t strips = (cols + kTileCols - 1) / kTileCols;
-  const int64_t row_tiles = (rows + kTileRows - 1) / kTileRows;
-  // Enough groups to fill the chip several times over; each walks a
-  // contiguous run of row tiles of its strip.
-  const int64_t target = (int64_t)device_cu_count() * 8;
-  int64_t splits = (target + strips - 1) / strips;
-  if (splits > row_tiles) splits = row_tiles;
-  if (splits < 1) splits = 1;
-  const int64_t tiles_per_group = (row_tiles + splits - 1) / splits;
-  splits = (row_tiles + tiles_per_group - 1) / tiles_per_group;
-  dim3 grid((unsigned)strips, (unsigned)splits);
-  quantize_cols_kernel<V><<<grid, kThreads, 0, s>>>(in, rows, cols, tiles_per_group * kTileRows,
-                                                   gscale, reinterpret_cast<uint32_t*>(packed),
-                                                   scales, err_sum);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !(V & kVarSelmap)) return e;
-  const int64_t nblocks = rows / 16 * cols;
-  int64_t groups = ((nblocks + 7) / 8 + kThreads - 1) / kThreads;
-  if (groups > 4096) groups = 4096;
+                                uint8_t* selmap, double* err_sum, hipStream_t s, Events ev) {
+  const int64_t ntiles =
+      ((cols + kTileCols - 1) / kTileCols) * ((rows + kTileRows - 1) / kTileRows);
+  int64_t groups = (int64_t)device_cu_count() * kColsGroupsPerCu;
+  if (groups > ntiles) groups = ntiles;
   if (groups < 1) groups = 1;
-  selmap_from_scales_kernel<<<(unsigned)groups, kThreads, 0, s>>>(scales, nblocks, selmap);
-  return hipGetLastError();
+  constexpr bool kSel = (V & kVarSelmap) != 0;
+  const bool two_pass = kSel && (rows / 16) % 8 != 0;
+  // With a second bitmap pass, that kernel ends the event bracket.
+  const Events first{ev.start, two_pass ? nullptr : ev.stop};
+  hipError_t e = launch_with_events(quantize_cols_kernel<V>, dim3((unsigned)groups),
+                                    dim3(kThreads), s, first, in, rows, cols, gscale, packed,
+                                    scales, selmap, err_sum);
+  if (e != hipSuccess || !two_pass) return e;
+  const int64_t nblocks = rows / 16 * cols;
+  int64_t g2 = ((nblocks + 7) / 8 + kThreads - 1) / kThreads;
+  if (g2 > 4096) g2 = 4096;
+  if (g2 < 1) g2 = 1;
+  return launch_with_events(selmap_from_scales_kernel, dim3((unsigned)g2), dim3(kThreads), s,
+                            Events{nullptr, ev.stop}, scales, nblocks, selmap);
 }
 
 hipError_t launch_quantize_cols(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint32_t variant, uint8_t* packed,
-                                uint8_t* scales, uint8_t* selmap, double* err_sum, hipStream_t s) {
+                                uint8_t* scales, uint8_t* selmap, double* err_sum, hipStream_t s,
+                                Events ev) {
 #define NVFP4_COLS_CASE(v) \
   case v:                  \
-    return launch_cols_v<v>(in, rows, cols, gscale, packed, scales, selmap, err_sum, s);
+    return launch_cols_v<v>(in, rows, cols, gscale, packed, scales, selmap, err_sum, s, ev);
   switch (variant) {
     NVFP4_COLS_CASE(0)
     NVFP4_COLS_CASE(1)

@@ -37,31 +37,6 @@
 
 namespace nvfp4 {
 
-// Chunks whose loads are in flight ahead of the one being processed, and
-// workgroups per compute unit.
-#ifndef NVFP4_ROWS_DEPTH
-#define NVFP4_ROWS_DEPTH 1
-#endif
-#ifndef NVFP4_ROWS_WAVES_PER_CU
-#define NVFP4_ROWS_WAVES_PER_CU 16
-#endif
-#ifndef NVFP4_ROWS_THREADS
-#define NVFP4_ROWS_THREADS 1024
-#endif
-constexpr int kDepth = NVFP4_ROWS_DEPTH;
-// One workgroup of 16 waves per compute unit: the 16 consecutive chunks a
-// workgroup handles in one round write whole 128-byte lines of the bitmap
-// (16 x 8 bytes) and of the scales from one XCD, and the error sum takes one
-// atomic per compute unit.
-constexpr int kRowsThreads = NVFP4_ROWS_THREADS;
-constexpr int kRowsWaves = kRowsThreads / 64;
-constexpr int kGroupsPerCu = NVFP4_ROWS_WAVES_PER_CU / kRowsWaves;
-// Non-temporal stores for the codes (512 contiguous bytes per wave step);
-// the scale bytes and bitmap bytes of neighbouring chunks fill their cache
-// lines piecewise, so they are written through the L2, which merges them.
-constexpr int kStreamStore = 2;
-constexpr int kMergedStore = 0;
-
 template <uint32_t V>
 __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
     const uint16_t* __restrict__ in, int64_t nblocks, const float* __restrict__ gscale,
@@ -95,7 +70,7 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
   double acc = 0.0;
 
   // Chunks past the end read as zeros (range-checked buffer loads); ch stays
-  // below nchunks + (kDepth + 1) * nwaves, so ch * 2048 cannot wrap.
+  // below nchunks + (kRowsDepth + 1) * nwaves, so ch * 2048 cannot wrap.
   struct Two {
     u32x4 a, b;
   };
@@ -141,18 +116,18 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
     return t;
   };
 
-  if constexpr (kDepth == 0) {
+  if constexpr (kRowsDepth == 0) {
     for (uint32_t ch = first; ch < nchunks; ch += nwaves) process(ch, load(ch));
   } else {
-    Two buf[kDepth > 0 ? kDepth : 1];
+    Two buf[kRowsDepth > 0 ? kRowsDepth : 1];
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) buf[k] = load(first + k * nwaves);
-    for (uint32_t base = first; base < nchunks; base += kDepth * nwaves) {
+    for (int k = 0; k < kRowsDepth; ++k) buf[k] = load(first + k * nwaves);
+    for (uint32_t base = first; base < nchunks; base += kRowsDepth * nwaves) {
 #pragma unroll
-      for (int k = 0; k < kDepth; ++k) {
+      for (int k = 0; k < kRowsDepth; ++k) {
         const uint32_t ch = base + k * nwaves;
         const Two w = buf[k];
-        buf[k] = prefetch(ch + kDepth * nwaves);
+        buf[k] = prefetch(ch + kRowsDepth * nwaves);
         if (ch >= nchunks) break;  // wave-uniform
         process(ch, w);
       }
@@ -174,7 +149,7 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
 template <uint32_t V>
 static hipError_t launch_rows_v(const uint16_t* in, int64_t nblocks, const float* gscale,
                                 uint8_t* packed, uint8_t* scales, uint8_t* selmap,
-                                double* err_sum, hipStream_t s) {
+                                double* err_sum, hipStream_t s, Events ev) {
   // Segments of at most 2^26 blocks (2^30 elements, 2 GiB of input) keep
   // every buffer offset within 32 bits; a multiple of 64 blocks, so each
   // segment's bitmap starts on a byte boundary.
@@ -186,10 +161,13 @@ static hipError_t launch_rows_v(const uint16_t* in, int64_t nblocks, const float
     int64_t groups = (nchunks + kRowsWaves - 1) / kRowsWaves;
     if (groups > cap) groups = cap;
     if (groups < 1) groups = 1;
-    quantize_rows_kernel<V><<<(unsigned)groups, kRowsThreads, 0, s>>>(
+    Events seg;  // the first segment starts the bracket, the last one ends it
+    if (b0 == 0) seg.start = ev.start;
+    if (b0 + nb >= nblocks) seg.stop = ev.stop;
+    const hipError_t e = launch_with_events(
+        quantize_rows_kernel<V>, dim3((unsigned)groups), dim3(kRowsThreads), s, seg,
         in + b0 * 16, nb, gscale, packed + b0 * 8, scales + b0,
         selmap ? selmap + b0 / 8 : nullptr, err_sum);
-    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -197,10 +175,10 @@ static hipError_t launch_rows_v(const uint16_t* in, int64_t nblocks, const float
 
 hipError_t launch_quantize_rows(const uint16_t* in, int64_t nblocks, const float* gscale,
                                 uint32_t variant, uint8_t* packed, uint8_t* scales,
-                                uint8_t* selmap, double* err_sum, hipStream_t s) {
+                                uint8_t* selmap, double* err_sum, hipStream_t s, Events ev) {
 #define NVFP4_ROWS_CASE(v) \
   case v:                  \
-    return launch_rows_v<v>(in, nblocks, gscale, packed, scales, selmap, err_sum, s);
+    return launch_rows_v<v>(in, nblocks, gscale, packed, scales, selmap, err_sum, s, ev);
   switch (variant) {
     NVFP4_ROWS_CASE(0)
     NVFP4_ROWS_CASE(1)

@@ -62,6 +62,59 @@ __global__ void decode_tables_kernel(float g, float* e2m1, float* e4m3, float* d
   }
 }
 
+// The row quantizer's memory traffic with none of its arithmetic: the same
+// launch shape, chunk order, non-temporal 2 x 16-byte loads per lane, lane
+// pairing, 8-byte code stores and L2-merged scale-byte stores, writing a
+// fold of the input instead of codes.  It moves exactly the quantizer's
+// 32 + 8 + 1 bytes per block, so its time is the bandwidth ceiling for that
+// pattern and its byte counters calibrate the profiler's.
+__global__ __launch_bounds__(kRowsThreads) void stream_pattern_kernel(
+    const uint16_t* __restrict__ in, int64_t nblocks, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ scales) {
+  const uint32_t nb = (uint32_t)nblocks;  // <= 2^26 per launch
+  const __amdgpu_buffer_rsrc_t r_in = make_rsrc(in, nb * 32u);
+  const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed, nb * 8u);
+  const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales, nb);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t off_in = (lane & 31u) * 32u + (lane >> 5) * 16u;
+  const uint32_t nchunks = (nb + 63u) / 64u;
+  const uint32_t nwaves = gridDim.x * kRowsWaves;
+  for (uint32_t ch = blockIdx.x * kRowsWaves + (threadIdx.x >> 6); ch < nchunks; ch += nwaves) {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r_in, ch * 2048u + off_in, 0, kStreamLoad);
+    const u32x4 b =
+        __builtin_amdgcn_raw_buffer_load_b128(r_in, ch * 2048u + 1024u + off_in, 0, kStreamLoad);
+    uint32_t f = 0u, h = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto p = __builtin_amdgcn_permlane32_swap(a[j], b[j], false, false);
+      f ^= p[0];
+      h ^= p[1];
+    }
+    u32x2 o;
+    o.x = f;
+    o.y = h;
+    __builtin_amdgcn_raw_buffer_store_b64(o, r_packed, ch * 512u + lane * 8u, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(f ^ h), r_scales, ch * 64u + lane, 0, kMergedStore);
+  }
+}
+
+hipError_t launch_stream_pattern(const uint16_t* in, int64_t nblocks, uint8_t* packed,
+                                 uint8_t* scales, hipStream_t s) {
+  constexpr int64_t kSeg = int64_t(1) << 26;
+  const int64_t cap = (int64_t)device_cu_count() * (kGroupsPerCu > 0 ? kGroupsPerCu : 1);
+  for (int64_t b0 = 0; b0 < nblocks; b0 += kSeg) {
+    const int64_t nb = nblocks - b0 < kSeg ? nblocks - b0 : kSeg;
+    int64_t groups = ((nb + 63) / 64 + kRowsWaves - 1) / kRowsWaves;
+    if (groups > cap) groups = cap;
+    if (groups < 1) groups = 1;
+    stream_pattern_kernel<<<(unsigned)groups, kRowsThreads, 0, s>>>(in + b0 * 16, nb,
+                                                                   packed + b0 * 8, scales + b0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 static int64_t sweep_groups(int64_t work) {
   int64_t g = (work + kThreads - 1) / kThreads;
   if (g > 16384) g = 16384;
@@ -96,6 +149,18 @@ nvfp4_status nvfp4v_decode_tables(float g, float* e2m1_out, float* e4m3_out, flo
   nvfp4::decode_tables_kernel<<<1, 128, 0, (hipStream_t)stream>>>(g, e2m1_out, e4m3_out, d_out,
                                                                   r_out);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4v_stream_pattern(const uint16_t* in_bf16, int64_t nblocks, uint8_t* packed_out,
+                                   uint8_t* scales_out, void* stream) {
+  if (!in_bf16 || !packed_out || !scales_out) return NVFP4_ERR_NULL;
+  if (nblocks <= 0 || nblocks > (int64_t(1) << 42)) return NVFP4_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(in_bf16) & 15u) || (reinterpret_cast<uintptr_t>(packed_out) & 7u))
+    return NVFP4_ERR_ALIGN;
+  return nvfp4::launch_stream_pattern(in_bf16, nblocks, packed_out, scales_out,
+                                      static_cast<hipStream_t>(stream)) == hipSuccess
+             ? NVFP4_OK
+             : NVFP4_ERR_HIP;
 }
 
 }  // extern "C"

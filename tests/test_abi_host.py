@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
@@ -45,12 +45,16 @@ def test_status_strings():
 
 
 def q(**kw):
+    """Status of nvfp4_quantize_ex for the given arguments; the timed variant
+    must return the same status for them."""
     args = dict(in_=A, rows=32, cols=64, axis=nv.AXIS_COLS, mode=nv.MODE_4OVER6, rule=nv.RULE_MSE,
                 flags=0, packed=B, scales=C, g=A, sel=None, err=None)
     args.update(kw)
-    return nv.lib().nvfp4_quantize_ex(args["in_"], args["rows"], args["cols"], args["axis"],
-                                      args["mode"], args["rule"], args["flags"], args["packed"],
-                                      args["scales"], args["g"], args["sel"], args["err"], None)
+    pos = (args["in_"], args["rows"], args["cols"], args["axis"], args["mode"], args["rule"],
+           args["flags"], args["packed"], args["scales"], args["g"], args["sel"], args["err"])
+    st = nv.lib().nvfp4_quantize_ex(*pos, None)
+    assert nv.lib().nvfp4_quantize_ex_timed(*pos, A, B, None) == st
+    return st
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -86,3 +90,6 @@ def test_other_entry_points_reject():
     assert L.nvfp4v_e2m1_encode_sweep(0, 0, A, None) == 3
     assert L.nvfp4v_e4m3_encode_sweep(0, 16, None, None) == 1
     assert L.nvfp4v_decode_tables(1.0, None, A, B, C, None) == 1
+    assert L.nvfp4v_stream_pattern(None, 16, A, B, None) == 1
+    assert L.nvfp4v_stream_pattern(A, 0, B, C, None) == 3
+    assert L.nvfp4v_stream_pattern(MIS, 16, B, C, None) == 4
