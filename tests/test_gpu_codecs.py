@@ -2,8 +2,9 @@
 and decoders, run on the GPU over every fp32 input of the ranges they see,
 against the CPU reference.
 
-* E2M1 encoder: every fp32 bit pattern in [0, 8] and a sampled negative
-  range, against the oracle.
+* E2M1 encoder: every fp32 bit pattern in [0, 8] and in [-8, -0], and
+  sampled ranges beyond 8 in magnitude (plus the infinities), against the
+  oracle.
 * E4M3 encoder: every fp32 bit pattern in [0, 464], against torch's
   float8_e4m3fn cast (pinned to the oracle by the CPU suite), plus a sampled
   comparison with the oracle itself and the saturation range.
