@@ -38,19 +38,20 @@ hipError_t launch_with_events(void (*kernel)(P...), dim3 grid, dim3 block, hipSt
 constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / 64;
 
-// Launch shape of the row-wise quantizer (quantize_rows.hip): chunks whose
-// loads are in flight ahead of the one being processed, waves per compute
-// unit and threads per workgroup.
-#ifndef NVFP4_ROWS_DEPTH
-#define NVFP4_ROWS_DEPTH 1
-#endif
+// Launch shape of the row-wise kernels (quantize_rows.hip, the byte-pattern
+// kernel, the row-layout dequantizer): waves per compute unit, threads per
+// workgroup, and how many steps the quantizer's waves take between
+// workgroup barriers.
 #ifndef NVFP4_ROWS_WAVES_PER_CU
 #define NVFP4_ROWS_WAVES_PER_CU 16
 #endif
 #ifndef NVFP4_ROWS_THREADS
 #define NVFP4_ROWS_THREADS 1024
 #endif
-constexpr int kRowsDepth = NVFP4_ROWS_DEPTH;
+#ifndef NVFP4_ROWS_SYNC_EVERY
+#define NVFP4_ROWS_SYNC_EVERY 2
+#endif
+constexpr int kRowsSyncEvery = NVFP4_ROWS_SYNC_EVERY;
 // One workgroup of 16 waves per compute unit: the 16 consecutive chunks a
 // workgroup handles in one round write whole 128-byte lines of the bitmap
 // (16 x 8 bytes) and of the scales from one XCD, and the error sum takes one

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
   double acc = 0.0;
 
   // Chunks past the end read as zeros (range-checked buffer loads); ch stays
-  // below nchunks + (kRowsDepth + 1) * nwaves, so ch * 2048 cannot wrap.
+  // below nchunks + 2 * nwaves, so ch * 2048 cannot wrap.
   struct Two {
     u32x4 a, b;
   };
@@ -116,21 +116,20 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
     return t;
   };
 
-  if constexpr (kRowsDepth == 0) {
-    for (uint32_t ch = first; ch < nchunks; ch += nwaves) process(ch, load(ch));
-  } else {
-    Two buf[kRowsDepth > 0 ? kRowsDepth : 1];
-#pragma unroll
-    for (int k = 0; k < kRowsDepth; ++k) buf[k] = load(first + k * nwaves);
-    for (uint32_t base = first; base < nchunks; base += kRowsDepth * nwaves) {
-#pragma unroll
-      for (int k = 0; k < kRowsDepth; ++k) {
-        const uint32_t ch = base + k * nwaves;
-        const Two w = buf[k];
-        buf[k] = prefetch(ch + kRowsDepth * nwaves);
-        if (ch >= nchunks) break;  // wave-uniform
-        process(ch, w);
-      }
+  // Every wave runs the same number of steps (a chunk index past the end is
+  // skipped, wave-uniformly), so the workgroup can meet at a barrier every
+  // kRowsSyncEvery steps.  Measured on MI355X: without it the 16 waves of a
+  // compute unit drift apart over the tensor and their loads spread over
+  // more DRAM pages; with it the kernel runs about 10% faster.
+  const uint32_t steps = (nchunks + nwaves - 1) / nwaves;
+  Two buf = load(first);
+  for (uint32_t k = 0; k < steps; ++k) {
+    const uint32_t ch = first + k * nwaves;
+    const Two w = buf;
+    buf = prefetch(ch + nwaves);
+    if (ch < nchunks) process(ch, w);
+    if constexpr (kRowsSyncEvery > 0) {
+      if (k % kRowsSyncEvery == kRowsSyncEvery - 1) __syncthreads();
     }
   }
 

@@ -237,6 +237,30 @@ def test_dequantize_round_trip(axis, shape, dtype):
     np.testing.assert_array_equal(got, want.view(got.dtype))
 
 
+@pytest.mark.parametrize("axis", [AXIS_COLS, AXIS_ROWS])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_tiny_scales_and_ragged(axis, dtype):
+    """Blocks spanning many decades near the bottom of the binary32 range, so
+    decoded values include binary32 and bf16 subnormals; the row layout has a
+    partial last chunk (37*80/16 = 185 blocks)."""
+    banner(f"dequantize tiny axis={axis} {dtype}")
+    rows, cols = (37, 80) if axis == AXIS_COLS else (80, 37)
+    rng = np.random.default_rng(7)
+    mag = 10.0 ** rng.uniform(-38, -33, (rows * cols) // 16)
+    v = (rng.standard_normal(rows * cols) * np.repeat(mag, 16)).astype(np.float32)
+    x = ((v.view(np.uint32) + 0x8000) >> 16).astype(np.uint16).reshape(rows, cols)
+    ref = oracle.quantize(x, axis, F46, MSE)
+    want = oracle.dequantize(ref["packed"], ref["scales"], ref["gscale"], rows, cols, axis,
+                             out_bf16=dtype == torch.bfloat16)
+    assert np.any((want.view(np.float32 if dtype == torch.float32 else np.uint16) != 0))
+    p = torch.from_numpy(ref["packed"]).cuda()
+    s = torch.from_numpy(ref["scales"]).cuda()
+    g = torch.tensor([ref["gscale"]], dtype=torch.float32, device="cuda")
+    out = nv.dequantize(p, s, g, rows, cols, axis, dtype)
+    got = out.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+    np.testing.assert_array_equal(got, want.view(got.dtype))
+
+
 def test_round_trip_config1_through_gpu_outputs():
     banner("config 1 round trip")
     x = testkit.make(1)
