@@ -5,11 +5,11 @@
 // are laid out as the row-blocked outputs of the transposed tensor: codes
 // [cols][rows/2], scales [cols][rows/16], bitmap bit c*(rows/16) + rb.
 //
-// Tiles of 256 rows x 64 columns.  Per tile a workgroup of 4 waves
+// Tiles of 256 rows x 64 columns.  Per tile a workgroup of 8 waves
 //   1. has the tile's 256 row segments of 128 contiguous bytes in registers
-//      (8 x 16-byte loads per lane, issued kColsDepth tiles ahead so they
+//      (4 x 16-byte loads per lane, issued kColsDepth tiles ahead so they
 //      are in flight while earlier tiles are computed) and writes them row-major
-//      into LDS with 16-byte writes (row pitch 144 bytes, 16-byte aligned);
+//      into LDS (row pitch 136 bytes, see the pitches below);
 //   2. lets every lane read a column pair over 16 rows (16 x 4-byte LDS
 //      reads, consecutive banks across each half-wave), which are two whole
 //      blocks; the lane repacks them and runs the same whole-block quantizer
@@ -45,12 +45,39 @@ constexpr int kColsOrder = NVFP4_COLS_ORDER;
 constexpr int kTileRows = 256;
 constexpr int kTileCols = 64;
 constexpr int kRowBlocks = kTileRows / 16;  // 16 row blocks per tile
-constexpr int kInPitch = 144;               // LDS bytes per tile row (128 + 16)
-constexpr int kCodePitch = 144;             // LDS bytes per column of codes (128 + 16)
-constexpr int kLoadsPerLane = kTileRows * kTileCols * 2 / (kThreads * 16);  // 8
+// LDS pitches, chosen against bank conflicts (64 banks of 4 bytes):
+//  - tile rows of 136 bytes (34 dwords): the two half-waves' column-pair
+//    reads are 16 rows apart, 16 * 34 = 544 = 32 (mod 64) dwords, so they
+//    fall in disjoint banks; rows are 8-byte aligned (two 8-byte writes);
+//  - code columns of 132 bytes (33 dwords): the 32 columns 2cp written by a
+//    half-wave start 66 cp = 2 cp (mod 64) dwords apart, all distinct;
+//  - scale-byte columns of 20 bytes: 10 cp (mod 64) dwords, all distinct.
+#ifndef NVFP4_COLS_IN_PITCH
+#define NVFP4_COLS_IN_PITCH 136
+#endif
+#ifndef NVFP4_COLS_CODE_PITCH
+#define NVFP4_COLS_CODE_PITCH 132
+#endif
+#ifndef NVFP4_COLS_S_PITCH
+#define NVFP4_COLS_S_PITCH 20
+#endif
+constexpr int kInPitch = NVFP4_COLS_IN_PITCH;
+constexpr int kCodePitch = NVFP4_COLS_CODE_PITCH;
+constexpr int kSPitch = NVFP4_COLS_S_PITCH;
+static_assert(kInPitch % 8 == 0 && kCodePitch % 4 == 0 && kSPitch % 4 == 0, "LDS alignment");
+#ifndef NVFP4_COLS_THREADS
+#define NVFP4_COLS_THREADS 512
+#endif
+constexpr int kColsThreads = NVFP4_COLS_THREADS;
+constexpr int kColsWaves = kColsThreads / 64;
+constexpr int kLoadsPerLane = kTileRows * kTileCols * 2 / (kColsThreads * 16);
+constexpr int kLoadRows = kColsThreads / 8;        // tile rows covered by one load
+constexpr int kPasses = 512 / kColsThreads;        // column-pair tasks per lane
+static_assert(kColsThreads == 256 || kColsThreads == 512, "tile mapping");
+
 
 template <uint32_t V>
-__global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
+__global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     const uint16_t* __restrict__ in, int64_t rows, int64_t cols, const float* __restrict__ gscale,
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
     double* __restrict__ err_sum) {
@@ -63,8 +90,8 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
   __shared__ float2 tab[128];
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileRows * kInPitch];
   __shared__ __attribute__((aligned(16))) uint8_t codes[kTileCols * kCodePitch];
-  __shared__ __attribute__((aligned(16))) uint8_t sbytes[kTileCols * kRowBlocks];
-  __shared__ double wsum[kWavesPerGroup];
+  __shared__ __attribute__((aligned(16))) uint8_t sbytes[kTileCols * kSPitch];
+  __shared__ double wsum[kColsWaves];
 
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
@@ -91,7 +118,8 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
   const uint32_t wg =
       (nwg % 8u == 0u) ? (blockIdx.x % 8u) * (nwg / 8u) + blockIdx.x / 8u : blockIdx.x;
 
-  // Load k of lane t covers tile row k*32 + t/8, columns (t%8)*8 .. +7.
+  // Load k of lane t covers tile row k * kLoadRows + t/8, columns
+  // (t%8)*8 .. +7.
   const int lrow = t >> 3, lseg = t & 7;
   auto tile_of = [&](int64_t tt, int64_t& strip, int64_t& rt) {
     if (kColsOrder == 0) {
@@ -108,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
     const int64_t r0 = rt * kTileRows, c = strip * kTileCols + lseg * 8;
 #pragma unroll
     for (int k = 0; k < kLoadsPerLane; ++k) {
-      const int64_t r = r0 + k * 32 + lrow;
+      const int64_t r = r0 + k * kLoadRows + lrow;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (tt < ntiles && r < rows) {
         const uint16_t* src = in + r * cols + c;
@@ -136,16 +164,20 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
 
     __syncthreads();  // the previous tile's staging has been stored (and tab built)
 #pragma unroll
-    for (int k = 0; k < kLoadsPerLane; ++k)
-      *reinterpret_cast<u32x4*>(&tile[(k * 32 + lrow) * kInPitch + lseg * 16]) = w[k];
+    for (int k = 0; k < kLoadsPerLane; ++k) {
+      u32x2* dst = reinterpret_cast<u32x2*>(&tile[(k * kLoadRows + lrow) * kInPitch + lseg * 16]);
+      dst[0] = u32x2{w[k].x, w[k].y};
+      dst[1] = u32x2{w[k].z, w[k].w};
+    }
     __syncthreads();
     load_tile(tt + kColsDepth * nwg, w);  // in flight during the next tiles' compute
 
-    // 16 row blocks x 32 column pairs = 512 lane tasks, two per lane: in pass
-    // p, wave w takes row block p*8 + w*2 + lane/32 and column pair lane%32.
+    // 16 row blocks x 32 column pairs = 512 lane tasks, kPasses per lane:
+    // in pass p, wave w takes row block (p * kColsWaves + w) * 2 + lane/32
+    // and column pair lane%32.
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int rb = p * 8 + wave * 2 + (lane >> 5);
+    for (int p = 0; p < kPasses; ++p) {
+      const int rb = (p * kColsWaves + wave) * 2 + (lane >> 5);
       const int cp = lane & 31;
       uint32_t v[16];
 #pragma unroll
@@ -165,10 +197,14 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
       pa.y = qa.hi;
       pb.x = qb.lo;
       pb.y = qb.hi;
-      *reinterpret_cast<u32x2*>(&codes[ca * kCodePitch + rb * 8]) = pa;
-      *reinterpret_cast<u32x2*>(&codes[cb * kCodePitch + rb * 8]) = pb;
-      sbytes[ca * kRowBlocks + rb] = (uint8_t)(qa.S | (kSel && qa.pick4 ? 0x80u : 0u));
-      sbytes[cb * kRowBlocks + rb] = (uint8_t)(qb.S | (kSel && qb.pick4 ? 0x80u : 0u));
+      uint32_t* ka = reinterpret_cast<uint32_t*>(&codes[ca * kCodePitch + rb * 8]);
+      uint32_t* kb = reinterpret_cast<uint32_t*>(&codes[cb * kCodePitch + rb * 8]);
+      ka[0] = pa.x;
+      ka[1] = pa.y;
+      kb[0] = pb.x;
+      kb[1] = pb.y;
+      sbytes[ca * kSPitch + rb] = (uint8_t)(qa.S | (kSel && qa.pick4 ? 0x80u : 0u));
+      sbytes[cb * kSPitch + rb] = (uint8_t)(qb.S | (kSel && qb.pick4 ? 0x80u : 0u));
       if (kErr && rb < nrb) {
         if (ca < ncol) acc += (double)qa.err;
         if (cb < ncol) acc += (double)qb.err;
@@ -176,13 +212,14 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
     }
     __syncthreads();
 
-    // Codes: column c's nrb * 8 bytes go to packed[c][r0/2 ..]; in each of
-    // two passes lane t stores 16 bytes (two row blocks) of column t/8.
+    // Codes: column c's nrb * 8 bytes go to packed[c][r0/2 ..]; in each pass
+    // lane t stores 16 bytes (two row blocks) of column p * kLoadRows + t/8.
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int c = p * 32 + (t >> 3), seg = t & 7;
+    for (int p = 0; p < kPasses; ++p) {
+      const int c = p * kLoadRows + (t >> 3), seg = t & 7;
       if (c < ncol && 2 * seg < nrb) {
-        const u32x4 cw = *reinterpret_cast<const u32x4*>(&codes[c * kCodePitch + seg * 16]);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(&codes[c * kCodePitch + seg * 16]);
+        const u32x4 cw = {src[0], src[1], src[2], src[3]};
         uint8_t* dst = packed + (c0 + c) * (rows / 2) + r0 / 2 + seg * 16;
         const bool both = 2 * seg + 1 < nrb;
         if (codes16 && both) {
@@ -200,8 +237,8 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
     }
     // Scale bytes (and bitmap bytes): lane t < 64 handles column t.
     if (t < ncol) {
-      const u32x4 sw = *reinterpret_cast<const u32x4*>(&sbytes[t * kRowBlocks]);
-      uint32_t s[4] = {sw.x, sw.y, sw.z, sw.w};
+      const uint32_t* sw = reinterpret_cast<const uint32_t*>(&sbytes[t * kSPitch]);
+      uint32_t s[4] = {sw[0], sw[1], sw[2], sw[3]};
       uint32_t bits = 0u;
       if (kSel && sel_direct) {
 #pragma unroll
@@ -250,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void quantize_cols_kernel(
     __syncthreads();
     if (t == 0) {
       double s = wsum[0];
-      for (int k = 1; k < kWavesPerGroup; ++k) s += wsum[k];
+      for (int k = 1; k < kColsWaves; ++k) s += wsum[k];
       unsafeAtomicAdd(err_sum, s);
     }
   }
@@ -282,17 +319,17 @@ template <uint32_t V>
 static hipError_t launch_cols_v(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint8_t* packed, uint8_t* scales,
                                 uint8_t* selmap, double* err_sum, hipStream_t s, Events ev) {
+  constexpr bool kSel = (V & kVarSelmap) != 0;
+  const bool two_pass = kSel && (rows / 16) % 8 != 0;
+  // With a second bitmap pass, that kernel ends the event bracket.
+  const Events first{ev.start, two_pass ? nullptr : ev.stop};
   const int64_t ntiles =
       ((cols + kTileCols - 1) / kTileCols) * ((rows + kTileRows - 1) / kTileRows);
   int64_t groups = (int64_t)device_cu_count() * kColsGroupsPerCu;
   if (groups > ntiles) groups = ntiles;
   if (groups < 1) groups = 1;
-  constexpr bool kSel = (V & kVarSelmap) != 0;
-  const bool two_pass = kSel && (rows / 16) % 8 != 0;
-  // With a second bitmap pass, that kernel ends the event bracket.
-  const Events first{ev.start, two_pass ? nullptr : ev.stop};
   hipError_t e = launch_with_events(quantize_cols_kernel<V>, dim3((unsigned)groups),
-                                    dim3(kThreads), s, first, in, rows, cols, gscale, packed,
+                                    dim3(kColsThreads), s, first, in, rows, cols, gscale, packed,
                                     scales, selmap, err_sum);
   if (e != hipSuccess || !two_pass) return e;
   const int64_t nblocks = rows / 16 * cols;
