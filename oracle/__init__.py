@@ -12,7 +12,7 @@ import numpy as np
 from . import build as _build
 
 MODE_STD, MODE_4OVER6 = 0, 1
-RULE_MSE, RULE_MAE = 0, 1
+RULE_MSE, RULE_MAE, RULE_MAX = 0, 1, 2
 AXIS_ROWS, AXIS_COLS = 0, 1
 
 _lib = None

@@ -14,7 +14,8 @@
  *        - "Core mechanism": the 4/6 alternative maps the block max to 4.
  *        - "Adaptive block scaling algorithm": quantize each block twice (max->6
  *          and max->4), measure both errors against the original values, keep
- *          the candidate with the smaller error (MSE or MAE rule).
+ *          the candidate with the smaller error.  The page evaluates three
+ *          rules: minimum maximum error, minimum MAE, minimum MSE.
  *        - "Implementation details": block scales are FP8 E4M3; under 4/6 the
  *          per-tensor scale is formed with 256 in place of 448.
  *  [MIN] "Why Gated DeltaNet in hybrid 27B LLMs withstands 4-bit quantization"
@@ -37,6 +38,7 @@
  *                reconstruction against the original value, rounded once)
  *   block error: two sequential halves of 8 elements (lo, hi), e = RN(lo + hi)
  *                MSE: h = fma(delta, delta, h)      MAE: h = RN(h + |delta|)
+ *                MAX: e = max |delta| over the block (exact, order-free)
  *   selection:   c* = 4 iff e_4 < e_6 (ties and NaN go to 6)
  * RN is one IEEE-754 binary32 operation with round-to-nearest-even.
  *
@@ -204,9 +206,10 @@ void nvfp4o_quantize_block(const float x[16], float g, int mode, int rule,
   const float G = encode_scale_of(g);
   const float cands[2] = {6.0f, 4.0f};
   const int ncand = (mode == NVFP4O_MODE_4OVER6) ? 2 : 1;
-  /* The error measure: MAE only when asked for under 4/6; the standard mode
-   * reports squared error. */
+  /* The error measure: MAE or maximum error only when asked for under 4/6;
+   * the standard mode reports squared error. */
   const int use_mae = (mode == NVFP4O_MODE_4OVER6 && rule == NVFP4O_RULE_MAE);
+  const int use_max = (mode == NVFP4O_MODE_4OVER6 && rule == NVFP4O_RULE_MAX);
 
   float b = 0.0f;
   for (int i = 0; i < 16; ++i) {
@@ -245,12 +248,16 @@ void nvfp4o_quantize_block(const float x[16], float g, int mode, int rule,
       out->xhat[c][i] = xhat;
       out->delta[c][i] = delta;
       float* h = &half[i >> 3];
-      if (use_mae)
+      if (use_max)
+        *h = fmaxf(*h, fabsf(delta));
+      else if (use_mae)
         *h = *h + fabsf(delta);
       else
         *h = fmaf(delta, delta, *h);
     }
-    out->err[c] = half[0] + half[1];
+    /* Minimum-maximum-error rule [FOS, "Adaptive block scaling algorithm"]:
+     * the block error is the largest |delta|, the larger of the halves'. */
+    out->err[c] = use_max ? fmaxf(half[0], half[1]) : half[0] + half[1];
   }
   out->chosen = 0;
   if (ncand == 2 && out->err[1] < out->err[0]) out->chosen = 1;
@@ -264,7 +271,8 @@ static int check_args(int64_t rows, int64_t cols, int block_axis, int mode, int 
   if (rows <= 0 || cols <= 0) return NVFP4O_ERR_SHAPE;
   if (block_axis != NVFP4O_AXIS_ROWS && block_axis != NVFP4O_AXIS_COLS) return NVFP4O_ERR_ENUM;
   if (mode != NVFP4O_MODE_STD && mode != NVFP4O_MODE_4OVER6) return NVFP4O_ERR_ENUM;
-  if (rule != NVFP4O_RULE_MSE && rule != NVFP4O_RULE_MAE) return NVFP4O_ERR_ENUM;
+  if (rule != NVFP4O_RULE_MSE && rule != NVFP4O_RULE_MAE && rule != NVFP4O_RULE_MAX)
+    return NVFP4O_ERR_ENUM;
   if (block_axis == NVFP4O_AXIS_COLS && cols % 16 != 0) return NVFP4O_ERR_SHAPE;
   if (block_axis == NVFP4O_AXIS_ROWS && rows % 16 != 0) return NVFP4O_ERR_SHAPE;
   return NVFP4O_OK;

@@ -22,7 +22,7 @@ enum {
  * a column (results stored in the layout of the transposed tensor). */
 enum { NVFP4O_AXIS_ROWS = 0, NVFP4O_AXIS_COLS = 1 };
 enum { NVFP4O_MODE_STD = 0, NVFP4O_MODE_4OVER6 = 1 };
-enum { NVFP4O_RULE_MSE = 0, NVFP4O_RULE_MAE = 1 };
+enum { NVFP4O_RULE_MSE = 0, NVFP4O_RULE_MAE = 1, NVFP4O_RULE_MAX = 2 };
 
 /* Everything the oracle computes for one 16-element block.  Candidate index 0
  * maps the block max to 6, index 1 maps it to 4 (4/6 mode only). */
@@ -38,7 +38,7 @@ typedef struct {
   uint8_t code[2][16];
   float xhat[2][16]; /* reconstructed values RN(v * d) */
   float delta[2][16]; /* fma(v, d, -x) */
-  float err[2];      /* block error (SSE, or SAE under the MAE rule) */
+  float err[2];      /* block error (SSE; SAE under the MAE rule; max |delta| under MAX) */
   int chosen;        /* 0 -> max mapped to 6, 1 -> max mapped to 4 */
 } nvfp4o_block_t;
 

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import testkit
-from oracle import AXIS_COLS, AXIS_ROWS, MODE_4OVER6, MODE_STD, RULE_MAE, RULE_MSE
+from oracle import AXIS_COLS, AXIS_ROWS, MODE_4OVER6, MODE_STD, RULE_MAE, RULE_MAX, RULE_MSE
 
 F32 = testkit.bf16_to_f32
 
@@ -125,6 +125,62 @@ def test_kept_candidate_has_smaller_error_binary64(rule):
     assert decided > 300
 
 
+def test_max_rule_error_is_largest_single_rounding_difference():
+    """Minimum-maximum-error rule ("Technical summary: Four Over Six (4/6)",
+    "Adaptive block scaling algorithm"): each candidate's error is the largest
+    |v*d - x| over the block.  v*d - x is exact in binary64 (v has 2
+    significant bits, d 24, x 8), so its single rounding to binary32 is
+    np.float32 of the binary64 value; the maximum is exact."""
+    rng = np.random.default_rng(41)
+    decided = 0
+    for _ in range(400):
+        x = (rng.standard_t(3, size=16) * 0.5).astype(np.float32)
+        x = F32(torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+        g = np.float32(np.abs(x).max() * rng.uniform(0.9, 3.0) / 1536)
+        q = oracle.quantize_block(x, g, MODE_4OVER6, RULE_MAX)
+        errs = []
+        for c in range(2):
+            d = float(np.float32(float(e4m3_values(q.S[c])) * float(g)))  # d = RN(dec(S) * g)
+            assert np.float32(d) == np.float32(q.d[c])
+            dlt = e2m1_values(np.array(q.code[c])) * d - x.astype(np.float64)
+            errs.append(np.max(np.abs(dlt.astype(np.float32))))
+            assert np.float32(q.err[c]) == errs[-1]
+        assert q.chosen == int(errs[1] < errs[0])  # exact: ties keep max->6
+        decided += errs[0] != errs[1]
+    assert decided > 300
+
+
+def test_max_rule_bounds_and_invariances():
+    """max |delta| lies between sqrt(SSE/16) and sqrt(SSE) of the same
+    candidate, scales exactly with powers of two and ignores the sign."""
+    x = small(77, 4, 64, dist=testkit.STUDENT_T3).reshape(-1, 16)
+    for blk in x:
+        xf = F32(blk)
+        g = np.float32(np.abs(xf).max() / 1536)
+        qm = oracle.quantize_block(xf, g, MODE_4OVER6, RULE_MAX)
+        qs = oracle.quantize_block(xf, g, MODE_4OVER6, RULE_MSE)
+        for c in range(2):
+            assert list(qm.code[c]) == list(qs.code[c])  # the rule changes only the choice
+            sse = float(np.sum(np.square(np.array(qs.delta[c], np.float64))))
+            assert np.sqrt(sse / 16) * (1 - 1e-6) <= qm.err[c] <= np.sqrt(sse) * (1 + 1e-6)
+        q2 = oracle.quantize_block(xf * np.float32(4), g * np.float32(4), MODE_4OVER6, RULE_MAX)
+        qn = oracle.quantize_block(-xf, g, MODE_4OVER6, RULE_MAX)
+        for c in range(2):
+            assert q2.err[c] == np.float32(4) * qm.err[c]
+            assert qn.err[c] == qm.err[c]
+        assert q2.chosen == qm.chosen == qn.chosen
+
+
+def test_max_rule_on_the_three_quarters_block():
+    """The block of the 'Core mechanism' worked fact ([4, 3, -3, 0, ...],
+    g = 1): max->6 reconstructs 4.125, 2.75, -2.75 (largest error 0.25),
+    max->4 reconstructs exactly, so the max rule keeps max->4 as well."""
+    x = np.zeros(16, np.float32)
+    x[:3] = [4.0, 3.0, -3.0]
+    q = oracle.quantize_block(x, 1.0, MODE_4OVER6, RULE_MAX)
+    assert q.err[0] == np.float32(0.25) and q.err[1] == 0.0 and q.chosen == 1
+
+
 def test_tie_goes_to_scale6():
     x = np.zeros(16, np.float32)  # both candidates have zero error
     q = oracle.quantize_block(x, 1.0, MODE_4OVER6, RULE_MSE)
@@ -138,13 +194,18 @@ def test_tie_goes_to_scale6():
 # ------------------------------------------------------------ statistics ----
 
 @pytest.mark.parametrize("mode,rule", [(MODE_STD, RULE_MSE), (MODE_4OVER6, RULE_MSE),
-                                       (MODE_4OVER6, RULE_MAE)])
+                                       (MODE_4OVER6, RULE_MAE), (MODE_4OVER6, RULE_MAX)])
 def test_err_sum_equals_binary64_recompute(mode, rule):
     x = small(303, 32, 512, dist=testkit.STUDENT_T3)
     r = oracle.quantize(x, AXIS_COLS, mode, rule)
     xhat = oracle.dequantize(r["packed"], r["scales"], r["gscale"], 32, 512, AXIS_COLS)
     dlt = xhat.astype(np.float64) - F32(x).astype(np.float64)
-    want = np.sum(np.abs(dlt)) if rule == RULE_MAE and mode == MODE_4OVER6 else np.sum(dlt * dlt)
+    if mode == MODE_4OVER6 and rule == RULE_MAE:
+        want = np.sum(np.abs(dlt))
+    elif mode == MODE_4OVER6 and rule == RULE_MAX:  # sum over blocks of the block maximum
+        want = np.sum(np.max(np.abs(dlt).reshape(-1, 16), axis=1))
+    else:
+        want = np.sum(dlt * dlt)
     assert r["err_sum"] == pytest.approx(want, rel=1e-6)
 
 
