@@ -11,8 +11,9 @@
  *     scaling: "Technical summary: Four Over Six (4/6)" (gist.science
  *     2512.02010), "Problem statement";
  *   - the max->4 alternative, quantizing each block both ways and keeping the
- *     one with lower MSE or MAE: same page, "Core mechanism" and "Adaptive
- *     block scaling algorithm";
+ *     one with the lower error under one of three rules (maximum error, MAE,
+ *     MSE): same page, "Core mechanism" and "Adaptive block scaling
+ *     algorithm";
  *   - E4M3 block scales and the tensor scale formed with 256 instead of 448
  *     under 4/6: same page, "Implementation details".
  *
@@ -25,10 +26,11 @@
  *     d_c = dec(S_c) * g              decode multiplier
  *     r_c = min(G * (1/dec(S_c)), FLT_MAX), and 0 when S_c == 0
  *     code_i = sign(x_i) | E2M1(|x_i * r_c|)   nearest even, saturating at 6
- *     e_c = sum of delta_i^2 (MSE) or of |delta_i| (MAE), delta_i =
- *           dec(code_i) * d_c - x_i evaluated exactly and rounded once (fused
- *           multiply-add), summed as two sequential halves of 8 elements
- *           (fused multiply-add for the squares) and then added
+ *     e_c = sum of delta_i^2 (MSE), of |delta_i| (MAE), or max |delta_i|
+ *           (maximum error), delta_i = dec(code_i) * d_c - x_i evaluated
+ *           exactly and rounded once (fused multiply-add); sums run as two
+ *           sequential halves of 8 elements (fused multiply-add for the
+ *           squares) and are then added; the maximum is exact
  *   keep c = 4 iff e_4 < e_6 (ties go to 6).
  *
  * Conventions shared by every call:
@@ -75,7 +77,7 @@ typedef enum nvfp4_status {
 
 enum { NVFP4_AXIS_ROWS = 0, NVFP4_AXIS_COLS = 1 };
 enum { NVFP4_MODE_STD = 0, NVFP4_MODE_4OVER6 = 1 };
-enum { NVFP4_RULE_MSE = 0, NVFP4_RULE_MAE = 1 }; /* ignored for NVFP4_MODE_STD */
+enum { NVFP4_RULE_MSE = 0, NVFP4_RULE_MAE = 1, NVFP4_RULE_MAX = 2 }; /* ignored for NVFP4_MODE_STD */
 enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
 enum {
   NVFP4_FLAG_GSCALE_GIVEN = 1u,   /* use *gscale_inout as g; skip the amax pass          */
@@ -114,11 +116,13 @@ nvfp4_status nvfp4_quantize(const uint16_t* in_bf16, int64_t rows, int64_t cols,
  *   err_sum_out (nullable): one double that receives the sum over blocks of
  *     the kept candidate's block error -- squared error under
  *     NVFP4_RULE_MSE and in standard mode, absolute error under
- *     NVFP4_RULE_MAE -- accumulated in binary64 in an unspecified order.
+ *     NVFP4_RULE_MAE, the block's largest absolute error under
+ *     NVFP4_RULE_MAX -- accumulated in binary64 in an unspecified order.
  *     The call zeroes it first unless flags has NVFP4_FLAG_ERR_ACCUMULATE,
  *     in which case the sum is added to its current value (e.g. a total over
  *     several tensors, or a value the caller zeroed on the same stream).
- *     Divide by rows*cols for the per-tensor MSE / MAE. */
+ *     Divide by rows*cols for the per-tensor MSE / MAE (by the number of
+ *     blocks for the mean block maximum error). */
 nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t cols,
                                int block_axis, int mode, int rule, uint32_t flags,
                                uint8_t* packed_out, uint8_t* scales_out, float* gscale_inout,

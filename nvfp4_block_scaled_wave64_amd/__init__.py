@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libnvfp4.so")
 
 AXIS_ROWS, AXIS_COLS = 0, 1
 MODE_STD, MODE_4OVER6 = 0, 1
-RULE_MSE, RULE_MAE = 0, 1
+RULE_MSE, RULE_MAE, RULE_MAX = 0, 1, 2
 OUT_F32, OUT_BF16 = 0, 1
 FLAG_GSCALE_GIVEN = 1
 FLAG_ERR_ACCUMULATE = 2

@@ -88,7 +88,8 @@ nvfp4_status quantize_impl(const uint16_t* in_bf16, int64_t rows, int64_t cols, 
   if (!in_bf16 || !packed_out || !scales_out || !gscale_inout) return NVFP4_ERR_NULL;
   if (block_axis != NVFP4_AXIS_ROWS && block_axis != NVFP4_AXIS_COLS) return NVFP4_ERR_ENUM;
   if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
-  if (rule != NVFP4_RULE_MSE && rule != NVFP4_RULE_MAE) return NVFP4_ERR_ENUM;
+  if (rule != NVFP4_RULE_MSE && rule != NVFP4_RULE_MAE && rule != NVFP4_RULE_MAX)
+    return NVFP4_ERR_ENUM;
   if (flags & ~uint32_t(NVFP4_FLAG_GSCALE_GIVEN | NVFP4_FLAG_ERR_ACCUMULATE))
     return NVFP4_ERR_ENUM;
   const nvfp4_status shape = check_shape(rows, cols, block_axis);
@@ -104,6 +105,7 @@ nvfp4_status quantize_impl(const uint16_t* in_bf16, int64_t rows, int64_t cols, 
   if (mode == NVFP4_MODE_4OVER6) {
     variant |= nvfp4::kVarFourOverSix;
     if (rule == NVFP4_RULE_MAE) variant |= nvfp4::kVarMae;
+    if (rule == NVFP4_RULE_MAX) variant |= nvfp4::kVarMax;
   }
   if (selmap_out) variant |= nvfp4::kVarSelmap;
   if (err_sum_out) variant |= nvfp4::kVarErr;

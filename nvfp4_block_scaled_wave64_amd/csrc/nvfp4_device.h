@@ -175,11 +175,16 @@ struct Block16 {
   float err;        // kept candidate's block error
 };
 
+// Error measure of a candidate (the method's three selection rules:
+// "Technical summary: Four Over Six (4/6)", "Adaptive block scaling
+// algorithm").
+enum : int { kRuleMse = 0, kRuleMae = 1, kRuleMax = 2 };
+
 // Error of one candidate over 8 elements (x) given its codes (w) and decode
-// multiplier d: sequential sum of squared (or absolute) differences between
-// the candidate's reconstruction v * d and x, each difference evaluated
-// exactly and rounded once (fused multiply-add).
-template <bool kMae>
+// multiplier d: sequential sum of squared (or absolute) differences, or
+// their maximum, between the candidate's reconstruction v * d and x, each
+// difference evaluated exactly and rounded once (fused multiply-add).
+template <int kRule>
 __device__ __forceinline__ float half_error(const float* x, uint32_t w, float d) {
   float v[8];
   e2m1_decode8(w, v);
@@ -187,9 +192,21 @@ __device__ __forceinline__ float half_error(const float* x, uint32_t w, float d)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float dl = __builtin_fmaf(v[i], d, -x[i]);
-    h = kMae ? h + fabsf(dl) : __builtin_fmaf(dl, dl, h);
+    if (kRule == kRuleMax)
+      h = __builtin_elementwise_maximum(h, fabsf(dl));
+    else if (kRule == kRuleMae)
+      h = h + fabsf(dl);
+    else
+      h = __builtin_fmaf(dl, dl, h);
   }
   return h;
+}
+
+// Block error from the two halves: their sum, or the larger for the
+// maximum-error rule.
+template <int kRule>
+__device__ __forceinline__ float block_error(float lo, float hi) {
+  return kRule == kRuleMax ? __builtin_elementwise_maximum(lo, hi) : lo + hi;
 }
 
 // One block of 16 elements in one lane: wd[0..7] are its bf16 values
@@ -198,8 +215,9 @@ __device__ __forceinline__ float half_error(const float* x, uint32_t w, float d)
 // error against the original values, selection ("Technical summary: Four
 // Over Six (4/6)", "Adaptive block scaling algorithm") -- with each
 // candidate's error summed over elements 0-7 and 8-15 sequentially and the
-// two partial sums then added.
-template <bool k46, bool kMae, bool kNeedErr>
+// two partial sums then added (or, for the maximum-error rule, the largest
+// single difference).
+template <bool k46, int kRule, bool kNeedErr>
 __device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float k6, float k4,
                                                     const float2* tab) {
   float x[16];
@@ -224,7 +242,8 @@ __device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float 
   for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t6.y;
   const uint32_t c6hi = e2m1_encode8(y);
   float e6 = 0.0f;
-  if (kNeedErr) e6 = half_error<kMae>(x, c6lo, t6.x) + half_error<kMae>(x + 8, c6hi, t6.x);
+  if (kNeedErr)
+    e6 = block_error<kRule>(half_error<kRule>(x, c6lo, t6.x), half_error<kRule>(x + 8, c6hi, t6.x));
 
   Block16 r;
   r.lo = c6lo;
@@ -240,7 +259,8 @@ __device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float 
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t4.y;
     const uint32_t c4hi = e2m1_encode8(y);
-    const float e4 = half_error<kMae>(x, c4lo, t4.x) + half_error<kMae>(x + 8, c4hi, t4.x);
+    const float e4 =
+        block_error<kRule>(half_error<kRule>(x, c4lo, t4.x), half_error<kRule>(x + 8, c4hi, t4.x));
     r.pick4 = e4 < e6;  // ties and NaN keep max->6
     r.lo = r.pick4 ? c4lo : c6lo;
     r.hi = r.pick4 ? c4hi : c6hi;

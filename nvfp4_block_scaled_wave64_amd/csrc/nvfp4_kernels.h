@@ -64,6 +64,7 @@ constexpr int kGroupsPerCu = NVFP4_ROWS_WAVES_PER_CU / kRowsWaves;
 enum : uint32_t {
   kVarFourOverSix = 1u,  // two candidates (max->6, max->4) instead of max->6 only
   kVarMae = 2u,          // MAE selection rule instead of MSE
+  kVarMax = 16u,         // minimum-maximum-error selection rule instead of MSE
   kVarSelmap = 4u,       // write the selection bitmap
   kVarErr = 8u,          // accumulate the per-tensor error sum
 };

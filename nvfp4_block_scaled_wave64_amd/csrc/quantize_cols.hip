@@ -82,7 +82,10 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
     double* __restrict__ err_sum) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
-  constexpr bool kMae = k46 && (V & kVarMae) != 0;
+  constexpr int kRule = !k46 ? kRuleMse
+                        : (V & kVarMax) ? kRuleMax
+                        : (V & kVarMae) ? kRuleMae
+                                        : kRuleMse;
   constexpr bool kSel = (V & kVarSelmap) != 0;
   constexpr bool kErr = (V & kVarErr) != 0;
   constexpr bool kNeedErr = k46 || kErr;
@@ -189,8 +192,8 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
         wa[j] = (v[2 * j] & 0xFFFFu) | (v[2 * j + 1] << 16);
         wb[j] = (v[2 * j] >> 16) | (v[2 * j + 1] & 0xFFFF0000u);
       }
-      const Block16 qa = quantize_block16<k46, kMae, kNeedErr>(wa, ts.k6, ts.k4, tab);
-      const Block16 qb = quantize_block16<k46, kMae, kNeedErr>(wb, ts.k6, ts.k4, tab);
+      const Block16 qa = quantize_block16<k46, kRule, kNeedErr>(wa, ts.k6, ts.k4, tab);
+      const Block16 qb = quantize_block16<k46, kRule, kNeedErr>(wb, ts.k6, ts.k4, tab);
       const int ca = 2 * cp, cb = 2 * cp + 1;
       u32x2 pa, pb;
       pa.x = qa.lo;
@@ -360,6 +363,10 @@ hipError_t launch_quantize_cols(const uint16_t* in, int64_t rows, int64_t cols,
     NVFP4_COLS_CASE(12)
     NVFP4_COLS_CASE(13)
     NVFP4_COLS_CASE(15)
+    NVFP4_COLS_CASE(17)
+    NVFP4_COLS_CASE(21)
+    NVFP4_COLS_CASE(25)
+    NVFP4_COLS_CASE(29)
     default:
       return hipErrorInvalidValue;
   }

@@ -43,7 +43,10 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
     double* __restrict__ err_sum) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
-  constexpr bool kMae = k46 && (V & kVarMae) != 0;
+  constexpr int kRule = !k46 ? kRuleMse
+                        : (V & kVarMax) ? kRuleMax
+                        : (V & kVarMae) ? kRuleMae
+                                        : kRuleMse;
   constexpr bool kSel = (V & kVarSelmap) != 0;
   constexpr bool kErr = (V & kVarErr) != 0;
   constexpr bool kNeedErr = k46 || kErr;
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
       wd[j] = p[0];
       wd[4 + j] = p[1];
     }
-    const Block16 q = quantize_block16<k46, kMae, kNeedErr>(wd, ts.k6, ts.k4, tab);
+    const Block16 q = quantize_block16<k46, kRule, kNeedErr>(wd, ts.k6, ts.k4, tab);
     u32x2 codes;
     codes.x = q.lo;
     codes.y = q.hi;
@@ -191,6 +194,10 @@ hipError_t launch_quantize_rows(const uint16_t* in, int64_t nblocks, const float
     NVFP4_ROWS_CASE(12)
     NVFP4_ROWS_CASE(13)
     NVFP4_ROWS_CASE(15)
+    NVFP4_ROWS_CASE(17)
+    NVFP4_ROWS_CASE(21)
+    NVFP4_ROWS_CASE(25)
+    NVFP4_ROWS_CASE(29)
     default:
       return hipErrorInvalidValue;
   }

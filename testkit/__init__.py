@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libsynth.so")
 
 NORMAL, STUDENT_T3, LAPLACE, UNIFORM = 0, 1, 2, 3
 MODE_STD, MODE_4OVER6 = 0, 1
-RULE_MSE, RULE_MAE = 0, 1
+RULE_MSE, RULE_MAE, RULE_MAX = 0, 1, 2
 AXIS_ROWS, AXIS_COLS = 0, 1
 
 GAMMA = 0x9E3779B97F4A7C15

@@ -59,7 +59,7 @@ def q(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(in_=None), 1), (dict(packed=None), 1), (dict(scales=None), 1), (dict(g=None), 1),
-    (dict(axis=2), 2), (dict(mode=3), 2), (dict(rule=-1), 2), (dict(flags=4), 2), (dict(flags=8), 2),
+    (dict(axis=2), 2), (dict(mode=3), 2), (dict(rule=-1), 2), (dict(rule=3), 2), (dict(flags=4), 2), (dict(flags=8), 2),
     (dict(rows=0), 3), (dict(cols=-16), 3), (dict(cols=40), 3),
     (dict(axis=nv.AXIS_ROWS, rows=24), 3), (dict(rows=1 << 40, cols=1 << 10), 3),
     (dict(in_=MIS), 4), (dict(sel=ctypes.c_void_p(0x10001)), 4),

@@ -1,0 +1,98 @@
+"""Tensors past the library's per-launch segment limits, checked on sampled
+rows or columns against the oracle (the oracle on the whole 2^30-element
+tensor would take a minute; the rows sampled include every segment seam).
+
+One 65600 x 16384 bf16 tensor (2^30 + 2^20 elements, 2 GiB) covers:
+  * the row quantizer's split at 2^26 blocks (block 2^26 starts row 65536),
+  * the dequantizer's splits at 2^25 and 2^26 blocks,
+  * the amax pass's split at 2^27 16-byte vectors (element 2^30),
+and a 16384 x 65600 view of the same bytes exercises the column-blocked
+kernel's 64-bit addressing on a tensor larger than 2^31 bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_wave64_amd as nv
+import oracle
+import testkit
+
+pytestmark = pytest.mark.gpu
+
+ROWS, COLS = 65600, 16384
+SEAM_ROWS = [0, 1, 32767, 32768, 65535, 65536, 65537, ROWS - 1]  # 2^25 / 2^26 block seams
+
+
+def banner(msg):
+    print(f"\n[gpu-large] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def big():
+    banner(f"generating {ROWS}x{COLS}")
+    x = testkit.fill((ROWS, COLS), testkit.STUDENT_T3, 0.5, 0x5E6)
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    g_ref = oracle.global_scale(oracle.amax(x), nv.MODE_4OVER6)
+    yield x, xd, g_ref
+    del xd
+    torch.cuda.empty_cache()
+
+
+def sample_rows():
+    rng = np.random.default_rng(3)
+    return np.unique(np.concatenate([SEAM_ROWS, rng.integers(0, ROWS, 24)]))
+
+
+def test_large_amax_and_global_scale(big):
+    x, xd, g_ref = big
+    banner("amax over 2^30 + 2^20 elements")
+    a = nv.amax(xd.view(-1))
+    assert a.cpu().numpy()[0].view(np.uint32) == oracle.amax(x).view(np.uint32)
+    r = nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE)
+    assert r["gscale"].cpu().numpy()[0].view(np.uint32) == g_ref.view(np.uint32)
+
+
+def test_large_rowwise_sampled_rows(big):
+    x, xd, g_ref = big
+    banner("row-wise quantize across segment seams")
+    r = nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, selmap=True)
+    torch.cuda.synchronize()
+    pick = sample_rows()
+    ref = oracle.quantize(x[pick], nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, gscale=g_ref,
+                          want_err=False)
+    np.testing.assert_array_equal(r["packed"][torch.from_numpy(pick).cuda()].cpu().numpy()
+                                  .reshape(-1), ref["packed"])
+    np.testing.assert_array_equal(r["scales"][torch.from_numpy(pick).cuda()].cpu().numpy()
+                                  .reshape(-1), ref["scales"])
+    bpr = COLS // 16
+    bits = np.unpackbits(r["selmap"].cpu().numpy(), bitorder="little")[: ROWS * bpr]
+    want = np.unpackbits(ref["selmap"], bitorder="little")[: pick.size * bpr]
+    np.testing.assert_array_equal(bits.reshape(ROWS, bpr)[pick].reshape(-1), want)
+
+    banner("dequantize across segment seams")
+    out = nv.dequantize(r["packed"], r["scales"], r["gscale"], ROWS, COLS, nv.AXIS_COLS,
+                        torch.bfloat16)
+    got = out[torch.from_numpy(pick).cuda()].view(torch.int16).cpu().numpy()
+    deq = oracle.dequantize(ref["packed"], ref["scales"], g_ref, pick.size, COLS, nv.AXIS_COLS,
+                            out_bf16=True)
+    np.testing.assert_array_equal(got, deq.view(np.int16))
+    del out, r
+
+
+def test_large_column_blocked_sampled_columns(big):
+    x, xd, _ = big
+    rows, cols = COLS, ROWS  # the same bytes viewed as 16384 x 65600
+    xv = x.reshape(rows, cols)
+    banner(f"column-blocked {rows}x{cols}")
+    g_ref = oracle.global_scale(oracle.amax(xv), nv.MODE_4OVER6)
+    r = nv.quantize(xd.view(rows, cols), nv.AXIS_ROWS, nv.MODE_4OVER6, nv.RULE_MAE)
+    torch.cuda.synchronize()
+    assert r["gscale"].cpu().numpy()[0].view(np.uint32) == g_ref.view(np.uint32)
+    rng = np.random.default_rng(4)
+    pick = np.unique(np.concatenate([[0, 63, 64, cols - 1], rng.integers(0, cols, 12)]))
+    ref = oracle.quantize(np.ascontiguousarray(xv[:, pick]), nv.AXIS_ROWS, nv.MODE_4OVER6,
+                          nv.RULE_MAE, gscale=g_ref, want_selmap=False, want_err=False)
+    idx = torch.from_numpy(pick).cuda()
+    np.testing.assert_array_equal(r["packed"][idx].cpu().numpy().reshape(-1), ref["packed"])
+    np.testing.assert_array_equal(r["scales"][idx].cpu().numpy().reshape(-1), ref["scales"])
+    del r

@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
 
 AXIS_ROWS, AXIS_COLS = nv.AXIS_ROWS, nv.AXIS_COLS
 STD, F46 = nv.MODE_STD, nv.MODE_4OVER6
-MSE, MAE = nv.RULE_MSE, nv.RULE_MAE
+MSE, MAE, MAXE = nv.RULE_MSE, nv.RULE_MAE, nv.RULE_MAX
+RULES = [(STD, MSE), (F46, MSE), (F46, MAE), (F46, MAXE)]
 
 
 def banner(msg):
@@ -36,6 +37,15 @@ def test_config_full_size(cid):
     check_against_oracle(x, cfg.block_axis, cfg.mode, cfg.rule, what=f"config {cid}")
 
 
+@pytest.mark.parametrize("axis", [AXIS_COLS, AXIS_ROWS])
+def test_max_error_rule_full_size(axis):
+    """The third selection rule of the method (minimum maximum error) on the
+    4096 x 5120 activation workload, in both block layouts."""
+    banner(f"max-error rule 4096x5120 axis={axis}")
+    x = testkit.make(2)
+    check_against_oracle(x, axis, F46, MAXE, what=f"max rule axis={axis}")
+
+
 # ------------------------------------------------------------ ragged ----
 
 RAGGED = [
@@ -45,7 +55,7 @@ RAGGED = [
 
 
 @pytest.mark.parametrize("rows,cols", RAGGED)
-@pytest.mark.parametrize("mode,rule", [(STD, MSE), (F46, MSE), (F46, MAE)])
+@pytest.mark.parametrize("mode,rule", RULES)
 def test_rowwise_ragged(rows, cols, mode, rule):
     banner(f"rowwise {rows}x{cols} mode={mode} rule={rule}")
     x = testkit.fill((rows, cols), testkit.STUDENT_T3, 0.7, 1000 + rows * 7 + cols)
@@ -60,7 +70,7 @@ RAGGED_COLS = [
 
 
 @pytest.mark.parametrize("rows,cols", RAGGED_COLS)
-@pytest.mark.parametrize("mode,rule", [(STD, MSE), (F46, MSE), (F46, MAE)])
+@pytest.mark.parametrize("mode,rule", RULES)
 def test_colblocked_ragged(rows, cols, mode, rule):
     banner(f"colblocked {rows}x{cols} mode={mode} rule={rule}")
     x = testkit.fill((rows, cols), testkit.NORMAL, 1e-3, 2000 + rows * 3 + cols)
@@ -87,7 +97,7 @@ def test_all_zero_and_negative_zero():
     x[3, 63] = 0x8000
     xc = np.zeros((32, 8), np.uint16)
     xc[17, 5] = 0x8000
-    for mode, rule in [(STD, MSE), (F46, MSE), (F46, MAE)]:
+    for mode, rule in RULES:
         gpu, _ = check_against_oracle(x, AXIS_COLS, mode, rule, what="zeros")
         assert gpu["gscale"] == 0 and gpu["err_sum"] == 0
         check_against_oracle(xc, AXIS_ROWS, mode, rule, what="zeros cols")
@@ -121,7 +131,7 @@ def test_subnormal_and_zero_block_scales():
         16, axis=1)).astype(np.float32)
     f[0, 0] = 1000.0
     x = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    for mode, rule in [(STD, MSE), (F46, MSE), (F46, MAE)]:
+    for mode, rule in RULES:
         gpu, ref = check_against_oracle(x, AXIS_COLS, mode, rule, what="subnormal scales")
     assert (ref["scales"] < 8).sum() > 10 and (ref["scales"] == 0).sum() > 10
 
@@ -139,7 +149,7 @@ def test_e2m1_midpoints_and_scale_ties():
         f[r, 32:32 + vals.size // 2] = np.roll(vals, 3 * r)[vals.size // 2:]
     x = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     for g in (1.0, 1.0 / 6, 0.5, 1.0 / 3, 2.0 ** -7):
-        for mode, rule in [(STD, MSE), (F46, MSE), (F46, MAE)]:
+        for mode, rule in RULES:
             check_against_oracle(x, AXIS_COLS, mode, rule, gscale=g, what=f"g={g}")
 
 
