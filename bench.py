@@ -110,18 +110,26 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
         return lambda e: nv.quantize(xd, nv.AXIS_COLS, mode, rule, gscale=g, out=po, events=e,
                                      **kw)
 
+    t_max = np.median(kernel_times(q(nv.MODE_4OVER6, nv.RULE_MAX), torch, 50))
     t_std = np.median(kernel_times(q(nv.MODE_STD), torch, 50))
     t_46 = np.median(kernel_times(q(nv.MODE_4OVER6), torch, 50))
     t_mae = np.median(kernel_times(q(nv.MODE_4OVER6, nv.RULE_MAE), torch, 50))
     res["std_quantize_gbps"] = gb(t_std)
     res["4over6_mse_quantize_gbps_no_bitmap_no_err"] = gb(t_46)
     res["4over6_mae_quantize_gbps_no_bitmap_no_err"] = gb(t_mae)
+    res["4over6_maxerr_quantize_gbps_no_bitmap_no_err"] = gb(t_max)
     res["4over6_overhead_vs_std_pct"] = round((t_46 / t_std - 1) * 100, 1)
     amax = torch.empty(1, dtype=torch.float32, device=dev)
     res["amax_call_gbps"] = gb(call_time(lambda: nv.amax(xd, out=amax), torch, stream), 2.0)
     res["e2e_call_gbps"] = gb(call_time(
         lambda: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, selmap=True,
                             err_sum=True, out=dict(out)), torch, stream))
+    # Delayed scaling: the whole step in one pass (given g, amax recorded).
+    dl_out = {"packed": packed, "scales": scales, "selmap": out["selmap"],
+              "err_sum": out["err_sum"], "amax": torch.empty(1, dtype=torch.float32, device=dev)}
+    res["delayed_scaling_call_gbps"] = gb(call_time(
+        lambda: nv.quantize_delayed(xd, g, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, selmap=True,
+                                    err_sum=True, out=dl_out), torch, stream))
     # Same bytes, no arithmetic: the attainable ceiling for this pattern.
     res["stream_pattern_gbps"] = gb(call_time(
         lambda: nv.stream_pattern(xd, packed, scales), torch, stream))

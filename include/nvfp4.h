@@ -39,7 +39,7 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued on it; no call synchronizes the host.
  *   - Arguments are checked before any HIP call, in the order null pointers,
- *     enums, shape, alignment.  On a failed check nothing is launched and
+ *     enums, shape, alignment, aliasing.  On a failed check nothing is launched and
  *     nothing is written.  NVFP4_ERR_HIP reports a failed launch; device
  *     faults surface at the caller's next synchronization.
  *   - Tensors are row-major [rows][cols] bf16 bit patterns.  Non-finite
@@ -72,7 +72,8 @@ typedef enum nvfp4_status {
   NVFP4_ERR_ENUM = 2,  /* block_axis, mode, rule, out_dtype or flags invalid */
   NVFP4_ERR_SHAPE = 3, /* non-positive extent, or block-axis extent % 16 != 0 */
   NVFP4_ERR_ALIGN = 4, /* a pointer violates the alignment listed above      */
-  NVFP4_ERR_HIP = 5    /* a kernel launch failed                            */
+  NVFP4_ERR_HIP = 5,   /* a kernel launch failed                            */
+  NVFP4_ERR_ALIAS = 6  /* an output aliases an input it must not overwrite  */
 } nvfp4_status;
 
 enum { NVFP4_AXIS_ROWS = 0, NVFP4_AXIS_COLS = 1 };
@@ -143,6 +144,25 @@ nvfp4_status nvfp4_quantize_ex_timed(const uint16_t* in_bf16, int64_t rows, int6
                                      float* gscale_inout, uint8_t* selmap_out,
                                      double* err_sum_out, void* start_event, void* stop_event,
                                      void* stream);
+
+/* Delayed scaling: quantize with a given tensor scale and record this
+ * tensor's amax for the next call, in one pass over the input (no separate
+ * amax read).  The per-tensor scale of NVFP4 is formed from the amax
+ * ("Technical summary: Four Over Six (4/6)", "Implementation details"); a
+ * calibrated or previous-step amax gives the same format with a scale that
+ * lags by one call.
+ *   gscale_in: device pointer to g (e.g. nvfp4_global_scale of the previous
+ *     call's *amax_out); read only; finite and in [0, 2^117].
+ *   amax_out: device float that receives A = max |x| of this tensor (zeroed
+ *     by the call first); must not alias gscale_in (NVFP4_ERR_ALIAS).
+ *   flags: 0 or NVFP4_FLAG_ERR_ACCUMULATE.  Other arguments, outputs and
+ *     checks as nvfp4_quantize_ex with NVFP4_FLAG_GSCALE_GIVEN; the codes,
+ *     scales, bitmap and error sum are identical to that call's. */
+nvfp4_status nvfp4_quantize_delayed(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                    int block_axis, int mode, int rule, uint32_t flags,
+                                    uint8_t* packed_out, uint8_t* scales_out,
+                                    const float* gscale_in, float* amax_out,
+                                    uint8_t* selmap_out, double* err_sum_out, void* stream);
 
 /* Dequantize: x_hat = dec(code) * (dec(S) * g), each product one binary32
  * rounding (x_hat is the rounding of the reconstruction dec(code) * d whose

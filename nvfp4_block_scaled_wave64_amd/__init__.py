@@ -27,7 +27,7 @@ FLAG_GSCALE_GIVEN = 1
 FLAG_ERR_ACCUMULATE = 2
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_ENUM", 3: "NVFP4_ERR_SHAPE",
-          4: "NVFP4_ERR_ALIGN", 5: "NVFP4_ERR_HIP"}
+          4: "NVFP4_ERR_ALIGN", 5: "NVFP4_ERR_HIP", 6: "NVFP4_ERR_ALIAS"}
 
 # Every symbol the public headers declare, with its ctypes signature.
 _P, _I64, _I, _U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
@@ -38,6 +38,8 @@ SIGNATURES = {
     "nvfp4_quantize_ex": ([_P, _I64, _I64, _I, _I, _I, _U32, _P, _P, _P, _P, _P, _P], _I),
     "nvfp4_quantize_ex_timed": ([_P, _I64, _I64, _I, _I, _I, _U32, _P, _P, _P, _P, _P, _P, _P,
                                  _P], _I),
+    "nvfp4_quantize_delayed": ([_P, _I64, _I64, _I, _I, _I, _U32, _P, _P, _P, _P, _P, _P, _P],
+                               _I),
     "nvfp4_dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _P], _I),
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
     "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _P, _P], _I),
@@ -194,6 +196,49 @@ def quantize(x, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE, gscale=No
         _check(lib().nvfp4_quantize_ex_timed(*args, ev0, ev1, _stream(stream)),
                "nvfp4_quantize_ex_timed")
     res = {"packed": packed, "scales": scales, "gscale": g}
+    if selmap:
+        res["selmap"] = sel
+    if err_sum:
+        res["err_sum"] = err
+    return res
+
+
+def quantize_delayed(x, gscale, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE,
+                     selmap=False, err_sum=False, err_accumulate=False, out=None, stream=None):
+    """Quantize with a given tensor scale g (1-element float32 device tensor,
+    e.g. global_scale(previous amax)) and record this tensor's amax in the
+    same pass (nvfp4_quantize_delayed).  Returns the dict of quantize() with
+    "amax" (1-element float32) in place of "gscale"."""
+    x = _bf16_input(x)
+    if x.dim() != 2:
+        raise ValueError("input must be 2-D [rows][cols]")
+    rows, cols = x.shape
+    pshape, sshape, nsel = output_shapes(rows, cols, block_axis)
+    dev = x.device
+    out = dict(out or {})
+    packed = out.get("packed")
+    if packed is None:
+        packed = torch.empty(pshape, dtype=torch.uint8, device=dev)
+    scales = out.get("scales")
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+    amax_t = out.get("amax")
+    if amax_t is None:
+        amax_t = torch.empty(1, dtype=torch.float32, device=dev)
+    sel = out.get("selmap") if selmap else None
+    if selmap and sel is None:
+        sel = torch.empty(max(nsel, 1), dtype=torch.uint8, device=dev)
+    err = out.get("err_sum") if err_sum else None
+    if err_sum and err is None:
+        if err_accumulate:
+            raise ValueError("err_accumulate needs out['err_sum']")
+        err = torch.empty(1, dtype=torch.float64, device=dev)
+    flags = FLAG_ERR_ACCUMULATE if (err_sum and err_accumulate) else 0
+    st = lib().nvfp4_quantize_delayed(_ptr(x), rows, cols, int(block_axis), int(mode), int(rule),
+                                      flags, _ptr(packed), _ptr(scales), _ptr(gscale),
+                                      _ptr(amax_t), _ptr(sel), _ptr(err), _stream(stream))
+    _check(st, "nvfp4_quantize_delayed")
+    res = {"packed": packed, "scales": scales, "amax": amax_t}
     if selmap:
         res["selmap"] = sel
     if err_sum:

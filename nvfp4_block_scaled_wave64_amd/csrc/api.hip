@@ -53,6 +53,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
     case NVFP4_ERR_SHAPE: return "invalid shape (extents must be positive, block axis a multiple of 16)";
     case NVFP4_ERR_ALIGN: return "misaligned pointer";
     case NVFP4_ERR_HIP: return "HIP kernel launch failed";
+    case NVFP4_ERR_ALIAS: return "an output aliases an input it must not overwrite";
   }
   return "unknown status";
 }
@@ -84,7 +85,8 @@ namespace {
 nvfp4_status quantize_impl(const uint16_t* in_bf16, int64_t rows, int64_t cols, int block_axis,
                            int mode, int rule, uint32_t flags, uint8_t* packed_out,
                            uint8_t* scales_out, float* gscale_inout, uint8_t* selmap_out,
-                           double* err_sum_out, nvfp4::Events ev, void* stream) {
+                           double* err_sum_out, float* amax_out, nvfp4::Events ev,
+                           void* stream) {
   if (!in_bf16 || !packed_out || !scales_out || !gscale_inout) return NVFP4_ERR_NULL;
   if (block_axis != NVFP4_AXIS_ROWS && block_axis != NVFP4_AXIS_COLS) return NVFP4_ERR_ENUM;
   if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
@@ -95,8 +97,10 @@ nvfp4_status quantize_impl(const uint16_t* in_bf16, int64_t rows, int64_t cols, 
   const nvfp4_status shape = check_shape(rows, cols, block_axis);
   if (shape != NVFP4_OK) return shape;
   if (!aligned(in_bf16, 16) || !aligned(packed_out, 4) || !aligned(gscale_inout, 4) ||
-      !aligned(selmap_out, 4) || !aligned(err_sum_out, 8))
+      !aligned(selmap_out, 4) || !aligned(err_sum_out, 8) || !aligned(amax_out, 4))
     return NVFP4_ERR_ALIGN;
+  if (amax_out && reinterpret_cast<void*>(amax_out) == reinterpret_cast<void*>(gscale_inout))
+    return NVFP4_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool given = (flags & NVFP4_FLAG_GSCALE_GIVEN) != 0;
@@ -112,9 +116,11 @@ nvfp4_status quantize_impl(const uint16_t* in_bf16, int64_t rows, int64_t cols, 
 
   hipError_t e = hipSuccess;
   uint32_t* acc = reinterpret_cast<uint32_t*>(gscale_inout);
-  // One small kernel zeroes the scale accumulator and the error sum; the
-  // amax pass then leaves g itself in *gscale_inout.
-  if (!given || err_zero) e = nvfp4::launch_init(given ? nullptr : acc, err_zero, nullptr, 0, s);
+  uint32_t* next = reinterpret_cast<uint32_t*>(amax_out);
+  // One small kernel zeroes the scale accumulator (or the amax output) and
+  // the error sum; the amax pass then leaves g itself in *gscale_inout.
+  if (!given || err_zero || next)
+    e = nvfp4::launch_init(given ? next : acc, err_zero, nullptr, 0, s);
   if (e == hipSuccess && !given) {
     const float six_m = mode == NVFP4_MODE_4OVER6 ? 6.0f * 256.0f : 6.0f * 448.0f;
     e = nvfp4::launch_amax(in_bf16, rows * cols, six_m, acc, s);
@@ -122,10 +128,11 @@ nvfp4_status quantize_impl(const uint16_t* in_bf16, int64_t rows, int64_t cols, 
   if (e == hipSuccess) {
     if (block_axis == NVFP4_AXIS_COLS)
       e = nvfp4::launch_quantize_rows(in_bf16, rows * cols / 16, gscale_inout, variant,
-                                      packed_out, scales_out, selmap_out, err_sum_out, s, ev);
+                                      packed_out, scales_out, selmap_out, err_sum_out, next, s,
+                                      ev);
     else
       e = nvfp4::launch_quantize_cols(in_bf16, rows, cols, gscale_inout, variant, packed_out,
-                                      scales_out, selmap_out, err_sum_out, s, ev);
+                                      scales_out, selmap_out, err_sum_out, next, s, ev);
   }
   return hip_status(e);
 }
@@ -139,8 +146,25 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t co
                                uint8_t* packed_out, uint8_t* scales_out, float* gscale_inout,
                                uint8_t* selmap_out, double* err_sum_out, void* stream) {
   return quantize_impl(in_bf16, rows, cols, block_axis, mode, rule, flags, packed_out,
-                       scales_out, gscale_inout, selmap_out, err_sum_out, nvfp4::Events{},
-                       stream);
+                       scales_out, gscale_inout, selmap_out, err_sum_out, nullptr,
+                       nvfp4::Events{}, stream);
+}
+
+nvfp4_status nvfp4_quantize_delayed(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                    int block_axis, int mode, int rule, uint32_t flags,
+                                    uint8_t* packed_out, uint8_t* scales_out,
+                                    const float* gscale_in, float* amax_out,
+                                    uint8_t* selmap_out, double* err_sum_out, void* stream) {
+  if (!gscale_in || !amax_out) return NVFP4_ERR_NULL;
+  if (flags & ~uint32_t(NVFP4_FLAG_ERR_ACCUMULATE)) {
+    if (!in_bf16 || !packed_out || !scales_out) return NVFP4_ERR_NULL;
+    return NVFP4_ERR_ENUM;
+  }
+  // g is only read (NVFP4_FLAG_GSCALE_GIVEN); the kernels take it as const.
+  return quantize_impl(in_bf16, rows, cols, block_axis, mode, rule,
+                       flags | NVFP4_FLAG_GSCALE_GIVEN, packed_out, scales_out,
+                       const_cast<float*>(gscale_in), selmap_out, err_sum_out, amax_out,
+                       nvfp4::Events{}, stream);
 }
 
 nvfp4_status nvfp4_quantize_ex_timed(const uint16_t* in_bf16, int64_t rows, int64_t cols,
@@ -150,7 +174,7 @@ nvfp4_status nvfp4_quantize_ex_timed(const uint16_t* in_bf16, int64_t rows, int6
                                      double* err_sum_out, void* start_event, void* stop_event,
                                      void* stream) {
   return quantize_impl(in_bf16, rows, cols, block_axis, mode, rule, flags, packed_out,
-                       scales_out, gscale_inout, selmap_out, err_sum_out,
+                       scales_out, gscale_inout, selmap_out, err_sum_out, nullptr,
                        nvfp4::Events{static_cast<hipEvent_t>(start_event),
                                      static_cast<hipEvent_t>(stop_event)},
                        stream);

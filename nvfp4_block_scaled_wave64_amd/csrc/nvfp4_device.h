@@ -170,6 +170,7 @@ namespace nvfp4 {
 // Result of one whole block of 16 elements held by one lane.
 struct Block16 {
   uint32_t lo, hi;  // codes of elements 0-7 and 8-15 (element i in bits 4i..)
+  float b;          // block max |x|
   uint32_t S;       // kept E4M3 scale byte
   bool pick4;       // the max->4 candidate was kept
   float err;        // kept candidate's block error
@@ -246,6 +247,7 @@ __device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float 
     e6 = block_error<kRule>(half_error<kRule>(x, c6lo, t6.x), half_error<kRule>(x + 8, c6hi, t6.x));
 
   Block16 r;
+  r.b = b;
   r.lo = c6lo;
   r.hi = c6hi;
   r.S = S6;
@@ -268,6 +270,23 @@ __device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float 
     r.err = r.pick4 ? e4 : e6;
   }
   return r;
+}
+
+// Folds each lane's running maximum m (a non-negative float) into
+// *amax_out: wave reduction on the bit patterns (non-negative floats order
+// like their bits), one LDS slot per wave, one atomic per workgroup.  Every
+// thread of the workgroup must call it (it contains a barrier).
+template <int kWaves>
+__device__ __forceinline__ void group_max_to(uint32_t* amax_out, float m, uint32_t* part) {
+  uint32_t v = __float_as_uint(m);
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+  if ((threadIdx.x & 63u) == 0u) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = part[0];
+    for (int k = 1; k < kWaves; ++k) r = max(r, part[k]);
+    atomicMax(amax_out, r);
+  }
 }
 
 // Build the per-workgroup table tab[S] = (d, r) for the 128 scale bytes.

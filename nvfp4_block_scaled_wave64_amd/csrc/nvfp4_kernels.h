@@ -81,15 +81,18 @@ hipError_t launch_amax(const uint16_t* in, int64_t numel, float six_m, uint32_t*
 hipError_t launch_global_scale(const float* amax, float six_m, float* gscale, hipStream_t s);
 
 // ---- quantize_rows.hip: blocks of 16 contiguous elements ----
+// amax_out (nullable): receives, by atomic max on its fp32 bit pattern, the
+// largest block max |x| of the tensor (the caller zeroes it first).
 hipError_t launch_quantize_rows(const uint16_t* in, int64_t nblocks, const float* gscale,
                                 uint32_t variant, uint8_t* packed, uint8_t* scales,
-                                uint8_t* selmap, double* err_sum, hipStream_t s, Events ev);
+                                uint8_t* selmap, double* err_sum, uint32_t* amax_out,
+                                hipStream_t s, Events ev);
 
 // ---- quantize_cols.hip: blocks of 16 rows within a column ----
 hipError_t launch_quantize_cols(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint32_t variant, uint8_t* packed,
-                                uint8_t* scales, uint8_t* selmap, double* err_sum, hipStream_t s,
-                                Events ev);
+                                uint8_t* scales, uint8_t* selmap, double* err_sum,
+                                uint32_t* amax_out, hipStream_t s, Events ev);
 
 // ---- dequantize.hip ----
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, const float* gscale,

@@ -80,7 +80,7 @@ template <uint32_t V>
 __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     const uint16_t* __restrict__ in, int64_t rows, int64_t cols, const float* __restrict__ gscale,
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
-    double* __restrict__ err_sum) {
+    double* __restrict__ err_sum, uint32_t* __restrict__ amax_out) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr int kRule = !k46 ? kRuleMse
                         : (V & kVarMax) ? kRuleMax
@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t codes[kTileCols * kCodePitch];
   __shared__ __attribute__((aligned(16))) uint8_t sbytes[kTileCols * kSPitch];
   __shared__ double wsum[kColsWaves];
+  __shared__ uint32_t wmax[kColsWaves];
 
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
   };
 
   double acc = 0.0;
+  float bmax = 0.0f;  // running block max for amax_out (padding blocks are 0)
   // Quantizes tile tt from the registers w, then refills w with tile
   // tt + kColsDepth * nwg.
   auto process = [&](int64_t tt, u32x4* w) {
@@ -194,6 +196,7 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
       }
       const Block16 qa = quantize_block16<k46, kRule, kNeedErr>(wa, ts.k6, ts.k4, tab);
       const Block16 qb = quantize_block16<k46, kRule, kNeedErr>(wb, ts.k6, ts.k4, tab);
+      bmax = __builtin_elementwise_maximum(bmax, __builtin_elementwise_maximum(qa.b, qb.b));
       const int ca = 2 * cp, cb = 2 * cp + 1;
       u32x2 pa, pb;
       pa.x = qa.lo;
@@ -284,6 +287,7 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     }
   }
 
+  if (amax_out) group_max_to<kColsWaves>(amax_out, bmax, wmax);  // uniform branch
   if (kErr) {
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (lane == 0) wsum[wave] = acc;
@@ -321,7 +325,8 @@ __global__ __launch_bounds__(kThreads) void selmap_from_scales_kernel(uint8_t* _
 template <uint32_t V>
 static hipError_t launch_cols_v(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint8_t* packed, uint8_t* scales,
-                                uint8_t* selmap, double* err_sum, hipStream_t s, Events ev) {
+                                uint8_t* selmap, double* err_sum, uint32_t* amax_out,
+                                hipStream_t s, Events ev) {
   constexpr bool kSel = (V & kVarSelmap) != 0;
   const bool two_pass = kSel && (rows / 16) % 8 != 0;
   // With a second bitmap pass, that kernel ends the event bracket.
@@ -333,7 +338,7 @@ static hipError_t launch_cols_v(const uint16_t* in, int64_t rows, int64_t cols,
   if (groups < 1) groups = 1;
   hipError_t e = launch_with_events(quantize_cols_kernel<V>, dim3((unsigned)groups),
                                     dim3(kColsThreads), s, first, in, rows, cols, gscale, packed,
-                                    scales, selmap, err_sum);
+                                    scales, selmap, err_sum, amax_out);
   if (e != hipSuccess || !two_pass) return e;
   const int64_t nblocks = rows / 16 * cols;
   int64_t g2 = ((nblocks + 7) / 8 + kThreads - 1) / kThreads;
@@ -345,11 +350,12 @@ static hipError_t launch_cols_v(const uint16_t* in, int64_t rows, int64_t cols,
 
 hipError_t launch_quantize_cols(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint32_t variant, uint8_t* packed,
-                                uint8_t* scales, uint8_t* selmap, double* err_sum, hipStream_t s,
-                                Events ev) {
+                                uint8_t* scales, uint8_t* selmap, double* err_sum,
+                                uint32_t* amax_out, hipStream_t s, Events ev) {
 #define NVFP4_COLS_CASE(v) \
   case v:                  \
-    return launch_cols_v<v>(in, rows, cols, gscale, packed, scales, selmap, err_sum, s, ev);
+    return launch_cols_v<v>(in, rows, cols, gscale, packed, scales, selmap, err_sum, amax_out, \
+                            s, ev);
   switch (variant) {
     NVFP4_COLS_CASE(0)
     NVFP4_COLS_CASE(1)

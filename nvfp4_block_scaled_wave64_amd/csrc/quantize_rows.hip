@@ -41,7 +41,7 @@ template <uint32_t V>
 __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
     const uint16_t* __restrict__ in, int64_t nblocks, const float* __restrict__ gscale,
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
-    double* __restrict__ err_sum) {
+    double* __restrict__ err_sum, uint32_t* __restrict__ amax_out) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr int kRule = !k46 ? kRuleMse
                         : (V & kVarMax) ? kRuleMax
@@ -53,6 +53,7 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
 
   __shared__ float2 tab[128];
   __shared__ double wsum[kRowsWaves];
+  __shared__ uint32_t wmax[kRowsWaves];
 
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
@@ -71,6 +72,7 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
   const uint32_t nwaves = gridDim.x * kRowsWaves;
   const uint32_t first = blockIdx.x * kRowsWaves + (threadIdx.x >> 6);
   double acc = 0.0;
+  float bmax = 0.0f;  // running block max for amax_out (blocks past the end are 0)
 
   // Chunks past the end read as zeros (range-checked buffer loads); ch stays
   // below nchunks + 2 * nwaves, so ch * 2048 cannot wrap.
@@ -95,6 +97,7 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
       wd[4 + j] = p[1];
     }
     const Block16 q = quantize_block16<k46, kRule, kNeedErr>(wd, ts.k6, ts.k4, tab);
+    bmax = __builtin_elementwise_maximum(bmax, q.b);
     u32x2 codes;
     codes.x = q.lo;
     codes.y = q.hi;
@@ -136,6 +139,7 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
     }
   }
 
+  if (amax_out) group_max_to<kRowsWaves>(amax_out, bmax, wmax);  // uniform branch
   if (kErr) {
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (lane == 0) wsum[threadIdx.x >> 6] = acc;
@@ -151,7 +155,8 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
 template <uint32_t V>
 static hipError_t launch_rows_v(const uint16_t* in, int64_t nblocks, const float* gscale,
                                 uint8_t* packed, uint8_t* scales, uint8_t* selmap,
-                                double* err_sum, hipStream_t s, Events ev) {
+                                double* err_sum, uint32_t* amax_out, hipStream_t s,
+                                Events ev) {
   // Segments of at most 2^26 blocks (2^30 elements, 2 GiB of input) keep
   // every buffer offset within 32 bits; a multiple of 64 blocks, so each
   // segment's bitmap starts on a byte boundary.
@@ -169,7 +174,7 @@ static hipError_t launch_rows_v(const uint16_t* in, int64_t nblocks, const float
     const hipError_t e = launch_with_events(
         quantize_rows_kernel<V>, dim3((unsigned)groups), dim3(kRowsThreads), s, seg,
         in + b0 * 16, nb, gscale, packed + b0 * 8, scales + b0,
-        selmap ? selmap + b0 / 8 : nullptr, err_sum);
+        selmap ? selmap + b0 / 8 : nullptr, err_sum, amax_out);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -177,10 +182,11 @@ static hipError_t launch_rows_v(const uint16_t* in, int64_t nblocks, const float
 
 hipError_t launch_quantize_rows(const uint16_t* in, int64_t nblocks, const float* gscale,
                                 uint32_t variant, uint8_t* packed, uint8_t* scales,
-                                uint8_t* selmap, double* err_sum, hipStream_t s, Events ev) {
+                                uint8_t* selmap, double* err_sum, uint32_t* amax_out,
+                                hipStream_t s, Events ev) {
 #define NVFP4_ROWS_CASE(v) \
   case v:                  \
-    return launch_rows_v<v>(in, nblocks, gscale, packed, scales, selmap, err_sum, s, ev);
+    return launch_rows_v<v>(in, nblocks, gscale, packed, scales, selmap, err_sum, amax_out, s, ev);
   switch (variant) {
     NVFP4_ROWS_CASE(0)
     NVFP4_ROWS_CASE(1)

@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
@@ -39,8 +39,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = nv.lib()
-    for s in range(6):
+    for s in range(7):
         assert L.nvfp4_status_string(s)
+    assert b"alias" in L.nvfp4_status_string(6)
     assert b"unknown" in L.nvfp4_status_string(99)
 
 
@@ -93,3 +94,25 @@ def test_other_entry_points_reject():
     assert L.nvfp4v_stream_pattern(None, 16, A, B, None) == 1
     assert L.nvfp4v_stream_pattern(A, 0, B, C, None) == 3
     assert L.nvfp4v_stream_pattern(MIS, 16, B, C, None) == 4
+
+
+def dq(**kw):
+    args = dict(in_=A, rows=32, cols=64, axis=nv.AXIS_COLS, mode=nv.MODE_4OVER6, rule=nv.RULE_MSE,
+                flags=0, packed=B, scales=C, g=A, amax=B, sel=None, err=None)
+    args.update(kw)
+    return nv.lib().nvfp4_quantize_delayed(args["in_"], args["rows"], args["cols"], args["axis"],
+                                           args["mode"], args["rule"], args["flags"],
+                                           args["packed"], args["scales"], args["g"],
+                                           args["amax"], args["sel"], args["err"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None), 1), (dict(amax=None), 1), (dict(in_=None), 1), (dict(packed=None, flags=1), 1),
+    (dict(flags=1), 2), (dict(flags=4), 2), (dict(rule=7), 2), (dict(rows=0), 3),
+    (dict(amax=ctypes.c_void_p(0x20002)), 4), (dict(amax=A), 6),
+])
+def test_delayed_rejects(kw, status):
+    """nvfp4_quantize_delayed: null, enum (GSCALE_GIVEN is implied, so only
+    the accumulate flag is accepted), shape, alignment, and amax_out
+    aliasing gscale_in."""
+    assert dq(**kw) == status

@@ -280,3 +280,48 @@ def test_round_trip_config1_through_gpu_outputs():
     ref = oracle.quantize(x, AXIS_COLS, STD, MSE)
     want = oracle.dequantize(ref["packed"], ref["scales"], ref["gscale"], 256, 1024, AXIS_COLS)
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------ delayed scaling ----
+
+@pytest.mark.parametrize("axis,shape", [(AXIS_COLS, (512, 5120)), (AXIS_COLS, (37, 80)),
+                                        (AXIS_ROWS, (1040, 72)), (AXIS_ROWS, (256, 130))])
+@pytest.mark.parametrize("rule", [MSE, MAXE])
+def test_delayed_scaling(axis, shape, rule):
+    """Quantize with the previous tensor's scale while recording this
+    tensor's amax: outputs equal the oracle's for that given g, the amax is
+    exact, and the next call's g follows from it."""
+    banner(f"delayed axis={axis} {shape} rule={rule}")
+    x_prev = testkit.fill(shape, testkit.NORMAL, 2.0, 11 + shape[0])
+    x = testkit.fill(shape, testkit.STUDENT_T3, 0.7, 13 + shape[1])
+    g = nv.global_scale(nv.amax(to_device(x_prev)), F46)
+    d = nv.quantize_delayed(to_device(x), g, axis, F46, rule, selmap=True, err_sum=True)
+    torch.cuda.synchronize()
+    g32 = np.float32(g.item())
+    ref = oracle.quantize(x, axis, F46, rule, gscale=g32)
+    np.testing.assert_array_equal(d["packed"].cpu().numpy().reshape(-1), ref["packed"])
+    np.testing.assert_array_equal(d["scales"].cpu().numpy().reshape(-1), ref["scales"])
+    np.testing.assert_array_equal(d["selmap"].cpu().numpy()[: ref["selmap"].size], ref["selmap"])
+    assert d["err_sum"].item() == pytest.approx(ref["err_sum"], rel=1e-6)
+    a = oracle.amax(x)
+    assert np.float32(d["amax"].item()).view(np.uint32) == a.view(np.uint32)
+    g_next = nv.global_scale(d["amax"], F46)
+    assert np.float32(g_next.item()).view(np.uint32) == oracle.global_scale(a, F46).view(np.uint32)
+
+
+def test_delayed_scaling_full_size_rows_sampled():
+    banner("delayed 32768x5120")
+    x = testkit.make(4)
+    xd = to_device(x)
+    g = torch.tensor([np.float32(0.75) * oracle.global_scale(oracle.amax(x), F46)],
+                     dtype=torch.float32, device="cuda")  # a stale, smaller amax
+    d = nv.quantize_delayed(xd, g, AXIS_COLS, F46, MSE)
+    torch.cuda.synchronize()
+    assert np.float32(d["amax"].item()).view(np.uint32) == oracle.amax(x).view(np.uint32)
+    rng = np.random.default_rng(8)
+    pick = np.unique(np.concatenate([[0, x.shape[0] - 1], rng.integers(0, x.shape[0], 30)]))
+    ref = oracle.quantize(x[pick], AXIS_COLS, F46, MSE, gscale=np.float32(g.item()),
+                          want_err=False)
+    idx = torch.from_numpy(pick).cuda()
+    np.testing.assert_array_equal(d["packed"][idx].cpu().numpy().reshape(-1), ref["packed"])
+    np.testing.assert_array_equal(d["scales"][idx].cpu().numpy().reshape(-1), ref["scales"])
