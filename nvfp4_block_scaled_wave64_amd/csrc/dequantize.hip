@@ -14,55 +14,19 @@
 // 16-byte halves in the order of the output, so each store instruction
 // writes 1 KiB contiguously (the inverse of the quantizer's load pairing).
 //
-// Blocks along the column (stored as the transpose): a lane handles 8
-// consecutive stored elements and writes them with strided stores.  E2M1
-// decode there is exact bit placement: the 3-bit magnitude index at bit 22
-// of a binary32 word is value * 2^-126 (0.5 lands on a subnormal), so one
-// multiply by 2^126 restores it, sign included.
+// Blocks along the column (stored as the transpose): tiles of 64 columns x
+// 256 rows are decoded into a row-major LDS tile and leave as 16-byte row
+// segments (see dequantize_cols_kernel).
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
 namespace nvfp4 {
 
-__device__ __forceinline__ float e2m1_value(uint32_t code) {
-  return __uint_as_float(((code & 7u) << 22) | ((code & 8u) << 28)) * 0x1p126f;
-}
-
-__device__ __forceinline__ uint32_t to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// Blocks along the column: the stored tensor is [n_rows][n_cols] in block
-// order, the transpose of the caller's [n_cols][n_rows].
-template <bool kBf16>
-__global__ __launch_bounds__(kThreads) void dequantize_transposed_kernel(
-    const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
-    const float* __restrict__ gscale, int64_t n_rows, int64_t n_cols, void* __restrict__ out) {
-  const float g = *gscale;
-  const int64_t nunits = n_rows * n_cols / 8;
-  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < nunits;
-       u += (int64_t)gridDim.x * kThreads) {
-    const uint32_t word = packed[u];
-    const float d = e4m3_decode(scales[u >> 1]) * g;
-    const int64_t e = u * 8;  // first stored element: row c of x^T, col r
-    const int64_t c = e / n_cols, r = e % n_cols;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float v = e2m1_value(word >> (4 * i)) * d;
-      const int64_t o = (r + i) * n_rows + c;  // x is [n_cols][n_rows]
-      if (kBf16)
-        reinterpret_cast<uint16_t*>(out)[o] = (uint16_t)to_bf16_rne(v);
-      else
-        reinterpret_cast<float*>(out)[o] = v;
-    }
-  }
-}
-
 #ifndef NVFP4_DEQ_STORE_AUX
 #define NVFP4_DEQ_STORE_AUX 16
 #endif
-// Cache policy of the output stores.
+// Cache policy of the output stores (each store instruction writes 1 KiB
+// contiguously): sc1.
 constexpr int kDeqStore = NVFP4_DEQ_STORE_AUX;
 
 template <bool kBf16>
@@ -70,6 +34,8 @@ __global__ __launch_bounds__(kRowsThreads) void dequantize_rows_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
     const float* __restrict__ gscale, int64_t nblocks, void* __restrict__ out) {
   constexpr uint32_t kOutBlock = kBf16 ? 32u : 64u;  // output bytes per block
+  constexpr uint32_t kStageBytes = 16u * 272u;        // fp32 staging per wave
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kBf16 ? 16u : kRowsWaves * kStageBytes];
   const float g = *gscale;
   const uint32_t nb = (uint32_t)nblocks;  // <= 2^25 per launch
   const __amdgpu_buffer_rsrc_t r_codes = make_rsrc(packed, nb * 8u);
@@ -120,15 +86,173 @@ __global__ __launch_bounds__(kRowsThreads) void dequantize_rows_kernel(
       __builtin_amdgcn_raw_buffer_store_b128(b, r_out, ch * 2048u + 1024u + off_pair, 0,
                                              kDeqStore);
     } else {
+      // fp32: a block is 64 output bytes, so lane l's 4 quarters would land
+      // 64 bytes apart.  The wave passes them through its own LDS region
+      // (groups of 4 blocks padded to 272 bytes, so the 16 lanes of each
+      // write pass hit distinct banks) and reads them back in output order:
+      // store q then writes bytes 1024q .. 1024q + 1023 of the chunk.
+      uint8_t* st = stage + (threadIdx.x >> 6) * kStageBytes;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        u32x4 o;
-        o.x = __float_as_uint(v[4 * q]);
-        o.y = __float_as_uint(v[4 * q + 1]);
-        o.z = __float_as_uint(v[4 * q + 2]);
-        o.w = __float_as_uint(v[4 * q + 3]);
-        __builtin_amdgcn_raw_buffer_store_b128(o, r_out, ch * 4096u + lane * 64u + q * 16u, 0,
+        const u32x4 o = {__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                         __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
+        *reinterpret_cast<u32x4*>(st + (lane >> 2) * 272u + (lane & 3u) * 64u + q * 16u) = o;
+      }
+      __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t blk = 16u * q + (lane >> 2);  // block of output bytes 1024q + 16 lane
+        const u32x4 o = *reinterpret_cast<const u32x4*>(st + (blk >> 2) * 272u + (blk & 3u) * 64u +
+                                                        (lane & 3u) * 16u);
+        __builtin_amdgcn_raw_buffer_store_b128(o, r_out, ch * 4096u + q * 1024u + lane * 16u, 0,
                                                kDeqStore);
+      }
+      __builtin_amdgcn_wave_barrier();  // the next step rewrites the region
+    }
+  }
+}
+
+// Blocks along the column: the stored codes are [n_rows = cols][rows/2]
+// (the layout of the transpose).  A workgroup of 512 threads takes a tile of
+// 64 stored rows (= columns of x) by 256 stored columns (= rows of x):
+//   1. each lane loads 16 bytes of codes (two blocks) of one column; lanes
+//      t < 64 load that tile column's 16 scale bytes into LDS;
+//   2. each lane decodes a column pair's block (two columns, 16 rows) and
+//      writes the 16 row pairs into a row-major LDS tile;
+//   3. the tile leaves as 16-byte row segments (128 contiguous bytes per row
+//      and tile for bf16, 256 for fp32).
+constexpr int kDtCols = 64;    // columns of x per tile
+constexpr int kDtRows = 256;   // rows of x per tile
+constexpr int kDtThreads = 512;
+
+template <bool kBf16>
+__global__ __launch_bounds__(kDtThreads) void dequantize_cols_kernel(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+    const float* __restrict__ gscale, int64_t rows, int64_t cols, void* __restrict__ out) {
+  constexpr int kEl = kBf16 ? 2 : 4;                 // output bytes per element
+  constexpr int kPitch = kDtCols * kEl + 16;         // LDS bytes per tile row
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kDtRows * kPitch];
+  __shared__ __attribute__((aligned(16))) uint32_t sc[kDtCols][4];  // 16 scale bytes per column
+  __shared__ __attribute__((aligned(16))) uint32_t cw[kDtCols][33];  // 128 code bytes + pad
+
+  const float g = *gscale;
+  const int t = threadIdx.x;
+  const int64_t nstrips = (cols + kDtCols - 1) / kDtCols;
+  const int64_t nrt = (rows + kDtRows - 1) / kDtRows;
+  const int64_t ntiles = nstrips * nrt;
+  const int64_t rb_col = rows / 16;
+  const bool scales16 = (reinterpret_cast<uintptr_t>(scales) % 16 == 0) && (rb_col % 16 == 0);
+
+  // A tile's inputs in registers: lane t holds blocks t and t + 512 of the
+  // 64 x 16 (column, block) grid (8 code bytes each); lanes t < 64 also hold
+  // column t's 16 scale bytes.  Loaded one tile ahead.
+  struct In {
+    uint32_t c[4];
+    uint32_t s[4];
+  };
+  auto load = [&](int64_t tt) -> In {
+    In in = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (tt >= ntiles) return in;
+    const int64_t strip = tt / nrt, rt = tt % nrt;
+    const int64_t c0 = strip * kDtCols, r0 = rt * kDtRows;
+    const int nrb = (int)((rows - r0) / 16 < 16 ? (rows - r0) / 16 : 16);
+    const int ncol = (int)(cols - c0 < kDtCols ? cols - c0 : kDtCols);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = t + h * kDtThreads, c = k >> 4, b = k & 15;
+      if (c < ncol && b < nrb) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(
+            packed + (c0 + c) * (rows / 2) + (r0 / 16 + b) * 8);
+        in.c[2 * h] = __builtin_nontemporal_load(src);
+        in.c[2 * h + 1] = __builtin_nontemporal_load(src + 1);
+      }
+    }
+    if (t < ncol) {
+      const uint8_t* src = scales + (c0 + t) * rb_col + r0 / 16;
+      if (scales16 && nrb == 16) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+        in.s[0] = w.x; in.s[1] = w.y; in.s[2] = w.z; in.s[3] = w.w;
+      } else {
+        for (int b = 0; b < nrb; ++b) in.s[b >> 2] |= (uint32_t)src[b] << (8 * (b & 3));
+      }
+    }
+    return in;
+  };
+
+  In nxt = load(blockIdx.x);
+  for (int64_t tt = blockIdx.x; tt < ntiles; tt += gridDim.x) {
+    const int64_t strip = tt / nrt, rt = tt % nrt;
+    const int64_t c0 = strip * kDtCols, r0 = rt * kDtRows;
+    const int nrb = (int)((rows - r0) / 16 < 16 ? (rows - r0) / 16 : 16);
+    const In cur = nxt;
+    __syncthreads();  // the previous tile has been written out
+    // 1. stage the codes and scale bytes in LDS.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = t + h * kDtThreads, c = k >> 4, b = k & 15;
+      cw[c][2 * b] = cur.c[2 * h];
+      cw[c][2 * b + 1] = cur.c[2 * h + 1];
+    }
+    if (t < kDtCols) {
+      sc[t][0] = cur.s[0];
+      sc[t][1] = cur.s[1];
+      sc[t][2] = cur.s[2];
+      sc[t][3] = cur.s[3];
+    }
+    __syncthreads();
+    nxt = load(tt + gridDim.x);  // in flight during the decode and the stores
+    // 2. lane t decodes block b = t / 32 of the column pair cp = t % 32.
+    {
+      const int cp = t & 31, b = t >> 5;
+      float v0[16], v1[16];
+      const int ca = 2 * cp, cb = 2 * cp + 1;
+      const float da = e4m3_decode((sc[ca][b >> 2] >> (8 * (b & 3))) & 0xFFu) * g;
+      const float db = e4m3_decode((sc[cb][b >> 2] >> (8 * (b & 3))) & 0xFFu) * g;
+      e2m1_decode8(cw[ca][2 * b], v0);
+      e2m1_decode8(cw[ca][2 * b + 1], v0 + 8);
+      e2m1_decode8(cw[cb][2 * b], v1);
+      e2m1_decode8(cw[cb][2 * b + 1], v1 + 8);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float xa = v0[i] * da, xb = v1[i] * db;
+        uint8_t* dst = &tile[(b * 16 + i) * kPitch + ca * kEl];
+        if (kBf16) {
+          const f32x2 p = {xa, xb};
+          *reinterpret_cast<uint32_t*>(dst) = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+        } else {
+          *reinterpret_cast<u32x2*>(dst) = u32x2{__float_as_uint(xa), __float_as_uint(xb)};
+        }
+      }
+    }
+    __syncthreads();
+    // 3. rows of x: 256 rows x (64 * kEl) bytes, 16 bytes per lane and step.
+    constexpr int kSegs = kDtCols * kEl / 16;  // 8 (bf16) or 16 (fp32) per row
+    for (int k = t; k < kDtRows * kSegs; k += kDtThreads) {
+      const int r = k / kSegs, sg = k % kSegs;
+      const int64_t gr = r0 + r;
+      const int64_t gc = c0 + sg * (16 / kEl);
+      if (gr < r0 + nrb * 16 && gc < cols) {
+        const uint8_t* src = &tile[r * kPitch + sg * 16];
+        const u32x2 a = *reinterpret_cast<const u32x2*>(src);
+        const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
+        uint8_t* dst = static_cast<uint8_t*>(out) + (gr * cols + gc) * kEl;
+        if (gc + 16 / kEl <= cols && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+          // Measured: non-temporal stores are faster for the bf16 rows
+          // (128 bytes per row and tile), the default policy for fp32 (256).
+          if (kBf16)
+            __builtin_nontemporal_store(u32x4{a.x, a.y, b.x, b.y}, reinterpret_cast<u32x4*>(dst));
+          else
+            *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b.x, b.y};
+        } else {
+          const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+          const int n = (int)((cols - gc) < 16 / kEl ? (cols - gc) : 16 / kEl);
+          for (int e = 0; e < n; ++e) {
+            if (kBf16)
+              reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            else
+              reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+          }
+        }
       }
     }
   }
@@ -160,19 +284,16 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, const
     }
     return hipSuccess;
   }
-  const int64_t n_rows = cols, n_cols = rows;
-  const int64_t nunits = rows * cols / 8;
-  int64_t groups = (nunits + kThreads - 1) / kThreads;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
-  if (groups > cap) groups = cap;
+  const int64_t ntiles = ((cols + kDtCols - 1) / kDtCols) * ((rows + kDtRows - 1) / kDtRows);
+  int64_t groups = (int64_t)device_cu_count() * 2;
+  if (groups > ntiles) groups = ntiles;
   if (groups < 1) groups = 1;
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
   if (out_bf16)
-    dequantize_transposed_kernel<true><<<(unsigned)groups, kThreads, 0, s>>>(p, scales, gscale,
-                                                                             n_rows, n_cols, out);
+    dequantize_cols_kernel<true><<<(unsigned)groups, kDtThreads, 0, s>>>(packed, scales, gscale,
+                                                                         rows, cols, out);
   else
-    dequantize_transposed_kernel<false><<<(unsigned)groups, kThreads, 0, s>>>(p, scales, gscale,
-                                                                              n_rows, n_cols, out);
+    dequantize_cols_kernel<false><<<(unsigned)groups, kDtThreads, 0, s>>>(packed, scales, gscale,
+                                                                          rows, cols, out);
   return hipGetLastError();
 }
 

@@ -271,6 +271,25 @@ def test_dequantize_tiny_scales_and_ragged(axis, dtype):
     np.testing.assert_array_equal(got, want.view(got.dtype))
 
 
+@pytest.mark.parametrize("axis,cid", [(AXIS_ROWS, 5), (AXIS_COLS, 2)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_full_size(axis, cid, dtype):
+    """Dequantize the full column-blocked gradient workload (and a row-wise
+    one) against the oracle's reconstruction, bit for bit."""
+    cfg = testkit.CONFIGS[cid]
+    banner(f"dequantize full {cfg.rows}x{cfg.cols} axis={axis} {dtype}")
+    x = testkit.make(cid)
+    ref = oracle.quantize(x, axis, cfg.mode, cfg.rule, want_err=False)
+    want = oracle.dequantize(ref["packed"], ref["scales"], ref["gscale"], cfg.rows, cfg.cols, axis,
+                             out_bf16=dtype == torch.bfloat16)
+    p = torch.from_numpy(ref["packed"]).cuda()
+    s = torch.from_numpy(ref["scales"]).cuda()
+    g = torch.tensor([ref["gscale"]], dtype=torch.float32, device="cuda")
+    out = nv.dequantize(p, s, g, cfg.rows, cfg.cols, axis, dtype)
+    got = out.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+    np.testing.assert_array_equal(got, want.view(got.dtype))
+
+
 def test_round_trip_config1_through_gpu_outputs():
     banner("config 1 round trip")
     x = testkit.make(1)
