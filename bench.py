@@ -124,6 +124,22 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     res["e2e_call_gbps"] = gb(call_time(
         lambda: nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, selmap=True,
                             err_sum=True, out=dict(out)), torch, stream))
+    # The same call captured once in a HIP graph and replayed.
+    e2e_out = dict(out)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, selmap=True, err_sum=True,
+                    out=e2e_out)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.quantize(xd, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE, selmap=True, err_sum=True,
+                    out=e2e_out)
+    torch.cuda.synchronize()
+    res["e2e_graph_replay_gbps"] = gb(call_time(graph.replay, torch, stream))
+    del graph
     # Delayed scaling: the whole step in one pass (given g, amax recorded).
     dl_out = {"packed": packed, "scales": scales, "selmap": out["selmap"],
               "err_sum": out["err_sum"], "amax": torch.empty(1, dtype=torch.float32, device=dev)}
