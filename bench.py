@@ -172,6 +172,21 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
         tm = float(np.median(t))
         res[f"workload{cid}_{cfg.rows}x{cfg.cols}_kernel_us_median"] = round(tm * 1e6, 2)
         res[f"workload{cid}_gbps"] = gb(tm, n=cfg.rows * cfg.cols)
+        if cid == 5:
+            # Both layouts from one read (given g) against the two single-layout calls.
+            n5 = cfg.rows * cfg.cols
+            od = nv.quantize_dual(xc, cfg.mode, cfg.rule, gscale=gc)
+            t_dual = call_time(lambda: nv.quantize_dual(xc, cfg.mode, cfg.rule, gscale=gc, out=od),
+                               torch, stream, 20)
+            o_other = nv.quantize(xc, nv.AXIS_COLS, cfg.mode, cfg.rule, gscale=gc)
+            t_both = call_time(lambda: (nv.quantize(xc, cfg.block_axis, cfg.mode, cfg.rule,
+                                                    gscale=gc, out=oc),
+                                        nv.quantize(xc, nv.AXIS_COLS, cfg.mode, cfg.rule,
+                                                    gscale=gc, out=o_other)), torch, stream, 20)
+            res["dual_layout_8192x5120_us"] = round(t_dual * 1e6, 2)
+            res["dual_layout_gbps"] = gb(t_dual, 3.125, n5)
+            res["two_single_layout_calls_us"] = round(t_both * 1e6, 2)
+            del od, o_other
         del xc, oc
     # Plain device copy of known size (the torch copy kernel).
     csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)

@@ -145,6 +145,26 @@ nvfp4_status nvfp4_quantize_ex_timed(const uint16_t* in_bf16, int64_t rows, int6
                                      double* err_sum_out, void* start_event, void* stop_event,
                                      void* stream);
 
+/* Both block layouts from one read of x: the row-blocked outputs
+ * (packed_r [rows][cols/2], scales_r [rows][cols/16], selmap_r, err_sum_r:
+ * those of nvfp4_quantize_ex with NVFP4_AXIS_COLS) and the column-blocked
+ * outputs (packed_c [cols][rows/2], scales_c [cols][rows/16], selmap_c,
+ * err_sum_c: those of NVFP4_AXIS_ROWS), with one tensor scale g.  Each set
+ * is bit-identical to the single-layout call with the same g.  For a tensor
+ * used along both of its dimensions (activations, weights and gradients in
+ * training: "Technical summary: Four Over Six (4/6)", "Key contributions"),
+ * this reads x once instead of twice.
+ *   rows and cols: positive multiples of 16.
+ *   selmap_r / selmap_c and err_sum_r / err_sum_c: both or neither
+ *     (NVFP4_ERR_NULL otherwise); the error sums are zeroed first unless
+ *     flags has NVFP4_FLAG_ERR_ACCUMULATE.
+ *   flags, gscale_inout, mode, rule, alignment: as nvfp4_quantize_ex. */
+nvfp4_status nvfp4_quantize_dual(const uint16_t* in_bf16, int64_t rows, int64_t cols, int mode,
+                                 int rule, uint32_t flags, uint8_t* packed_r, uint8_t* scales_r,
+                                 uint8_t* packed_c, uint8_t* scales_c, float* gscale_inout,
+                                 uint8_t* selmap_r, uint8_t* selmap_c, double* err_sum_r,
+                                 double* err_sum_c, void* stream);
+
 /* Delayed scaling: quantize with a given tensor scale and record this
  * tensor's amax for the next call, in one pass over the input (no separate
  * amax read).  The per-tensor scale of NVFP4 is formed from the amax

@@ -40,6 +40,8 @@ SIGNATURES = {
                                  _P], _I),
     "nvfp4_quantize_delayed": ([_P, _I64, _I64, _I, _I, _I, _U32, _P, _P, _P, _P, _P, _P, _P],
                                _I),
+    "nvfp4_quantize_dual": ([_P, _I64, _I64, _I, _I, _U32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+                            _I),
     "nvfp4_dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _P], _I),
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
     "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _P, _P], _I),
@@ -201,6 +203,60 @@ def quantize(x, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE, gscale=No
     if err_sum:
         res["err_sum"] = err
     return res
+
+
+def quantize_dual(x, mode=MODE_4OVER6, rule=RULE_MSE, gscale=None, selmap=False, err_sum=False,
+                  err_accumulate=False, out=None, stream=None):
+    """Both block layouts of a [rows][cols] bf16 tensor from one read
+    (nvfp4_quantize_dual).  Returns {"gscale": g, "rows": {...}, "cols": {...}}
+    where "rows" holds the row-blocked outputs (those of quantize with
+    AXIS_COLS) and "cols" the column-blocked ones (AXIS_ROWS): packed,
+    scales and, when asked for, selmap and err_sum.  `out` may supply
+    {"gscale": ..., "rows": {...}, "cols": {...}} tensors."""
+    x = _bf16_input(x)
+    if x.dim() != 2:
+        raise ValueError("input must be 2-D [rows][cols]")
+    rows, cols = x.shape
+    dev = x.device
+    out = dict(out or {})
+    sides = {}
+    for key, axis in (("rows", AXIS_COLS), ("cols", AXIS_ROWS)):
+        pshape, sshape, nsel = output_shapes(rows, cols, axis)
+        o = dict(out.get(key) or {})
+        d = {"packed": o.get("packed"), "scales": o.get("scales")}
+        if d["packed"] is None:
+            d["packed"] = torch.empty(pshape, dtype=torch.uint8, device=dev)
+        if d["scales"] is None:
+            d["scales"] = torch.empty(sshape, dtype=torch.uint8, device=dev)
+        if selmap:
+            d["selmap"] = o.get("selmap")
+            if d["selmap"] is None:
+                d["selmap"] = torch.empty(max(nsel, 1), dtype=torch.uint8, device=dev)
+        if err_sum:
+            d["err_sum"] = o.get("err_sum")
+            if d["err_sum"] is None:
+                if err_accumulate:
+                    raise ValueError("err_accumulate needs out[side]['err_sum']")
+                d["err_sum"] = torch.empty(1, dtype=torch.float64, device=dev)
+        sides[key] = d
+    flags = 0
+    if gscale is not None:
+        g = gscale
+        flags |= FLAG_GSCALE_GIVEN
+    else:
+        g = out.get("gscale")
+        if g is None:
+            g = torch.empty(1, dtype=torch.float32, device=dev)
+    if err_sum and err_accumulate:
+        flags |= FLAG_ERR_ACCUMULATE
+    r, c = sides["rows"], sides["cols"]
+    st = lib().nvfp4_quantize_dual(_ptr(x), rows, cols, int(mode), int(rule), flags,
+                                   _ptr(r["packed"]), _ptr(r["scales"]), _ptr(c["packed"]),
+                                   _ptr(c["scales"]), _ptr(g), _ptr(r.get("selmap")),
+                                   _ptr(c.get("selmap")), _ptr(r.get("err_sum")),
+                                   _ptr(c.get("err_sum")), _stream(stream))
+    _check(st, "nvfp4_quantize_dual")
+    return {"gscale": g, "rows": r, "cols": c}
 
 
 def quantize_delayed(x, gscale, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE,

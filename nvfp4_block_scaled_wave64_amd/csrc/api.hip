@@ -132,7 +132,7 @@ nvfp4_status quantize_impl(const uint16_t* in_bf16, int64_t rows, int64_t cols, 
                                       ev);
     else
       e = nvfp4::launch_quantize_cols(in_bf16, rows, cols, gscale_inout, variant, packed_out,
-                                      scales_out, selmap_out, err_sum_out, next, s, ev);
+                                      scales_out, selmap_out, err_sum_out, next, nullptr, s, ev);
   }
   return hip_status(e);
 }
@@ -148,6 +148,60 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t co
   return quantize_impl(in_bf16, rows, cols, block_axis, mode, rule, flags, packed_out,
                        scales_out, gscale_inout, selmap_out, err_sum_out, nullptr,
                        nvfp4::Events{}, stream);
+}
+
+nvfp4_status nvfp4_quantize_dual(const uint16_t* in_bf16, int64_t rows, int64_t cols, int mode,
+                                 int rule, uint32_t flags, uint8_t* packed_r, uint8_t* scales_r,
+                                 uint8_t* packed_c, uint8_t* scales_c, float* gscale_inout,
+                                 uint8_t* selmap_r, uint8_t* selmap_c, double* err_sum_r,
+                                 double* err_sum_c, void* stream) {
+  if (!in_bf16 || !packed_r || !scales_r || !packed_c || !scales_c || !gscale_inout)
+    return NVFP4_ERR_NULL;
+  if ((selmap_r == nullptr) != (selmap_c == nullptr)) return NVFP4_ERR_NULL;
+  if ((err_sum_r == nullptr) != (err_sum_c == nullptr)) return NVFP4_ERR_NULL;
+  if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
+  if (rule != NVFP4_RULE_MSE && rule != NVFP4_RULE_MAE && rule != NVFP4_RULE_MAX)
+    return NVFP4_ERR_ENUM;
+  if (flags & ~uint32_t(NVFP4_FLAG_GSCALE_GIVEN | NVFP4_FLAG_ERR_ACCUMULATE))
+    return NVFP4_ERR_ENUM;
+  nvfp4_status shape = check_shape(rows, cols, NVFP4_AXIS_COLS);
+  if (shape == NVFP4_OK) shape = check_shape(rows, cols, NVFP4_AXIS_ROWS);
+  if (shape != NVFP4_OK) return shape;
+  if (!aligned(in_bf16, 16) || !aligned(packed_r, 4) || !aligned(packed_c, 4) ||
+      !aligned(gscale_inout, 4) || !aligned(selmap_r, 4) || !aligned(selmap_c, 4) ||
+      !aligned(err_sum_r, 8) || !aligned(err_sum_c, 8))
+    return NVFP4_ERR_ALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool given = (flags & NVFP4_FLAG_GSCALE_GIVEN) != 0;
+  const bool zero_err = err_sum_c && !(flags & NVFP4_FLAG_ERR_ACCUMULATE);
+  uint32_t variant = 0;
+  if (mode == NVFP4_MODE_4OVER6) {
+    variant |= nvfp4::kVarFourOverSix;
+    if (rule == NVFP4_RULE_MAE) variant |= nvfp4::kVarMae;
+    if (rule == NVFP4_RULE_MAX) variant |= nvfp4::kVarMax;
+  }
+  if (selmap_c) variant |= nvfp4::kVarSelmap;
+  if (err_sum_c) variant |= nvfp4::kVarErr;
+
+  hipError_t e = hipSuccess;
+  uint32_t* acc = reinterpret_cast<uint32_t*>(gscale_inout);
+  // Zero the scale accumulator and both error sums (the row-blocked one as
+  // two 32-bit words) in one small kernel.
+  if (!given || zero_err)
+    e = nvfp4::launch_init(given ? nullptr : acc, zero_err ? err_sum_c : nullptr,
+                           zero_err ? reinterpret_cast<uint32_t*>(err_sum_r) : nullptr,
+                           zero_err ? 2 : 0, s);
+  if (e == hipSuccess && !given) {
+    const float six_m = mode == NVFP4_MODE_4OVER6 ? 6.0f * 256.0f : 6.0f * 448.0f;
+    e = nvfp4::launch_amax(in_bf16, rows * cols, six_m, acc, s);
+  }
+  if (e == hipSuccess) {
+    const nvfp4::DualOut dual{packed_r, scales_r, selmap_r, err_sum_r};
+    e = nvfp4::launch_quantize_cols(in_bf16, rows, cols, gscale_inout, variant, packed_c, scales_c,
+                                    selmap_c, err_sum_c, nullptr, &dual, s, nvfp4::Events{});
+  }
+  return hip_status(e);
 }
 
 nvfp4_status nvfp4_quantize_delayed(const uint16_t* in_bf16, int64_t rows, int64_t cols,

@@ -89,10 +89,18 @@ hipError_t launch_quantize_rows(const uint16_t* in, int64_t nblocks, const float
                                 hipStream_t s, Events ev);
 
 // ---- quantize_cols.hip: blocks of 16 rows within a column ----
+// Row-blocked outputs of a dual call (both block layouts from one read).
+struct DualOut {
+  uint8_t* packed_r;
+  uint8_t* scales_r;
+  uint8_t* selmap_r;  // nullable
+  double* err_r;      // nullable (only with kVarErr)
+};
 hipError_t launch_quantize_cols(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint32_t variant, uint8_t* packed,
                                 uint8_t* scales, uint8_t* selmap, double* err_sum,
-                                uint32_t* amax_out, hipStream_t s, Events ev);
+                                uint32_t* amax_out, const DualOut* dual, hipStream_t s,
+                                Events ev);
 
 // ---- dequantize.hip ----
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, const float* gscale,

@@ -7,8 +7,8 @@
 //
 // Tiles of 256 rows x 64 columns.  Per tile a workgroup of 8 waves
 //   1. has the tile's 256 row segments of 128 contiguous bytes in registers
-//      (4 x 16-byte loads per lane, issued kColsDepth tiles ahead so they
-//      are in flight while earlier tiles are computed) and writes them row-major
+//      (4 x 16-byte loads per lane, issued one tile ahead so they are in
+//      flight while the previous tile is computed) and writes them row-major
 //      into LDS (row pitch 136 bytes, see the pitches below);
 //   2. lets every lane read a column pair over 16 rows (16 x 4-byte LDS
 //      reads, consecutive banks across each half-wave), which are two whole
@@ -23,6 +23,11 @@
 // renumbered so that consecutive tiles run on one XCD: the 8 row tiles that
 // share a 128-byte line of a column's scale bytes are then written through
 // the same L2, which merges them.
+//
+// Dual emission (nvfp4_quantize_dual): the same tile also yields its 1024
+// row-direction blocks, read from the LDS tile (32 contiguous bytes each),
+// quantized by the same block quantizer and written in the row-blocked
+// layout; such a call walks strips fastest instead.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -31,17 +36,7 @@ namespace nvfp4 {
 #ifndef NVFP4_COLS_GROUPS_PER_CU
 #define NVFP4_COLS_GROUPS_PER_CU 2
 #endif
-#ifndef NVFP4_COLS_DEPTH
-#define NVFP4_COLS_DEPTH 1
-#endif
 constexpr int kColsGroupsPerCu = NVFP4_COLS_GROUPS_PER_CU;
-// Tiles whose loads are in flight (in registers) ahead of the one computed.
-constexpr int kColsDepth = NVFP4_COLS_DEPTH;
-#ifndef NVFP4_COLS_ORDER
-#define NVFP4_COLS_ORDER 0
-#endif
-// Tile walk: 0 = row tiles fastest within a strip, 1 = strips fastest.
-constexpr int kColsOrder = NVFP4_COLS_ORDER;
 constexpr int kTileRows = 256;
 constexpr int kTileCols = 64;
 constexpr int kRowBlocks = kTileRows / 16;  // 16 row blocks per tile
@@ -76,11 +71,16 @@ constexpr int kPasses = 512 / kColsThreads;        // column-pair tasks per lane
 static_assert(kColsThreads == 256 || kColsThreads == 512, "tile mapping");
 
 
-template <uint32_t V>
+// kDual: also quantize the tile's row-direction blocks (16 contiguous
+// elements of a row) into the row-blocked outputs packed_r / scales_r (scale
+// bit 7 marks the kept max->4 candidate for the bitmap pass) and err_r.
+// order: 0 walks row tiles fastest within a strip, 1 strips fastest.
+template <uint32_t V, bool kDual>
 __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     const uint16_t* __restrict__ in, int64_t rows, int64_t cols, const float* __restrict__ gscale,
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
-    double* __restrict__ err_sum, uint32_t* __restrict__ amax_out) {
+    double* __restrict__ err_sum, uint32_t* __restrict__ amax_out, uint8_t* __restrict__ packed_r,
+    uint8_t* __restrict__ scales_r, double* __restrict__ err_r, int order) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr int kRule = !k46 ? kRuleMse
                         : (V & kVarMax) ? kRuleMax
@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t codes[kTileCols * kCodePitch];
   __shared__ __attribute__((aligned(16))) uint8_t sbytes[kTileCols * kSPitch];
   __shared__ double wsum[kColsWaves];
+  __shared__ double wsum_r[kColsWaves];
   __shared__ uint32_t wmax[kColsWaves];
 
   const TensorScales ts = tensor_scales(*gscale);
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
   // (t%8)*8 .. +7.
   const int lrow = t >> 3, lseg = t & 7;
   auto tile_of = [&](int64_t tt, int64_t& strip, int64_t& rt) {
-    if (kColsOrder == 0) {
+    if (order == 0) {
       strip = tt / nrt;
       rt = tt % nrt;
     } else {
@@ -156,10 +157,12 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     }
   };
 
-  double acc = 0.0;
+  double acc = 0.0, acc_r = 0.0;
   float bmax = 0.0f;  // running block max for amax_out (padding blocks are 0)
+  const bool codes_r16 =
+      kDual && (reinterpret_cast<uintptr_t>(packed_r) % 16 == 0) && ((cols / 2) % 16 == 0);
   // Quantizes tile tt from the registers w, then refills w with tile
-  // tt + kColsDepth * nwg.
+  // tt + nwg.
   auto process = [&](int64_t tt, u32x4* w) {
     int64_t strip, rt;
     tile_of(tt, strip, rt);
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
       dst[1] = u32x2{w[k].z, w[k].w};
     }
     __syncthreads();
-    load_tile(tt + kColsDepth * nwg, w);  // in flight during the next tiles' compute
+    load_tile(tt + nwg, w);  // in flight during this tile's compute
 
     // 16 row blocks x 32 column pairs = 512 lane tasks, kPasses per lane:
     // in pass p, wave w takes row block (p * kColsWaves + w) * 2 + lane/32
@@ -273,29 +276,70 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
         if (nrb > 8) bd[1] = (uint8_t)(bits >> 8);
       }
     }
+
+    if constexpr (kDual) {
+      // Row-direction blocks of the same tile (still intact in LDS until the
+      // next tile's first barrier): lane t takes tile row t/2 (per pass) and
+      // its blocks 2*(t%2) and 2*(t%2) + 1, 32 contiguous bytes each.
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const int rr = p * (kColsThreads / 2) + (t >> 1), j0 = (t & 1) * 2;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(&tile[rr * kInPitch + j0 * 32]);
+        uint32_t wa[8], wb[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          wa[i] = src[i];
+          wb[i] = src[8 + i];
+        }
+        const Block16 ra = quantize_block16<k46, kRule, kNeedErr>(wa, ts.k6, ts.k4, tab);
+        const Block16 rb2 = quantize_block16<k46, kRule, kNeedErr>(wb, ts.k6, ts.k4, tab);
+        const int64_t gr = r0 + rr, gc = c0 + 16 * j0;
+        if (gr < rows && gc < cols) {
+          const bool vb = gc + 16 < cols;
+          uint8_t* dst = packed_r + gr * (cols / 2) + gc / 2;
+          if (vb && codes_r16) {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{ra.lo, ra.hi, rb2.lo, rb2.hi};
+          } else {
+            uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);  // 4-byte aligned
+            d32[0] = ra.lo;
+            d32[1] = ra.hi;
+            if (vb) {
+              d32[2] = rb2.lo;
+              d32[3] = rb2.hi;
+            }
+          }
+          uint8_t* sd = scales_r + gr * (cols / 16) + gc / 16;
+          sd[0] = (uint8_t)(ra.S | (kSel && ra.pick4 ? 0x80u : 0u));
+          if (vb) sd[1] = (uint8_t)(rb2.S | (kSel && rb2.pick4 ? 0x80u : 0u));
+          if (kErr) acc_r += (double)ra.err + (vb ? (double)rb2.err : 0.0);
+        }
+      }
+    }
   };
 
-  u32x4 w0[kLoadsPerLane], w1[kLoadsPerLane];
-  load_tile(wg, w0);
-  if (kColsDepth == 1) {
-    for (int64_t tt = wg; tt < ntiles; tt += nwg) process(tt, w0);
-  } else {
-    load_tile(wg + nwg, w1);
-    for (int64_t tt = wg; tt < ntiles; tt += 2 * nwg) {
-      process(tt, w0);
-      if (tt + nwg < ntiles) process(tt + nwg, w1);  // uniform per workgroup
-    }
-  }
+  u32x4 w[kLoadsPerLane];
+  load_tile(wg, w);
+  for (int64_t tt = wg; tt < ntiles; tt += nwg) process(tt, w);
 
   if (amax_out) group_max_to<kColsWaves>(amax_out, bmax, wmax);  // uniform branch
   if (kErr) {
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) wsum[wave] = acc;
+    for (int off = 32; off > 0; off >>= 1) {
+      acc += __shfl_xor(acc, off);
+      if (kDual) acc_r += __shfl_xor(acc_r, off);
+    }
+    if (lane == 0) {
+      wsum[wave] = acc;
+      wsum_r[wave] = acc_r;
+    }
     __syncthreads();
     if (t == 0) {
-      double s = wsum[0];
-      for (int k = 1; k < kColsWaves; ++k) s += wsum[k];
+      double s = wsum[0], sr = wsum_r[0];
+      for (int k = 1; k < kColsWaves; ++k) {
+        s += wsum[k];
+        sr += wsum_r[k];
+      }
       unsafeAtomicAdd(err_sum, s);
+      if (kDual) unsafeAtomicAdd(err_r, sr);
     }
   }
 }
@@ -322,40 +366,54 @@ __global__ __launch_bounds__(kThreads) void selmap_from_scales_kernel(uint8_t* _
   }
 }
 
-template <uint32_t V>
+template <uint32_t V, bool kDual>
 static hipError_t launch_cols_v(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint8_t* packed, uint8_t* scales,
                                 uint8_t* selmap, double* err_sum, uint32_t* amax_out,
-                                hipStream_t s, Events ev) {
+                                const DualOut* dual, hipStream_t s, Events ev) {
   constexpr bool kSel = (V & kVarSelmap) != 0;
-  const bool two_pass = kSel && (rows / 16) % 8 != 0;
-  // With a second bitmap pass, that kernel ends the event bracket.
-  const Events first{ev.start, two_pass ? nullptr : ev.stop};
+  // Bitmap passes: the column-blocked bitmap when its columns' bits do not
+  // start on byte boundaries, the row-blocked one of a dual call always.
+  const bool pass_c = kSel && selmap && (rows / 16) % 8 != 0;
+  const bool pass_r = kSel && kDual && dual->selmap_r;
+  // The last kernel of the call ends the event bracket.
+  const Events first{ev.start, (pass_c || pass_r) ? nullptr : ev.stop};
   const int64_t ntiles =
       ((cols + kTileCols - 1) / kTileCols) * ((rows + kTileRows - 1) / kTileRows);
   int64_t groups = (int64_t)device_cu_count() * kColsGroupsPerCu;
   if (groups > ntiles) groups = ntiles;
   if (groups < 1) groups = 1;
-  hipError_t e = launch_with_events(quantize_cols_kernel<V>, dim3((unsigned)groups),
-                                    dim3(kColsThreads), s, first, in, rows, cols, gscale, packed,
-                                    scales, selmap, err_sum, amax_out);
-  if (e != hipSuccess || !two_pass) return e;
-  const int64_t nblocks = rows / 16 * cols;
-  int64_t g2 = ((nblocks + 7) / 8 + kThreads - 1) / kThreads;
-  if (g2 > 4096) g2 = 4096;
-  if (g2 < 1) g2 = 1;
-  return launch_with_events(selmap_from_scales_kernel, dim3((unsigned)g2), dim3(kThreads), s,
-                            Events{nullptr, ev.stop}, scales, nblocks, selmap);
+  // A dual call walks strips fastest, so that the four strips sharing each
+  // 128-byte line of a row's codes are written through one L2 at once.
+  hipError_t e = launch_with_events(
+      quantize_cols_kernel<V, kDual>, dim3((unsigned)groups), dim3(kColsThreads), s, first, in,
+      rows, cols, gscale, packed, scales, selmap, err_sum, amax_out,
+      kDual ? dual->packed_r : nullptr, kDual ? dual->scales_r : nullptr,
+      kDual ? dual->err_r : nullptr, kDual ? 1 : 0);
+  if (e != hipSuccess) return e;
+  auto bitmap_pass = [&](uint8_t* sc, int64_t nblocks, uint8_t* sel, bool last) {
+    int64_t g2 = ((nblocks + 7) / 8 + kThreads - 1) / kThreads;
+    if (g2 > 4096) g2 = 4096;
+    if (g2 < 1) g2 = 1;
+    return launch_with_events(selmap_from_scales_kernel, dim3((unsigned)g2), dim3(kThreads), s,
+                              Events{nullptr, last ? ev.stop : nullptr}, sc, nblocks, sel);
+  };
+  if (pass_c) e = bitmap_pass(scales, rows / 16 * cols, selmap, !pass_r);
+  if (e == hipSuccess && pass_r) e = bitmap_pass(dual->scales_r, rows * cols / 16, dual->selmap_r, true);
+  return e;
 }
 
 hipError_t launch_quantize_cols(const uint16_t* in, int64_t rows, int64_t cols,
                                 const float* gscale, uint32_t variant, uint8_t* packed,
                                 uint8_t* scales, uint8_t* selmap, double* err_sum,
-                                uint32_t* amax_out, hipStream_t s, Events ev) {
-#define NVFP4_COLS_CASE(v) \
-  case v:                  \
-    return launch_cols_v<v>(in, rows, cols, gscale, packed, scales, selmap, err_sum, amax_out, \
-                            s, ev);
+                                uint32_t* amax_out, const DualOut* dual, hipStream_t s,
+                                Events ev) {
+#define NVFP4_COLS_CASE(v)                                                                    \
+  case v:                                                                                     \
+    return dual ? launch_cols_v<v, true>(in, rows, cols, gscale, packed, scales, selmap,     \
+                                         err_sum, amax_out, dual, s, ev)                     \
+                : launch_cols_v<v, false>(in, rows, cols, gscale, packed, scales, selmap,    \
+                                          err_sum, amax_out, dual, s, ev);
   switch (variant) {
     NVFP4_COLS_CASE(0)
     NVFP4_COLS_CASE(1)

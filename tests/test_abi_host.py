@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
@@ -116,3 +116,28 @@ def test_delayed_rejects(kw, status):
     the accumulate flag is accepted), shape, alignment, and amax_out
     aliasing gscale_in."""
     assert dq(**kw) == status
+
+
+def du(**kw):
+    args = dict(in_=A, rows=32, cols=64, mode=nv.MODE_4OVER6, rule=nv.RULE_MSE, flags=0,
+                pr=B, sr=C, pc=B, sc=C, g=A, selr=None, selc=None, errr=None, errc=None)
+    args.update(kw)
+    return nv.lib().nvfp4_quantize_dual(args["in_"], args["rows"], args["cols"], args["mode"],
+                                        args["rule"], args["flags"], args["pr"], args["sr"],
+                                        args["pc"], args["sc"], args["g"], args["selr"],
+                                        args["selc"], args["errr"], args["errc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_=None), 1), (dict(pc=None), 1), (dict(sr=None), 1), (dict(g=None), 1),
+    (dict(selr=A), 1), (dict(errc=ctypes.c_void_p(0x40000)), 1),
+    (dict(mode=2), 2), (dict(rule=3), 2), (dict(flags=4), 2),
+    (dict(rows=24), 3), (dict(cols=40), 3), (dict(rows=0), 3),
+    (dict(in_=MIS), 4), (dict(pc=ctypes.c_void_p(0x20002)), 4),
+    (dict(selr=ctypes.c_void_p(0x10001), selc=A), 4),
+])
+def test_dual_rejects(kw, status):
+    """nvfp4_quantize_dual: nulls (the bitmaps and the error sums come in
+    pairs), enums, both extents multiples of 16, alignment."""
+    assert du(**kw) == status
+

@@ -344,3 +344,43 @@ def test_delayed_scaling_full_size_rows_sampled():
     idx = torch.from_numpy(pick).cuda()
     np.testing.assert_array_equal(d["packed"][idx].cpu().numpy().reshape(-1), ref["packed"])
     np.testing.assert_array_equal(d["scales"][idx].cpu().numpy().reshape(-1), ref["scales"])
+
+
+# ------------------------------------------------------------ dual layout ----
+
+DUAL_SHAPES = [(16, 16), (48, 80), (272, 48), (1040, 80), (256, 144), (2048, 208)]
+
+
+@pytest.mark.parametrize("rows,cols", DUAL_SHAPES)
+@pytest.mark.parametrize("mode,rule", RULES)
+def test_dual_layout_equals_single_layouts(rows, cols, mode, rule):
+    """Both layouts from one read are bit-identical to the two single-layout
+    calls with the same g, and to the oracle."""
+    banner(f"dual {rows}x{cols} mode={mode} rule={rule}")
+    x = testkit.fill((rows, cols), testkit.STUDENT_T3, 0.6, 3000 + rows + 7 * cols)
+    xd = to_device(x)
+    d = nv.quantize_dual(xd, mode, rule, selmap=True, err_sum=True)
+    g = d["gscale"]
+    for side, axis in (("rows", AXIS_COLS), ("cols", AXIS_ROWS)):
+        s = nv.quantize(xd, axis, mode, rule, gscale=g.clone(), selmap=True, err_sum=True)
+        for k in ("packed", "scales", "selmap"):
+            assert torch.equal(d[side][k], s[k]), (side, k)
+        assert d[side]["err_sum"].item() == pytest.approx(s["err_sum"].item(), rel=1e-12)
+        ref = oracle.quantize(x, axis, mode, rule)
+        assert np.float32(g.item()).view(np.uint32) == ref["gscale"].view(np.uint32)
+        np.testing.assert_array_equal(d[side]["packed"].cpu().numpy().reshape(-1), ref["packed"])
+        np.testing.assert_array_equal(d[side]["scales"].cpu().numpy().reshape(-1), ref["scales"])
+        np.testing.assert_array_equal(d[side]["selmap"].cpu().numpy()[: ref["selmap"].size],
+                                      ref["selmap"])
+        assert d[side]["err_sum"].item() == pytest.approx(ref["err_sum"], rel=1e-6)
+
+
+def test_dual_layout_full_size():
+    banner("dual 8192x5120")
+    x = testkit.make(5)
+    xd = to_device(x)
+    d = nv.quantize_dual(xd, F46, MAE)
+    for side, axis in (("rows", AXIS_COLS), ("cols", AXIS_ROWS)):
+        ref = oracle.quantize(x, axis, F46, MAE, want_err=False)
+        np.testing.assert_array_equal(d[side]["packed"].cpu().numpy().reshape(-1), ref["packed"])
+        np.testing.assert_array_equal(d[side]["scales"].cpu().numpy().reshape(-1), ref["scales"])
