@@ -76,6 +76,13 @@ def lib():
         L.nvfp4o_dequantize.argtypes = [P, P, ctypes.c_float, i64, i64, ctypes.c_int,
                                         ctypes.c_int, P]
         L.nvfp4o_dequantize.restype = ctypes.c_int
+        L.nvfp4o_channel_absmax.argtypes = [P, i64, i64, P]
+        L.nvfp4o_channel_absmax.restype = None
+        L.nvfp4o_channel_order.argtypes = [P, i64, P]
+        L.nvfp4o_channel_order.restype = None
+        L.nvfp4o_quantize_residual.argtypes = [P, i64, i64, P, i64, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, P, P, P]
+        L.nvfp4o_quantize_residual.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -197,3 +204,46 @@ def dequantize(packed, scales, gscale, rows, cols, block_axis, out_bf16=False):
     if st != 0:
         raise ValueError(f"oracle dequantize failed with status {st}")
     return out
+
+
+# --- residual channels --------------------------------------------------------
+
+def channel_absmax(x_bf16):
+    """absmax[c] = max over rows of |x[r][c]| for a [rows][cols] bf16 tensor."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    out = np.zeros(cols, np.float32)
+    lib().nvfp4o_channel_absmax(_ptr(x), rows, cols, _ptr(out))
+    return out
+
+
+def channel_order(absmax):
+    """Channel order by absolute maximum, largest first, ties by lower index."""
+    a = np.ascontiguousarray(absmax, dtype=np.float32)
+    perm = np.zeros(a.size, np.int32)
+    lib().nvfp4o_channel_order(_ptr(a), a.size, _ptr(perm))
+    return perm
+
+
+def quantize_residual(x_bf16, perm, nres, mode, rule, gscale=None):
+    """Two-stage quantization with reordered channels and nres residual channels.
+
+    Returns dict(packed [rows][(cols+nres)/2], scales [rows][(cols+nres)/16],
+    gscale).
+    """
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    pm = np.ascontiguousarray(perm, dtype=np.int32)
+    width = cols + int(nres)
+    packed = np.zeros((rows, max(width, 0) // 2), np.uint8)
+    scales = np.zeros((rows, max(width, 0) // 16), np.uint8)
+    g = np.zeros(1, np.float32)
+    given = 0
+    if gscale is not None:
+        g[0] = np.float32(gscale)
+        given = 1
+    st = lib().nvfp4o_quantize_residual(_ptr(x), rows, cols, _ptr(pm), int(nres), int(mode),
+                                        int(rule), given, _ptr(g), _ptr(packed), _ptr(scales))
+    if st != 0:
+        raise ValueError(f"oracle quantize_residual failed with status {st}")
+    return {"packed": packed, "scales": scales, "gscale": np.float32(g[0])}

@@ -21,7 +21,10 @@
  *  [MIN] "Why Gated DeltaNet in hybrid 27B LLMs withstands 4-bit quantization"
  *        (sns.style) - "Deep analysis": NVFP4 scales blocks of 16 elements.
  *  [ARC] "ARCQuant" summary (gist.science, paper 2601.07475) - "Problem
- *        definition": NVFP4 requires block size 16.
+ *        definition": NVFP4 requires block size 16; "Methodology": channels
+ *        reordered by absolute maximum, the top-S outlier channels get a
+ *        residual stage (original minus primary reconstruction) quantized as
+ *        a second NVFP4 channel set appended along the reduction dimension.
  *
  * The pages fix the formats and the steps, not the floating-point operation
  * order.  This file fixes it, taking the plainest reading where the pages are
@@ -347,6 +350,87 @@ int nvfp4o_dequantize(const uint8_t* packed, const uint8_t* scales, float g, int
         ((uint16_t*)out)[o] = nvfp4o_f32_to_bf16(xhat);
       else
         ((float*)out)[o] = xhat;
+    }
+  }
+  return NVFP4O_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Residual channels [ARC, "Methodology"]                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Per-channel statistic of the outlier identification: absmax[c] = max over
+ * rows of |x[r][c]|. */
+void nvfp4o_channel_absmax(const uint16_t* x, int64_t rows, int64_t cols, float* absmax) {
+  for (int64_t c = 0; c < cols; ++c) absmax[c] = 0.0f;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      const float a = fabsf(nvfp4o_bf16_to_f32(x[r * cols + c]));
+      if (a > absmax[c]) absmax[c] = a;
+    }
+}
+
+/* Channels reordered by absolute maximum, largest first; equal maxima keep
+ * the lower channel index first.  perm[j] = channel placed at position j.
+ * (Insertion into a sorted list: O(cols^2), plain.) */
+void nvfp4o_channel_order(const float* absmax, int64_t cols, int32_t* perm) {
+  for (int64_t i = 0; i < cols; ++i) {
+    int64_t j = i;
+    while (j > 0 && absmax[perm[j - 1]] < absmax[i]) {
+      perm[j] = perm[j - 1];
+      --j;
+    }
+    perm[j] = (int32_t)i;
+  }
+}
+
+/* Two-stage quantization of x [rows][cols] with reordered channels.
+ * Primary stage: row r's reordered values x[r][perm[j]] quantized in blocks
+ * of 16 consecutive positions (nvfp4o_quantize_block), stored as blocks
+ * 0 .. cols/16 - 1 of output row r.  Residual stage: for the first nres
+ * positions (the largest channels), the residual of each element against
+ * its primary reconstruction, x - v*d rounded once, quantized in blocks of 16 with the same tensor scale g and
+ * stored as blocks cols/16 .. (cols + nres)/16 - 1.  Output rows hold
+ * (cols + nres)/2 code bytes and (cols + nres)/16 scale bytes. */
+int nvfp4o_quantize_residual(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* perm,
+                             int64_t nres, int mode, int rule, int gscale_given, float* gscale,
+                             uint8_t* packed, uint8_t* scales) {
+  int st = check_args(rows, cols, NVFP4O_AXIS_COLS, mode, rule);
+  if (st != NVFP4O_OK) return st;
+  if (nres < 0 || nres > cols || nres % 16 != 0) return NVFP4O_ERR_SHAPE;
+  if (!x || !perm || !gscale || !packed || !scales) return NVFP4O_ERR_NULL;
+  for (int64_t j = 0; j < cols; ++j)
+    if (perm[j] < 0 || perm[j] >= cols) return NVFP4O_ERR_SHAPE;
+  const float g = gscale_given ? *gscale : nvfp4o_global_scale(nvfp4o_amax(x, rows * cols), mode);
+  *gscale = g;
+  const int64_t bpr = cols / 16, bout = (cols + nres) / 16;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < bpr; ++b) {
+      float xb[16];
+      for (int i = 0; i < 16; ++i) xb[i] = nvfp4o_bf16_to_f32(x[r * cols + perm[b * 16 + i]]);
+      nvfp4o_block_t q;
+      nvfp4o_quantize_block(xb, g, mode, rule, &q);
+      const int c = q.chosen;
+      uint8_t* pk = packed + (r * bout + b) * 8;
+      for (int j = 0; j < 8; ++j) pk[j] = (uint8_t)(q.code[c][2 * j] | (q.code[c][2 * j + 1] << 4));
+      scales[r * bout + b] = q.S[c];
+      if (b * 16 < nres) {
+        /* Residual x - v*d of the kept candidate, rounded once.  An exact
+         * reconstruction leaves +0 (not the -0 that negating delta gives). */
+        float res[16];
+        for (int i = 0; i < 16; ++i) {
+          const uint8_t code = q.code[c][i];
+          const float v = (code & 8u) ? -E2M1_VAL[code & 7u] : E2M1_VAL[code & 7u];
+          res[i] = fmaf(-v, q.d[c], xb[i]);
+        }
+        nvfp4o_block_t qr;
+        nvfp4o_quantize_block(res, g, mode, rule, &qr);
+        const int cr = qr.chosen;
+        uint8_t* pr = packed + (r * bout + bpr + b) * 8;
+        for (int j = 0; j < 8; ++j)
+          pr[j] = (uint8_t)(qr.code[cr][2 * j] | (qr.code[cr][2 * j + 1] << 4));
+        scales[r * bout + bpr + b] = qr.S[cr];
+      }
     }
   }
   return NVFP4O_OK;

@@ -59,6 +59,11 @@ int nvfp4o_quantize(const uint16_t* x, int64_t rows, int64_t cols, int block_axi
                     uint8_t* selmap, double* err_sum);
 int nvfp4o_dequantize(const uint8_t* packed, const uint8_t* scales, float g, int64_t rows,
                       int64_t cols, int block_axis, int out_bf16, void* out);
+void nvfp4o_channel_absmax(const uint16_t* x, int64_t rows, int64_t cols, float* absmax);
+void nvfp4o_channel_order(const float* absmax, int64_t cols, int32_t* perm);
+int nvfp4o_quantize_residual(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* perm,
+                             int64_t nres, int mode, int rule, int gscale_given, float* gscale,
+                             uint8_t* packed, uint8_t* scales);
 
 #ifdef __cplusplus
 }
