@@ -82,7 +82,8 @@ enum { NVFP4_RULE_MSE = 0, NVFP4_RULE_MAE = 1, NVFP4_RULE_MAX = 2 }; /* ignored 
 enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
 enum {
   NVFP4_FLAG_GSCALE_GIVEN = 1u,   /* use *gscale_inout as g; skip the amax pass          */
-  NVFP4_FLAG_ERR_ACCUMULATE = 2u  /* add the error sum to *err_sum_out, do not zero it  */
+  NVFP4_FLAG_ERR_ACCUMULATE = 2u, /* add the error sum to *err_sum_out, do not zero it  */
+  NVFP4_FLAG_STATS_ACCUMULATE = 4u /* fold channel maxima into *absmax_inout's values    */
 };
 
 /* Tensor amax A = max |x| over `numel` bf16 values, written as fp32 to
@@ -194,6 +195,49 @@ nvfp4_status nvfp4_quantize_delayed(const uint16_t* in_bf16, int64_t rows, int64
 nvfp4_status nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, const float* gscale,
                               int64_t rows, int64_t cols, int block_axis, int out_dtype,
                               void* out, void* stream);
+
+/* Outlier channels, step 1 (calibration): the per-channel statistic and the
+ * channel order of the "ARCQuant" summary (gist.science 2601.07475),
+ * "Methodology" -- channels ranked by their absolute maximum.
+ *   in_bf16: [rows][cols] activations (channels are columns).
+ *   absmax_inout: cols floats; receives absmax[c] = max_r |x[r][c]|.  With
+ *     flags NVFP4_FLAG_STATS_ACCUMULATE the maxima are folded into the
+ *     values already there (non-negative floats, e.g. a previous call's
+ *     output: a running maximum over calibration batches); otherwise the
+ *     call zeroes them first.
+ *   perm_out: cols int32; perm_out[k] = the channel of rank k, largest
+ *     maximum first, equal maxima in increasing channel order.
+ *   cols: a positive multiple of 16, at most 32768.  absmax_inout and
+ *   perm_out must not overlap each other or the input (NVFP4_ERR_ALIAS). */
+nvfp4_status nvfp4_channel_order(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                 uint32_t flags, float* absmax_inout, int32_t* perm_out,
+                                 void* stream);
+
+/* Outlier channels, step 2 (per step): two-stage quantization with
+ * reordered channels ("ARCQuant" summary, gist.science 2601.07475,
+ * "Methodology": the leading channels get a residual stage, x minus its
+ * first-stage reconstruction, quantized again and appended along the
+ * reduction dimension).  Output row r holds W = cols + nres channels:
+ *   block j < cols/16: the 16 values x[r][perm[16j + i]], quantized as by
+ *     nvfp4_quantize_ex (NVFP4_AXIS_COLS) with tensor scale g;
+ *   block cols/16 + j, j < nres/16: the residual of block j, each element
+ *     x - dec(code) * d rounded once (an exact reconstruction gives +0),
+ *     quantized the same way with the same g, mode and rule.
+ *   packed_out [rows][W/2] and scales_out [rows][W/16], layouts as
+ *   nvfp4_quantize; dequantizing them as a [rows][W] tensor and adding
+ *   column cols + k to column k (k < nres) reconstructs the reordered x.
+ *   perm: cols int32 (device), normally nvfp4_channel_order's; any entry is
+ *     allowed (a gather), and entries outside [0, cols) read channel
+ *     cols - 1.
+ *   nres: residual channels, a multiple of 16 in [0, cols].
+ *   cols: a positive multiple of 16, at most 32768.
+ *   flags: 0 (g computed from the tensor amax as nvfp4_quantize does and
+ *     written to *gscale_inout) or NVFP4_FLAG_GSCALE_GIVEN (read g from it).
+ *   Outputs must not overlap the input, perm or each other (NVFP4_ERR_ALIAS). */
+nvfp4_status nvfp4_quantize_residual(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                     const int32_t* perm, int64_t nres, int mode, int rule,
+                                     uint32_t flags, uint8_t* packed_out, uint8_t* scales_out,
+                                     float* gscale_inout, void* stream);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(nvfp4_status s);

@@ -25,6 +25,7 @@ RULE_MSE, RULE_MAE, RULE_MAX = 0, 1, 2
 OUT_F32, OUT_BF16 = 0, 1
 FLAG_GSCALE_GIVEN = 1
 FLAG_ERR_ACCUMULATE = 2
+FLAG_STATS_ACCUMULATE = 4
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_ENUM", 3: "NVFP4_ERR_SHAPE",
           4: "NVFP4_ERR_ALIGN", 5: "NVFP4_ERR_HIP", 6: "NVFP4_ERR_ALIAS"}
@@ -43,6 +44,8 @@ SIGNATURES = {
     "nvfp4_quantize_dual": ([_P, _I64, _I64, _I, _I, _U32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
                             _I),
     "nvfp4_dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _P], _I),
+    "nvfp4_channel_order": ([_P, _I64, _I64, _U32, _P, _P, _P], _I),
+    "nvfp4_quantize_residual": ([_P, _I64, _I64, _P, _I64, _I, _I, _U32, _P, _P, _P, _P], _I),
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
     "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _P, _P], _I),
     "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _P, _P], _I),
@@ -300,6 +303,65 @@ def quantize_delayed(x, gscale, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RUL
     if err_sum:
         res["err_sum"] = err
     return res
+
+
+def channel_order(x, absmax=None, accumulate=False, perm=None, stream=None):
+    """Channel statistic and order of a [rows][cols] bf16 activation tensor
+    (nvfp4_channel_order): absmax[c] = max_r |x[r][c]| (float32, cols) and
+    perm (int32, cols), the channels by decreasing absmax, ties by index.
+    accumulate folds this tensor's maxima into the given `absmax` (a running
+    maximum over calibration batches).  Returns (absmax, perm)."""
+    x = _bf16_input(x)
+    if x.dim() != 2:
+        raise ValueError("input must be 2-D [rows][cols]")
+    rows, cols = x.shape
+    if absmax is None:
+        if accumulate:
+            raise ValueError("accumulate needs absmax")
+        absmax = torch.empty(cols, dtype=torch.float32, device=x.device)
+    if perm is None:
+        perm = torch.empty(cols, dtype=torch.int32, device=x.device)
+    flags = FLAG_STATS_ACCUMULATE if accumulate else 0
+    _check(lib().nvfp4_channel_order(_ptr(x), rows, cols, flags, _ptr(absmax), _ptr(perm),
+                                     _stream(stream)), "nvfp4_channel_order")
+    return absmax, perm
+
+
+def quantize_residual(x, perm, nres, mode=MODE_4OVER6, rule=RULE_MSE, gscale=None, out=None,
+                      stream=None):
+    """Two-stage quantization with reordered channels
+    (nvfp4_quantize_residual).  perm: int32 device tensor of cols channel
+    indices; nres: residual channels (multiple of 16, <= cols).  Returns a
+    dict with packed [rows][(cols+nres)/2], scales [rows][(cols+nres)/16] and
+    gscale; `gscale` given skips the amax pass."""
+    x = _bf16_input(x)
+    if x.dim() != 2:
+        raise ValueError("input must be 2-D [rows][cols]")
+    if perm.dtype != torch.int32 or not perm.is_cuda or not perm.is_contiguous():
+        raise TypeError("perm must be a contiguous int32 device tensor")
+    rows, cols = x.shape
+    width = cols + int(nres)
+    dev = x.device
+    out = dict(out or {})
+    packed = out.get("packed")
+    if packed is None:
+        packed = torch.empty((rows, max(width, 0) // 2), dtype=torch.uint8, device=dev)
+    scales = out.get("scales")
+    if scales is None:
+        scales = torch.empty((rows, max(width, 0) // 16), dtype=torch.uint8, device=dev)
+    flags = 0
+    if gscale is not None:
+        g = gscale
+        flags |= FLAG_GSCALE_GIVEN
+    else:
+        g = out.get("gscale")
+        if g is None:
+            g = torch.empty(1, dtype=torch.float32, device=dev)
+    st = lib().nvfp4_quantize_residual(_ptr(x), rows, cols, _ptr(perm), int(nres), int(mode),
+                                       int(rule), flags, _ptr(packed), _ptr(scales), _ptr(g),
+                                       _stream(stream))
+    _check(st, "nvfp4_quantize_residual")
+    return {"packed": packed, "scales": scales, "gscale": g}
 
 
 def dequantize(packed, scales, gscale, rows, cols, block_axis=AXIS_COLS, out_dtype=torch.float32,

@@ -29,6 +29,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
+// Whether the byte ranges [a, a + an) and [b, b + bn) overlap.
+bool overlap(const void* a, int64_t an, const void* b, int64_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)bn && y < x + (uintptr_t)an;
+}
+
 // Largest supported element count: keeps every byte offset and the bitmap
 // bit index comfortably inside int64.
 constexpr int64_t kMaxNumel = int64_t(1) << 46;
@@ -253,6 +259,83 @@ nvfp4_status nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, cons
   return hip_status(nvfp4::launch_dequantize(packed, scales, gscale, rows, cols, block_axis,
                                              out_dtype == NVFP4_OUT_BF16, out,
                                              static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+nvfp4_status nvfp4_channel_order(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                 uint32_t flags, float* absmax_inout, int32_t* perm_out,
+                                 void* stream) {
+  if (!in_bf16 || !absmax_inout || !perm_out) return NVFP4_ERR_NULL;
+  if (flags & ~uint32_t(NVFP4_FLAG_STATS_ACCUMULATE)) return NVFP4_ERR_ENUM;
+  const nvfp4_status shape = check_shape(rows, cols, NVFP4_AXIS_COLS);
+  if (shape != NVFP4_OK) return shape;
+  if (cols > nvfp4::kResidualMaxCols) return NVFP4_ERR_SHAPE;
+  if (!aligned(in_bf16, 16) || !aligned(absmax_inout, 4) || !aligned(perm_out, 4))
+    return NVFP4_ERR_ALIGN;
+  const int64_t in_bytes = rows * cols * 2, vec_bytes = cols * 4;
+  if (overlap(absmax_inout, vec_bytes, in_bf16, in_bytes) ||
+      overlap(perm_out, vec_bytes, in_bf16, in_bytes) ||
+      overlap(perm_out, vec_bytes, absmax_inout, vec_bytes))
+    return NVFP4_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(absmax_inout);
+  hipError_t e = hipSuccess;
+  if (!(flags & NVFP4_FLAG_STATS_ACCUMULATE))
+    e = nvfp4::launch_init(nullptr, nullptr, bits, cols, s);
+  if (e == hipSuccess) e = nvfp4::launch_channel_absmax(in_bf16, rows, cols, bits, s);
+  if (e == hipSuccess) e = nvfp4::launch_channel_rank(bits, cols, perm_out, s);
+  return hip_status(e);
+}
+
+nvfp4_status nvfp4_quantize_residual(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                     const int32_t* perm, int64_t nres, int mode, int rule,
+                                     uint32_t flags, uint8_t* packed_out, uint8_t* scales_out,
+                                     float* gscale_inout, void* stream) {
+  if (!in_bf16 || !perm || !packed_out || !scales_out || !gscale_inout) return NVFP4_ERR_NULL;
+  if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
+  if (rule != NVFP4_RULE_MSE && rule != NVFP4_RULE_MAE && rule != NVFP4_RULE_MAX)
+    return NVFP4_ERR_ENUM;
+  if (flags & ~uint32_t(NVFP4_FLAG_GSCALE_GIVEN)) return NVFP4_ERR_ENUM;
+  const nvfp4_status shape = check_shape(rows, cols, NVFP4_AXIS_COLS);
+  if (shape != NVFP4_OK) return shape;
+  if (cols > nvfp4::kResidualMaxCols || nres < 0 || nres > cols || nres % 16 != 0)
+    return NVFP4_ERR_SHAPE;
+  if (!aligned(in_bf16, 16) || !aligned(perm, 4) || !aligned(packed_out, 4) ||
+      !aligned(gscale_inout, 4))
+    return NVFP4_ERR_ALIGN;
+  const int64_t in_bytes = rows * cols * 2, width = cols + nres;
+  const int64_t p_bytes = rows * width / 2, s_bytes = rows * width / 16;
+  const void* outs[3] = {packed_out, scales_out, gscale_inout};
+  const int64_t out_bytes[3] = {p_bytes, s_bytes, 4};
+  for (int k = 0; k < 3; ++k) {
+    if (overlap(outs[k], out_bytes[k], in_bf16, in_bytes) ||
+        overlap(outs[k], out_bytes[k], perm, cols * 4))
+      return NVFP4_ERR_ALIAS;
+    for (int m = k + 1; m < 3; ++m)
+      if (overlap(outs[k], out_bytes[k], outs[m], out_bytes[m])) return NVFP4_ERR_ALIAS;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t variant = 0;
+  if (mode == NVFP4_MODE_4OVER6) {
+    variant |= nvfp4::kVarFourOverSix;
+    if (rule == NVFP4_RULE_MAE) variant |= nvfp4::kVarMae;
+    if (rule == NVFP4_RULE_MAX) variant |= nvfp4::kVarMax;
+  }
+  hipError_t e = hipSuccess;
+  if (!(flags & NVFP4_FLAG_GSCALE_GIVEN)) {
+    uint32_t* acc = reinterpret_cast<uint32_t*>(gscale_inout);
+    const float six_m = mode == NVFP4_MODE_4OVER6 ? 6.0f * 256.0f : 6.0f * 448.0f;
+    e = nvfp4::launch_init(acc, nullptr, nullptr, 0, s);
+    if (e == hipSuccess) e = nvfp4::launch_amax(in_bf16, rows * cols, six_m, acc, s);
+  }
+  if (e == hipSuccess)
+    e = nvfp4::launch_quantize_residual(in_bf16, rows, cols, perm, nres, gscale_inout, variant,
+                                        packed_out, scales_out, s);
+  return hip_status(e);
 }
 
 }  // extern "C"

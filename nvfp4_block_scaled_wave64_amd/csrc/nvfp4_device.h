@@ -210,23 +210,16 @@ __device__ __forceinline__ float block_error(float lo, float hi) {
   return kRule == kRuleMax ? __builtin_elementwise_maximum(lo, hi) : lo + hi;
 }
 
-// One block of 16 elements in one lane: wd[0..7] are its bf16 values
-// (element 2j in the low half of wd[j]).  Implements the block steps of the
-// method -- block max, the candidate scales, E2M1 codes, reconstruction
-// error against the original values, selection ("Technical summary: Four
-// Over Six (4/6)", "Adaptive block scaling algorithm") -- with each
-// candidate's error summed over elements 0-7 and 8-15 sequentially and the
-// two partial sums then added (or, for the maximum-error rule, the largest
-// single difference).
+// One block of 16 fp32 values x[0..15] in one lane.  Implements the block
+// steps of the method -- block max, the candidate scales, E2M1 codes,
+// reconstruction error against the original values, selection ("Technical
+// summary: Four Over Six (4/6)", "Adaptive block scaling algorithm") -- with
+// each candidate's error summed over elements 0-7 and 8-15 sequentially and
+// the two partial sums then added (or, for the maximum-error rule, the
+// largest single difference).
 template <bool k46, int kRule, bool kNeedErr>
-__device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float k6, float k4,
-                                                    const float2* tab) {
-  float x[16];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    x[2 * j] = bf16_lo(wd[j]);
-    x[2 * j + 1] = bf16_hi(wd[j]);
-  }
+__device__ __forceinline__ Block16 quantize_block16f(const float x[16], float k6, float k4,
+                                                     const float2* tab) {
   const float b = __builtin_elementwise_maximum(
       absmax3(absmax3(x[0], x[1], x[2]), absmax3(x[3], x[4], x[5]), absmax3(x[6], x[7], x[8])),
       absmax3(absmax3(x[9], x[10], x[11]), absmax3(x[12], x[13], x[14]), x[15]));
@@ -270,6 +263,20 @@ __device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float 
     r.err = r.pick4 ? e4 : e6;
   }
   return r;
+}
+
+// The same for a block of 16 bf16 values: wd[0..7] hold them in pairs
+// (element 2j in the low half of wd[j]).
+template <bool k46, int kRule, bool kNeedErr>
+__device__ __forceinline__ Block16 quantize_block16(const uint32_t wd[8], float k6, float k4,
+                                                    const float2* tab) {
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[2 * j] = bf16_lo(wd[j]);
+    x[2 * j + 1] = bf16_hi(wd[j]);
+  }
+  return quantize_block16f<k46, kRule, kNeedErr>(x, k6, k4, tab);
 }
 
 // Folds each lane's running maximum m (a non-negative float) into

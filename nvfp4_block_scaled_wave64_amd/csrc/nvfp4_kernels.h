@@ -107,6 +107,23 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, const
                              int64_t rows, int64_t cols, int block_axis, int out_bf16, void* out,
                              hipStream_t s);
 
+// ---- residual.hip: outlier channels with a residual stage ----
+// Atomic max of each column's max |x| into absmax_bits[c] (fp32 bit
+// patterns; the caller zeroes them, or keeps earlier values to fold several
+// tensors).
+hipError_t launch_channel_absmax(const uint16_t* in, int64_t rows, int64_t cols,
+                                 uint32_t* absmax_bits, hipStream_t s);
+// perm[k] = the channel of rank k (largest max first, ties by index).
+hipError_t launch_channel_rank(const uint32_t* absmax_bits, int64_t cols, int32_t* perm,
+                               hipStream_t s);
+// Primary blocks of the reordered channels and residual blocks of the first
+// nres of them; cols <= kResidualMaxCols (LDS holds a row and the order).
+constexpr int64_t kResidualMaxCols = 32768;
+hipError_t launch_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,
+                                    const int32_t* perm, int64_t nres, const float* gscale,
+                                    uint32_t variant, uint8_t* packed, uint8_t* scales,
+                                    hipStream_t s);
+
 // ---- verify.hip: the row quantizer's memory traffic without its arithmetic ----
 hipError_t launch_stream_pattern(const uint16_t* in, int64_t nblocks, uint8_t* packed,
                                  uint8_t* scales, hipStream_t s);

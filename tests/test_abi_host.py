@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
@@ -141,3 +141,63 @@ def test_dual_rejects(kw, status):
     pairs), enums, both extents multiples of 16, alignment."""
     assert du(**kw) == status
 
+
+D = ctypes.c_void_p(0x40000)
+E = ctypes.c_void_p(0x50000)
+
+
+def co(**kw):
+    args = dict(in_=A, rows=32, cols=64, flags=0, absmax=B, perm=C)
+    args.update(kw)
+    return nv.lib().nvfp4_channel_order(args["in_"], args["rows"], args["cols"], args["flags"],
+                                        args["absmax"], args["perm"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_=None), 1), (dict(absmax=None), 1), (dict(perm=None), 1),
+    (dict(flags=1), 2), (dict(flags=2), 2),
+    (dict(rows=0), 3), (dict(cols=40), 3), (dict(cols=32784), 3),
+    (dict(in_=MIS), 4), (dict(absmax=ctypes.c_void_p(0x20002)), 4),
+    (dict(perm=ctypes.c_void_p(0x30001)), 4),
+    (dict(absmax=ctypes.c_void_p(0x10100)), 6), (dict(perm=ctypes.c_void_p(0x200F0)), 6),
+])
+def test_channel_order_rejects(kw, status):
+    """nvfp4_channel_order: nulls, flags (only the accumulate flag), shape
+    (cols a multiple of 16 and at most 32768), alignment, and outputs that
+    overlap the input or each other."""
+    assert co(**kw) == status
+
+
+def test_channel_order_accumulate_flag_passes_the_enum_check():
+    # With the accumulate flag the first failing check is the shape's (a
+    # call with every argument valid would launch, so none is made here).
+    assert co(flags=4, rows=-1) == 3
+
+
+def qr(**kw):
+    args = dict(in_=A, rows=32, cols=64, perm=B, nres=16, mode=nv.MODE_4OVER6, rule=nv.RULE_MSE,
+                flags=0, packed=C, scales=D, g=E)
+    args.update(kw)
+    return nv.lib().nvfp4_quantize_residual(args["in_"], args["rows"], args["cols"], args["perm"],
+                                            args["nres"], args["mode"], args["rule"],
+                                            args["flags"], args["packed"], args["scales"],
+                                            args["g"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_=None), 1), (dict(perm=None), 1), (dict(packed=None), 1), (dict(scales=None), 1),
+    (dict(g=None), 1),
+    (dict(mode=2), 2), (dict(rule=3), 2), (dict(flags=2), 2), (dict(flags=4), 2),
+    (dict(rows=0), 3), (dict(cols=40), 3), (dict(cols=32784), 3), (dict(nres=-16), 3),
+    (dict(nres=8), 3), (dict(nres=80), 3),
+    (dict(in_=MIS), 4), (dict(perm=ctypes.c_void_p(0x20002)), 4),
+    (dict(packed=ctypes.c_void_p(0x30002)), 4), (dict(g=ctypes.c_void_p(0x50001)), 4),
+    (dict(packed=ctypes.c_void_p(0x10800)), 6), (dict(scales=ctypes.c_void_p(0x200F0)), 6),
+    (dict(g=ctypes.c_void_p(0x30100)), 6), (dict(scales=ctypes.c_void_p(0x30200)), 6),
+])
+def test_quantize_residual_rejects(kw, status):
+    """nvfp4_quantize_residual: nulls, enums (only GSCALE_GIVEN is a valid
+    flag), shape (cols a multiple of 16 up to 32768, nres a multiple of 16
+    in [0, cols]), alignment, and outputs overlapping the input, perm or
+    each other."""
+    assert qr(**kw) == status

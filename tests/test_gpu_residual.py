@@ -1,0 +1,191 @@
+"""GPU parity of the outlier-channel path ("ARCQuant" summary, gist.science
+2601.07475, "Methodology"): the per-channel maxima, the channel order and the
+two-stage (primary + residual) quantization through the C ABI, bit-exact
+against the oracle on the same seeded inputs.
+
+Shapes span the kernels' launch regimes: several rows per workgroup step
+(narrow tensors), one row per step with 256 threads (cols <= 8192) and with
+1024 threads (wider rows, up to the 32768-channel limit), ragged row counts,
+column tiles with a partial last tile, and the 32768 x 5120 prefill
+activations at full size."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_wave64_amd as nv
+import oracle
+import testkit
+from tests._parity import Guarded, to_device
+
+pytestmark = pytest.mark.gpu
+
+STD, F46 = nv.MODE_STD, nv.MODE_4OVER6
+MSE, MAE, MAXE = nv.RULE_MSE, nv.RULE_MAE, nv.RULE_MAX
+RULES = [(STD, MSE), (F46, MSE), (F46, MAE), (F46, MAXE)]
+
+
+def banner(msg):
+    print(f"\n[gpu-residual] {msg}", flush=True)
+
+
+def outlier_tensor(seed, rows, cols, n_out=8, factor=50.0):
+    x = testkit.fill((rows, cols), testkit.STUDENT_T3, 0.5, seed)
+    if n_out:
+        testkit.scale_columns(x, testkit.sample(seed + 1, cols, min(n_out, cols)), factor)
+    return x
+
+
+def gpu_channel_order(x, absmax=None, accumulate=False):
+    rows, cols = x.shape
+    a = Guarded(cols * 4, torch.float32)
+    p = Guarded(cols * 4, torch.int32)
+    if absmax is not None:
+        a.view.copy_(torch.from_numpy(absmax))
+    nv.channel_order(to_device(x), absmax=a.view, accumulate=accumulate, perm=p.view)
+    torch.cuda.synchronize()
+    a.check()
+    p.check()
+    return a.view.cpu().numpy(), p.view.cpu().numpy()
+
+
+def gpu_residual(x, perm, nres, mode, rule, gscale=None):
+    rows, cols = x.shape
+    width = cols + nres
+    bufs = {"packed": Guarded(rows * width // 2), "scales": Guarded(rows * width // 16),
+            "gscale": Guarded(4, torch.float32)}
+    g_arg = None
+    if gscale is not None:
+        bufs["gscale"].view.fill_(float(np.float32(gscale)))
+        g_arg = bufs["gscale"].view
+    out = {k: b.view for k, b in bufs.items()}
+    pd = torch.from_numpy(np.ascontiguousarray(perm, np.int32)).cuda()
+    nv.quantize_residual(to_device(x), pd, nres, mode, rule, gscale=g_arg, out=out)
+    torch.cuda.synchronize()
+    for b in bufs.values():
+        b.check()
+    return {"packed": bufs["packed"].view.cpu().numpy().reshape(rows, width // 2),
+            "scales": bufs["scales"].view.cpu().numpy().reshape(rows, width // 16),
+            "gscale": np.float32(bufs["gscale"].view.cpu().numpy()[0])}
+
+
+def assert_residual_same(got, ref, what):
+    assert got["gscale"].view(np.uint32) == np.float32(ref["gscale"]).view(np.uint32), what
+    for key in ("scales", "packed"):
+        a, b = got[key], ref[key]
+        bad = np.argwhere(a != b)
+        assert bad.size == 0, f"{what}: {key} differs at {bad[:5].tolist()} ({len(bad)} total)"
+
+
+# ------------------------------------------------------- channel order ----
+
+ORDER_SHAPES = [(1, 16), (7, 48), (33, 1040), (1000, 80), (129, 5120), (64, 8208), (9, 32768)]
+
+
+@pytest.mark.parametrize("rows,cols", ORDER_SHAPES)
+def test_channel_order_matches_oracle(rows, cols):
+    banner(f"channel order {rows}x{cols}")
+    x = outlier_tensor(1000 + cols, rows, cols)
+    a, p = gpu_channel_order(x)
+    a_ref = oracle.channel_absmax(x)
+    np.testing.assert_array_equal(a.view(np.uint32), a_ref.view(np.uint32))
+    np.testing.assert_array_equal(p, oracle.channel_order(a_ref))
+
+
+def test_channel_order_ties_and_zero_columns():
+    """Equal maxima keep increasing channel order; all-zero and -0 columns
+    rank last with maximum +0."""
+    banner("channel order ties")
+    rows, cols = 40, 512
+    rng = np.random.default_rng(7)
+    grid = np.array([0.5, 1.0, 1.5, 2.0], np.float32)
+    xf = grid[rng.integers(0, 4, (rows, cols))] * rng.choice([-1, 1], (rows, cols))
+    x = (xf.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x[:, 3] = 0
+    x[:, 100] = 0x8000
+    a, p = gpu_channel_order(x)
+    a_ref = oracle.channel_absmax(x)
+    np.testing.assert_array_equal(a.view(np.uint32), a_ref.view(np.uint32))
+    np.testing.assert_array_equal(p, oracle.channel_order(a_ref))
+    assert a[3] == 0 and a[100] == 0 and not np.signbit(a[100])
+
+
+def test_channel_order_accumulates_over_batches():
+    """The running maximum over calibration batches: the order of two
+    batches folded together equals the order of their concatenation."""
+    banner("channel order accumulate")
+    x1 = outlier_tensor(11, 300, 2048, n_out=4)
+    x2 = outlier_tensor(12, 200, 2048, n_out=4)
+    a1, _ = gpu_channel_order(x1)
+    a, p = gpu_channel_order(x2, absmax=a1, accumulate=True)
+    a_ref = oracle.channel_absmax(np.concatenate([x1, x2]))
+    np.testing.assert_array_equal(a.view(np.uint32), a_ref.view(np.uint32))
+    np.testing.assert_array_equal(p, oracle.channel_order(a_ref))
+
+
+# -------------------------------------------------- residual quantize ----
+
+RES_SHAPES = [
+    # (rows, cols, nres): several rows per step (narrow), ragged row counts,
+    # 256-thread and 1024-thread workgroups, nres = 0 and nres = cols
+    (1, 16, 16), (5, 48, 16), (37, 64, 0), (1000, 80, 32), (129, 1040, 112), (33, 5120, 256),
+    (16, 8192, 512), (20, 8208, 1024), (3, 32768, 2048), (7, 256, 256),
+]
+
+
+@pytest.mark.parametrize("rows,cols,nres", RES_SHAPES)
+@pytest.mark.parametrize("mode,rule", RULES)
+def test_quantize_residual_matches_oracle(rows, cols, nres, mode, rule):
+    banner(f"residual {rows}x{cols} nres={nres} mode={mode} rule={rule}")
+    x = outlier_tensor(2000 + cols + nres, rows, cols)
+    perm = oracle.channel_order(oracle.channel_absmax(x))
+    got = gpu_residual(x, perm, nres, mode, rule)
+    ref = oracle.quantize_residual(x, perm, nres, mode, rule)
+    assert_residual_same(got, ref, f"{rows}x{cols} nres={nres}")
+
+
+def test_quantize_residual_given_scale_and_any_index_vector():
+    """A given tensor scale, and an index vector that is not a permutation
+    (repeated channels, entries out of range read the last channel)."""
+    banner("residual given scale, general index vector")
+    rows, cols, nres = 50, 640, 64
+    x = outlier_tensor(31, rows, cols)
+    rng = np.random.default_rng(9)
+    idx = rng.integers(0, cols, cols).astype(np.int32)
+    idx[:5] = [-1, cols, cols + 7, 2 ** 31 - 1, -(2 ** 31)]
+    clamped = np.where((idx < 0) | (idx >= cols), cols - 1, idx).astype(np.int32)
+    g = np.float32(0.0123)
+    got = gpu_residual(x, idx, nres, F46, MSE, gscale=g)
+    ref = oracle.quantize_residual(x, clamped, nres, F46, MSE, gscale=g)
+    assert_residual_same(got, ref, "index vector")
+
+
+def test_quantize_residual_all_zero_tensor():
+    banner("residual zero tensor")
+    x = np.zeros((24, 128), np.uint16)
+    x[5, :] = 0x8000
+    perm = np.arange(128, dtype=np.int32)
+    got = gpu_residual(x, perm, 128, F46, MSE)
+    ref = oracle.quantize_residual(x, perm, 128, F46, MSE)
+    assert_residual_same(got, ref, "zeros")
+
+
+def test_quantize_residual_full_size_prefill():
+    """32768 x 5120 prefill activations (the Student-t recipe with 8 outlier
+    channels x100), order from the GPU, 256 residual channels: the whole
+    order and sampled rows of the outputs against the oracle."""
+    banner("residual 32768x5120 full size")
+    x = testkit.make(4)
+    rows, cols, nres = 32768, 5120, 256
+    a, p = gpu_channel_order(x)
+    a_ref = oracle.channel_absmax(x)
+    np.testing.assert_array_equal(a.view(np.uint32), a_ref.view(np.uint32))
+    perm = oracle.channel_order(a_ref)
+    np.testing.assert_array_equal(p, perm)
+    got = gpu_residual(x, perm, nres, F46, MSE)
+    g_ref = oracle.global_scale(oracle.amax(x), F46)
+    rng = np.random.default_rng(5)
+    pick = np.unique(np.concatenate([[0, 1, rows - 1], rng.integers(0, rows, 61)]))
+    ref = oracle.quantize_residual(x[pick], perm, nres, F46, MSE, gscale=g_ref)
+    assert got["gscale"].view(np.uint32) == g_ref.view(np.uint32)
+    sub = {"packed": got["packed"][pick], "scales": got["scales"][pick], "gscale": got["gscale"]}
+    assert_residual_same(sub, ref, "full size sampled rows")
