@@ -161,6 +161,20 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
                                             torch.bfloat16, out=deq), torch, stream)
     res["dequantize_bf16_gbps"] = gb(t_deq, 0.5 + 1 / 16 + 2)
     del deq
+    # Outlier channels with a residual stage on the same activations:
+    # calibration (channel maxima + order) and the per-step two-stage
+    # quantize with 256 residual channels (given g).
+    absmax_c, perm = nv.channel_order(xd)
+    res["channel_order_call_us"] = round(call_time(
+        lambda: nv.channel_order(xd, absmax=absmax_c, perm=perm), torch, stream, 20) * 1e6, 2)
+    nres = 256
+    ro = nv.quantize_residual(xd, perm, nres, nv.MODE_4OVER6, nv.RULE_MSE, gscale=g)
+    t_res = call_time(lambda: nv.quantize_residual(xd, perm, nres, nv.MODE_4OVER6, nv.RULE_MSE,
+                                                   gscale=g, out=ro), torch, stream)
+    res_bytes = numel * 2 + rows * (cols + nres) * (0.5 + 1 / 16)
+    res["residual_quantize_256ch_us"] = round(t_res * 1e6, 2)
+    res["residual_quantize_256ch_gbps"] = round(res_bytes / t_res / 1e9, 1)
+    del ro, absmax_c, perm
     # The quantize kernel on the other workloads' shapes and modes.
     for cid in (2, 3, 5):
         cfg = testkit.CONFIGS[cid]

@@ -8,7 +8,7 @@
 // the reduction dimension, so that one NVFP4 GEMM over cols + nres channels
 // adds the compensation by itself.
 //
-// Three kernels:
+// Kernels:
 //   channel_absmax_kernel  absmax[c] = max_r |x[r][c]|: a pure 2-byte-per-
 //       element read.  A workgroup owns a tile of 512 columns (64 lanes x 8
 //       bf16 per 16-byte load) and a range of rows; its 8 waves interleave
@@ -17,19 +17,23 @@
 //       the fp32 bit pattern (which orders the same way).
 //   channel_rank_kernel    perm[rank(c)] = c with rank(c) = the number of
 //       channels with a larger maximum, or an equal one and a lower index
-//       (largest first, stable).  O(cols^2) comparisons against LDS tiles of
-//       the maxima; a few microseconds at transformer widths, and run once
-//       per calibration, not per step.
-//   quantize_residual_kernel  the per-step pass.  A workgroup stages R whole
-//       rows in LDS with coalesced 16-byte loads (the next rows' loads are in
-//       flight while it works on the current ones), keeps the channel order
-//       in LDS as 16-bit indices, and gives each thread one output block: it
-//       gathers the block's 16 channels from LDS, quantizes them (the same
-//       block quantizer as the row-wise path), stores the codes and the
-//       scale byte, and for the first nres/16 blocks forms the residual
-//       x - v*d of the kept codes (one fused multiply-add per element, so an
-//       exact reconstruction leaves +0) and quantizes it as a second block
-//       with the same tensor scale, stored after the row's primary blocks.
+//       (largest first, stable): O(cols^2) comparisons, one 64-bit compare
+//       each, split over 16 waves per 64 channels; run once per calibration,
+//       not per step.
+//   the per-step pass, in two shapes.  Both keep the channel order in LDS
+//       as 16-bit indices and stage whole rows in LDS with coalesced 16-byte
+//       loads (the next rows' loads in flight while the current ones are
+//       quantized); each output block is then one thread's work: gather the
+//       block's 16 channels from LDS, quantize them (the row-wise path's
+//       block quantizer), store codes and scale byte, and for the first
+//       nres/16 blocks form the residual x - v*d of the kept codes (one fused
+//       multiply-add per element, so an exact reconstruction leaves +0) and
+//       quantize it as a second block with the same tensor scale, stored
+//       after the row's primary blocks.
+//     quantize_residual_wave_kernel (cols <= 8192): every wave owns a row
+//       buffer and streams its own rows, with no workgroup barrier.
+//     quantize_residual_kernel (wider rows): a 1024-thread workgroup shares
+//       R staged rows per step between two barriers.
 #include <algorithm>
 
 #include "nvfp4_device.h"
@@ -100,36 +104,93 @@ __global__ __launch_bounds__(kAbsThreads) void channel_absmax_kernel(
 
 // ------------------------------------------------------------------ rank --
 
-constexpr int kRankThreads = 64;
-constexpr uint32_t kRankTile = 1024;
+// A workgroup ranks 64 channels (one per lane); its 16 waves split the
+// channels compared against, and the partial counts meet in LDS.  Channel
+// j precedes i iff key_j > key_i with key = (max bits, ~index): a larger
+// maximum, or an equal one and a lower index -- one 64-bit compare per
+// pair.  The compared maxima are wave-uniform loads (scalar cache).
+constexpr int kRankThreads = 1024;
+constexpr int kRankWaves = kRankThreads / 64;
 
 __global__ __launch_bounds__(kRankThreads) void channel_rank_kernel(
     const uint32_t* __restrict__ absmax_bits, uint32_t cols, int32_t* __restrict__ perm) {
-  __shared__ uint32_t tile[kRankTile];
-  const uint32_t i = blockIdx.x * kRankThreads + threadIdx.x;
-  const uint32_t ai = i < cols ? absmax_bits[i] : 0u;
+  __shared__ uint32_t part[kRankWaves][64];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t i = blockIdx.x * 64u + lane;
+  const uint64_t key_i = ((uint64_t)(i < cols ? absmax_bits[i] : 0u) << 32) | (uint32_t)~i;
+  const uint32_t per = (cols + kRankWaves - 1) / kRankWaves;
+  const uint32_t j0 = std::min(cols, wave * per), j1 = std::min(cols, j0 + per);
   uint32_t rank = 0u;
-  for (uint32_t j0 = 0; j0 < cols; j0 += kRankTile) {
-    const uint32_t n = std::min(kRankTile, cols - j0);
-    __syncthreads();
-    for (uint32_t t = threadIdx.x; t < n; t += kRankThreads) tile[t] = absmax_bits[j0 + t];
-    __syncthreads();
-    // Non-negative fp32 maxima order like their bit patterns.  Channel j
-    // precedes i if larger, or equal with a lower index.
-    for (uint32_t t = 0; t < n; ++t) {
-      const uint32_t a = tile[t];
-      rank += (a > ai) | ((a == ai) & (j0 + t < i));
-    }
+#pragma unroll 8
+  for (uint32_t j = j0; j < j1; ++j) {
+    const uint64_t key_j = ((uint64_t)absmax_bits[j] << 32) | (uint32_t)~j;
+    rank += key_j > key_i ? 1u : 0u;
   }
-  if (i < cols) perm[rank] = (int32_t)i;
+  part[wave][lane] = rank;
+  __syncthreads();
+  if (threadIdx.x < 64u) {
+    uint32_t r = 0u;
+    for (int k = 0; k < kRankWaves; ++k) r += part[k][lane];
+    if (i < cols) perm[r] = (int32_t)i;
+  }
 }
 
 // -------------------------------------------------------------- quantize --
 
-constexpr int kResVec = 4;  // 16-byte staging loads per thread and iteration
+// Output block j of one staged row xr (bf16 in LDS): gathers the channels
+// pm[16j .. 16j+15], quantizes them, stores codes and scale as block ob of
+// the output, and with `res` also the residual block ob + nb.
+template <bool k46, int kRule>
+__device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_t* pm,
+                                               uint32_t j, uint32_t ob, uint32_t nb, bool res,
+                                               __amdgpu_buffer_rsrc_t r_packed,
+                                               __amdgpu_buffer_rsrc_t r_scales,
+                                               const TensorScales& ts, const float2* tab) {
+  constexpr bool kNeedErr = k46;
+  const u32x4* p4 = reinterpret_cast<const u32x4*>(pm + j * 16u);
+  const u32x4 i0 = p4[0], i1 = p4[1];
+  const uint32_t ix[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+  uint32_t wd[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    wd[k] = (uint32_t)xr[ix[k] & 0xFFFFu] | ((uint32_t)xr[ix[k] >> 16] << 16);
+  const Block16 q = quantize_block16<k46, kRule, kNeedErr>(wd, ts.k6, ts.k4, tab);
+  u32x2 codes;
+  codes.x = q.lo;
+  codes.y = q.hi;
+  __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, ob * 8u, 0, kStreamStore);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q.S, r_scales, ob, 0, kMergedStore);
+  if (res) {
+    // Residual of the kept candidate, x - v*d rounded once.
+    float v[16], rx[16];
+    e2m1_decode8(q.lo, v);
+    e2m1_decode8(q.hi, v + 8);
+    const float d = tab[q.S].x;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      rx[2 * k] = __builtin_fmaf(-v[2 * k], d, bf16_lo(wd[k]));
+      rx[2 * k + 1] = __builtin_fmaf(-v[2 * k + 1], d, bf16_hi(wd[k]));
+    }
+    const Block16 qr = quantize_block16f<k46, kRule, kNeedErr>(rx, ts.k6, ts.k4, tab);
+    u32x2 rc;
+    rc.x = qr.lo;
+    rc.y = qr.hi;
+    __builtin_amdgcn_raw_buffer_store_b64(rc, r_packed, (ob + nb) * 8u, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)qr.S, r_scales, ob + nb, 0, kMergedStore);
+  }
+}
 
-template <uint32_t V, int T>
-__global__ __launch_bounds__(T) void quantize_residual_kernel(
+// Wide rows (cols > 8192): a workgroup of 1024 threads stages R rows in LDS
+// per step (coalesced 16-byte loads; the group's next rows are in flight
+// while it quantizes the current ones) and gives each thread one output
+// block at a time.
+constexpr int kResThreads = 1024;
+constexpr int kResVec = 8;    // 16-byte staging loads per thread and step
+constexpr int kResItems = 2;  // output blocks per thread and step, at least
+
+template <uint32_t V>
+__global__ __launch_bounds__(kResThreads) void quantize_residual_kernel(
     const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
     uint32_t nres, const float* __restrict__ gscale, uint8_t* __restrict__ packed,
     uint8_t* __restrict__ scales, uint32_t R) {
@@ -138,7 +199,6 @@ __global__ __launch_bounds__(T) void quantize_residual_kernel(
                         : (V & kVarMax) ? kRuleMax
                         : (V & kVarMae) ? kRuleMae
                                         : kRuleMse;
-  constexpr bool kNeedErr = k46;
 
   // LDS: scale table (1 KiB), channel order (cols 16-bit indices), R rows.
   extern __shared__ __align__(16) uint8_t lds[];
@@ -150,7 +210,7 @@ __global__ __launch_bounds__(T) void quantize_residual_kernel(
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
   // Indices are clamped into the row, so no entry can read outside it.
-  for (uint32_t c = threadIdx.x; c < cols; c += T)
+  for (uint32_t c = threadIdx.x; c < cols; c += kResThreads)
     pm[c] = (uint16_t)std::min((uint32_t)perm[c], cols - 1u);
 
   const uint32_t nb = cols >> 4, nrb = nres >> 4, bout = nb + nrb;
@@ -160,73 +220,116 @@ __global__ __launch_bounds__(T) void quantize_residual_kernel(
   auto rows_at = [&](int64_t it) -> uint32_t {
     return (uint32_t)std::min<int64_t>((int64_t)R, rows - it * R);
   };
-  // Rows of one iteration are contiguous: R * cols * 2 bytes from row it*R.
+  // Rows of one step are contiguous: R * cols * 2 bytes from row it*R.
   auto load = [&](int64_t it, u32x4 (&buf)[kResVec]) {
     const uint32_t nv = rows_at(it) * vrow;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(in + it * R * cols, nv * 16u);
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int k = 0; k < kResVec; ++k)
-      buf[k] = __builtin_amdgcn_raw_buffer_load_b128(r, (threadIdx.x + k * T) * 16u, 0,
+      buf[k] = __builtin_amdgcn_raw_buffer_load_b128(r, (threadIdx.x + k * kResThreads) * 16u, 0,
                                                      kStreamLoad);
+    __builtin_amdgcn_s_setprio(0);
   };
 
+  // The waves take turns at the extra items (blocks past a multiple of the
+  // thread count, residual blocks): the first item rotates one wave per step.
   u32x4 buf[kResVec];
   if ((int64_t)blockIdx.x < niter) load(blockIdx.x, buf);
+  uint32_t rot = 0u;
   for (int64_t it = blockIdx.x; it < niter; it += gridDim.x) {
     const uint32_t nr = rows_at(it);
     __syncthreads();  // the previous rows are consumed (and pm, tab written)
 #pragma unroll
     for (int k = 0; k < kResVec; ++k) {
-      const uint32_t v = threadIdx.x + k * T;
+      const uint32_t v = threadIdx.x + k * kResThreads;
       if (v < nr * vrow) xs4[v] = buf[k];
     }
     __syncthreads();
-    if (it + gridDim.x < niter) {
-      __builtin_amdgcn_s_setprio(3);
-      load(it + gridDim.x, buf);
-      __builtin_amdgcn_s_setprio(0);
-    }
+    if (it + gridDim.x < niter) load(it + gridDim.x, buf);
 
     const int64_t r0 = it * R;
     const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed + r0 * bout * 8, nr * bout * 8u);
     const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + r0 * bout, nr * bout);
     const uint32_t nitems = nr * nb;
-    for (uint32_t item = threadIdx.x; item < nitems; item += T) {
+#pragma unroll 1
+    for (uint32_t item = (threadIdx.x + rot) & (kResThreads - 1u); item < nitems;
+         item += kResThreads) {
       const uint32_t rr = item / nb, j = item - rr * nb;
-      const uint16_t* xr = xs + rr * cols;
-      const u32x4* p4 = reinterpret_cast<const u32x4*>(pm + j * 16u);
-      const u32x4 i0 = p4[0], i1 = p4[1];
-      const uint32_t ix[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-      uint32_t wd[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        wd[k] = (uint32_t)xr[ix[k] & 0xFFFFu] | ((uint32_t)xr[ix[k] >> 16] << 16);
-      const Block16 q = quantize_block16<k46, kRule, kNeedErr>(wd, ts.k6, ts.k4, tab);
-      const uint32_t ob = rr * bout + j;
-      u32x2 codes;
-      codes.x = q.lo;
-      codes.y = q.hi;
-      __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, ob * 8u, 0, kStreamStore);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q.S, r_scales, ob, 0, kMergedStore);
-      if (j < nrb) {
-        // Residual of the kept candidate, x - v*d rounded once.
-        float v[16], res[16];
-        e2m1_decode8(q.lo, v);
-        e2m1_decode8(q.hi, v + 8);
-        const float d = tab[q.S].x;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          res[2 * k] = __builtin_fmaf(-v[2 * k], d, bf16_lo(wd[k]));
-          res[2 * k + 1] = __builtin_fmaf(-v[2 * k + 1], d, bf16_hi(wd[k]));
-        }
-        const Block16 qr = quantize_block16f<k46, kRule, kNeedErr>(res, ts.k6, ts.k4, tab);
-        u32x2 rc;
-        rc.x = qr.lo;
-        rc.y = qr.hi;
-        __builtin_amdgcn_raw_buffer_store_b64(rc, r_packed, (ob + nb) * 8u, 0, kStreamStore);
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)qr.S, r_scales, ob + nb, 0, kMergedStore);
-      }
+      residual_block<k46, kRule>(xs + rr * cols, pm, j, rr * bout + j, nb, j < nrb, r_packed,
+                                 r_scales, ts, tab);
     }
+    rot = (rot + 64u) & (kResThreads - 1u);
+  }
+}
+
+// Narrow rows (cols <= 8192): every wave owns one LDS row buffer and
+// streams its own rows with no workgroup barrier.  The next row's loads
+// (kVpl 16-byte vectors per lane) are in flight while the wave quantizes the
+// current one; lane l handles the row's blocks l, l + 64, ...  The workgroup
+// shares the scale table and the channel order.
+template <uint32_t V, int kVpl>
+__global__ __launch_bounds__(1024) void quantize_residual_wave_kernel(
+    const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
+    uint32_t nres, const float* __restrict__ gscale, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ scales) {
+  constexpr bool k46 = (V & kVarFourOverSix) != 0;
+  constexpr int kRule = !k46 ? kRuleMse
+                        : (V & kVarMax) ? kRuleMax
+                        : (V & kVarMae) ? kRuleMae
+                                        : kRuleMse;
+  // LDS: scale table (1 KiB), channel order (cols 16-bit indices), one row
+  // per wave.
+  extern __shared__ __align__(16) uint8_t lds[];
+  float2* tab = reinterpret_cast<float2*>(lds);
+  uint16_t* pm = reinterpret_cast<uint16_t*>(lds + 1024);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t nwaves_g = blockDim.x >> 6;
+  uint16_t* xr = pm + cols * (1u + wave);  // cols * 2 bytes is a multiple of 32
+  u32x4* xr4 = reinterpret_cast<u32x4*>(xr);
+
+  const TensorScales ts = tensor_scales(*gscale);
+  build_scale_table(tab, ts);
+  for (uint32_t c = threadIdx.x; c < cols; c += blockDim.x)
+    pm[c] = (uint16_t)std::min((uint32_t)perm[c], cols - 1u);
+  __syncthreads();
+
+  const uint32_t nb = cols >> 4, nrb = nres >> 4, bout = nb + nrb;
+  const uint32_t vrow = cols >> 3;
+  const int64_t first = (int64_t)blockIdx.x * nwaves_g + wave;
+  const int64_t stride = (int64_t)gridDim.x * nwaves_g;
+
+  auto load = [&](int64_t row, u32x4 (&buf)[kVpl]) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(in + row * cols, vrow * 16u);
+#pragma unroll
+    for (int m = 0; m < kVpl; ++m)
+      buf[m] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + 64u * m) * 16u, 0, kStreamLoad);
+  };
+
+  u32x4 buf[kVpl];
+  if (first < rows) load(first, buf);
+  for (int64_t row = first; row < rows; row += stride) {
+    // LDS operations of one wave complete in order: the previous row's
+    // gathers are done before these writes, and the writes before the
+    // gathers below.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int m = 0; m < kVpl; ++m) {
+      const uint32_t v = lane + 64u * m;
+      if (v < vrow) xr4[v] = buf[m];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (row + stride < rows) {
+      __builtin_amdgcn_s_setprio(3);
+      load(row + stride, buf);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed + row * bout * 8, bout * 8u);
+    const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + row * bout, bout);
+#pragma unroll 1
+    for (uint32_t j = lane; j < nb; j += 64u)
+      residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, r_packed, r_scales, ts, tab);
   }
 }
 
@@ -251,36 +354,60 @@ hipError_t launch_channel_absmax(const uint16_t* in, int64_t rows, int64_t cols,
 
 hipError_t launch_channel_rank(const uint32_t* absmax_bits, int64_t cols, int32_t* perm,
                                hipStream_t s) {
-  const unsigned groups = (unsigned)((cols + kRankThreads - 1) / kRankThreads);
+  const unsigned groups = (unsigned)((cols + 63) / 64);
   channel_rank_kernel<<<groups, kRankThreads, 0, s>>>(absmax_bits, (uint32_t)cols, perm);
   return hipGetLastError();
 }
 
-template <uint32_t V, int T>
-static hipError_t launch_residual_vt(const uint16_t* in, int64_t rows, int64_t cols,
-                                     const int32_t* perm, int64_t nres, const float* gscale,
-                                     uint8_t* packed, uint8_t* scales, hipStream_t s) {
-  // Rows per iteration: enough output blocks for every thread, within the
-  // staging capacity of T * kResVec 16-byte vectors.
+template <uint32_t V>
+static hipError_t launch_residual_group(const uint16_t* in, int64_t rows, int64_t cols,
+                                        const int32_t* perm, int64_t nres, const float* gscale,
+                                        uint8_t* packed, uint8_t* scales, hipStream_t s) {
+  // Rows per step: at least kResItems output blocks per thread, within the
+  // staging capacity of kResThreads * kResVec 16-byte vectors and the
+  // compute unit's 160 KiB of LDS.
   const int64_t nb = cols / 16;
-  const int64_t cap_rows = (int64_t)T * kResVec * 8 / cols;
-  int64_t R = (T + nb - 1) / nb;
-  if (R > cap_rows) R = cap_rows;
+  int64_t R = ((int64_t)kResItems * kResThreads + nb - 1) / nb;
+  R = std::min<int64_t>(R, (int64_t)kResThreads * kResVec * 8 / cols);
+  R = std::min<int64_t>(R, (163840 - 1024 - cols * 2) / (cols * 2));
   if (R < 1) R = 1;
   const size_t lds = 1024 + (size_t)cols * 2 + (size_t)R * cols * 2;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&quantize_residual_kernel<V, T>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)lds);
+        reinterpret_cast<const void*>(&quantize_residual_kernel<V>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int64_t per_cu =
-      std::max<int64_t>(1, std::min<int64_t>(163840 / (int64_t)lds, 2048 / T));
+  // One workgroup per compute unit, persistent over steps.
   const int64_t niter = (rows + R - 1) / R;
-  const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(niter, per_cu * device_cu_count()));
-  quantize_residual_kernel<V, T><<<(unsigned)groups, T, lds, s>>>(
+  const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(niter, device_cu_count()));
+  quantize_residual_kernel<V><<<(unsigned)groups, kResThreads, lds, s>>>(
       in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, (uint32_t)R);
+  return hipGetLastError();
+}
+
+template <uint32_t V, int kVpl>
+static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t cols,
+                                       const int32_t* perm, int64_t nres, const float* gscale,
+                                       uint8_t* packed, uint8_t* scales, hipStream_t s) {
+  // As many waves per compute unit as their row buffers fit in LDS (at most
+  // 16), one workgroup per compute unit.
+  const int64_t row_bytes = cols * 2;
+  int64_t waves = (163840 - 1024 - row_bytes) / row_bytes;
+  if (waves > 16) waves = 16;
+  if (waves < 1) waves = 1;
+  const int64_t per_group = waves;
+  int64_t groups = (rows + per_group - 1) / per_group;
+  if (groups > device_cu_count()) groups = device_cu_count();
+  const size_t lds = 1024 + (size_t)row_bytes * (1 + waves);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&quantize_residual_wave_kernel<V, kVpl>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  quantize_residual_wave_kernel<V, kVpl><<<(unsigned)groups, (unsigned)(waves * 64), lds, s>>>(
+      in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales);
   return hipGetLastError();
 }
 
@@ -288,9 +415,18 @@ template <uint32_t V>
 static hipError_t launch_residual_v(const uint16_t* in, int64_t rows, int64_t cols,
                                     const int32_t* perm, int64_t nres, const float* gscale,
                                     uint8_t* packed, uint8_t* scales, hipStream_t s) {
+  // Rows of up to 8192 channels: one row per wave (kVpl = cols / 512 vectors
+  // per lane, rounded up to the next instantiated size); wider rows: rows
+  // shared by a workgroup.
+  if (cols <= 2048)
+    return launch_residual_wave<V, 4>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+  if (cols <= 4096)
+    return launch_residual_wave<V, 8>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+  if (cols <= 6144)
+    return launch_residual_wave<V, 12>(in, rows, cols, perm, nres, gscale, packed, scales, s);
   if (cols <= 8192)
-    return launch_residual_vt<V, 256>(in, rows, cols, perm, nres, gscale, packed, scales, s);
-  return launch_residual_vt<V, 1024>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+    return launch_residual_wave<V, 16>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+  return launch_residual_group<V>(in, rows, cols, perm, nres, gscale, packed, scales, s);
 }
 
 hipError_t launch_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,

@@ -3,9 +3,10 @@
 two-stage (primary + residual) quantization through the C ABI, bit-exact
 against the oracle on the same seeded inputs.
 
-Shapes span the kernels' launch regimes: several rows per workgroup step
-(narrow tensors), one row per step with 256 threads (cols <= 8192) and with
-1024 threads (wider rows, up to the 32768-channel limit), ragged row counts,
+Shapes span the kernels' launch regimes: one row per wave (cols <= 8192,
+each row-buffer size class, including rows shorter than a wave's 64
+blocks), rows shared by a 1024-thread workgroup (wider rows, one to several
+rows per step with a ragged last step, up to the 32768-channel limit),
 column tiles with a partial last tile, and the 32768 x 5120 prefill
 activations at full size."""
 import numpy as np
@@ -125,10 +126,12 @@ def test_channel_order_accumulates_over_batches():
 # -------------------------------------------------- residual quantize ----
 
 RES_SHAPES = [
-    # (rows, cols, nres): several rows per step (narrow), ragged row counts,
-    # 256-thread and 1024-thread workgroups, nres = 0 and nres = cols
+    # (rows, cols, nres): one row per wave for cols <= 8192 (every row-buffer
+    # size class, fewer rows than waves), workgroup-shared rows above (one,
+    # two and three rows per step, ragged last step), nres = 0 and nres = cols
     (1, 16, 16), (5, 48, 16), (37, 64, 0), (1000, 80, 32), (129, 1040, 112), (33, 5120, 256),
-    (16, 8192, 512), (20, 8208, 1024), (3, 32768, 2048), (7, 256, 256),
+    (16, 8192, 512), (20, 8208, 1024), (3, 32768, 2048), (7, 256, 256), (37, 12288, 512),
+    (300, 16384, 1024), (500, 4112, 64),
 ]
 
 
