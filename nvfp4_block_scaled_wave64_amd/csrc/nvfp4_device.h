@@ -133,33 +133,15 @@ __device__ __forceinline__ TensorScales tensor_scales(float g) {
   return t;
 }
 
-// Value of an E4M3 byte, for constant evaluation (exact scalings by 2).
-constexpr float e4m3_value_c(uint32_t S) {
-  const uint32_t e = (S >> 3) & 15u, m = S & 7u;
-  float v = (e == 0u) ? (float)m : (float)(8u + m);
-  int sh = (e == 0u) ? -9 : (int)e - 10;
-  for (; sh > 0; --sh) v *= 2.0f;
-  for (; sh < 0; ++sh) v *= 0.5f;
-  return v;
-}
-struct RecipTable {
-  float v[128];
-};
-// T[S] = RN(1/dec(S)) for every finite scale byte, evaluated by the compiler
-// (IEEE division, round to nearest even); T[0] = 0.
-constexpr RecipTable make_recip_table() {
-  RecipTable t{};
-  for (uint32_t S = 1; S < 127; ++S) t.v[S] = 1.0f / e4m3_value_c(S);
-  return t;
-}
-__device__ constexpr RecipTable kRecip = make_recip_table();
-
 // Decode multiplier d = dec(S) * g and encode multiplier
-// r = min(G * T[S], FLT_MAX) (r = 0 for S = 0) of block scale S.
+// r = min(G * T[S], FLT_MAX) of block scale S, with T[S] = RN(1/dec(S)) by
+// IEEE division (round to nearest even) for the finite scales S = 1..126
+// and T = 0 otherwise (S = 0 gives r = 0).
 __device__ __forceinline__ float2 scale_pair(uint32_t S, const TensorScales& t) {
+  const float dec = e4m3_decode(S);
   float2 dr;
-  dr.x = e4m3_decode(S) * t.g;
-  dr.y = fminf(t.G * kRecip.v[S], kFltMax);
+  dr.x = dec * t.g;
+  dr.y = (S - 1u) < 126u ? fminf(t.G * (1.0f / dec), kFltMax) : 0.0f;
   return dr;
 }
 
@@ -217,16 +199,17 @@ __device__ __forceinline__ float block_error(float lo, float hi) {
 // each candidate's error summed over elements 0-7 and 8-15 sequentially and
 // the two partial sums then added (or, for the maximum-error rule, the
 // largest single difference).
-template <bool k46, int kRule, bool kNeedErr>
-__device__ __forceinline__ Block16 quantize_block16f(const float x[16], float k6, float k4,
-                                                     const float2* tab) {
+//   `scales(S)` gives the (d, r) pair of scale byte S.
+template <bool k46, int kRule, bool kNeedErr, typename Scales>
+__device__ __forceinline__ Block16 quantize_block16_with(const float x[16], float k6, float k4,
+                                                         const Scales& scales) {
   const float b = __builtin_elementwise_maximum(
       absmax3(absmax3(x[0], x[1], x[2]), absmax3(x[3], x[4], x[5]), absmax3(x[6], x[7], x[8])),
       absmax3(absmax3(x[9], x[10], x[11]), absmax3(x[12], x[13], x[14]), x[15]));
 
   const uint32_t S2 = e4m3_encode2(b * k6, k46 ? b * k4 : 0.0f);
   const uint32_t S6 = S2 & 0xFFu, S4 = (S2 >> 8) & 0xFFu;
-  const float2 t6 = tab[S6];  // (d, r)
+  const float2 t6 = scales(S6);  // (d, r)
 
   float y[8];
 #pragma unroll
@@ -247,7 +230,7 @@ __device__ __forceinline__ Block16 quantize_block16f(const float x[16], float k6
   r.pick4 = false;
   r.err = e6;
   if (k46) {
-    const float2 t4 = tab[S4];
+    const float2 t4 = scales(S4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = x[i] * t4.y;
     const uint32_t c4lo = e2m1_encode8(y);
@@ -263,6 +246,14 @@ __device__ __forceinline__ Block16 quantize_block16f(const float x[16], float k6
     r.err = r.pick4 ? e4 : e6;
   }
   return r;
+}
+
+// The same with the (d, r) pairs read from a table tab[S] (LDS).
+template <bool k46, int kRule, bool kNeedErr>
+__device__ __forceinline__ Block16 quantize_block16f(const float x[16], float k6, float k4,
+                                                     const float2* tab) {
+  return quantize_block16_with<k46, kRule, kNeedErr>(x, k6, k4,
+                                                     [tab](uint32_t S) { return tab[S]; });
 }
 
 // The same for a block of 16 bf16 values: wd[0..7] hold them in pairs

@@ -148,14 +148,21 @@ __device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_
                                                __amdgpu_buffer_rsrc_t r_scales,
                                                const TensorScales& ts, const float2* tab) {
   constexpr bool kNeedErr = k46;
+  // pm holds byte offsets into the row, two per dword; each gathered bf16
+  // becomes its fp32 value by a 16-bit shift.
   const u32x4* p4 = reinterpret_cast<const u32x4*>(pm + j * 16u);
   const u32x4 i0 = p4[0], i1 = p4[1];
   const uint32_t ix[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-  uint32_t wd[8];
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(xr);
+  float x[16];
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    wd[k] = (uint32_t)xr[ix[k] & 0xFFFFu] | ((uint32_t)xr[ix[k] >> 16] << 16);
-  const Block16 q = quantize_block16<k46, kRule, kNeedErr>(wd, ts.k6, ts.k4, tab);
+  for (int k = 0; k < 8; ++k) {
+    x[2 * k] = __uint_as_float(
+        (uint32_t)*reinterpret_cast<const uint16_t*>(xb + (ix[k] & 0xFFFFu)) << 16);
+    x[2 * k + 1] =
+        __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(xb + (ix[k] >> 16)) << 16);
+  }
+  const Block16 q = quantize_block16f<k46, kRule, kNeedErr>(x, ts.k6, ts.k4, tab);
   u32x2 codes;
   codes.x = q.lo;
   codes.y = q.hi;
@@ -168,10 +175,7 @@ __device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_
     e2m1_decode8(q.hi, v + 8);
     const float d = tab[q.S].x;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      rx[2 * k] = __builtin_fmaf(-v[2 * k], d, bf16_lo(wd[k]));
-      rx[2 * k + 1] = __builtin_fmaf(-v[2 * k + 1], d, bf16_hi(wd[k]));
-    }
+    for (int k = 0; k < 16; ++k) rx[k] = __builtin_fmaf(-v[k], d, x[k]);
     const Block16 qr = quantize_block16f<k46, kRule, kNeedErr>(rx, ts.k6, ts.k4, tab);
     u32x2 rc;
     rc.x = qr.lo;
@@ -200,7 +204,8 @@ __global__ __launch_bounds__(kResThreads) void quantize_residual_kernel(
                         : (V & kVarMae) ? kRuleMae
                                         : kRuleMse;
 
-  // LDS: scale table (1 KiB), channel order (cols 16-bit indices), R rows.
+  // LDS: scale table (1 KiB), channel order (cols 16-bit byte offsets), R
+  // rows.
   extern __shared__ __align__(16) uint8_t lds[];
   float2* tab = reinterpret_cast<float2*>(lds);
   uint16_t* pm = reinterpret_cast<uint16_t*>(lds + 1024);
@@ -209,9 +214,10 @@ __global__ __launch_bounds__(kResThreads) void quantize_residual_kernel(
 
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
-  // Indices are clamped into the row, so no entry can read outside it.
+  // Byte offsets of the channels in a row; indices are clamped into the
+  // row, so no entry can read outside it.
   for (uint32_t c = threadIdx.x; c < cols; c += kResThreads)
-    pm[c] = (uint16_t)std::min((uint32_t)perm[c], cols - 1u);
+    pm[c] = (uint16_t)(2u * std::min((uint32_t)perm[c], cols - 1u));
 
   const uint32_t nb = cols >> 4, nrb = nres >> 4, bout = nb + nrb;
   const uint32_t vrow = cols >> 3;
@@ -278,7 +284,7 @@ __global__ __launch_bounds__(1024) void quantize_residual_wave_kernel(
                         : (V & kVarMax) ? kRuleMax
                         : (V & kVarMae) ? kRuleMae
                                         : kRuleMse;
-  // LDS: scale table (1 KiB), channel order (cols 16-bit indices), one row
+  // LDS: scale table (1 KiB), channel order (cols 16-bit byte offsets), one row
   // per wave.
   extern __shared__ __align__(16) uint8_t lds[];
   float2* tab = reinterpret_cast<float2*>(lds);
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(1024) void quantize_residual_wave_kernel(
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
   for (uint32_t c = threadIdx.x; c < cols; c += blockDim.x)
-    pm[c] = (uint16_t)std::min((uint32_t)perm[c], cols - 1u);
+    pm[c] = (uint16_t)(2u * std::min((uint32_t)perm[c], cols - 1u));
   __syncthreads();
 
   const uint32_t nb = cols >> 4, nrb = nres >> 4, bout = nb + nrb;
