@@ -174,6 +174,7 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     res_bytes = numel * 2 + rows * (cols + nres) * (0.5 + 1 / 16)
     res["residual_quantize_256ch_us"] = round(t_res * 1e6, 2)
     res["residual_quantize_256ch_gbps"] = round(res_bytes / t_res / 1e9, 1)
+    res["residual_quantize_256ch_frac_of_hbm_peak"] = round(res_bytes / t_res / 1e9 / HBM_PEAK_GBPS, 4)
     del ro, absmax_c, perm
     # The quantize kernel on the other workloads' shapes and modes.
     for cid in (2, 3, 5):
