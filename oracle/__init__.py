@@ -83,6 +83,10 @@ def lib():
         L.nvfp4o_quantize_residual.argtypes = [P, i64, i64, P, i64, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, P, P, P]
         L.nvfp4o_quantize_residual.restype = ctypes.c_int
+        L.nvfp4o_rms_rstd.argtypes = [P, i64, ctypes.c_float]
+        L.nvfp4o_rms_rstd.restype = ctypes.c_float
+        L.nvfp4o_rmsnorm.argtypes = [P, i64, i64, P, ctypes.c_float, P]
+        L.nvfp4o_rmsnorm.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -247,3 +251,21 @@ def quantize_residual(x_bf16, perm, nres, mode, rule, gscale=None):
     if st != 0:
         raise ValueError(f"oracle quantize_residual failed with status {st}")
     return {"packed": packed, "scales": scales, "gscale": np.float32(g[0])}
+
+
+def rms_rstd(xrow_bf16, eps):
+    x = np.ascontiguousarray(xrow_bf16, dtype=np.uint16)
+    return np.float32(lib().nvfp4o_rms_rstd(_ptr(x), x.size, float(np.float32(eps))))
+
+
+def rmsnorm(x_bf16, weight_bf16, eps):
+    """RMSNorm of a [rows][cols] bf16 tensor as the fused path defines it;
+    returns bf16 bit patterns (uint16)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    w = None if weight_bf16 is None else np.ascontiguousarray(weight_bf16, dtype=np.uint16)
+    y = np.zeros((rows, cols), np.uint16)
+    st = lib().nvfp4o_rmsnorm(_ptr(x), rows, cols, _ptr(w), float(np.float32(eps)), _ptr(y))
+    if st != 0:
+        raise ValueError(f"oracle rmsnorm failed with status {st}")
+    return y

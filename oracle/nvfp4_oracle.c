@@ -24,7 +24,9 @@
  *        definition": NVFP4 requires block size 16; "Methodology": channels
  *        reordered by absolute maximum, the top-S outlier channels get a
  *        residual stage (original minus primary reconstruction) quantized as
- *        a second NVFP4 channel set appended along the reduction dimension.
+ *        a second NVFP4 channel set appended along the reduction dimension;
+ *        the authors fuse channel reordering, RMSNorm and both quantization
+ *        stages into one kernel.
  *
  * The pages fix the formats and the steps, not the floating-point operation
  * order.  This file fixes it, taking the plainest reading where the pages are
@@ -431,6 +433,62 @@ int nvfp4o_quantize_residual(const uint16_t* x, int64_t rows, int64_t cols, cons
           pr[j] = (uint8_t)(qr.code[cr][2 * j] | (qr.code[cr][2 * j + 1] << 4));
         scales[r * bout + bpr + b] = qr.S[cr];
       }
+    }
+  }
+  return NVFP4O_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm before the two stages [ARC, "Methodology": the fused kernel]     */
+/* ------------------------------------------------------------------------ */
+
+/* Reciprocal RMS of one row of bf16 values, with the operation order fixed
+ * here (the page names RMSNorm only; these are readings):
+ *   s_v = sum of x*x over the 8 consecutive elements 8v .. 8v+7, sequential
+ *         fma from 0 (every product of two bf16 values is exact in binary32);
+ *   ss  = pairwise sum of the s_v: the array s_0 .. s_{V-1} is padded with
+ *         zeros to P entries (P the smallest power of two >= V, at least 64)
+ *         and adjacent pairs are added level by level;
+ *   rstd = RN(1 / RN(sqrt(RN(RN(ss / cols) + eps)))).
+ * cols is a positive multiple of 8. */
+float nvfp4o_rms_rstd(const uint16_t* xrow, int64_t cols, float eps) {
+  const int64_t nv = cols / 8;
+  int64_t p = 64;
+  while (p < nv) p *= 2;
+  float* a = (float*)calloc((size_t)p, sizeof(float));
+  if (!a) return 0.0f;
+  for (int64_t v = 0; v < nv; ++v) {
+    float t = 0.0f;
+    for (int i = 0; i < 8; ++i) {
+      const float x = nvfp4o_bf16_to_f32(xrow[v * 8 + i]);
+      t = fmaf(x, x, t);
+    }
+    a[v] = t;
+  }
+  for (int64_t n = p; n > 1; n /= 2)
+    for (int64_t i = 0; i < n / 2; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+  const float ss = a[0];
+  free(a);
+  const float ms = ss / (float)cols;
+  const float var = ms + eps;
+  const float sd = sqrtf(var);
+  return 1.0f / sd;
+}
+
+/* y = bf16(x * rstd), then, with a weight vector, bf16(w[c] * y) (the
+ * product of two bf16 values is exact in binary32, so that step rounds
+ * once).  x, y: [rows][cols] bf16; w: cols bf16 or NULL. */
+int nvfp4o_rmsnorm(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* w, float eps,
+                   uint16_t* y) {
+  if (!x || !y) return NVFP4O_ERR_NULL;
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0) return NVFP4O_ERR_SHAPE;
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* xr = x + r * cols;
+    const float rstd = nvfp4o_rms_rstd(xr, cols, eps);
+    for (int64_t c = 0; c < cols; ++c) {
+      uint16_t t = nvfp4o_f32_to_bf16(nvfp4o_bf16_to_f32(xr[c]) * rstd);
+      if (w) t = nvfp4o_f32_to_bf16(nvfp4o_bf16_to_f32(w[c]) * nvfp4o_bf16_to_f32(t));
+      y[r * cols + c] = t;
     }
   }
   return NVFP4O_OK;

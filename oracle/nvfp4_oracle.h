@@ -64,6 +64,9 @@ void nvfp4o_channel_order(const float* absmax, int64_t cols, int32_t* perm);
 int nvfp4o_quantize_residual(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* perm,
                              int64_t nres, int mode, int rule, int gscale_given, float* gscale,
                              uint8_t* packed, uint8_t* scales);
+float nvfp4o_rms_rstd(const uint16_t* xrow, int64_t cols, float eps);
+int nvfp4o_rmsnorm(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* w, float eps,
+                   uint16_t* y);
 
 #ifdef __cplusplus
 }
