@@ -175,7 +175,20 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     res["residual_quantize_256ch_us"] = round(t_res * 1e6, 2)
     res["residual_quantize_256ch_gbps"] = round(res_bytes / t_res / 1e9, 1)
     res["residual_quantize_256ch_frac_of_hbm_peak"] = round(res_bytes / t_res / 1e9 / HBM_PEAK_GBPS, 4)
-    del ro, absmax_c, perm
+    # RMSNorm in front (the fused path): one pass with a given g, and with g
+    # computed from max |y| by a first pass.
+    wgt = torch.from_numpy(testkit.fill((cols,), testkit.NORMAL, 1.0, 99).view(np.int16)).to(
+        dev).view(torch.bfloat16)
+    fo = nv.rmsnorm_quantize_residual(xd, perm, nres, weight=wgt, gscale=g)
+    t_f1 = call_time(lambda: nv.rmsnorm_quantize_residual(xd, perm, nres, weight=wgt, gscale=g,
+                                                          out=fo), torch, stream)
+    fo2 = nv.rmsnorm_quantize_residual(xd, perm, nres, weight=wgt)
+    t_f2 = call_time(lambda: nv.rmsnorm_quantize_residual(xd, perm, nres, weight=wgt, out=fo2),
+                     torch, stream)
+    res["rmsnorm_residual_given_g_us"] = round(t_f1 * 1e6, 2)
+    res["rmsnorm_residual_given_g_gbps"] = round(res_bytes / t_f1 / 1e9, 1)
+    res["rmsnorm_residual_two_pass_us"] = round(t_f2 * 1e6, 2)
+    del ro, absmax_c, perm, fo, fo2, wgt
     # The quantize kernel on the other workloads' shapes and modes.
     for cid in (2, 3, 5):
         cfg = testkit.CONFIGS[cid]

@@ -69,7 +69,7 @@ extern "C" {
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
   NVFP4_ERR_NULL = 1,  /* a required pointer is NULL                        */
-  NVFP4_ERR_ENUM = 2,  /* block_axis, mode, rule, out_dtype or flags invalid */
+  NVFP4_ERR_ENUM = 2,  /* block_axis, mode, rule, out_dtype, flags or eps invalid */
   NVFP4_ERR_SHAPE = 3, /* non-positive extent, or block-axis extent % 16 != 0 */
   NVFP4_ERR_ALIGN = 4, /* a pointer violates the alignment listed above      */
   NVFP4_ERR_HIP = 5,   /* a kernel launch failed                            */
@@ -238,6 +238,34 @@ nvfp4_status nvfp4_quantize_residual(const uint16_t* in_bf16, int64_t rows, int6
                                      const int32_t* perm, int64_t nres, int mode, int rule,
                                      uint32_t flags, uint8_t* packed_out, uint8_t* scales_out,
                                      float* gscale_inout, void* stream);
+
+/* Outlier channels with RMSNorm in front, in one pass over x: the fused
+ * kernel of the "ARCQuant" summary (gist.science 2601.07475),
+ * "Methodology" -- channel reordering, RMSNorm, the primary and the residual
+ * stage.  The result is that of nvfp4_quantize_residual applied to
+ * y = RMSNorm(x), bf16 [rows][cols], defined here as
+ *   ss   = sum over the row of x^2: per 8 consecutive elements a sequential
+ *          fma sum, those sums added pairwise (zero-padded power-of-two tree)
+ *   rstd = 1 / sqrt(ss / cols + eps)   (each step one IEEE binary32 operation)
+ *   y    = bf16(w[c] * bf16(x * rstd)), w = 1 without a weight vector
+ * (bf16 rounding to nearest even).
+ *   weight_bf16: cols bf16 (16-byte aligned), or NULL.
+ *   eps: finite and >= 0 (NVFP4_ERR_ENUM otherwise).
+ *   cols: a positive multiple of 16, at most 8192 (one row per wave in LDS).
+ *   flags: 0 -- a first pass over x computes g from max |y| (g = A/(6M) as
+ *     nvfp4_quantize) and writes it to *gscale_inout; or
+ *     NVFP4_FLAG_GSCALE_GIVEN -- read g from *gscale_inout (one pass).
+ *   amax_out (nullable): receives max |y| of this tensor (for a delayed
+ *     scale); must not overlap *gscale_inout.
+ *   perm, nres, mode, rule, packed_out, scales_out: as
+ *   nvfp4_quantize_residual.  Outputs must not overlap the inputs or each
+ *   other (NVFP4_ERR_ALIAS). */
+nvfp4_status nvfp4_rmsnorm_quantize_residual(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                             const uint16_t* weight_bf16, float eps,
+                                             const int32_t* perm, int64_t nres, int mode,
+                                             int rule, uint32_t flags, uint8_t* packed_out,
+                                             uint8_t* scales_out, float* gscale_inout,
+                                             float* amax_out, void* stream);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(nvfp4_status s);

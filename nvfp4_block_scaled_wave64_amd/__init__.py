@@ -46,6 +46,8 @@ SIGNATURES = {
     "nvfp4_dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _P], _I),
     "nvfp4_channel_order": ([_P, _I64, _I64, _U32, _P, _P, _P], _I),
     "nvfp4_quantize_residual": ([_P, _I64, _I64, _P, _I64, _I, _I, _U32, _P, _P, _P, _P], _I),
+    "nvfp4_rmsnorm_quantize_residual": ([_P, _I64, _I64, _P, ctypes.c_float, _P, _I64, _I, _I,
+                                         _U32, _P, _P, _P, _P, _P], _I),
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
     "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _P, _P], _I),
     "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _P, _P], _I),
@@ -362,6 +364,53 @@ def quantize_residual(x, perm, nres, mode=MODE_4OVER6, rule=RULE_MSE, gscale=Non
                                        _stream(stream))
     _check(st, "nvfp4_quantize_residual")
     return {"packed": packed, "scales": scales, "gscale": g}
+
+
+def rmsnorm_quantize_residual(x, perm, nres, weight=None, eps=1e-6, mode=MODE_4OVER6,
+                              rule=RULE_MSE, gscale=None, amax=False, out=None, stream=None):
+    """RMSNorm, channel reordering and the two quantization stages in one pass
+    over x (nvfp4_rmsnorm_quantize_residual).  weight: bf16 device tensor of
+    cols values, or None.  Returns the dict of quantize_residual, plus
+    "amax" (max |y|, 1-element float32) when asked for."""
+    x = _bf16_input(x)
+    if x.dim() != 2:
+        raise ValueError("input must be 2-D [rows][cols]")
+    if perm.dtype != torch.int32 or not perm.is_cuda or not perm.is_contiguous():
+        raise TypeError("perm must be a contiguous int32 device tensor")
+    if weight is not None:
+        weight = _bf16_input(weight)
+    rows, cols = x.shape
+    width = cols + int(nres)
+    dev = x.device
+    out = dict(out or {})
+    packed = out.get("packed")
+    if packed is None:
+        packed = torch.empty((rows, max(width, 0) // 2), dtype=torch.uint8, device=dev)
+    scales = out.get("scales")
+    if scales is None:
+        scales = torch.empty((rows, max(width, 0) // 16), dtype=torch.uint8, device=dev)
+    flags = 0
+    if gscale is not None:
+        g = gscale
+        flags |= FLAG_GSCALE_GIVEN
+    else:
+        g = out.get("gscale")
+        if g is None:
+            g = torch.empty(1, dtype=torch.float32, device=dev)
+    a = None
+    if amax:
+        a = out.get("amax")
+        if a is None:
+            a = torch.empty(1, dtype=torch.float32, device=dev)
+    st = lib().nvfp4_rmsnorm_quantize_residual(_ptr(x), rows, cols, _ptr(weight), float(eps),
+                                               _ptr(perm), int(nres), int(mode), int(rule), flags,
+                                               _ptr(packed), _ptr(scales), _ptr(g), _ptr(a),
+                                               _stream(stream))
+    _check(st, "nvfp4_rmsnorm_quantize_residual")
+    res = {"packed": packed, "scales": scales, "gscale": g}
+    if amax:
+        res["amax"] = a
+    return res
 
 
 def dequantize(packed, scales, gscale, rows, cols, block_axis=AXIS_COLS, out_dtype=torch.float32,

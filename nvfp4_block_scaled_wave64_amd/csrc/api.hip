@@ -55,7 +55,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   switch (s) {
     case NVFP4_OK: return "ok";
     case NVFP4_ERR_NULL: return "a required pointer is NULL";
-    case NVFP4_ERR_ENUM: return "invalid block_axis, mode, rule, out_dtype or flags";
+    case NVFP4_ERR_ENUM: return "invalid block_axis, mode, rule, out_dtype, flags or eps";
     case NVFP4_ERR_SHAPE: return "invalid shape (extents must be positive, block axis a multiple of 16)";
     case NVFP4_ERR_ALIGN: return "misaligned pointer";
     case NVFP4_ERR_HIP: return "HIP kernel launch failed";
@@ -335,6 +335,69 @@ nvfp4_status nvfp4_quantize_residual(const uint16_t* in_bf16, int64_t rows, int6
   if (e == hipSuccess)
     e = nvfp4::launch_quantize_residual(in_bf16, rows, cols, perm, nres, gscale_inout, variant,
                                         packed_out, scales_out, s);
+  return hip_status(e);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+nvfp4_status nvfp4_rmsnorm_quantize_residual(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                             const uint16_t* weight_bf16, float eps,
+                                             const int32_t* perm, int64_t nres, int mode,
+                                             int rule, uint32_t flags, uint8_t* packed_out,
+                                             uint8_t* scales_out, float* gscale_inout,
+                                             float* amax_out, void* stream) {
+  if (!in_bf16 || !perm || !packed_out || !scales_out || !gscale_inout) return NVFP4_ERR_NULL;
+  if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
+  if (rule != NVFP4_RULE_MSE && rule != NVFP4_RULE_MAE && rule != NVFP4_RULE_MAX)
+    return NVFP4_ERR_ENUM;
+  if (flags & ~uint32_t(NVFP4_FLAG_GSCALE_GIVEN)) return NVFP4_ERR_ENUM;
+  if (!(eps >= 0.0f && eps <= 3.0e38f)) return NVFP4_ERR_ENUM;  // finite, non-negative
+  const nvfp4_status shape = check_shape(rows, cols, NVFP4_AXIS_COLS);
+  if (shape != NVFP4_OK) return shape;
+  if (cols > nvfp4::kRmsMaxCols || nres < 0 || nres > cols || nres % 16 != 0)
+    return NVFP4_ERR_SHAPE;
+  if (!aligned(in_bf16, 16) || !aligned(weight_bf16, 16) || !aligned(perm, 4) ||
+      !aligned(packed_out, 4) || !aligned(gscale_inout, 4) || !aligned(amax_out, 4))
+    return NVFP4_ERR_ALIGN;
+  const int64_t in_bytes = rows * cols * 2, width = cols + nres;
+  const void* outs[4] = {packed_out, scales_out, gscale_inout, amax_out};
+  const int64_t out_bytes[4] = {rows * width / 2, rows * width / 16, 4, amax_out ? 4 : 0};
+  for (int k = 0; k < 4; ++k) {
+    if (overlap(outs[k], out_bytes[k], in_bf16, in_bytes) ||
+        overlap(outs[k], out_bytes[k], perm, cols * 4) ||
+        (weight_bf16 && overlap(outs[k], out_bytes[k], weight_bf16, cols * 2)))
+      return NVFP4_ERR_ALIAS;
+    for (int m = k + 1; m < 4; ++m)
+      if (overlap(outs[k], out_bytes[k], outs[m], out_bytes[m])) return NVFP4_ERR_ALIAS;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t variant = 0;
+  if (mode == NVFP4_MODE_4OVER6) {
+    variant |= nvfp4::kVarFourOverSix;
+    if (rule == NVFP4_RULE_MAE) variant |= nvfp4::kVarMae;
+    if (rule == NVFP4_RULE_MAX) variant |= nvfp4::kVarMax;
+  }
+  const bool given = (flags & NVFP4_FLAG_GSCALE_GIVEN) != 0;
+  uint32_t* acc = reinterpret_cast<uint32_t*>(gscale_inout);
+  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(amax_out);
+  const nvfp4::RmsArgs ra{weight_bf16, eps, amax_bits};
+  hipError_t e = hipSuccess;
+  // One small kernel zeroes the scale accumulator (when g is computed) and
+  // the amax output (when asked for).
+  if (!given)
+    e = nvfp4::launch_init(acc, nullptr, amax_bits, amax_bits ? 1 : 0, s);
+  else if (amax_bits)
+    e = nvfp4::launch_init(amax_bits, nullptr, nullptr, 0, s);
+  if (e == hipSuccess && !given) {
+    const float six_m = mode == NVFP4_MODE_4OVER6 ? 6.0f * 256.0f : 6.0f * 448.0f;
+    e = nvfp4::launch_rms_amax(in_bf16, rows, cols, ra, six_m, acc, s);
+  }
+  if (e == hipSuccess)
+    e = nvfp4::launch_rms_quantize_residual(in_bf16, rows, cols, perm, nres, gscale_inout,
+                                            variant, packed_out, scales_out, ra, s);
   return hip_status(e);
 }
 

@@ -124,6 +124,23 @@ hipError_t launch_quantize_residual(const uint16_t* in, int64_t rows, int64_t co
                                     uint32_t variant, uint8_t* packed, uint8_t* scales,
                                     hipStream_t s);
 
+// RMSNorm in front of the residual path: y = bf16(x * rstd), then
+// bf16(w * y) with a weight vector; amax_out (fp32 bits, nullable) receives
+// max |y| by atomic max (the caller zeroes it).
+struct RmsArgs {
+  const uint16_t* weight;  // cols bf16 (16-byte aligned), or null
+  float eps;
+  uint32_t* amax_out;
+};
+constexpr int64_t kRmsMaxCols = 8192;  // one row per wave in LDS
+hipError_t launch_rms_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,
+                                        const int32_t* perm, int64_t nres, const float* gscale,
+                                        uint32_t variant, uint8_t* packed, uint8_t* scales,
+                                        const RmsArgs& ra, hipStream_t s);
+// Atomic max of RN(max |y| / six_m) into *acc (fp32 bits; the caller zeroes it).
+hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const RmsArgs& ra,
+                           float six_m, uint32_t* acc, hipStream_t s);
+
 // ---- verify.hip: the row quantizer's memory traffic without its arithmetic ----
 hipError_t launch_stream_pattern(const uint16_t* in, int64_t nblocks, uint8_t* packed,
                                  uint8_t* scales, hipStream_t s);

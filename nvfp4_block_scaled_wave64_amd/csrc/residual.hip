@@ -269,42 +269,227 @@ __global__ __launch_bounds__(kResThreads) void quantize_residual_kernel(
   }
 }
 
+// ------------------------------------------------------------ RMSNorm --
+
+// RMSNorm applied in front of the two stages (the fused kernel of the
+// "ARCQuant" summary, "Methodology").  The operation order is fixed so that
+// any implementation reproduces it bit for bit: per 8 consecutive elements a
+// sequential fma sum of squares, those sums added pairwise (a zero-padded
+// power-of-two tree), then rstd = 1 / sqrt(ss / cols + eps) with IEEE sqrt
+// and division, y = bf16(x * rstd) and, with a weight, bf16(w * y).
+
+constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
+
+// Pairwise sum over the 64 lanes, levels in the order of the lane index
+// bits (lane l and l ^ 2^k at level k): ds_swizzle exchanges within 32
+// lanes, then the two halves' (uniform) values.  Every lane gets the sum.
+__device__ __forceinline__ float wave_pair_sum(float t) {
+  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (1 << 10)));
+  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (2 << 10)));
+  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (4 << 10)));
+  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (8 << 10)));
+  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (16 << 10)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 32));
+}
+
+// Sum of squares of the row a wave holds as kVpl 16-byte vectors per lane
+// (vector v = lane + 64 m covers elements 8v .. 8v+7; vectors past the row
+// were loaded as zeros).  Lane xor-shuffles add the pairs of the tree's
+// first six levels, the vectors of one lane the rest; every lane ends with
+// the same value.
+template <int kVpl>
+__device__ __forceinline__ float row_sumsq(const u32x4 (&buf)[kVpl]) {
+  constexpr int kM = pow2_at_least(kVpl);
+  float a[kM];
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    a[m] = 0.0f;
+    if (m < kVpl) {
+      float t = 0.0f;
+      t = __builtin_fmaf(bf16_lo(buf[m].x), bf16_lo(buf[m].x), t);
+      t = __builtin_fmaf(bf16_hi(buf[m].x), bf16_hi(buf[m].x), t);
+      t = __builtin_fmaf(bf16_lo(buf[m].y), bf16_lo(buf[m].y), t);
+      t = __builtin_fmaf(bf16_hi(buf[m].y), bf16_hi(buf[m].y), t);
+      t = __builtin_fmaf(bf16_lo(buf[m].z), bf16_lo(buf[m].z), t);
+      t = __builtin_fmaf(bf16_hi(buf[m].z), bf16_hi(buf[m].z), t);
+      t = __builtin_fmaf(bf16_lo(buf[m].w), bf16_lo(buf[m].w), t);
+      t = __builtin_fmaf(bf16_hi(buf[m].w), bf16_hi(buf[m].w), t);
+      a[m] = wave_pair_sum(t);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int n = kM; n > 1; n >>= 1) {
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+  }
+  return a[0];
+}
+
+__device__ __forceinline__ float rms_rstd(float ss, uint32_t cols, float eps) {
+  const float ms = ss / (float)cols;
+  const float var = ms + eps;
+  const float sd = __builtin_sqrtf(var);
+  return 1.0f / sd;
+}
+
+// bf16 pair (round to nearest even) of two fp32 values.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 p;
+  p.x = lo;
+  p.y = hi;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+}
+
+// One bf16 pair of y: bf16(x * rstd), then bf16(w * y).  Without a weight
+// vector w is 1, which leaves y unchanged (the product is exact).
+// ymax keeps the two halves' running max |y| as bf16 bit patterns
+// (non-negative bf16 values order like their patterns).
+__device__ __forceinline__ uint32_t rms_pair(uint32_t x, uint32_t w, float rstd, uint32_t& ymax) {
+  uint32_t y = pack_bf16(bf16_lo(x) * rstd, bf16_hi(x) * rstd);
+  y = pack_bf16(bf16_lo(w) * bf16_lo(y), bf16_hi(w) * bf16_hi(y));
+  ymax = max_u16x2_r(ymax, y & 0x7FFF7FFFu);
+  return y;
+}
+
+// fp32 value of the larger half of a packed bf16 maximum.
+__device__ __forceinline__ float bf16_pair_max(uint32_t m) {
+  return __uint_as_float(max(m & 0xFFFFu, m >> 16) << 16);
+}
+
+// Replaces the row held in buf by y = RMSNorm(x) (bf16) and folds max |y|
+// into ymax.  w4: the weight vector in LDS (ones without one), zero-padded
+// to 64 * kVpl 16-byte vectors.  Vectors past the row hold zeros and stay
+// zero.
+template <int kVpl>
+__device__ __forceinline__ void rms_apply(u32x4 (&buf)[kVpl], const u32x4* w4, uint32_t lane,
+                                          float rstd, uint32_t& ymax) {
+  // The widened values of the sum of squares are not reused here: an empty
+  // register constraint makes the compiler re-read the packed words, rather
+  // than keep 8 fp32 values per vector alive across the reduction.
+#pragma unroll
+  for (int m = 0; m < kVpl; ++m)
+    asm volatile("" : "+v"(buf[m].x), "+v"(buf[m].y), "+v"(buf[m].z), "+v"(buf[m].w));
+#pragma unroll
+  for (int m = 0; m < kVpl; ++m) {
+    const u32x4 w = w4[lane + 64u * m];
+    buf[m].x = rms_pair(buf[m].x, w.x, rstd, ymax);
+    buf[m].y = rms_pair(buf[m].y, w.y, rstd, ymax);
+    buf[m].z = rms_pair(buf[m].z, w.z, rstd, ymax);
+    buf[m].w = rms_pair(buf[m].w, w.w, rstd, ymax);
+  }
+}
+
+// Stages the weight vector in LDS as 64 * kVpl 16-byte vectors: the weights
+// (bf16 ones without a weight vector), then zeros.
+template <int kVpl>
+__device__ __forceinline__ void stage_weight(u32x4* w4, const uint16_t* weight, uint32_t vrow) {
+  const u32x4* wg = reinterpret_cast<const u32x4*>(weight);
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  for (uint32_t v = threadIdx.x; v < 64u * kVpl; v += blockDim.x)
+    w4[v] = v < vrow ? (weight ? wg[v] : ones) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Wave maximum of a non-negative float, then one atomic max per wave on its
+// bit pattern (of m / six_m when six_m > 0: the tensor scale's quotient,
+// monotone in m).
+__device__ __forceinline__ void wave_max_to(uint32_t* dst, float m, float six_m) {
+  uint32_t v = __float_as_uint(m);
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+  if ((threadIdx.x & 63u) == 0u) {
+    if (six_m > 0.0f) v = __float_as_uint(__uint_as_float(v) / six_m);
+    atomicMax(dst, v);
+  }
+}
+
+// First pass of the fused path when g is not given: max |y| over the
+// normalized tensor, folded into *acc as RN(max / six_m) = g.  One row per
+// wave, the weight vector in LDS.
+// Workgroup size of the kernels that normalize rows of kVpl >= 12 vectors
+// per lane: 12 waves, which leaves each wave room for its row, the
+// normalization and (fused) the block quantizer in registers.
+constexpr int rms_threads(int kVpl) { return kVpl >= 12 ? 768 : 1024; }
+
+template <int kVpl>
+__global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint16_t* __restrict__ in,
+                                                        int64_t rows, uint32_t cols,
+                                                        RmsArgs ra, float six_m,
+                                                        uint32_t* __restrict__ acc) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  u32x4* w4 = reinterpret_cast<u32x4*>(lds);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t vrow = cols >> 3;
+  stage_weight<kVpl>(w4, ra.weight, vrow);
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * (blockDim.x >> 6);
+  uint32_t ymax = 0u;
+  auto load = [&](int64_t row, u32x4 (&buf)[kVpl]) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(in + row * cols, vrow * 16u);
+#pragma unroll
+    for (int m = 0; m < kVpl; ++m)
+      buf[m] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + 64u * m) * 16u, 0, kStreamLoad);
+  };
+  // The next row's loads are in flight while the current row is reduced.
+  const int64_t first = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  u32x4 nxt[kVpl];
+  if (first < rows) load(first, nxt);
+  for (int64_t row = first; row < rows; row += stride) {
+    u32x4 buf[kVpl];
+#pragma unroll
+    for (int m = 0; m < kVpl; ++m) buf[m] = nxt[m];
+    if (row + stride < rows) load(row + stride, nxt);
+    const float rstd = rms_rstd(row_sumsq<kVpl>(buf), cols, ra.eps);
+    rms_apply<kVpl>(buf, w4, lane, rstd, ymax);
+  }
+  wave_max_to(acc, bf16_pair_max(ymax), six_m);
+}
+
 // Narrow rows (cols <= 8192): every wave owns one LDS row buffer and
 // streams its own rows with no workgroup barrier.  The next row's loads
 // (kVpl 16-byte vectors per lane) are in flight while the wave quantizes the
 // current one; lane l handles the row's blocks l, l + 64, ...  The workgroup
-// shares the scale table and the channel order.
-template <uint32_t V, int kVpl>
-__global__ __launch_bounds__(1024) void quantize_residual_wave_kernel(
+// shares the scale table, the channel order and (kRms) the weight vector.
+// With kRms the staged row is normalized in LDS (RMSNorm above; its sum of
+// squares comes from the row's registers), so the gathers, both stages and
+// the residual see y.
+template <uint32_t V, int kVpl, bool kRms>
+__global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_residual_wave_kernel(
     const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
     uint32_t nres, const float* __restrict__ gscale, uint8_t* __restrict__ packed,
-    uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ scales, RmsArgs ra) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr int kRule = !k46 ? kRuleMse
                         : (V & kVarMax) ? kRuleMax
                         : (V & kVarMae) ? kRuleMae
                                         : kRuleMse;
-  // LDS: scale table (1 KiB), channel order (cols 16-bit byte offsets), one row
-  // per wave.
+  // LDS: scale table (1 KiB), channel order (cols 16-bit byte offsets),
+  // with kRms the zero-padded weight vector, one row per wave.
   extern __shared__ __align__(16) uint8_t lds[];
   float2* tab = reinterpret_cast<float2*>(lds);
   uint16_t* pm = reinterpret_cast<uint16_t*>(lds + 1024);
+  u32x4* w4 = reinterpret_cast<u32x4*>(pm + cols);
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t nwaves_g = blockDim.x >> 6;
-  uint16_t* xr = pm + cols * (1u + wave);  // cols * 2 bytes is a multiple of 32
+  // cols * 2 bytes is a multiple of 32; the weight area is 64 * kVpl
+  // 16-byte vectors.
+  uint16_t* xr = pm + cols + (kRms ? 512u * kVpl : 0u) + cols * wave;
   u32x4* xr4 = reinterpret_cast<u32x4*>(xr);
 
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
   for (uint32_t c = threadIdx.x; c < cols; c += blockDim.x)
     pm[c] = (uint16_t)(2u * std::min((uint32_t)perm[c], cols - 1u));
+  const uint32_t vrow = cols >> 3;
+  if constexpr (kRms) stage_weight<kVpl>(w4, ra.weight, vrow);
   __syncthreads();
 
   const uint32_t nb = cols >> 4, nrb = nres >> 4, bout = nb + nrb;
-  const uint32_t vrow = cols >> 3;
   const int64_t first = (int64_t)blockIdx.x * nwaves_g + wave;
   const int64_t stride = (int64_t)gridDim.x * nwaves_g;
+  uint32_t ymax = 0u;  // packed bf16 max |y| (kRms)
 
   auto load = [&](int64_t row, u32x4 (&buf)[kVpl]) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(in + row * cols, vrow * 16u);
@@ -316,6 +501,8 @@ __global__ __launch_bounds__(1024) void quantize_residual_wave_kernel(
   u32x4 buf[kVpl];
   if (first < rows) load(first, buf);
   for (int64_t row = first; row < rows; row += stride) {
+    float rstd = 0.0f;
+    if constexpr (kRms) rstd = rms_rstd(row_sumsq<kVpl>(buf), cols, ra.eps);
     // LDS operations of one wave complete in order: the previous row's
     // gathers are done before these writes, and the writes before the
     // gathers below.
@@ -331,12 +518,24 @@ __global__ __launch_bounds__(1024) void quantize_residual_wave_kernel(
       load(row + stride, buf);
       __builtin_amdgcn_s_setprio(0);
     }
+    if constexpr (kRms) {
+      // Normalize the staged row in place, each lane its own vectors, while
+      // the next row's loads are in flight (its registers are taken).
+#pragma unroll 1
+      for (uint32_t v = lane; v < vrow; v += 64u) {
+        const u32x4 x = xr4[v], w = w4[v];
+        xr4[v] = u32x4{rms_pair(x.x, w.x, rstd, ymax), rms_pair(x.y, w.y, rstd, ymax),
+                       rms_pair(x.z, w.z, rstd, ymax), rms_pair(x.w, w.w, rstd, ymax)};
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
     const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed + row * bout * 8, bout * 8u);
     const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + row * bout, bout);
 #pragma unroll 1
     for (uint32_t j = lane; j < nb; j += 64u)
       residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, r_packed, r_scales, ts, tab);
   }
+  if (kRms && ra.amax_out) wave_max_to(ra.amax_out, bf16_pair_max(ymax), 0.0f);
 }
 
 // ------------------------------------------------------------- launchers --
@@ -392,28 +591,31 @@ static hipError_t launch_residual_group(const uint16_t* in, int64_t rows, int64_
   return hipGetLastError();
 }
 
-template <uint32_t V, int kVpl>
+template <uint32_t V, int kVpl, bool kRms>
 static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t cols,
                                        const int32_t* perm, int64_t nres, const float* gscale,
-                                       uint8_t* packed, uint8_t* scales, hipStream_t s) {
+                                       uint8_t* packed, uint8_t* scales, const RmsArgs& ra,
+                                       hipStream_t s) {
   // As many waves per compute unit as their row buffers fit in LDS (at most
   // 16), one workgroup per compute unit.
   const int64_t row_bytes = cols * 2;
-  int64_t waves = (163840 - 1024 - row_bytes) / row_bytes;
-  if (waves > 16) waves = 16;
+  const int64_t shared = 1024 + row_bytes + (kRms ? 1024 * kVpl : 0);
+  int64_t waves = (163840 - shared) / row_bytes;
+  const int64_t max_waves = (kRms ? rms_threads(kVpl) : 1024) / 64;
+  if (waves > max_waves) waves = max_waves;
   if (waves < 1) waves = 1;
-  const int64_t per_group = waves;
-  int64_t groups = (rows + per_group - 1) / per_group;
+  int64_t groups = (rows + waves - 1) / waves;
   if (groups > device_cu_count()) groups = device_cu_count();
-  const size_t lds = 1024 + (size_t)row_bytes * (1 + waves);
+  const size_t lds = (size_t)shared + (size_t)row_bytes * waves;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&quantize_residual_wave_kernel<V, kVpl>),
+        reinterpret_cast<const void*>(&quantize_residual_wave_kernel<V, kVpl, kRms>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  quantize_residual_wave_kernel<V, kVpl><<<(unsigned)groups, (unsigned)(waves * 64), lds, s>>>(
-      in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales);
+  quantize_residual_wave_kernel<V, kVpl, kRms>
+      <<<(unsigned)groups, (unsigned)(waves * 64), lds, s>>>(
+          in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, ra);
   return hipGetLastError();
 }
 
@@ -425,14 +627,70 @@ static hipError_t launch_residual_v(const uint16_t* in, int64_t rows, int64_t co
   // per lane, rounded up to the next instantiated size); wider rows: rows
   // shared by a workgroup.
   if (cols <= 2048)
-    return launch_residual_wave<V, 4>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+    return launch_residual_wave<V, 4, false>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                           RmsArgs{}, s);
   if (cols <= 4096)
-    return launch_residual_wave<V, 8>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+    return launch_residual_wave<V, 8, false>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                           RmsArgs{}, s);
   if (cols <= 6144)
-    return launch_residual_wave<V, 12>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+    return launch_residual_wave<V, 12, false>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                           RmsArgs{}, s);
   if (cols <= 8192)
-    return launch_residual_wave<V, 16>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+    return launch_residual_wave<V, 16, false>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                           RmsArgs{}, s);
   return launch_residual_group<V>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+}
+
+template <uint32_t V>
+static hipError_t launch_rms_residual_v(const uint16_t* in, int64_t rows, int64_t cols,
+                                        const int32_t* perm, int64_t nres, const float* gscale,
+                                        uint8_t* packed, uint8_t* scales, const RmsArgs& ra,
+                                        hipStream_t s) {
+  if (cols <= 2048)
+    return launch_residual_wave<V, 4, true>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                            ra, s);
+  if (cols <= 4096)
+    return launch_residual_wave<V, 8, true>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                            ra, s);
+  if (cols <= 6144)
+    return launch_residual_wave<V, 12, true>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                             ra, s);
+  return launch_residual_wave<V, 16, true>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                           ra, s);
+}
+
+hipError_t launch_rms_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,
+                                        const int32_t* perm, int64_t nres, const float* gscale,
+                                        uint32_t variant, uint8_t* packed, uint8_t* scales,
+                                        const RmsArgs& ra, hipStream_t s) {
+  switch (variant) {
+    case 0: return launch_rms_residual_v<0>(in, rows, cols, perm, nres, gscale, packed, scales, ra, s);
+    case 1: return launch_rms_residual_v<1>(in, rows, cols, perm, nres, gscale, packed, scales, ra, s);
+    case 3: return launch_rms_residual_v<3>(in, rows, cols, perm, nres, gscale, packed, scales, ra, s);
+    case 17: return launch_rms_residual_v<17>(in, rows, cols, perm, nres, gscale, packed, scales, ra, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int kVpl>
+static hipError_t launch_rms_amax_v(const uint16_t* in, int64_t rows, int64_t cols,
+                                    const RmsArgs& ra, float six_m, uint32_t* acc, hipStream_t s) {
+  // One workgroup per compute unit; LDS holds the weight vector.
+  const int64_t waves = rms_threads(kVpl) / 64;
+  int64_t groups = (rows + waves - 1) / waves;
+  if (groups > device_cu_count()) groups = device_cu_count();
+  const size_t lds = (size_t)1024 * kVpl;
+  rms_amax_kernel<kVpl><<<(unsigned)groups, (unsigned)(waves * 64), lds, s>>>(
+      in, rows, (uint32_t)cols, ra, six_m, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const RmsArgs& ra,
+                           float six_m, uint32_t* acc, hipStream_t s) {
+  if (cols <= 2048) return launch_rms_amax_v<4>(in, rows, cols, ra, six_m, acc, s);
+  if (cols <= 4096) return launch_rms_amax_v<8>(in, rows, cols, ra, six_m, acc, s);
+  if (cols <= 6144) return launch_rms_amax_v<12>(in, rows, cols, ra, six_m, acc, s);
+  return launch_rms_amax_v<16>(in, rows, cols, ra, six_m, acc, s);
 }
 
 hipError_t launch_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,

@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
@@ -201,3 +201,32 @@ def test_quantize_residual_rejects(kw, status):
     in [0, cols]), alignment, and outputs overlapping the input, perm or
     each other."""
     assert qr(**kw) == status
+
+
+F = ctypes.c_void_p(0x60000)
+
+
+def rq(**kw):
+    args = dict(in_=A, rows=32, cols=64, w=None, eps=1e-6, perm=B, nres=16, mode=nv.MODE_4OVER6,
+                rule=nv.RULE_MSE, flags=0, packed=C, scales=D, g=E, amax=None)
+    args.update(kw)
+    return nv.lib().nvfp4_rmsnorm_quantize_residual(
+        args["in_"], args["rows"], args["cols"], args["w"], args["eps"], args["perm"], args["nres"],
+        args["mode"], args["rule"], args["flags"], args["packed"], args["scales"], args["g"],
+        args["amax"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_=None), 1), (dict(perm=None), 1), (dict(packed=None), 1), (dict(g=None), 1),
+    (dict(mode=5), 2), (dict(rule=4), 2), (dict(flags=2), 2), (dict(eps=-1.0), 2),
+    (dict(eps=float("inf")), 2), (dict(eps=float("nan")), 2),
+    (dict(cols=8208), 3), (dict(cols=40), 3), (dict(rows=0), 3), (dict(nres=24), 3),
+    (dict(w=ctypes.c_void_p(0x60008)), 4), (dict(amax=ctypes.c_void_p(0x60002)), 4),
+    (dict(in_=MIS), 4),
+    (dict(amax=E), 6), (dict(w=ctypes.c_void_p(0x30000)), 6), (dict(g=ctypes.c_void_p(0x10010)), 6),
+])
+def test_rmsnorm_quantize_residual_rejects(kw, status):
+    """nvfp4_rmsnorm_quantize_residual: nulls, enums (eps finite and >= 0,
+    only GSCALE_GIVEN), shape (cols <= 8192), alignment (weight 16 bytes),
+    outputs overlapping inputs or each other."""
+    assert rq(**kw) == status

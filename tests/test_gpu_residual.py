@@ -192,3 +192,109 @@ def test_quantize_residual_full_size_prefill():
     assert got["gscale"].view(np.uint32) == g_ref.view(np.uint32)
     sub = {"packed": got["packed"][pick], "scales": got["scales"][pick], "gscale": got["gscale"]}
     assert_residual_same(sub, ref, "full size sampled rows")
+
+
+# ------------------------------------------ RMSNorm + residual, fused ----
+
+def gpu_rms_residual(x, w, eps, perm, nres, mode, rule, gscale=None, amax=False):
+    rows, cols = x.shape
+    width = cols + nres
+    bufs = {"packed": Guarded(rows * width // 2), "scales": Guarded(rows * width // 16),
+            "gscale": Guarded(4, torch.float32)}
+    if amax:
+        bufs["amax"] = Guarded(4, torch.float32)
+    g_arg = None
+    if gscale is not None:
+        bufs["gscale"].view.fill_(float(np.float32(gscale)))
+        g_arg = bufs["gscale"].view
+    out = {k: b.view for k, b in bufs.items()}
+    pd = torch.from_numpy(np.ascontiguousarray(perm, np.int32)).cuda()
+    wd = None if w is None else to_device(w)
+    nv.rmsnorm_quantize_residual(to_device(x), pd, nres, weight=wd, eps=eps, mode=mode, rule=rule,
+                                 gscale=g_arg, amax=amax, out=out)
+    torch.cuda.synchronize()
+    for b in bufs.values():
+        b.check()
+    res = {"packed": bufs["packed"].view.cpu().numpy().reshape(rows, width // 2),
+           "scales": bufs["scales"].view.cpu().numpy().reshape(rows, width // 16),
+           "gscale": np.float32(bufs["gscale"].view.cpu().numpy()[0])}
+    if amax:
+        res["amax"] = np.float32(bufs["amax"].view.cpu().numpy()[0])
+    return res
+
+
+RMS_SHAPES = [
+    # (rows, cols, nres): every row-buffer size class of the fused kernel,
+    # fewer rows than waves, ragged row counts, nres = 0 and nres = cols
+    (1, 16, 16), (7, 48, 0), (100, 1040, 64), (33, 2048, 256), (65, 2064, 128), (40, 4096, 512),
+    (19, 5120, 256), (25, 6144, 96), (13, 6160, 1024), (9, 8192, 8192),
+]
+
+
+@pytest.mark.parametrize("rows,cols,nres", RMS_SHAPES)
+@pytest.mark.parametrize("weighted", [False, True])
+def test_rmsnorm_residual_matches_oracle(rows, cols, nres, weighted):
+    banner(f"rmsnorm+residual {rows}x{cols} nres={nres} weighted={weighted}")
+    x = outlier_tensor(3000 + cols + nres, rows, cols)
+    w = testkit.fill((cols,), testkit.NORMAL, 1.0, 77 + cols) if weighted else None
+    eps = 1e-6
+    y = oracle.rmsnorm(x, w, eps)
+    perm = oracle.channel_order(oracle.channel_absmax(y))
+    got = gpu_rms_residual(x, w, eps, perm, nres, F46, MSE, amax=True)
+    ref = oracle.quantize_residual(y, perm, nres, F46, MSE)
+    assert_residual_same(got, ref, f"{rows}x{cols}")
+    assert got["amax"].view(np.uint32) == oracle.amax(y).view(np.uint32)
+
+
+@pytest.mark.parametrize("mode,rule", RULES)
+def test_rmsnorm_residual_rules_and_given_scale(mode, rule):
+    banner(f"rmsnorm+residual rules mode={mode} rule={rule}")
+    rows, cols, nres = 64, 3072, 192
+    x = outlier_tensor(41, rows, cols)
+    w = testkit.fill((cols,), testkit.NORMAL, 0.5, 42)
+    for eps in (0.0, 1e-2):
+        y = oracle.rmsnorm(x, w, eps)
+        perm = oracle.channel_order(oracle.channel_absmax(y))
+        g = np.float32(0.0071)
+        got = gpu_rms_residual(x, w, eps, perm, nres, mode, rule, gscale=g)
+        ref = oracle.quantize_residual(y, perm, nres, mode, rule, gscale=g)
+        assert_residual_same(got, ref, f"eps={eps}")
+
+
+def test_rmsnorm_residual_zero_rows_and_large_values():
+    """All-zero rows (y = 0 with eps > 0) and rows scaled near the bf16 top,
+    whose squares stay finite in binary32."""
+    banner("rmsnorm+residual zero rows, large values")
+    rows, cols, nres = 12, 256, 32
+    x = outlier_tensor(51, rows, cols)
+    x[3] = 0
+    x[7] = 0x8000
+    xf = testkit.bf16_to_f32(x[5]) * np.float32(2.0 ** 40)
+    x[5] = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    y = oracle.rmsnorm(x, None, 1e-5)
+    perm = oracle.channel_order(oracle.channel_absmax(y))
+    got = gpu_rms_residual(x, None, 1e-5, perm, nres, F46, MAE)
+    ref = oracle.quantize_residual(y, perm, nres, F46, MAE)
+    assert_residual_same(got, ref, "zeros/large")
+
+
+def test_rmsnorm_residual_full_size_prefill():
+    """32768 x 5120 prefill activations through the fused path (weight,
+    256 residual channels, g from the first pass), sampled rows against the
+    oracle."""
+    banner("rmsnorm+residual 32768x5120 full size")
+    x = testkit.make(4)
+    rows, cols, nres = 32768, 5120, 256
+    w = testkit.fill((cols,), testkit.NORMAL, 1.0, 99)
+    eps = 1e-6
+    y = oracle.rmsnorm(x, w, eps)
+    perm = oracle.channel_order(oracle.channel_absmax(y))
+    got = gpu_rms_residual(x, w, eps, perm, nres, F46, MSE, amax=True)
+    g_ref = oracle.global_scale(oracle.amax(y), F46)
+    assert got["gscale"].view(np.uint32) == g_ref.view(np.uint32)
+    assert got["amax"].view(np.uint32) == oracle.amax(y).view(np.uint32)
+    rng = np.random.default_rng(6)
+    pick = np.unique(np.concatenate([[0, 1, rows - 1], rng.integers(0, rows, 61)]))
+    ref = oracle.quantize_residual(y[pick], perm, nres, F46, MSE, gscale=g_ref)
+    sub = {"packed": got["packed"][pick], "scales": got["scales"][pick], "gscale": got["gscale"]}
+    assert_residual_same(sub, ref, "full size sampled rows")
