@@ -35,6 +35,7 @@
 //     quantize_residual_kernel (wider rows): a 1024-thread workgroup shares
 //       R staged rows per step between two barriers.
 #include <algorithm>
+#include <atomic>
 
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
@@ -540,6 +541,21 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
 
 // ------------------------------------------------------------- launchers --
 
+// Raises a kernel's dynamic-LDS limit above 64 KiB once per size it needs
+// (hipFuncSetAttribute), not on every launch.
+template <auto Kernel>
+static hipError_t allow_lds(size_t bytes) {
+  static std::atomic<size_t> allowed{65536};
+  size_t cur = allowed.load(std::memory_order_relaxed);
+  if (bytes <= cur) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  while (cur < bytes && !allowed.compare_exchange_weak(cur, bytes, std::memory_order_relaxed)) {
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_channel_absmax(const uint16_t* in, int64_t rows, int64_t cols,
                                  uint32_t* absmax_bits, hipStream_t s) {
   const int64_t ctiles = (cols / 8 + 63) / 64;
@@ -577,12 +593,8 @@ static hipError_t launch_residual_group(const uint16_t* in, int64_t rows, int64_
   R = std::min<int64_t>(R, (163840 - 1024 - cols * 2) / (cols * 2));
   if (R < 1) R = 1;
   const size_t lds = 1024 + (size_t)cols * 2 + (size_t)R * cols * 2;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&quantize_residual_kernel<V>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  const hipError_t e = allow_lds<&quantize_residual_kernel<V>>(lds);
+  if (e != hipSuccess) return e;
   // One workgroup per compute unit, persistent over steps.
   const int64_t niter = (rows + R - 1) / R;
   const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(niter, device_cu_count()));
@@ -607,12 +619,8 @@ static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t
   int64_t groups = (rows + waves - 1) / waves;
   if (groups > device_cu_count()) groups = device_cu_count();
   const size_t lds = (size_t)shared + (size_t)row_bytes * waves;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&quantize_residual_wave_kernel<V, kVpl, kRms>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  const hipError_t e = allow_lds<&quantize_residual_wave_kernel<V, kVpl, kRms>>(lds);
+  if (e != hipSuccess) return e;
   quantize_residual_wave_kernel<V, kVpl, kRms>
       <<<(unsigned)groups, (unsigned)(waves * 64), lds, s>>>(
           in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, ra);
