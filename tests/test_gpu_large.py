@@ -7,7 +7,8 @@ One 65600 x 16384 bf16 tensor (2^30 + 2^20 elements, 2 GiB) covers:
   * the dequantizer's splits at 2^25 and 2^26 blocks,
   * the amax pass's split at 2^27 16-byte vectors (element 2^30),
 and a 16384 x 65600 view of the same bytes exercises the column-blocked
-kernel's 64-bit addressing on a tensor larger than 2^31 bytes.
+kernel's 64-bit addressing on a tensor larger than 2^31 bytes.  A 140000 x
+8192 tensor (2.3 GB) does the same for the outlier-channel calls.
 """
 import numpy as np
 import pytest
@@ -95,4 +96,54 @@ def test_large_column_blocked_sampled_columns(big):
     idx = torch.from_numpy(pick).cuda()
     np.testing.assert_array_equal(r["packed"][idx].cpu().numpy().reshape(-1), ref["packed"])
     np.testing.assert_array_equal(r["scales"][idx].cpu().numpy().reshape(-1), ref["scales"])
+    del r
+
+
+# ------------------------------------------------ outlier-channel path ----
+
+RES_ROWS, RES_COLS, RES_NRES = 140000, 8192, 512  # 2.3 GB of bf16: offsets past 2^31 bytes
+
+
+@pytest.fixture(scope="module")
+def big_res():
+    banner(f"generating {RES_ROWS}x{RES_COLS}")
+    x = testkit.fill((RES_ROWS, RES_COLS), testkit.STUDENT_T3, 0.5, 0x7E5)
+    testkit.scale_columns(x, testkit.sample(0x7E6, RES_COLS, 16), 40.0)
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    yield x, xd
+    del xd
+    torch.cuda.empty_cache()
+
+
+def test_large_channel_order(big_res):
+    """Column maxima over 2.3 GB (the absmax pass splits its rows below 2^31
+    bytes per workgroup range) against numpy, in row chunks."""
+    x, xd = big_res
+    banner("channel maxima and order over 2.3 GB")
+    absmax, perm = nv.channel_order(xd)
+    got = absmax.cpu().numpy()
+    want = np.zeros(RES_COLS, np.float32)
+    for r0 in range(0, RES_ROWS, 8192):
+        want = np.maximum(want, np.abs(testkit.bf16_to_f32(x[r0:r0 + 8192])).max(axis=0))
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    np.testing.assert_array_equal(perm.cpu().numpy(), oracle.channel_order(want))
+
+
+def test_large_residual_sampled_rows(big_res):
+    """Two-stage quantize of rows past 2^31 input bytes (64-bit row offsets in
+    the per-wave kernel), sampled rows against the oracle with the same g."""
+    x, xd = big_res
+    banner("residual quantize over 2.3 GB")
+    rng = np.random.default_rng(8)
+    perm = rng.permutation(RES_COLS).astype(np.int32)
+    r = nv.quantize_residual(xd, torch.from_numpy(perm).cuda(), RES_NRES)
+    torch.cuda.synchronize()
+    g = np.float32(r["gscale"].cpu().numpy()[0])
+    assert g.view(np.uint32) == oracle.global_scale(oracle.amax(x), nv.MODE_4OVER6).view(np.uint32)
+    pick = np.unique(np.concatenate([[0, 131071, 131072, RES_ROWS - 1],
+                                     rng.integers(0, RES_ROWS, 28)]))
+    ref = oracle.quantize_residual(x[pick], perm, RES_NRES, nv.MODE_4OVER6, nv.RULE_MSE, gscale=g)
+    idx = torch.from_numpy(pick).cuda()
+    np.testing.assert_array_equal(r["packed"][idx].cpu().numpy(), ref["packed"])
+    np.testing.assert_array_equal(r["scales"][idx].cpu().numpy(), ref["scales"])
     del r
