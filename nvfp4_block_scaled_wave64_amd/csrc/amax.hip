@@ -16,8 +16,6 @@
 
 namespace nvfp4 {
 
-typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
-
 __global__ void init_kernel(uint32_t* zero_u32, double* zero_f64, uint32_t* zero_words,
                             int64_t nwords) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -26,11 +24,6 @@ __global__ void init_kernel(uint32_t* zero_u32, double* zero_f64, uint32_t* zero
     if (zero_f64) *zero_f64 = 0.0;
   }
   for (int64_t w = i; w < nwords; w += (int64_t)gridDim.x * blockDim.x) zero_words[w] = 0u;
-}
-
-__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
-  ushort2_t va = __builtin_bit_cast(ushort2_t, a), vb = __builtin_bit_cast(ushort2_t, b);
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(va, vb));
 }
 
 // amax reads with 16-byte non-temporal buffer loads, kAmaxUnroll of them in

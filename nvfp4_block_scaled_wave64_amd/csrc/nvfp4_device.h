@@ -99,6 +99,14 @@ __device__ __forceinline__ void e2m1_decode8(uint32_t w, float v[8]) {
   v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
 }
 
+// Packed maximum of two pairs of 16-bit unsigned values (v_pk_max_u16):
+// non-negative bf16 values order like their bit patterns.
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  const ushort2_t va = __builtin_bit_cast(ushort2_t, a), vb = __builtin_bit_cast(ushort2_t, b);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(va, vb));
+}
+
 // max(|a|, |b|, |c|) without canonicalising the operands (gfx950
 // v_maximum3_f32); the inputs are never NaN.
 __device__ __forceinline__ float absmax3(float a, float b, float c) {

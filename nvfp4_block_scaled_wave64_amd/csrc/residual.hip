@@ -21,19 +21,23 @@
 //       each, split over 16 waves per 64 channels; run once per calibration,
 //       not per step.
 //   the per-step pass, in two shapes.  Both keep the channel order in LDS
-//       as 16-bit indices and stage whole rows in LDS with coalesced 16-byte
-//       loads (the next rows' loads in flight while the current ones are
-//       quantized); each output block is then one thread's work: gather the
-//       block's 16 channels from LDS, quantize them (the row-wise path's
-//       block quantizer), store codes and scale byte, and for the first
-//       nres/16 blocks form the residual x - v*d of the kept codes (one fused
-//       multiply-add per element, so an exact reconstruction leaves +0) and
-//       quantize it as a second block with the same tensor scale, stored
-//       after the row's primary blocks.
+//       as 16-bit byte offsets into a row and stage whole rows in LDS with
+//       coalesced 16-byte loads (the next rows' loads in flight while the
+//       current ones are quantized); each output block is then one thread's
+//       work: gather the block's 16 channels from LDS, quantize them (the
+//       row-wise path's block quantizer), store codes and scale byte, and for
+//       the first nres/16 blocks form the residual x - v*d of the kept codes
+//       (one fused multiply-add per element, so an exact reconstruction
+//       leaves +0) and quantize it as a second block with the same tensor
+//       scale, stored after the row's primary blocks.
 //     quantize_residual_wave_kernel (cols <= 8192): every wave owns a row
-//       buffer and streams its own rows, with no workgroup barrier.
+//       buffer and streams its own rows, with no workgroup barrier.  With
+//       kRms it applies RMSNorm to each staged row first (the fused kernel
+//       of the same section).
 //     quantize_residual_kernel (wider rows): a 1024-thread workgroup shares
 //       R staged rows per step between two barriers.
+//   rms_amax_kernel  the fused path's first pass when the tensor scale is
+//       not given: max |RMSNorm(x)| folded into g.
 #include <algorithm>
 #include <atomic>
 
@@ -41,13 +45,6 @@
 #include "nvfp4_kernels.h"
 
 namespace nvfp4 {
-
-typedef unsigned short ushort2_r __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t max_u16x2_r(uint32_t a, uint32_t b) {
-  ushort2_r va = __builtin_bit_cast(ushort2_r, a), vb = __builtin_bit_cast(ushort2_r, b);
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(va, vb));
-}
 
 // ---------------------------------------------------------------- absmax --
 
@@ -82,10 +79,10 @@ __global__ __launch_bounds__(kAbsThreads) void channel_absmax_kernel(
     }
 #pragma unroll
     for (int k = 0; k < kAbsUnroll; ++k) {
-      m.x = max_u16x2_r(m.x, w[k].x & 0x7FFF7FFFu);
-      m.y = max_u16x2_r(m.y, w[k].y & 0x7FFF7FFFu);
-      m.z = max_u16x2_r(m.z, w[k].z & 0x7FFF7FFFu);
-      m.w = max_u16x2_r(m.w, w[k].w & 0x7FFF7FFFu);
+      m.x = max_u16x2(m.x, w[k].x & 0x7FFF7FFFu);
+      m.y = max_u16x2(m.y, w[k].y & 0x7FFF7FFFu);
+      m.z = max_u16x2(m.z, w[k].z & 0x7FFF7FFFu);
+      m.w = max_u16x2(m.w, w[k].w & 0x7FFF7FFFu);
     }
   }
   part[wave][lane] = m;
@@ -94,7 +91,7 @@ __global__ __launch_bounds__(kAbsThreads) void channel_absmax_kernel(
   if (threadIdx.x < 256u) {
     const uint32_t l = threadIdx.x >> 2, word = threadIdx.x & 3u;
     uint32_t v = 0u;
-    for (int k = 0; k < kAbsWaves; ++k) v = max_u16x2_r(v, part[k][l][word]);
+    for (int k = 0; k < kAbsWaves; ++k) v = max_u16x2(v, part[k][l][word]);
     const uint32_t c = (tile * 64u + l) * 8u + word * 2u;
     if (c < cols) {
       if (v & 0xFFFFu) atomicMax(absmax_bits + c, (v & 0xFFFFu) << 16);
@@ -350,7 +347,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ uint32_t rms_pair(uint32_t x, uint32_t w, float rstd, uint32_t& ymax) {
   uint32_t y = pack_bf16(bf16_lo(x) * rstd, bf16_hi(x) * rstd);
   y = pack_bf16(bf16_lo(w) * bf16_lo(y), bf16_hi(w) * bf16_hi(y));
-  ymax = max_u16x2_r(ymax, y & 0x7FFF7FFFu);
+  ymax = max_u16x2(ymax, y & 0x7FFF7FFFu);
   return y;
 }
 

@@ -230,7 +230,9 @@ def test_amax_and_global_scale(n):
 # ------------------------------------------------------------ dequantize ----
 
 @pytest.mark.parametrize("axis,shape", [(AXIS_COLS, (256, 1024)), (AXIS_ROWS, (256, 96)),
-                                        (AXIS_COLS, (3, 48)), (AXIS_ROWS, (48, 5))])
+                                        (AXIS_COLS, (3, 48)), (AXIS_ROWS, (48, 5)),
+                                        (AXIS_ROWS, (400, 200)), (AXIS_ROWS, (272, 130)),
+                                        (AXIS_ROWS, (1040, 257))])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_dequantize_round_trip(axis, shape, dtype):
     banner(f"dequantize axis={axis} shape={shape} {dtype}")
