@@ -12,6 +12,7 @@ Over Six (4/6)", gist.science 2512.02010, "Adaptive block scaling
 algorithm" and "Implementation details").
 """
 import ctypes
+import math
 import os
 
 import torch
@@ -112,6 +113,26 @@ def _bf16_input(x):
     return x
 
 
+def _need(t, numel, dtype, dev, name):
+    """t, checked to be a contiguous `dtype` tensor on `dev` holding at least
+    `numel` elements (what the library reads or writes there)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype or t.device != dev or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {dtype} tensor on {dev}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; {numel} are needed")
+    return t
+
+
+def _out(out, key, shape, dtype, dev):
+    """out[key] checked against `shape`, or a new tensor of that shape."""
+    t = out.get(key)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    return _need(t, math.prod(shape), dtype, dev, f"out[{key!r}]")
+
+
 def output_shapes(rows, cols, block_axis):
     """Shapes of (packed, scales) and the bitmap length for a [rows][cols] tensor."""
     n_rows, n_cols = (rows, cols) if block_axis == AXIS_COLS else (cols, rows)
@@ -122,16 +143,16 @@ def output_shapes(rows, cols, block_axis):
 def amax(x, out=None, stream=None):
     """A = max |x| of a bf16 tensor, as a 1-element float32 device tensor."""
     x = _bf16_input(x)
-    if out is None:
-        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    out = _out({"amax": out}, "amax", (1,), torch.float32, x.device)
     _check(lib().nvfp4_amax(_ptr(x), x.numel(), _ptr(out), _stream(stream)), "nvfp4_amax")
     return out
 
 
 def global_scale(amax_t, mode, out=None, stream=None):
     """g = A / (6*M) (M = 448 standard, 256 under 4/6) from a device amax."""
-    if out is None:
-        out = torch.empty(1, dtype=torch.float32, device=amax_t.device)
+    dev = amax_t.device
+    amax_t = _need(amax_t, 1, torch.float32, dev, "amax")
+    out = _out({"gscale": out}, "gscale", (1,), torch.float32, dev)
     _check(lib().nvfp4_global_scale(_ptr(amax_t), int(mode), _ptr(out), _stream(stream)),
            "nvfp4_global_scale")
     return out
@@ -169,28 +190,18 @@ def quantize(x, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RULE_MSE, gscale=No
     pshape, sshape, nsel = output_shapes(rows, cols, block_axis)
     dev = x.device
     out = dict(out or {})
-    packed = out.get("packed")
-    if packed is None:
-        packed = torch.empty(pshape, dtype=torch.uint8, device=dev)
-    scales = out.get("scales")
-    if scales is None:
-        scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+    packed = _out(out, "packed", pshape, torch.uint8, dev)
+    scales = _out(out, "scales", sshape, torch.uint8, dev)
     flags = 0
     if gscale is not None:
-        g = gscale
+        g = _need(gscale, 1, torch.float32, dev, "gscale")
         flags |= FLAG_GSCALE_GIVEN
     else:
-        g = out.get("gscale")
-        if g is None:
-            g = torch.empty(1, dtype=torch.float32, device=dev)
-    sel = out.get("selmap") if selmap else None
-    if selmap and sel is None:
-        sel = torch.empty(max(nsel, 1), dtype=torch.uint8, device=dev)
-    err = out.get("err_sum") if err_sum else None
-    if err_sum and err is None:
-        if err_accumulate:
-            raise ValueError("err_accumulate needs out['err_sum']")
-        err = torch.empty(1, dtype=torch.float64, device=dev)
+        g = _out(out, "gscale", (1,), torch.float32, dev)
+    sel = _out(out, "selmap", (max(nsel, 1),), torch.uint8, dev) if selmap else None
+    if err_sum and err_accumulate and out.get("err_sum") is None:
+        raise ValueError("err_accumulate needs out['err_sum']")
+    err = _out(out, "err_sum", (1,), torch.float64, dev) if err_sum else None
     if err_sum and err_accumulate:
         flags |= FLAG_ERR_ACCUMULATE
     args = (_ptr(x), rows, cols, int(block_axis), int(mode), int(rule), flags, _ptr(packed),
@@ -228,30 +239,21 @@ def quantize_dual(x, mode=MODE_4OVER6, rule=RULE_MSE, gscale=None, selmap=False,
     for key, axis in (("rows", AXIS_COLS), ("cols", AXIS_ROWS)):
         pshape, sshape, nsel = output_shapes(rows, cols, axis)
         o = dict(out.get(key) or {})
-        d = {"packed": o.get("packed"), "scales": o.get("scales")}
-        if d["packed"] is None:
-            d["packed"] = torch.empty(pshape, dtype=torch.uint8, device=dev)
-        if d["scales"] is None:
-            d["scales"] = torch.empty(sshape, dtype=torch.uint8, device=dev)
+        d = {"packed": _out(o, "packed", pshape, torch.uint8, dev),
+             "scales": _out(o, "scales", sshape, torch.uint8, dev)}
         if selmap:
-            d["selmap"] = o.get("selmap")
-            if d["selmap"] is None:
-                d["selmap"] = torch.empty(max(nsel, 1), dtype=torch.uint8, device=dev)
+            d["selmap"] = _out(o, "selmap", (max(nsel, 1),), torch.uint8, dev)
         if err_sum:
-            d["err_sum"] = o.get("err_sum")
-            if d["err_sum"] is None:
-                if err_accumulate:
-                    raise ValueError("err_accumulate needs out[side]['err_sum']")
-                d["err_sum"] = torch.empty(1, dtype=torch.float64, device=dev)
+            if err_accumulate and o.get("err_sum") is None:
+                raise ValueError("err_accumulate needs out[side]['err_sum']")
+            d["err_sum"] = _out(o, "err_sum", (1,), torch.float64, dev)
         sides[key] = d
     flags = 0
     if gscale is not None:
-        g = gscale
+        g = _need(gscale, 1, torch.float32, dev, "gscale")
         flags |= FLAG_GSCALE_GIVEN
     else:
-        g = out.get("gscale")
-        if g is None:
-            g = torch.empty(1, dtype=torch.float32, device=dev)
+        g = _out(out, "gscale", (1,), torch.float32, dev)
     if err_sum and err_accumulate:
         flags |= FLAG_ERR_ACCUMULATE
     r, c = sides["rows"], sides["cols"]
@@ -277,23 +279,13 @@ def quantize_delayed(x, gscale, block_axis=AXIS_COLS, mode=MODE_4OVER6, rule=RUL
     pshape, sshape, nsel = output_shapes(rows, cols, block_axis)
     dev = x.device
     out = dict(out or {})
-    packed = out.get("packed")
-    if packed is None:
-        packed = torch.empty(pshape, dtype=torch.uint8, device=dev)
-    scales = out.get("scales")
-    if scales is None:
-        scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
-    amax_t = out.get("amax")
-    if amax_t is None:
-        amax_t = torch.empty(1, dtype=torch.float32, device=dev)
-    sel = out.get("selmap") if selmap else None
-    if selmap and sel is None:
-        sel = torch.empty(max(nsel, 1), dtype=torch.uint8, device=dev)
-    err = out.get("err_sum") if err_sum else None
-    if err_sum and err is None:
-        if err_accumulate:
-            raise ValueError("err_accumulate needs out['err_sum']")
-        err = torch.empty(1, dtype=torch.float64, device=dev)
+    packed = _out(out, "packed", pshape, torch.uint8, dev)
+    scales = _out(out, "scales", sshape, torch.uint8, dev)
+    amax_t = _out(out, "amax", (1,), torch.float32, dev)
+    sel = _out(out, "selmap", (max(nsel, 1),), torch.uint8, dev) if selmap else None
+    if err_sum and err_accumulate and out.get("err_sum") is None:
+        raise ValueError("err_accumulate needs out['err_sum']")
+    err = _out(out, "err_sum", (1,), torch.float64, dev) if err_sum else None
     flags = FLAG_ERR_ACCUMULATE if (err_sum and err_accumulate) else 0
     st = lib().nvfp4_quantize_delayed(_ptr(x), rows, cols, int(block_axis), int(mode), int(rule),
                                       flags, _ptr(packed), _ptr(scales), _ptr(gscale),
@@ -317,12 +309,10 @@ def channel_order(x, absmax=None, accumulate=False, perm=None, stream=None):
     if x.dim() != 2:
         raise ValueError("input must be 2-D [rows][cols]")
     rows, cols = x.shape
-    if absmax is None:
-        if accumulate:
-            raise ValueError("accumulate needs absmax")
-        absmax = torch.empty(cols, dtype=torch.float32, device=x.device)
-    if perm is None:
-        perm = torch.empty(cols, dtype=torch.int32, device=x.device)
+    if absmax is None and accumulate:
+        raise ValueError("accumulate needs absmax")
+    absmax = _out({"absmax": absmax}, "absmax", (cols,), torch.float32, x.device)
+    perm = _out({"perm": perm}, "perm", (cols,), torch.int32, x.device)
     flags = FLAG_STATS_ACCUMULATE if accumulate else 0
     _check(lib().nvfp4_channel_order(_ptr(x), rows, cols, flags, _ptr(absmax), _ptr(perm),
                                      _stream(stream)), "nvfp4_channel_order")
@@ -339,26 +329,19 @@ def quantize_residual(x, perm, nres, mode=MODE_4OVER6, rule=RULE_MSE, gscale=Non
     x = _bf16_input(x)
     if x.dim() != 2:
         raise ValueError("input must be 2-D [rows][cols]")
-    if perm.dtype != torch.int32 or not perm.is_cuda or not perm.is_contiguous():
-        raise TypeError("perm must be a contiguous int32 device tensor")
     rows, cols = x.shape
     width = cols + int(nres)
     dev = x.device
+    perm = _need(perm, cols, torch.int32, dev, "perm")
     out = dict(out or {})
-    packed = out.get("packed")
-    if packed is None:
-        packed = torch.empty((rows, max(width, 0) // 2), dtype=torch.uint8, device=dev)
-    scales = out.get("scales")
-    if scales is None:
-        scales = torch.empty((rows, max(width, 0) // 16), dtype=torch.uint8, device=dev)
+    packed = _out(out, "packed", (rows, max(width, 0) // 2), torch.uint8, dev)
+    scales = _out(out, "scales", (rows, max(width, 0) // 16), torch.uint8, dev)
     flags = 0
     if gscale is not None:
-        g = gscale
+        g = _need(gscale, 1, torch.float32, dev, "gscale")
         flags |= FLAG_GSCALE_GIVEN
     else:
-        g = out.get("gscale")
-        if g is None:
-            g = torch.empty(1, dtype=torch.float32, device=dev)
+        g = _out(out, "gscale", (1,), torch.float32, dev)
     st = lib().nvfp4_quantize_residual(_ptr(x), rows, cols, _ptr(perm), int(nres), int(mode),
                                        int(rule), flags, _ptr(packed), _ptr(scales), _ptr(g),
                                        _stream(stream))
@@ -375,33 +358,26 @@ def rmsnorm_quantize_residual(x, perm, nres, weight=None, eps=1e-6, mode=MODE_4O
     x = _bf16_input(x)
     if x.dim() != 2:
         raise ValueError("input must be 2-D [rows][cols]")
-    if perm.dtype != torch.int32 or not perm.is_cuda or not perm.is_contiguous():
-        raise TypeError("perm must be a contiguous int32 device tensor")
-    if weight is not None:
-        weight = _bf16_input(weight)
     rows, cols = x.shape
     width = cols + int(nres)
     dev = x.device
+    perm = _need(perm, cols, torch.int32, dev, "perm")
+    if weight is not None:
+        weight = _bf16_input(weight)
+        if weight.numel() < cols or weight.device != dev:
+            raise ValueError(f"weight must hold {cols} bf16 values on {dev}")
     out = dict(out or {})
-    packed = out.get("packed")
-    if packed is None:
-        packed = torch.empty((rows, max(width, 0) // 2), dtype=torch.uint8, device=dev)
-    scales = out.get("scales")
-    if scales is None:
-        scales = torch.empty((rows, max(width, 0) // 16), dtype=torch.uint8, device=dev)
+    packed = _out(out, "packed", (rows, max(width, 0) // 2), torch.uint8, dev)
+    scales = _out(out, "scales", (rows, max(width, 0) // 16), torch.uint8, dev)
     flags = 0
     if gscale is not None:
-        g = gscale
+        g = _need(gscale, 1, torch.float32, dev, "gscale")
         flags |= FLAG_GSCALE_GIVEN
     else:
-        g = out.get("gscale")
-        if g is None:
-            g = torch.empty(1, dtype=torch.float32, device=dev)
+        g = _out(out, "gscale", (1,), torch.float32, dev)
     a = None
     if amax:
-        a = out.get("amax")
-        if a is None:
-            a = torch.empty(1, dtype=torch.float32, device=dev)
+        a = _out(out, "amax", (1,), torch.float32, dev)
     st = lib().nvfp4_rmsnorm_quantize_residual(_ptr(x), rows, cols, _ptr(weight), float(eps),
                                                _ptr(perm), int(nres), int(mode), int(rule), flags,
                                                _ptr(packed), _ptr(scales), _ptr(g), _ptr(a),
@@ -417,8 +393,11 @@ def dequantize(packed, scales, gscale, rows, cols, block_axis=AXIS_COLS, out_dty
                out=None, stream=None):
     """x_hat [rows][cols] (float32 or bfloat16) from packed codes and scales."""
     code = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
-    if out is None:
-        out = torch.empty((rows, cols), dtype=out_dtype, device=packed.device)
+    dev = packed.device
+    packed = _need(packed, rows * cols // 2, torch.uint8, dev, "packed")
+    scales = _need(scales, rows * cols // 16, torch.uint8, dev, "scales")
+    gscale = _need(gscale, 1, torch.float32, dev, "gscale")
+    out = _out({"out": out}, "out", (rows, cols), out_dtype, dev)
     st = lib().nvfp4_dequantize(_ptr(packed), _ptr(scales), _ptr(gscale), int(rows), int(cols),
                                 int(block_axis), code, _ptr(out), _stream(stream))
     _check(st, "nvfp4_dequantize")
@@ -431,7 +410,7 @@ def stream_pattern(x, packed, scales, stream=None):
     sizes, launch shape and access order.  Measurement only; the bytes
     written are not NVFP4 codes."""
     x = _bf16_input(x)
-    if packed.numel() * 2 != x.numel() or scales.numel() * 16 != x.numel():
-        raise ValueError("packed / scales sizes do not match the input")
+    packed = _need(packed, x.numel() // 2, torch.uint8, x.device, "packed")
+    scales = _need(scales, x.numel() // 16, torch.uint8, x.device, "scales")
     _check(lib().nvfp4v_stream_pattern(_ptr(x), x.numel() // 16, _ptr(packed), _ptr(scales),
                                        _stream(stream)), "nvfp4v_stream_pattern")

@@ -230,3 +230,26 @@ def test_rmsnorm_quantize_residual_rejects(kw, status):
     only GSCALE_GIVEN), shape (cols <= 8192), alignment (weight 16 bytes),
     outputs overlapping inputs or each other."""
     assert rq(**kw) == status
+
+
+def test_binding_checks_caller_tensors():
+    """The binding refuses a caller-supplied tensor of the wrong dtype,
+    device, layout or size before any library call (CPU tensors stand in for
+    device ones here)."""
+    import torch
+    cpu = torch.device("cpu")
+    t = torch.zeros(8, dtype=torch.float32)
+    assert nv._need(t, 8, torch.float32, cpu, "t") is t
+    with pytest.raises(ValueError):
+        nv._need(t, 9, torch.float32, cpu, "t")
+    with pytest.raises(TypeError):
+        nv._need(t, 8, torch.int32, cpu, "t")
+    with pytest.raises(TypeError):
+        nv._need(torch.zeros(4, 4)[:, ::2], 8, torch.float32, cpu, "t")
+    with pytest.raises(TypeError):
+        nv._need(t.numpy(), 8, torch.float32, cpu, "t")
+    assert nv._out({}, "k", (3, 5), torch.uint8, cpu).shape == (3, 5)
+    with pytest.raises(ValueError):
+        nv._out({"k": torch.zeros(14, dtype=torch.uint8)}, "k", (3, 5), torch.uint8, cpu)
+    with pytest.raises(ValueError):
+        nv.quantize(torch.zeros(16, 16, dtype=torch.bfloat16))  # host memory
