@@ -83,6 +83,11 @@ def lib():
         L.nvfp4o_quantize_residual.argtypes = [P, i64, i64, P, i64, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, P, P, P]
         L.nvfp4o_quantize_residual.restype = ctypes.c_int
+        L.nvfp4o_quantize_augmented.argtypes = [P, i64, i64, P, i64, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, P, P, P, ctypes.c_int]
+        L.nvfp4o_quantize_augmented.restype = ctypes.c_int
+        L.nvfp4o_gemm.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, i64, i64, i64, P, P]
+        L.nvfp4o_gemm.restype = ctypes.c_int
         L.nvfp4o_rms_rstd.argtypes = [P, i64, ctypes.c_float]
         L.nvfp4o_rms_rstd.restype = ctypes.c_float
         L.nvfp4o_rmsnorm.argtypes = [P, i64, i64, P, ctypes.c_float, P]
@@ -229,9 +234,11 @@ def channel_order(absmax):
     return perm
 
 
-def quantize_residual(x_bf16, perm, nres, mode, rule, gscale=None):
+def quantize_residual(x_bf16, perm, nres, mode, rule, gscale=None, duplicate=False):
     """Two-stage quantization with reordered channels and nres residual channels.
 
+    duplicate=True gives the weight side of the augmented product instead: the
+    appended blocks repeat the primary blocks of the first nres positions.
     Returns dict(packed [rows][(cols+nres)/2], scales [rows][(cols+nres)/16],
     gscale).
     """
@@ -246,8 +253,9 @@ def quantize_residual(x_bf16, perm, nres, mode, rule, gscale=None):
     if gscale is not None:
         g[0] = np.float32(gscale)
         given = 1
-    st = lib().nvfp4o_quantize_residual(_ptr(x), rows, cols, _ptr(pm), int(nres), int(mode),
-                                        int(rule), given, _ptr(g), _ptr(packed), _ptr(scales))
+    st = lib().nvfp4o_quantize_augmented(_ptr(x), rows, cols, _ptr(pm), int(nres), int(mode),
+                                         int(rule), given, _ptr(g), _ptr(packed), _ptr(scales),
+                                         int(bool(duplicate)))
     if st != 0:
         raise ValueError(f"oracle quantize_residual failed with status {st}")
     return {"packed": packed, "scales": scales, "gscale": np.float32(g[0])}
@@ -269,3 +277,25 @@ def rmsnorm(x_bf16, weight_bf16, eps):
     if st != 0:
         raise ValueError(f"oracle rmsnorm failed with status {st}")
     return y
+
+
+def gemm(a_packed, a_scales, ga, b_packed, b_scales, gb, M, N, K, want_abs=False):
+    """W4A4 product of two NVFP4 tensors blocked along K (AXIS_COLS layout):
+    out [M][N] = ga * gb * sum_k a(m,k) b(n,k) in binary64, and with want_abs
+    also ga * gb * sum_k |a(m,k) b(n,k)|.  Returns out or (out, abs)."""
+    pa = np.ascontiguousarray(a_packed, dtype=np.uint8)
+    sa = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    pb = np.ascontiguousarray(b_packed, dtype=np.uint8)
+    sb = np.ascontiguousarray(b_scales, dtype=np.uint8)
+    M, N, K = int(M), int(N), int(K)
+    if K % 16 or pa.size != M * K // 2 or sa.size != M * K // 16 or \
+            pb.size != N * K // 2 or sb.size != N * K // 16:
+        raise ValueError("gemm: operand sizes do not match M, N, K")
+    out = np.zeros((M, N), np.float64)
+    aout = np.zeros((M, N), np.float64) if want_abs else None
+    st = lib().nvfp4o_gemm(_ptr(pa), _ptr(sa), float(np.float32(ga)), _ptr(pb), _ptr(sb),
+                           float(np.float32(gb)), M, N, K, _ptr(out),
+                           _ptr(aout) if want_abs else None)
+    if st != 0:
+        raise ValueError(f"oracle gemm failed with status {st}")
+    return (out, aout) if want_abs else out

@@ -397,6 +397,19 @@ void nvfp4o_channel_order(const float* absmax, int64_t cols, int32_t* perm) {
 int nvfp4o_quantize_residual(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* perm,
                              int64_t nres, int mode, int rule, int gscale_given, float* gscale,
                              uint8_t* packed, uint8_t* scales) {
+  return nvfp4o_quantize_augmented(x, rows, cols, perm, nres, mode, rule, gscale_given, gscale,
+                                   packed, scales, 0);
+}
+
+/* The two sides of the augmented product [ARC, "Methodology"].  duplicate = 0:
+ * the activation side above (residual blocks appended).  duplicate = 1: the
+ * weight side, whose channels matching the residual ones are repeated: the
+ * appended blocks hold the same codes and scales as the primary blocks of the
+ * first nres positions, so the product over K + nres adds w * (x - v*d) for
+ * those channels. */
+int nvfp4o_quantize_augmented(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* perm,
+                              int64_t nres, int mode, int rule, int gscale_given, float* gscale,
+                              uint8_t* packed, uint8_t* scales, int duplicate) {
   int st = check_args(rows, cols, NVFP4O_AXIS_COLS, mode, rule);
   if (st != NVFP4O_OK) return st;
   if (nres < 0 || nres > cols || nres % 16 != 0) return NVFP4O_ERR_SHAPE;
@@ -416,7 +429,11 @@ int nvfp4o_quantize_residual(const uint16_t* x, int64_t rows, int64_t cols, cons
       uint8_t* pk = packed + (r * bout + b) * 8;
       for (int j = 0; j < 8; ++j) pk[j] = (uint8_t)(q.code[c][2 * j] | (q.code[c][2 * j + 1] << 4));
       scales[r * bout + b] = q.S[c];
-      if (b * 16 < nres) {
+      if (b * 16 < nres && duplicate) {
+        uint8_t* pr = packed + (r * bout + bpr + b) * 8;
+        for (int j = 0; j < 8; ++j) pr[j] = pk[j];
+        scales[r * bout + bpr + b] = q.S[c];
+      } else if (b * 16 < nres) {
         /* Residual x - v*d of the kept candidate, rounded once.  An exact
          * reconstruction leaves +0 (not the -0 that negating delta gives). */
         float res[16];
@@ -491,5 +508,46 @@ int nvfp4o_rmsnorm(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t
       y[r * cols + c] = t;
     }
   }
+  return NVFP4O_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* W4A4 product [ARC, "Methodology"; MIN, "Background"]                      */
+/* ------------------------------------------------------------------------ */
+
+/* Element value without the tensor scale: a = v * dec(S) for the code at
+ * position k of a row blocked along k (the AXIS_COLS layout).  At most 6
+ * significant bits, so a and a product of two are exact in binary64. */
+static double element_value(const uint8_t* packed_row, const uint8_t* scales_row, int64_t k) {
+  const uint8_t byte = packed_row[k / 2];
+  const uint8_t code = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15u);
+  const double v = (code & 8u) ? -(double)E2M1_VAL[code & 7u] : (double)E2M1_VAL[code & 7u];
+  return v * (double)nvfp4o_e4m3_decode(scales_row[k / 16]);
+}
+
+/* out[m][n] = ga * gb * sum_k a(m,k) * b(n,k) for A [M][K] and B [N][K], both
+ * NVFP4 with blocks of 16 along K (packed [rows][K/2], scales [rows][K/16]):
+ * Y = X W^T for activations X and a weight W stored [out][in].  The sum runs
+ * over k in order in binary64 (each product exact; the sum within
+ * K * 2^-53 of sum |a b| of the exact value).  abs_out (nullable) gets
+ * ga * gb * sum_k |a(m,k) * b(n,k)|, the scale of any summation error. */
+int nvfp4o_gemm(const uint8_t* pa, const uint8_t* sa, float ga, const uint8_t* pb,
+                const uint8_t* sb, float gb, int64_t M, int64_t N, int64_t K, double* out,
+                double* abs_out) {
+  if (!pa || !sa || !pb || !sb || !out) return NVFP4O_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return NVFP4O_ERR_SHAPE;
+  const double gab = (double)ga * (double)gb;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double sum = 0.0, asum = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double t = element_value(pa + m * (K / 2), sa + m * (K / 16), k) *
+                         element_value(pb + n * (K / 2), sb + n * (K / 16), k);
+        sum += t;
+        asum += fabs(t);
+      }
+      out[m * N + n] = gab * sum;
+      if (abs_out) abs_out[m * N + n] = gab * asum;
+    }
   return NVFP4O_OK;
 }

@@ -64,6 +64,12 @@ void nvfp4o_channel_order(const float* absmax, int64_t cols, int32_t* perm);
 int nvfp4o_quantize_residual(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* perm,
                              int64_t nres, int mode, int rule, int gscale_given, float* gscale,
                              uint8_t* packed, uint8_t* scales);
+int nvfp4o_quantize_augmented(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* perm,
+                              int64_t nres, int mode, int rule, int gscale_given, float* gscale,
+                              uint8_t* packed, uint8_t* scales, int duplicate);
+int nvfp4o_gemm(const uint8_t* pa, const uint8_t* sa, float ga, const uint8_t* pb,
+                const uint8_t* sb, float gb, int64_t M, int64_t N, int64_t K, double* out,
+                double* abs_out);
 float nvfp4o_rms_rstd(const uint16_t* xrow, int64_t cols, float eps);
 int nvfp4o_rmsnorm(const uint16_t* x, int64_t rows, int64_t cols, const uint16_t* w, float eps,
                    uint16_t* y);
