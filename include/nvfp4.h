@@ -83,7 +83,8 @@ enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
 enum {
   NVFP4_FLAG_GSCALE_GIVEN = 1u,   /* use *gscale_inout as g; skip the amax pass          */
   NVFP4_FLAG_ERR_ACCUMULATE = 2u, /* add the error sum to *err_sum_out, do not zero it  */
-  NVFP4_FLAG_STATS_ACCUMULATE = 4u /* fold channel maxima into *absmax_inout's values    */
+  NVFP4_FLAG_STATS_ACCUMULATE = 4u, /* fold channel maxima into *absmax_inout's values   */
+  NVFP4_FLAG_RESIDUAL_DUPLICATE = 8u /* appended blocks repeat the primary ones (weights)  */
 };
 
 /* Tensor amax A = max |x| over `numel` bf16 values, written as fp32 to
@@ -232,7 +233,14 @@ nvfp4_status nvfp4_channel_order(const uint16_t* in_bf16, int64_t rows, int64_t 
  *   nres: residual channels, a multiple of 16 in [0, cols].
  *   cols: a positive multiple of 16, at most 32768.
  *   flags: 0 (g computed from the tensor amax as nvfp4_quantize does and
- *     written to *gscale_inout) or NVFP4_FLAG_GSCALE_GIVEN (read g from it).
+ *     written to *gscale_inout) or NVFP4_FLAG_GSCALE_GIVEN (read g from it),
+ *     optionally with NVFP4_FLAG_RESIDUAL_DUPLICATE: the weight side of the
+ *     augmented product (same page: the weight channels matching the
+ *     residual ones are duplicated), where block cols/16 + j repeats the
+ *     codes and scale of block j instead of quantizing a residual.  With it,
+ *     nvfp4_gemm over K = cols + nres of an activation quantized without the
+ *     flag and a weight [out][cols] quantized with it (the same perm and
+ *     nres) adds w * (x - dec(code) * d) for the nres leading channels.
  *   Outputs must not overlap the input, perm or each other (NVFP4_ERR_ALIAS). */
 nvfp4_status nvfp4_quantize_residual(const uint16_t* in_bf16, int64_t rows, int64_t cols,
                                      const int32_t* perm, int64_t nres, int mode, int rule,
@@ -266,6 +274,34 @@ nvfp4_status nvfp4_rmsnorm_quantize_residual(const uint16_t* in_bf16, int64_t ro
                                              int rule, uint32_t flags, uint8_t* packed_out,
                                              uint8_t* scales_out, float* gscale_inout,
                                              float* amax_out, void* stream);
+
+/* W4A4 product of two NVFP4 tensors blocked along the reduction axis:
+ *   out[m][n] = ga * gb * sum over k of a(m,k) * b(n,k),  a = v * dec(S)
+ * with v the E2M1 value of the code and dec(S) its block's E4M3 scale: a
+ * linear layer Y = X W^T with NVFP4 activations X [m][k] and weights W
+ * [n][k] ("Why Gated DeltaNet in hybrid 27B LLMs withstands 4-bit
+ * quantization", "Background": W4A4), and the augmented product of the
+ * "ARCQuant" summary ("Methodology": one GEMM over K_in + S; pass the
+ * outputs of nvfp4_quantize_residual without and with
+ * NVFP4_FLAG_RESIDUAL_DUPLICATE and k = cols + nres).
+ *   a_packed [m][k/2], a_scales [m][k/16], *a_gscale: A in the
+ *     NVFP4_AXIS_COLS layout of nvfp4_quantize (e.g. its outputs);
+ *   b_packed [n][k/2], b_scales [n][k/16], *b_gscale: B likewise.
+ *   out: [m][n] row-major, fp32 (out_dtype NVFP4_OUT_F32) or bf16
+ *     (NVFP4_OUT_BF16, the fp32 result rounded to nearest even).
+ * Arithmetic: a(m,k) and b(n,k) are exact in binary16 and their products in
+ * fp32 (matrix cores, fp32 accumulation); the sum runs in fp32 in an order
+ * the library chooses, then is multiplied by RN(ga * gb).  So
+ *   |out - exact| <= (k + k/16 + 2) * 2^-23 * ga * gb * sum_k |a b|
+ * (plus the bf16 rounding with NVFP4_OUT_BF16); results are deterministic
+ * for a given library build and shape.
+ *   k: a positive multiple of 16, at most 2^24; m, n positive, each of
+ *     m*n, m*k and n*k at most 2^46.
+ *   Alignment: packed codes 4 bytes, scalars 4 bytes, out 4 (fp32) or 2
+ *   (bf16) bytes.  out must not overlap any input (NVFP4_ERR_ALIAS). */
+nvfp4_status nvfp4_gemm(const uint8_t* a_packed, const uint8_t* a_scales, const float* a_gscale,
+                        const uint8_t* b_packed, const uint8_t* b_scales, const float* b_gscale,
+                        int64_t m, int64_t n, int64_t k, int out_dtype, void* out, void* stream);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(nvfp4_status s);

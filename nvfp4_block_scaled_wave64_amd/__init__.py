@@ -27,6 +27,7 @@ OUT_F32, OUT_BF16 = 0, 1
 FLAG_GSCALE_GIVEN = 1
 FLAG_ERR_ACCUMULATE = 2
 FLAG_STATS_ACCUMULATE = 4
+FLAG_RESIDUAL_DUPLICATE = 8
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_ENUM", 3: "NVFP4_ERR_SHAPE",
           4: "NVFP4_ERR_ALIGN", 5: "NVFP4_ERR_HIP", 6: "NVFP4_ERR_ALIAS"}
@@ -49,6 +50,7 @@ SIGNATURES = {
     "nvfp4_quantize_residual": ([_P, _I64, _I64, _P, _I64, _I, _I, _U32, _P, _P, _P, _P], _I),
     "nvfp4_rmsnorm_quantize_residual": ([_P, _I64, _I64, _P, ctypes.c_float, _P, _I64, _I, _I,
                                          _U32, _P, _P, _P, _P, _P], _I),
+    "nvfp4_gemm": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P], _I),
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
     "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _P, _P], _I),
     "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _P, _P], _I),
@@ -320,12 +322,14 @@ def channel_order(x, absmax=None, accumulate=False, perm=None, stream=None):
 
 
 def quantize_residual(x, perm, nres, mode=MODE_4OVER6, rule=RULE_MSE, gscale=None, out=None,
-                      stream=None):
+                      stream=None, duplicate=False):
     """Two-stage quantization with reordered channels
     (nvfp4_quantize_residual).  perm: int32 device tensor of cols channel
     indices; nres: residual channels (multiple of 16, <= cols).  Returns a
     dict with packed [rows][(cols+nres)/2], scales [rows][(cols+nres)/16] and
-    gscale; `gscale` given skips the amax pass."""
+    gscale; `gscale` given skips the amax pass.  duplicate=True quantizes the
+    weight side of the augmented product (the appended blocks repeat the
+    primary blocks of the first nres channels)."""
     x = _bf16_input(x)
     if x.dim() != 2:
         raise ValueError("input must be 2-D [rows][cols]")
@@ -336,7 +340,7 @@ def quantize_residual(x, perm, nres, mode=MODE_4OVER6, rule=RULE_MSE, gscale=Non
     out = dict(out or {})
     packed = _out(out, "packed", (rows, max(width, 0) // 2), torch.uint8, dev)
     scales = _out(out, "scales", (rows, max(width, 0) // 16), torch.uint8, dev)
-    flags = 0
+    flags = FLAG_RESIDUAL_DUPLICATE if duplicate else 0
     if gscale is not None:
         g = _need(gscale, 1, torch.float32, dev, "gscale")
         flags |= FLAG_GSCALE_GIVEN
@@ -401,6 +405,32 @@ def dequantize(packed, scales, gscale, rows, cols, block_axis=AXIS_COLS, out_dty
     st = lib().nvfp4_dequantize(_ptr(packed), _ptr(scales), _ptr(gscale), int(rows), int(cols),
                                 int(block_axis), code, _ptr(out), _stream(stream))
     _check(st, "nvfp4_dequantize")
+    return out
+
+
+def gemm(a, b, out_dtype=torch.float32, out=None, stream=None):
+    """W4A4 product out [M][N] = ga * gb * sum_k a(m,k) b(n,k) (nvfp4_gemm):
+    Y = X W^T for NVFP4 activations X [M][K] and weights W [N][K], both
+    blocked along K.  a, b: dicts with "packed" ([rows][K/2] uint8),
+    "scales" ([rows][K/16] uint8) and "gscale" (1-element float32), e.g. the
+    results of quantize (AXIS_COLS) or quantize_residual.  Returns out, float32
+    or bfloat16."""
+    code = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    pa, pb = a["packed"], b["packed"]
+    if pa.dim() != 2 or pb.dim() != 2 or pa.shape[1] != pb.shape[1]:
+        raise ValueError("operands must be [rows][K/2] with the same K")
+    M, N, K = pa.shape[0], pb.shape[0], pa.shape[1] * 2
+    dev = pa.device
+    pa = _need(pa, M * K // 2, torch.uint8, dev, "a['packed']")
+    sa = _need(a["scales"], M * K // 16, torch.uint8, dev, "a['scales']")
+    ga = _need(a["gscale"], 1, torch.float32, dev, "a['gscale']")
+    pb = _need(pb, N * K // 2, torch.uint8, dev, "b['packed']")
+    sb = _need(b["scales"], N * K // 16, torch.uint8, dev, "b['scales']")
+    gb = _need(b["gscale"], 1, torch.float32, dev, "b['gscale']")
+    out = _out({"out": out}, "out", (M, N), out_dtype, dev)
+    st = lib().nvfp4_gemm(_ptr(pa), _ptr(sa), _ptr(ga), _ptr(pb), _ptr(sb), _ptr(gb), M, N, K,
+                          code, _ptr(out), _stream(stream))
+    _check(st, "nvfp4_gemm")
     return out
 
 

@@ -298,7 +298,8 @@ nvfp4_status nvfp4_quantize_residual(const uint16_t* in_bf16, int64_t rows, int6
   if (mode != NVFP4_MODE_STD && mode != NVFP4_MODE_4OVER6) return NVFP4_ERR_ENUM;
   if (rule != NVFP4_RULE_MSE && rule != NVFP4_RULE_MAE && rule != NVFP4_RULE_MAX)
     return NVFP4_ERR_ENUM;
-  if (flags & ~uint32_t(NVFP4_FLAG_GSCALE_GIVEN)) return NVFP4_ERR_ENUM;
+  if (flags & ~uint32_t(NVFP4_FLAG_GSCALE_GIVEN | NVFP4_FLAG_RESIDUAL_DUPLICATE))
+    return NVFP4_ERR_ENUM;
   const nvfp4_status shape = check_shape(rows, cols, NVFP4_AXIS_COLS);
   if (shape != NVFP4_OK) return shape;
   if (cols > nvfp4::kResidualMaxCols || nres < 0 || nres > cols || nres % 16 != 0)
@@ -334,7 +335,8 @@ nvfp4_status nvfp4_quantize_residual(const uint16_t* in_bf16, int64_t rows, int6
   }
   if (e == hipSuccess)
     e = nvfp4::launch_quantize_residual(in_bf16, rows, cols, perm, nres, gscale_inout, variant,
-                                        packed_out, scales_out, s);
+                                        packed_out, scales_out,
+                                        (flags & NVFP4_FLAG_RESIDUAL_DUPLICATE) != 0, s);
   return hip_status(e);
 }
 
@@ -399,6 +401,34 @@ nvfp4_status nvfp4_rmsnorm_quantize_residual(const uint16_t* in_bf16, int64_t ro
     e = nvfp4::launch_rms_quantize_residual(in_bf16, rows, cols, perm, nres, gscale_inout,
                                             variant, packed_out, scales_out, ra, s);
   return hip_status(e);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+nvfp4_status nvfp4_gemm(const uint8_t* a_packed, const uint8_t* a_scales, const float* a_gscale,
+                        const uint8_t* b_packed, const uint8_t* b_scales, const float* b_gscale,
+                        int64_t m, int64_t n, int64_t k, int out_dtype, void* out,
+                        void* stream) {
+  if (!a_packed || !a_scales || !a_gscale || !b_packed || !b_scales || !b_gscale || !out)
+    return NVFP4_ERR_NULL;
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_ENUM;
+  if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || k > (int64_t(1) << 24))
+    return NVFP4_ERR_SHAPE;
+  if (m > kMaxNumel / n || m > kMaxNumel / k || n > kMaxNumel / k) return NVFP4_ERR_SHAPE;
+  const int64_t esz = out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
+  if (!aligned(a_packed, 4) || !aligned(b_packed, 4) || !aligned(a_gscale, 4) ||
+      !aligned(b_gscale, 4) || !aligned(out, (uintptr_t)esz))
+    return NVFP4_ERR_ALIGN;
+  const int64_t out_bytes = m * n * esz;
+  const void* ins[6] = {a_packed, a_scales, a_gscale, b_packed, b_scales, b_gscale};
+  const int64_t in_bytes[6] = {m * k / 2, m * k / 16, 4, n * k / 2, n * k / 16, 4};
+  for (int i = 0; i < 6; ++i)
+    if (overlap(out, out_bytes, ins[i], in_bytes[i])) return NVFP4_ERR_ALIAS;
+  return hip_status(nvfp4::launch_gemm(a_packed, a_scales, a_gscale, b_packed, b_scales,
+                                       b_gscale, m, n, k, out_dtype == NVFP4_OUT_BF16, out,
+                                       static_cast<hipStream_t>(stream), nvfp4::Events{}));
 }
 
 }  // extern "C"

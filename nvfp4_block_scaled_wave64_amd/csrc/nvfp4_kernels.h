@@ -117,11 +117,12 @@ hipError_t launch_channel_absmax(const uint16_t* in, int64_t rows, int64_t cols,
 hipError_t launch_channel_rank(const uint32_t* absmax_bits, int64_t cols, int32_t* perm,
                                hipStream_t s);
 // Primary blocks of the reordered channels and residual blocks of the first
-// nres of them; cols <= kResidualMaxCols (LDS holds a row and the order).
+// nres of them (with dup: copies of their primary blocks); cols <=
+// kResidualMaxCols (LDS holds a row and the order).
 constexpr int64_t kResidualMaxCols = 32768;
 hipError_t launch_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,
                                     const int32_t* perm, int64_t nres, const float* gscale,
-                                    uint32_t variant, uint8_t* packed, uint8_t* scales,
+                                    uint32_t variant, uint8_t* packed, uint8_t* scales, bool dup,
                                     hipStream_t s);
 
 // RMSNorm in front of the residual path: y = bf16(x * rstd), then
@@ -137,6 +138,12 @@ hipError_t launch_rms_quantize_residual(const uint16_t* in, int64_t rows, int64_
                                         const int32_t* perm, int64_t nres, const float* gscale,
                                         uint32_t variant, uint8_t* packed, uint8_t* scales,
                                         const RmsArgs& ra, hipStream_t s);
+// ---- gemm.hip: W4A4 product of two NVFP4 tensors blocked along K ----
+// out [M][N] (fp32, or bf16 when out_bf16) = ga * gb * sum_k a(m,k) b(n,k).
+hipError_t launch_gemm(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
+                       const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
+                       int out_bf16, void* out, hipStream_t s, Events ev);
+
 // Atomic max of RN(max |y| / six_m) into *acc (fp32 bits; the caller zeroes it).
 hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const RmsArgs& ra,
                            float six_m, uint32_t* acc, hipStream_t s);

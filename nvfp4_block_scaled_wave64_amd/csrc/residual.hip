@@ -138,10 +138,12 @@ __global__ __launch_bounds__(kRankThreads) void channel_rank_kernel(
 
 // Output block j of one staged row xr (bf16 in LDS): gathers the channels
 // pm[16j .. 16j+15], quantizes them, stores codes and scale as block ob of
-// the output, and with `res` also the residual block ob + nb.
+// the output, and with `res` also block ob + nb: the residual block, or with
+// `dup` (the weight side of the augmented product) a copy of block ob.
 template <bool k46, int kRule>
 __device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_t* pm,
                                                uint32_t j, uint32_t ob, uint32_t nb, bool res,
+                                               bool dup,
                                                __amdgpu_buffer_rsrc_t r_packed,
                                                __amdgpu_buffer_rsrc_t r_scales,
                                                const TensorScales& ts, const float2* tab) {
@@ -166,7 +168,10 @@ __device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_
   codes.y = q.hi;
   __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, ob * 8u, 0, kStreamStore);
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q.S, r_scales, ob, 0, kMergedStore);
-  if (res) {
+  if (res && dup) {
+    __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, (ob + nb) * 8u, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q.S, r_scales, ob + nb, 0, kMergedStore);
+  } else if (res) {
     // Residual of the kept candidate, x - v*d rounded once.
     float v[16], rx[16];
     e2m1_decode8(q.lo, v);
@@ -195,7 +200,7 @@ template <uint32_t V>
 __global__ __launch_bounds__(kResThreads) void quantize_residual_kernel(
     const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
     uint32_t nres, const float* __restrict__ gscale, uint8_t* __restrict__ packed,
-    uint8_t* __restrict__ scales, uint32_t R) {
+    uint8_t* __restrict__ scales, uint32_t R, uint32_t dup) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr int kRule = !k46 ? kRuleMse
                         : (V & kVarMax) ? kRuleMax
@@ -260,8 +265,8 @@ __global__ __launch_bounds__(kResThreads) void quantize_residual_kernel(
     for (uint32_t item = (threadIdx.x + rot) & (kResThreads - 1u); item < nitems;
          item += kResThreads) {
       const uint32_t rr = item / nb, j = item - rr * nb;
-      residual_block<k46, kRule>(xs + rr * cols, pm, j, rr * bout + j, nb, j < nrb, r_packed,
-                                 r_scales, ts, tab);
+      residual_block<k46, kRule>(xs + rr * cols, pm, j, rr * bout + j, nb, j < nrb, dup != 0u,
+                                 r_packed, r_scales, ts, tab);
     }
     rot = (rot + 64u) & (kResThreads - 1u);
   }
@@ -456,7 +461,7 @@ template <uint32_t V, int kVpl, bool kRms>
 __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_residual_wave_kernel(
     const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
     uint32_t nres, const float* __restrict__ gscale, uint8_t* __restrict__ packed,
-    uint8_t* __restrict__ scales, RmsArgs ra) {
+    uint8_t* __restrict__ scales, RmsArgs ra, uint32_t dup) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr int kRule = !k46 ? kRuleMse
                         : (V & kVarMax) ? kRuleMax
@@ -531,7 +536,8 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
     const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + row * bout, bout);
 #pragma unroll 1
     for (uint32_t j = lane; j < nb; j += 64u)
-      residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, r_packed, r_scales, ts, tab);
+      residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts,
+                                 tab);
   }
   if (kRms && ra.amax_out) wave_max_to(ra.amax_out, bf16_pair_max(ymax), 0.0f);
 }
@@ -580,7 +586,8 @@ hipError_t launch_channel_rank(const uint32_t* absmax_bits, int64_t cols, int32_
 template <uint32_t V>
 static hipError_t launch_residual_group(const uint16_t* in, int64_t rows, int64_t cols,
                                         const int32_t* perm, int64_t nres, const float* gscale,
-                                        uint8_t* packed, uint8_t* scales, hipStream_t s) {
+                                        uint8_t* packed, uint8_t* scales, bool dup,
+                                        hipStream_t s) {
   // Rows per step: at least kResItems output blocks per thread, within the
   // staging capacity of kResThreads * kResVec 16-byte vectors and the
   // compute unit's 160 KiB of LDS.
@@ -596,7 +603,8 @@ static hipError_t launch_residual_group(const uint16_t* in, int64_t rows, int64_
   const int64_t niter = (rows + R - 1) / R;
   const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(niter, device_cu_count()));
   quantize_residual_kernel<V><<<(unsigned)groups, kResThreads, lds, s>>>(
-      in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, (uint32_t)R);
+      in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, (uint32_t)R,
+      (uint32_t)dup);
   return hipGetLastError();
 }
 
@@ -604,7 +612,7 @@ template <uint32_t V, int kVpl, bool kRms>
 static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t cols,
                                        const int32_t* perm, int64_t nres, const float* gscale,
                                        uint8_t* packed, uint8_t* scales, const RmsArgs& ra,
-                                       hipStream_t s) {
+                                       bool dup, hipStream_t s) {
   // As many waves per compute unit as their row buffers fit in LDS (at most
   // 16), one workgroup per compute unit.
   const int64_t row_bytes = cols * 2;
@@ -620,30 +628,31 @@ static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t
   if (e != hipSuccess) return e;
   quantize_residual_wave_kernel<V, kVpl, kRms>
       <<<(unsigned)groups, (unsigned)(waves * 64), lds, s>>>(
-          in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, ra);
+          in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, ra,
+          (uint32_t)dup);
   return hipGetLastError();
 }
 
 template <uint32_t V>
 static hipError_t launch_residual_v(const uint16_t* in, int64_t rows, int64_t cols,
                                     const int32_t* perm, int64_t nres, const float* gscale,
-                                    uint8_t* packed, uint8_t* scales, hipStream_t s) {
+                                    uint8_t* packed, uint8_t* scales, bool dup, hipStream_t s) {
   // Rows of up to 8192 channels: one row per wave (kVpl = cols / 512 vectors
   // per lane, rounded up to the next instantiated size); wider rows: rows
   // shared by a workgroup.
   if (cols <= 2048)
     return launch_residual_wave<V, 4, false>(in, rows, cols, perm, nres, gscale, packed, scales,
-                                           RmsArgs{}, s);
+                                           RmsArgs{}, dup, s);
   if (cols <= 4096)
     return launch_residual_wave<V, 8, false>(in, rows, cols, perm, nres, gscale, packed, scales,
-                                           RmsArgs{}, s);
+                                           RmsArgs{}, dup, s);
   if (cols <= 6144)
     return launch_residual_wave<V, 12, false>(in, rows, cols, perm, nres, gscale, packed, scales,
-                                           RmsArgs{}, s);
+                                           RmsArgs{}, dup, s);
   if (cols <= 8192)
     return launch_residual_wave<V, 16, false>(in, rows, cols, perm, nres, gscale, packed, scales,
-                                           RmsArgs{}, s);
-  return launch_residual_group<V>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+                                           RmsArgs{}, dup, s);
+  return launch_residual_group<V>(in, rows, cols, perm, nres, gscale, packed, scales, dup, s);
 }
 
 template <uint32_t V>
@@ -653,15 +662,15 @@ static hipError_t launch_rms_residual_v(const uint16_t* in, int64_t rows, int64_
                                         hipStream_t s) {
   if (cols <= 2048)
     return launch_residual_wave<V, 4, true>(in, rows, cols, perm, nres, gscale, packed, scales,
-                                            ra, s);
+                                            ra, false, s);
   if (cols <= 4096)
     return launch_residual_wave<V, 8, true>(in, rows, cols, perm, nres, gscale, packed, scales,
-                                            ra, s);
+                                            ra, false, s);
   if (cols <= 6144)
     return launch_residual_wave<V, 12, true>(in, rows, cols, perm, nres, gscale, packed, scales,
-                                             ra, s);
+                                             ra, false, s);
   return launch_residual_wave<V, 16, true>(in, rows, cols, perm, nres, gscale, packed, scales,
-                                           ra, s);
+                                           ra, false, s);
 }
 
 hipError_t launch_rms_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,
@@ -701,12 +710,13 @@ hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const
 hipError_t launch_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,
                                     const int32_t* perm, int64_t nres, const float* gscale,
                                     uint32_t variant, uint8_t* packed, uint8_t* scales,
-                                    hipStream_t s) {
+                                    bool dup, hipStream_t s) {
   switch (variant) {
-    case 0: return launch_residual_v<0>(in, rows, cols, perm, nres, gscale, packed, scales, s);
-    case 1: return launch_residual_v<1>(in, rows, cols, perm, nres, gscale, packed, scales, s);
-    case 3: return launch_residual_v<3>(in, rows, cols, perm, nres, gscale, packed, scales, s);
-    case 17: return launch_residual_v<17>(in, rows, cols, perm, nres, gscale, packed, scales, s);
+    case 0: return launch_residual_v<0>(in, rows, cols, perm, nres, gscale, packed, scales, dup, s);
+    case 1: return launch_residual_v<1>(in, rows, cols, perm, nres, gscale, packed, scales, dup, s);
+    case 3: return launch_residual_v<3>(in, rows, cols, perm, nres, gscale, packed, scales, dup, s);
+    case 17:
+      return launch_residual_v<17>(in, rows, cols, perm, nres, gscale, packed, scales, dup, s);
     default: return hipErrorInvalidValue;
   }
 }

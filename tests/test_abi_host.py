@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
@@ -188,7 +188,9 @@ def qr(**kw):
     (dict(in_=None), 1), (dict(perm=None), 1), (dict(packed=None), 1), (dict(scales=None), 1),
     (dict(g=None), 1),
     (dict(mode=2), 2), (dict(rule=3), 2), (dict(flags=2), 2), (dict(flags=4), 2),
+    (dict(flags=16), 2),
     (dict(rows=0), 3), (dict(cols=40), 3), (dict(cols=32784), 3), (dict(nres=-16), 3),
+    (dict(flags=8, rows=0), 3), (dict(flags=9, rows=0), 3),
     (dict(nres=8), 3), (dict(nres=80), 3),
     (dict(in_=MIS), 4), (dict(perm=ctypes.c_void_p(0x20002)), 4),
     (dict(packed=ctypes.c_void_p(0x30002)), 4), (dict(g=ctypes.c_void_p(0x50001)), 4),
@@ -196,8 +198,8 @@ def qr(**kw):
     (dict(g=ctypes.c_void_p(0x30100)), 6), (dict(scales=ctypes.c_void_p(0x30200)), 6),
 ])
 def test_quantize_residual_rejects(kw, status):
-    """nvfp4_quantize_residual: nulls, enums (only GSCALE_GIVEN is a valid
-    flag), shape (cols a multiple of 16 up to 32768, nres a multiple of 16
+    """nvfp4_quantize_residual: nulls, enums (GSCALE_GIVEN and
+    RESIDUAL_DUPLICATE are the valid flags), shape (cols a multiple of 16 up to 32768, nres a multiple of 16
     in [0, cols]), alignment, and outputs overlapping the input, perm or
     each other."""
     assert qr(**kw) == status
@@ -253,3 +255,34 @@ def test_binding_checks_caller_tensors():
         nv._out({"k": torch.zeros(14, dtype=torch.uint8)}, "k", (3, 5), torch.uint8, cpu)
     with pytest.raises(ValueError):
         nv.quantize(torch.zeros(16, 16, dtype=torch.bfloat16))  # host memory
+
+
+G = ctypes.c_void_p(0x70000)
+
+
+def gm(**kw):
+    args = dict(pa=A, sa=B, ga=C, pb=D, sb=E, gb=F, m=32, n=32, k=64, dtype=nv.OUT_F32, out=G)
+    args.update(kw)
+    return nv.lib().nvfp4_gemm(args["pa"], args["sa"], args["ga"], args["pb"], args["sb"],
+                               args["gb"], args["m"], args["n"], args["k"], args["dtype"],
+                               args["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pa=None), 1), (dict(sa=None), 1), (dict(ga=None), 1), (dict(pb=None), 1),
+    (dict(sb=None), 1), (dict(gb=None), 1), (dict(out=None), 1),
+    (dict(dtype=2), 2), (dict(dtype=-1), 2),
+    (dict(m=0), 3), (dict(n=-4), 3), (dict(k=0), 3), (dict(k=40), 3),
+    (dict(k=(1 << 24) + 16), 3), (dict(m=1 << 40, n=1 << 10), 3), (dict(m=1 << 31, k=1 << 16), 3),
+    (dict(pa=ctypes.c_void_p(0x10002)), 4), (dict(pb=ctypes.c_void_p(0x40001)), 4),
+    (dict(ga=ctypes.c_void_p(0x30002)), 4), (dict(out=ctypes.c_void_p(0x70002)), 4),
+    (dict(out=ctypes.c_void_p(0x70001), dtype=nv.OUT_BF16), 4),
+    (dict(out=A), 6), (dict(out=ctypes.c_void_p(0x10200)), 6),
+    (dict(out=ctypes.c_void_p(0x5FFF0)), 6), (dict(out=ctypes.c_void_p(0x4FF00)), 6),
+])
+def test_gemm_rejects(kw, status):
+    """nvfp4_gemm: nulls, out_dtype, shape (positive extents, k a multiple of
+    16 up to 2^24, products of extents up to 2^46), alignment (codes and
+    scalars 4 bytes, out its element size) and an output overlapping any
+    input."""
+    assert gm(**kw) == status

@@ -1,0 +1,186 @@
+"""GPU parity of the W4A4 product (nvfp4_gemm): out = ga * gb * sum_k a b for
+NVFP4 activations and weights blocked along K ("Why Gated DeltaNet in hybrid
+27B LLMs withstands 4-bit quantization", 'Background'; the augmented product
+over K_in + S of the "ARCQuant" summary, 'Methodology').
+
+The operands decode exactly and their products are exact in fp32, so the
+only difference from the oracle's binary64 sum is the fp32 accumulation and
+the final scaling.  The tests use the bound the header states,
+|out - exact| <= (K + K/16 + 2) * 2^-23 * ga * gb * sum |a b|, and are
+bit-exact where every partial sum is representable (unit scales, g = 1).
+Shapes cover ragged tile edges in M and N, K tails that are not a multiple
+of the 64-wide chunk, one block, and the 32768 x 5120 x 5120 prefill product
+at full size (sampled rows and columns against the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_wave64_amd as nv
+import oracle
+import testkit
+from tests._parity import Guarded, to_device
+
+pytestmark = pytest.mark.gpu
+
+F46, STD, MSE = nv.MODE_4OVER6, nv.MODE_STD, nv.RULE_MSE
+
+
+def banner(msg):
+    print(f"\n[gpu-gemm] {msg}", flush=True)
+
+
+def random_nvfp4(seed, rows, K, scale_lo=0x00, scale_hi=0x7E):
+    """Seeded random codes and E4M3 scale bytes (the NaN byte excluded)."""
+    rng = np.random.default_rng(seed)
+    packed = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi + 1, (rows, K // 16), dtype=np.uint8)
+    return packed, scales
+
+
+def dev_operand(packed, scales, g):
+    return {"packed": torch.from_numpy(np.ascontiguousarray(packed)).cuda(),
+            "scales": torch.from_numpy(np.ascontiguousarray(scales)).cuda(),
+            "gscale": torch.tensor([float(np.float32(g))], dtype=torch.float32, device="cuda")}
+
+
+def gpu_gemm(pa, sa, ga, pb, sb, gb, out_dtype=torch.float32):
+    M, N = pa.shape[0], pb.shape[0]
+    esz = 4 if out_dtype == torch.float32 else 2
+    buf = Guarded(M * N * esz, out_dtype)
+    nv.gemm(dev_operand(pa, sa, ga), dev_operand(pb, sb, gb), out_dtype, out=buf.view)
+    torch.cuda.synchronize()
+    buf.check()
+    return buf.view.float().cpu().numpy().astype(np.float64).reshape(M, N)
+
+
+def bound(K, gabs):
+    return (K + K // 16 + 2) * 2.0 ** -23 * gabs + 2.0 ** -126
+
+
+def assert_within(got, want, gabs, K, extra_rel=0.0, what=""):
+    err = np.abs(got - want)
+    tol = bound(K, gabs) + extra_rel * np.abs(want)
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, (what, bad[:5].tolist(), got[tuple(bad[0])], want[tuple(bad[0])])
+
+
+SHAPES = [(1, 1, 16), (31, 17, 48), (32, 32, 64), (256, 256, 64), (257, 255, 80),
+          (300, 270, 320), (513, 259, 336), (1000, 700, 1040), (64, 640, 5120),
+          (200, 96, 5376)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_unit_scales_are_bit_exact(M, N, K):
+    banner(f"unit scales {M}x{N}x{K}")
+    pa, _ = random_nvfp4(M * 7 + K, M, K)
+    pb, _ = random_nvfp4(N * 11 + K, N, K)
+    sa = np.full((M, K // 16), 0x38, np.uint8)  # E4M3 1.0
+    sb = np.full((N, K // 16), 0x38, np.uint8)
+    got = gpu_gemm(pa, sa, 1.0, pb, sb, 1.0)
+    want = oracle.gemm(pa, sa, 1.0, pb, sb, 1.0, M, N, K)
+    # Every partial sum is a multiple of 1/4 below 2^22: exact in fp32.
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_random_operands_within_the_bound(M, N, K, out_dtype):
+    banner(f"random operands {M}x{N}x{K} {out_dtype}")
+    pa, sa = random_nvfp4(M + 3 * K, M, K)
+    pb, sb = random_nvfp4(N + 5 * K + 1, N, K)
+    ga, gb = np.float32(0.37), np.float32(1.9e-3)
+    got = gpu_gemm(pa, sa, ga, pb, sb, gb, out_dtype)
+    want, gabs = oracle.gemm(pa, sa, ga, pb, sb, gb, M, N, K, want_abs=True)
+    extra = 2.0 ** -8 if out_dtype == torch.bfloat16 else 0.0
+    assert_within(got, want, gabs, K, extra, f"{M}x{N}x{K}")
+
+
+def test_bf16_output_is_the_rounded_fp32_output():
+    banner("bf16 = RNE(fp32)")
+    M, N, K = 300, 270, 336
+    pa, sa = random_nvfp4(41, M, K)
+    pb, sb = random_nvfp4(42, N, K)
+    f = gpu_gemm(pa, sa, 0.5, pb, sb, 0.25, torch.float32)
+    b = gpu_gemm(pa, sa, 0.5, pb, sb, 0.25, torch.bfloat16)
+    want = torch.from_numpy(f.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(b, want.astype(np.float64))
+
+
+@pytest.mark.parametrize("mode", [STD, F46])
+def test_quantized_activations_and_weights(mode):
+    banner(f"quantized X W^T mode={mode}")
+    M, N, K = 384, 320, 1024
+    x = testkit.fill((M, K), testkit.STUDENT_T3, 0.5, 51)
+    testkit.scale_columns(x, testkit.sample(52, K, 8), 100.0)
+    w = testkit.fill((N, K), testkit.NORMAL, 0.02, 53)
+    qx = oracle.quantize(x, nv.AXIS_COLS, mode, MSE, want_selmap=False, want_err=False)
+    qw = oracle.quantize(w, nv.AXIS_COLS, mode, MSE, want_selmap=False, want_err=False)
+    shp = lambda q, r: (q["packed"].reshape(r, K // 2), q["scales"].reshape(r, K // 16))
+    pa, sa = shp(qx, M)
+    pb, sb = shp(qw, N)
+    got = gpu_gemm(pa, sa, qx["gscale"], pb, sb, qw["gscale"])
+    want, gabs = oracle.gemm(pa, sa, qx["gscale"], pb, sb, qw["gscale"], M, N, K, want_abs=True)
+    assert_within(got, want, gabs, K)
+
+
+@pytest.mark.parametrize("mode", [STD, F46])
+def test_augmented_product(mode):
+    banner(f"augmented product mode={mode}")
+    M, N, K, S = 256, 192, 2048, 128
+    x = testkit.fill((M, K), testkit.STUDENT_T3, 0.5, 61)
+    testkit.scale_columns(x, testkit.sample(62, K, 16), 60.0)
+    w = testkit.fill((N, K), testkit.NORMAL, 0.02, 63)
+    perm = oracle.channel_order(oracle.channel_absmax(x))
+    qa = oracle.quantize_residual(x, perm, S, mode, MSE)
+    qb = oracle.quantize_residual(w, perm, S, mode, MSE, duplicate=True)
+    # The weight side through the library matches the oracle bit for bit.
+    bufs = {"packed": Guarded(N * (K + S) // 2), "scales": Guarded(N * (K + S) // 16),
+            "gscale": Guarded(4, torch.float32)}
+    pd = torch.from_numpy(np.ascontiguousarray(perm, np.int32)).cuda()
+    nv.quantize_residual(to_device(w), pd, S, mode, MSE, out={k: b.view for k, b in bufs.items()},
+                         duplicate=True)
+    torch.cuda.synchronize()
+    for b in bufs.values():
+        b.check()
+    np.testing.assert_array_equal(bufs["packed"].view.cpu().numpy(), qb["packed"].reshape(-1))
+    np.testing.assert_array_equal(bufs["scales"].view.cpu().numpy(), qb["scales"].reshape(-1))
+    assert bufs["gscale"].view.cpu().numpy()[0] == qb["gscale"]
+    got = gpu_gemm(qa["packed"], qa["scales"], qa["gscale"], qb["packed"], qb["scales"],
+                   qb["gscale"])
+    want, gabs = oracle.gemm(qa["packed"], qa["scales"], qa["gscale"], qb["packed"],
+                             qb["scales"], qb["gscale"], M, N, K + S, want_abs=True)
+    assert_within(got, want, gabs, K + S)
+
+
+def test_full_size_prefill_product_sampled():
+    M, N, K = 32768, 5120, 5120
+    banner(f"full size {M}x{N}x{K}")
+    pa, sa = random_nvfp4(71, M, K, 0x28, 0x50)
+    pb, sb = random_nvfp4(72, N, K, 0x28, 0x50)
+    ga, gb = np.float32(2.5e-3), np.float32(4.0e-5)
+    got = gpu_gemm(pa, sa, ga, pb, sb, gb)
+    rng = np.random.default_rng(73)
+    rows = np.concatenate([[0, 255, 256, M - 1], rng.choice(M, 44, replace=False)])
+    cols = np.concatenate([[0, 127, 128, N - 1], rng.choice(N, 44, replace=False)])
+    want, gabs = oracle.gemm(pa[rows], sa[rows], ga, pb[cols], sb[cols], gb, len(rows), len(cols),
+                             K, want_abs=True)
+    assert_within(got[np.ix_(rows, cols)], want, gabs, K, what="sampled")
+    assert np.isfinite(got).all()
+
+
+def test_deterministic_and_exact_scalings():
+    banner("determinism, g scaling, zero g")
+    M, N, K = 257, 255, 1040
+    pa, sa = random_nvfp4(81, M, K)
+    pb, sb = random_nvfp4(82, N, K)
+    a = gpu_gemm(pa, sa, 0.75, pb, sb, 0.5)
+    np.testing.assert_array_equal(a, gpu_gemm(pa, sa, 0.75, pb, sb, 0.5))
+    # Scaling ga by 4 scales RN(ga * gb) and every output by 4 exactly.
+    np.testing.assert_array_equal(gpu_gemm(pa, sa, 3.0, pb, sb, 0.5), 4.0 * a)
+    # Swapping the operands transposes the product (same terms, same order
+    # within each 16-wide step is not guaranteed, so within the bound).
+    t = gpu_gemm(pb, sb, 0.5, pa, sa, 0.75)
+    want, gabs = oracle.gemm(pa, sa, 0.75, pb, sb, 0.5, M, N, K, want_abs=True)
+    assert_within(t.T, want, gabs, K)
+    z = gpu_gemm(pa, sa, 0.0, pb, sb, 0.5)
+    assert (z == 0).all()
