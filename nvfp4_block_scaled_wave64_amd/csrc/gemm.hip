@@ -20,9 +20,22 @@
 // consecutive k values, lanes 0-31 the first 8 and lanes 32-63 the next 8;
 // accumulator element r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
 // column l % 32.  The sum over k does not depend on how k is split between
-// the lanes, so a lane loads 32 consecutive codes (16 bytes, two blocks) of
-// its row per 64-wide chunk of K and feeds them to four MFMA steps; A and B
-// use the same split, so the k values meet their partners.
+// the lanes, so within a 128-wide stage of K lane half h takes the stage's
+// k values 64h .. 64h + 63 (four blocks) and feeds 8 of them to each of the
+// eight MFMA steps; A and B use the same split, so the k values meet their
+// partners.
+//
+// Data path.  A workgroup computes a 256 x 256 tile with four waves of
+// 128 x 128 (the accumulators fill the 256 AGPRs).  K is walked in stages of
+// 128 (eight blocks): the workgroup copies the stage's codes (256 rows x 64
+// bytes per operand, four lanes per row so that every request is one
+// contiguous 64-byte piece) and scale bytes into LDS, three stages deep, so
+// the loads of stage c + 2 are in flight while the matrix cores work on
+// stage c.  In LDS the 16-byte pieces of a row are XOR-swizzled by bits 2-3
+// of the row, which makes both the 16-byte writes and the fragment reads
+// (16 lanes on 16 consecutive rows) free of bank conflicts.
+#include <type_traits>
+
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -33,53 +46,18 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmThreads = 256;           // 4 waves as 2 x 2
-constexpr int kTileM = 256, kTileN = 256;   // workgroup tile
-constexpr int kWaveM = 128, kWaveN = 128;   // wave tile
-constexpr int kFm = kWaveM / 32, kFn = kWaveN / 32;  // 32 x 32 MFMA tiles per wave
-constexpr int kGroupM = 4;                  // tile rows per group of the walk
-
-// The operand fragment of one 32-row slice for one chunk: 32 codes of the
-// lane's row (two blocks) and those blocks' scale bytes.
-struct Frag {
-  u32x4 codes;
-  uint32_t scales;  // byte 0: first block, byte 1: second block
-};
-
-// Loads the fragment of tile row `r` (relative to the resource base) for
-// chunk c; half h of the wave takes blocks 4c + 2h and 4c + 2h + 1.  A block
-// at or past the end of K gets scale offset out of range (scale 0, so its
-// values are 0 whatever its codes); rows past the end read 0.
-__device__ __forceinline__ Frag load_frag(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
-                                          uint32_t r, uint32_t c, uint32_t h, uint32_t nblk) {
-  Frag f;
-  const uint32_t blk = 4u * c + 2u * h;
-  f.codes = __builtin_amdgcn_raw_buffer_load_b128(rc, r * (nblk * 8u) + blk * 8u, 0, 0);
-  const uint32_t so = r * nblk + blk;
-  const uint32_t s0 = __builtin_amdgcn_raw_buffer_load_b8(rs, blk < nblk ? so : 0xFFFFFFF0u, 0, 0);
-  const uint32_t s1 =
-      __builtin_amdgcn_raw_buffer_load_b8(rs, blk + 1u < nblk ? so + 1u : 0xFFFFFFF0u, 0, 0);
-  f.scales = s0 | (s1 << 8);
-  return f;
-}
-
-// The 8 f16 operand values of MFMA step t (0..3) of a fragment: codes
-// 8t .. 8t+7 times dec(S) of their block (block 0 for t < 2).
-__device__ __forceinline__ f16x8 decode_step(const Frag& f, f16x2 dec2, int t) {
-  const uint32_t w = f.codes[t];
-  const _Float16 d = (t < 2) ? dec2[0] : dec2[1];
-  const f16x2 dd = {d, d};
-  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * dd;
-  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * dd;
-  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * dd;
-  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * dd;
-  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// dec(S) of the fragment's two blocks as f16 (E4M3 -> f16 is exact).
-__device__ __forceinline__ f16x2 decode_scales(const Frag& f) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.scales, 1.0f, false);
-}
+constexpr int kGemmThreads = 256;                 // 4 waves as 2 x 2
+constexpr int kTile = 256;                        // workgroup tile, rows of A and of B
+constexpr int kWaveTile = 128;                    // wave tile
+constexpr int kFrags = kWaveTile / 32;            // 32 x 32 MFMA tiles per wave and side
+constexpr int kStageBlocks = 8;                   // blocks of K per stage (K = 128)
+constexpr int kStages = 4;                        // LDS buffers
+constexpr int kAhead = 3;                         // stages in flight ahead of the one computed
+constexpr int kRowBytes = kStageBlocks * 8;       // code bytes per row and stage
+constexpr int kCodeBytes = kTile * kRowBytes;     // one operand's codes per stage
+constexpr int kScaleBytes = kTile * kStageBlocks; // one operand's scales per stage
+constexpr int kStageBytes = 2 * kCodeBytes + 2 * kScaleBytes;
+constexpr int kGroupM = 4;                        // tile rows per group of the walk
 
 // Buffer resource from values the compiler may hold in vector registers but
 // that are the same in every lane (keeps the resource in scalar registers).
@@ -89,6 +67,117 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint8_t* p,
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
   return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo),
                    __builtin_amdgcn_readfirstlane(bytes));
+}
+
+// LDS offset of 16-byte piece `piece` (0..3) of tile row `row` in a code area.
+__device__ __forceinline__ uint32_t code_slot(uint32_t row, uint32_t piece) {
+  return row * kRowBytes + 16u * (piece ^ ((row >> 2) & 3u));
+}
+
+// The loads of one stage go out in parts spread over the MFMA steps of the
+// stage before (a burst of them would stall the in-order issue of the
+// MFMAs): part q < 4 is the q-th code load of each operand, part 4 the
+// scale loads of A, part 5 those of B.
+//
+// Code loads go straight to LDS (buffer_load ... lds): lane l of load q
+// writes bytes 16l .. 16l + 15 of the 1 KiB that holds tile rows
+// 64w + 16q .. 64w + 16q + 15, which is physical piece l % 4 of row
+// 64w + 16q + l / 4, so the lane loads the row's logical piece
+// (l % 4) ^ ((row >> 2) & 3).  Scale bytes (eight per tile row) go to LDS
+// the same way when every row's start is 4-byte aligned (lane l of load k
+// writes word l % 2 of row 64w + 32k + l / 2); otherwise they come back in
+// registers, those of tile row `thread`.  Rows past the tile's valid rows
+// read 0 (resource range); blocks at or past the end of K get scale 0, so
+// their codes (whatever they read) contribute 0.  With `live` false (no
+// such stage) every load is out of range and writes zeros to a buffer that
+// is not read again.
+constexpr uint32_t kOut = 0xFFFFFFF0u;  // past any resource range: reads 0
+
+__device__ __forceinline__ void issue_codes(__amdgpu_buffer_rsrc_t rc, uint8_t* codes_lds,
+                                            uint32_t c, int q, bool live, uint32_t nblk,
+                                            uint32_t wave, uint32_t lane) {
+  const uint32_t first = 64u * wave + 16u * (uint32_t)q;
+  const uint32_t row = first + (lane >> 2);
+  const uint32_t piece = (lane & 3u) ^ ((row >> 2) & 3u);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rc, (__attribute__((address_space(3))) void*)(codes_lds + first * kRowBytes), 16,
+      live ? row * (nblk * 8u) + c * kRowBytes + 16u * piece : kOut, 0, 0, 0);
+}
+
+template <bool kAligned>
+__device__ __forceinline__ u32x2 issue_scales(__amdgpu_buffer_rsrc_t rs, uint8_t* scales_lds,
+                                              uint32_t c, bool live, uint32_t nblk,
+                                              uint32_t wave, uint32_t lane) {
+  const uint32_t b0 = c * kStageBlocks;
+  u32x2 sc = {0u, 0u};
+  if constexpr (kAligned) {
+    // nblk % 4 == 0: each 4-block word is either wholly inside K or past it.
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t first = 64u * wave + 32u * k;
+      const uint32_t srow = first + (lane >> 1), word = lane & 1u;
+      const bool valid = live && b0 + 4u * word + 4u <= nblk;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(scales_lds + first * kStageBlocks), 4,
+          valid ? srow * nblk + b0 + 4u * word : kOut, 0, 0, 0);
+    }
+  } else {
+    const uint32_t base = threadIdx.x * nblk + b0;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(
+          rs, live && b0 + b < nblk ? base + (uint32_t)b : kOut, 0, 0);
+      w[b >> 2] |= v << (8 * (b & 3));
+    }
+    sc.x = w[0];
+    sc.y = w[1];
+  }
+  return sc;
+}
+
+// Vector-memory operations one thread issues per stage (both operands):
+// four code loads and the scale loads.
+template <bool kAligned>
+constexpr int kLoadsPerStage = 2 * (4 + (kAligned ? 2 : 8));
+
+// Waits until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier after this wave's LDS writes have completed; the
+// loads still in flight (the stages ahead) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Codes of tile row `row` for lane half h: piece 2h holds the stage's
+// codes for MFMA steps 0-3, piece 2h + 1 those for steps 4-7.
+__device__ __forceinline__ u32x4 read_codes(const uint8_t* codes, uint32_t row, uint32_t piece) {
+  return *reinterpret_cast<const u32x4*>(codes + code_slot(row, piece));
+}
+
+// dec(S) of the four blocks of lane half h as f16 (E4M3 -> f16 is exact):
+// lo = blocks 4h, 4h + 1 (steps 0-3), hi = blocks 4h + 2, 4h + 3 (steps 4-7).
+__device__ __forceinline__ void read_scales(const uint8_t* scales, uint32_t row, uint32_t h,
+                                            f16x2& lo, f16x2& hi) {
+  const uint32_t s = *reinterpret_cast<const uint32_t*>(scales + row * kStageBlocks + 4u * h);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true);
+}
+
+// The 8 f16 operand values of one MFMA step: the 8 codes of word w times
+// dec(S) of their block.
+__device__ __forceinline__ f16x8 decode8(uint32_t w, _Float16 d) {
+  const f16x2 dd = {d, d};
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * dd;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * dd;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * dd;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * dd;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
@@ -102,12 +191,13 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
 // kGroupM tile rows (the workgroups running together share A and B panels
 // in L2), and consecutive tiles of the walk go to one XCD (workgroups are
 // dealt round-robin over the 8 XCDs).
-template <bool kBf16>
+template <bool kBf16, bool kAligned>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const uint8_t* __restrict__ pa, const uint8_t* __restrict__ sa, const float* __restrict__ ga,
     const uint8_t* __restrict__ pb, const uint8_t* __restrict__ sb, const float* __restrict__ gb,
     int64_t M, int64_t N, int64_t K, uint32_t tiles_m, uint32_t tiles_n, uint32_t per_xcd,
     void* __restrict__ out) {
+  __shared__ __align__(16) uint8_t lds[kStages * kStageBytes];
   const uint32_t total = tiles_m * tiles_n;
   const uint32_t L = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
   if (L >= total) return;
@@ -123,72 +213,184 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   const uint32_t wm = wave >> 1, wn = wave & 1u;
   const uint32_t h = lane >> 5, l32 = lane & 31u;
   const uint32_t nblk = (uint32_t)(K / 16);
-  const uint32_t nchunks = (nblk + 3u) / 4u;
+  const uint32_t nstages = (nblk + kStageBlocks - 1) / kStageBlocks;
 
   // Resources over this tile's rows of A and B (rows past M or N read 0).
-  const int64_t m0 = (int64_t)tm * kTileM + wm * kWaveM;
-  const int64_t n0 = (int64_t)tn * kTileN + wn * kWaveN;
-  const uint32_t rows_a = (uint32_t)max<int64_t>(0, min<int64_t>(kWaveM, M - m0));
-  const uint32_t rows_b = (uint32_t)max<int64_t>(0, min<int64_t>(kWaveN, N - n0));
+  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+  const uint32_t rows_a = (uint32_t)min<int64_t>(kTile, M - m0);
+  const uint32_t rows_b = (uint32_t)min<int64_t>(kTile, N - n0);
   const __amdgpu_buffer_rsrc_t rca = uniform_rsrc(pa + m0 * (K / 2), rows_a * nblk * 8u);
   const __amdgpu_buffer_rsrc_t rsa = uniform_rsrc(sa + m0 * (K / 16), rows_a * nblk);
   const __amdgpu_buffer_rsrc_t rcb = uniform_rsrc(pb + n0 * (K / 2), rows_b * nblk * 8u);
   const __amdgpu_buffer_rsrc_t rsb = uniform_rsrc(sb + n0 * (K / 16), rows_b * nblk);
 
-  f32x16 acc[kFm][kFn];
+  f32x16 acc[kFrags][kFrags];
 #pragma unroll
-  for (int i = 0; i < kFm; ++i)
+  for (int i = 0; i < kFrags; ++i)
 #pragma unroll
-    for (int j = 0; j < kFn; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < kFrags; ++j) acc[i][j] = f32x16{};
 
-  Frag fa[kFm], fb[kFn];
+  auto stage_ptr = [&](uint32_t c) { return lds + (c % kStages) * kStageBytes; };
+  // Part q (0..5) of the loads of stage c (see issue_codes).
+  auto issue_part = [&](uint32_t c, int q, bool live, u32x2& qa, u32x2& qb) {
+    uint8_t* st = stage_ptr(c);
+    if (q < 4) {
+      issue_codes(rca, st, c, q, live, nblk, wave, lane);
+      issue_codes(rcb, st + kCodeBytes, c, q, live, nblk, wave, lane);
+    } else if (q == 4) {
+      qa = issue_scales<kAligned>(rsa, st + 2 * kCodeBytes, c, live, nblk, wave, lane);
+    } else {
+      qb = issue_scales<kAligned>(rsb, st + 2 * kCodeBytes + kScaleBytes, c, live, nblk, wave,
+                                  lane);
+    }
+  };
+  auto issue = [&](uint32_t c, u32x2& qa, u32x2& qb) {
 #pragma unroll
-  for (int i = 0; i < kFm; ++i) fa[i] = load_frag(rca, rsa, 32u * i + l32, 0u, h, nblk);
-#pragma unroll
-  for (int j = 0; j < kFn; ++j) fb[j] = load_frag(rcb, rsb, 32u * j + l32, 0u, h, nblk);
+    for (int q = 0; q < 6; ++q) issue_part(c, q, true, qa, qb);
+  };
+  auto put_scales = [&](uint32_t c, u32x2 qa, u32x2 qb) {
+    uint8_t* sc = stage_ptr(c) + 2 * kCodeBytes + threadIdx.x * kStageBlocks;
+    *reinterpret_cast<u32x2*>(sc) = qa;
+    *reinterpret_cast<u32x2*>(sc + kScaleBytes) = qb;
+  };
 
-  for (uint32_t c = 0; c < nchunks; ++c) {
-    Frag na[kFm], nb[kFn];
-    const uint32_t cn = c + 1u < nchunks ? c + 1u : c;
-#pragma unroll
-    for (int i = 0; i < kFm; ++i) na[i] = load_frag(rca, rsa, 32u * i + l32, cn, h, nblk);
-#pragma unroll
-    for (int j = 0; j < kFn; ++j) nb[j] = load_frag(rcb, rsb, 32u * j + l32, cn, h, nblk);
+  // Pipeline: stage c is computed while the loads of stages c + 1 .. c + 3
+  // are in flight; at the end of stage c this wave waits for its loads of
+  // stage c + 2 (only stage c + 3's may stay outstanding), writes that
+  // stage's scale bytes, and the barrier publishes it.  So during stage c,
+  // stages c and c + 1 are complete in LDS; buffer (c + 3) % 4 receives
+  // stage c + 3 and buffer (c + 2) % 4 the scales of stage c + 2, neither
+  // read by anyone during stage c.
+  u32x2 s0a = {}, s0b = {}, s1a = {}, s1b = {}, pa2 = {}, pb2 = {};
+  issue(0, s0a, s0b);
+  if (nstages > 1) issue(1, s1a, s1b);
+  if (nstages > 2) {
+    issue(2, pa2, pb2);
+    wait_vm<kLoadsPerStage<kAligned>>();
+  } else {
+    wait_vm<0>();
+  }
+  if constexpr (!kAligned) {
+    put_scales(0, s0a, s0b);
+    if (nstages > 1) put_scales(1, s1a, s1b);
+  }
+  lds_barrier();
 
-    f16x2 da[kFm], db[kFn];
+  // Operand r < kFrags is A fragment r (tile row wm*128 + 32r + l32), the
+  // others B fragments.  Software pipeline across stages: the codes of
+  // steps 4-7 are read from LDS while steps 0-3 run, those of the next
+  // stage's steps 0-3 (already in LDS: written before the previous barrier)
+  // while steps 4-7 run, and each step's operands are decoded while the
+  // matrix cores work on the step before.
+  constexpr int kOps = 2 * kFrags;
+  auto op_row = [&](int r) {
+    return (r < kFrags ? wm : wn) * kWaveTile + 32u * (uint32_t)(r % kFrags) + l32;
+  };
+  auto codes_of = [&](const uint8_t* st, int r) { return st + (r < kFrags ? 0 : kCodeBytes); };
+  auto scales_of = [&](const uint8_t* st, int r) {
+    return st + 2 * kCodeBytes + (r < kFrags ? 0 : kScaleBytes);
+  };
+  u32x4 lo[kOps], hi[kOps];
+  f16x2 dlo[kOps], dhi[kOps], ndlo[kOps], ndhi[kOps];
+  f16x8 op[2][kOps];
+  {
+    const uint8_t* st = stage_ptr(0);
 #pragma unroll
-    for (int i = 0; i < kFm; ++i) da[i] = decode_scales(fa[i]);
-#pragma unroll
-    for (int j = 0; j < kFn; ++j) db[j] = decode_scales(fb[j]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f16x8 a[kFm], b[kFn];
-#pragma unroll
-      for (int i = 0; i < kFm; ++i) a[i] = decode_step(fa[i], da[i], t);
-#pragma unroll
-      for (int j = 0; j < kFn; ++j) b[j] = decode_step(fb[j], db[j], t);
-#pragma unroll
-      for (int i = 0; i < kFm; ++i)
-#pragma unroll
-        for (int j = 0; j < kFn; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int r = 0; r < kOps; ++r) {
+      lo[r] = read_codes(codes_of(st, r), op_row(r), 2u * h);
+      read_scales(scales_of(st, r), op_row(r), h, dlo[r], dhi[r]);
     }
 #pragma unroll
-    for (int i = 0; i < kFm; ++i) fa[i] = na[i];
+    for (int r = 0; r < kOps; ++r) op[0][r] = decode8(lo[r][0], dlo[r][0]);
+  }
+  // vm: vector-memory instructions to place among this step's MFMAs.
+  auto mfma_step = [&](int cur, auto vm_c) {
+    constexpr int vm = decltype(vm_c)::value;
 #pragma unroll
-    for (int j = 0; j < kFn; ++j) fb[j] = nb[j];
+    for (int i = 0; i < kFrags; ++i)
+#pragma unroll
+      for (int j = 0; j < kFrags; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][i], op[cur][kFrags + j],
+                                                           acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < kFrags * kFrags; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+      if constexpr (vm > 0)
+        if (k == 2) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // loads
+    }
+  };
+
+  for (uint32_t c = 0; c < nstages; ++c) {
+    const bool more = c + kAhead < nstages;
+    u32x2 qa = {}, qb = {};
+    const uint8_t* st = stage_ptr(c);
+#pragma unroll
+    for (int r = 0; r < kOps; ++r) hi[r] = read_codes(codes_of(st, r), op_row(r), 2u * h + 1u);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int cur = t & 1, nxt = cur ^ 1;
+      issue_part(c + kAhead, t, more, qa, qb);
+#pragma unroll
+      for (int r = 0; r < kOps; ++r)
+        op[nxt][r] = t < 3 ? decode8(lo[r][t + 1], dlo[r][(t + 1) >> 1])
+                           : decode8(hi[r][0], dhi[r][0]);
+      mfma_step(cur, std::integral_constant<int, 2>{});
+    }
+    // The next stage's first codes and scales (stage c + 1 is in LDS; on the
+    // last stage this reads a stale buffer whose values are never used).
+    const uint8_t* sn = stage_ptr(c + 1);
+#pragma unroll
+    for (int r = 0; r < kOps; ++r) {
+      lo[r] = read_codes(codes_of(sn, r), op_row(r), 2u * h);
+      read_scales(scales_of(sn, r), op_row(r), h, ndlo[r], ndhi[r]);
+    }
+#pragma unroll
+    for (int t = 4; t < 8; ++t) {
+      const int cur = t & 1, nxt = cur ^ 1;
+      if (t < 6) issue_part(c + kAhead, t, more, qa, qb);
+#pragma unroll
+      for (int r = 0; r < kOps; ++r)
+        op[nxt][r] = t < 7 ? decode8(hi[r][t - 3], dhi[r][(t - 3) >> 1])
+                           : decode8(lo[r][0], ndlo[r][0]);
+      if (t < 6)
+        mfma_step(cur, std::integral_constant<int, kAligned ? 2 : 8>{});
+      else
+        mfma_step(cur, std::integral_constant<int, 0>{});
+    }
+#pragma unroll
+    for (int r = 0; r < kOps; ++r) {
+      dlo[r] = ndlo[r];
+      dhi[r] = ndhi[r];
+    }
+    // This stage's loads of stage c + 3 (issued even past the last stage,
+    // then out of range) may stay in flight; stage c + 2's are complete.
+    wait_vm<kLoadsPerStage<kAligned>>();
+    if constexpr (!kAligned) {
+      // Scale bytes through registers (rows not 4-byte aligned): the copy
+      // below waits for this stage's loads, so this variant keeps fewer
+      // loads in flight.
+      if (c + 2 < nstages) put_scales(c + 2, pa2, pb2);
+    }
+    lds_barrier();
+    if constexpr (!kAligned) {
+      pa2 = qa;
+      pb2 = qb;
+    }
   }
 
+  wait_vm<0>();
   const float gab = (*ga) * (*gb);
+  const int64_t mw = m0 + wm * kWaveTile, nw = n0 + wn * kWaveTile;
 #pragma unroll
-  for (int i = 0; i < kFm; ++i)
+  for (int i = 0; i < kFrags; ++i)
 #pragma unroll
-    for (int j = 0; j < kFn; ++j) {
-      const int64_t col = n0 + 32 * j + l32;
+    for (int j = 0; j < kFrags; ++j) {
+      const int64_t col = nw + 32 * j + l32;
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+        const int64_t row = mw + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
         if (row >= M) continue;
         const float y = acc[i][j][r] * gab;
         if constexpr (kBf16)
@@ -199,21 +401,32 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     }
 }
 
+template <bool kBf16, bool kAligned>
+hipError_t launch_gemm_v(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
+                         const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
+                         void* out, hipStream_t s, Events ev) {
+  const uint32_t tiles_m = (uint32_t)((M + kTile - 1) / kTile);
+  const uint32_t tiles_n = (uint32_t)((N + kTile - 1) / kTile);
+  const uint32_t per_xcd = (tiles_m * tiles_n + 7u) / 8u;
+  return launch_with_events(gemm_kernel<kBf16, kAligned>, dim3(per_xcd * 8u),
+                            dim3(kGemmThreads), s, ev, pa, sa, ga, pb, sb, gb, M, N, K, tiles_m,
+                            tiles_n, per_xcd, out);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
                        const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
                        int out_bf16, void* out, hipStream_t s, Events ev) {
-  const uint32_t tiles_m = (uint32_t)((M + kTileM - 1) / kTileM);
-  const uint32_t tiles_n = (uint32_t)((N + kTileN - 1) / kTileN);
-  const uint32_t total = tiles_m * tiles_n;
-  const uint32_t per_xcd = (total + 7u) / 8u;
-  const dim3 grid(per_xcd * 8u), block(kGemmThreads);
+  // Scale rows start 4-byte aligned when K / 16 is a multiple of 4 (and the
+  // scale pointers are): then each stage's scales load as two words.
+  const bool aligned = (K / 16) % 4 == 0 && (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(sb) & 3u) == 0;
   if (out_bf16)
-    return launch_with_events(gemm_kernel<true>, grid, block, s, ev, pa, sa, ga, pb, sb, gb, M,
-                              N, K, tiles_m, tiles_n, per_xcd, out);
-  return launch_with_events(gemm_kernel<false>, grid, block, s, ev, pa, sa, ga, pb, sb, gb, M, N,
-                            K, tiles_m, tiles_n, per_xcd, out);
+    return aligned ? launch_gemm_v<true, true>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev)
+                   : launch_gemm_v<true, false>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
+  return aligned ? launch_gemm_v<false, true>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev)
+                 : launch_gemm_v<false, false>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
 }
 
 }  // namespace nvfp4
