@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_quantize_rows_4over6_mse_32768x5120.txt")
 KERNEL_SOURCES = ["quantize_rows.hip", "nvfp4_device.h", "nvfp4_kernels.h"]
 
@@ -188,6 +189,27 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     res["rmsnorm_residual_given_g_us"] = round(t_f1 * 1e6, 2)
     res["rmsnorm_residual_given_g_gbps"] = round(res_bytes / t_f1 / 1e9, 1)
     res["rmsnorm_residual_two_pass_us"] = round(t_f2 * 1e6, 2)
+    # W4A4 product on the matrix cores: these activations (as quantized by
+    # the step) times a 5120 x 5120 weight, and the augmented product over
+    # K = 5120 + 256 (residual activations, duplicated weight channels).
+    w_bf = torch.from_numpy(testkit.fill((cols, cols), testkit.NORMAL, 0.02, 98).view(np.int16)).to(
+        dev).view(torch.bfloat16)
+    qw = nv.quantize(w_bf, nv.AXIS_COLS, nv.MODE_4OVER6, nv.RULE_MSE)
+    qw = {"packed": qw["packed"].view(cols, cols // 2), "scales": qw["scales"].view(cols, cols // 16),
+          "gscale": qw["gscale"]}
+    qa = {"packed": packed.view(rows, cols // 2), "scales": scales.view(rows, cols // 16),
+          "gscale": g}
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    t_mm = call_time(lambda: nv.gemm(qa, qw, torch.bfloat16, out=y), torch, stream, 20)
+    flops = 2.0 * rows * cols * cols
+    res["gemm_w4a4_32768x5120x5120_bf16_us"] = round(t_mm * 1e6, 1)
+    res["gemm_w4a4_tflops"] = round(flops / t_mm / 1e12, 1)
+    res["gemm_w4a4_frac_of_f16_mfma_peak"] = round(flops / t_mm / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+    qwa = nv.quantize_residual(w_bf, perm, nres, nv.MODE_4OVER6, nv.RULE_MSE, duplicate=True)
+    t_aug = call_time(lambda: nv.gemm(ro, qwa, torch.bfloat16, out=y), torch, stream, 20)
+    res["gemm_augmented_k5376_bf16_us"] = round(t_aug * 1e6, 1)
+    res["gemm_augmented_tflops"] = round(2.0 * rows * cols * (cols + nres) / t_aug / 1e12, 1)
+    del w_bf, qw, qa, y, qwa
     del ro, absmax_c, perm, fo, fo2, wgt
     # The quantize kernel on the other workloads' shapes and modes.
     for cid in (2, 3, 5):
