@@ -295,8 +295,8 @@ nvfp4_status nvfp4_rmsnorm_quantize_residual(const uint16_t* in_bf16, int64_t ro
  *   |out - exact| <= (k + k/16 + 2) * 2^-23 * ga * gb * sum_k |a b|
  * (plus the bf16 rounding with NVFP4_OUT_BF16); results are deterministic
  * for a given library build and shape.
- *   k: a positive multiple of 16, at most 2^24; m, n positive, each of
- *     m*n, m*k and n*k at most 2^46.
+ *   k: a positive multiple of 16, at most 2^24; n positive, at most 2^24;
+ *     m positive; each of m*n, m*k and n*k at most 2^46.
  *   Alignment: packed codes 4 bytes, scalars 4 bytes, out 4 (fp32) or 2
  *   (bf16) bytes.  out must not overlap any input (NVFP4_ERR_ALIAS). */
 nvfp4_status nvfp4_gemm(const uint8_t* a_packed, const uint8_t* a_scales, const float* a_gscale,

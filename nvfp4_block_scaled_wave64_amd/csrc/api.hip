@@ -416,6 +416,7 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_packed, const uint8_t* a_scales, const 
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_ENUM;
   if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || k > (int64_t(1) << 24))
     return NVFP4_ERR_SHAPE;
+  if (n > (int64_t(1) << 24)) return NVFP4_ERR_SHAPE;
   if (m > kMaxNumel / n || m > kMaxNumel / k || n > kMaxNumel / k) return NVFP4_ERR_SHAPE;
   const int64_t esz = out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
   if (!aligned(a_packed, 4) || !aligned(b_packed, 4) || !aligned(a_gscale, 4) ||

@@ -380,25 +380,36 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   }
 
   wait_vm<0>();
+  // Epilogue: out = acc * RN(ga * gb).  One buffer resource per 32-row slice
+  // (its range drops rows past M); a lane's column offset is per lane, the
+  // row offset of accumulator element r a scalar (N <= 2^24 keeps a slice's
+  // byte offsets in 32 bits).
   const float gab = (*ga) * (*gb);
   const int64_t mw = m0 + wm * kWaveTile, nw = n0 + wn * kWaveTile;
+  constexpr uint32_t kEsz = kBf16 ? 2u : 4u;
+  const uint32_t row_bytes = (uint32_t)N * kEsz;
 #pragma unroll
-  for (int i = 0; i < kFrags; ++i)
+  for (int i = 0; i < kFrags; ++i) {
+    const int64_t r0 = mw + 32 * i;
+    const uint32_t rows = (uint32_t)max<int64_t>(0, min<int64_t>(32, M - r0));
+    const __amdgpu_buffer_rsrc_t ro =
+        uniform_rsrc(static_cast<uint8_t*>(out) + r0 * (int64_t)row_bytes, rows * row_bytes);
 #pragma unroll
     for (int j = 0; j < kFrags; ++j) {
       const int64_t col = nw + 32 * j + l32;
       if (col >= N) continue;
+      const uint32_t voff = 4u * h * row_bytes + (uint32_t)col * kEsz;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = mw + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-        if (row >= M) continue;
+        const uint32_t soff = (uint32_t)(8 * (r / 4) + (r % 4)) * row_bytes;
         const float y = acc[i][j][r] * gab;
         if constexpr (kBf16)
-          static_cast<uint16_t*>(out)[row * N + col] = to_bf16_bits(y);
+          __builtin_amdgcn_raw_buffer_store_b16(to_bf16_bits(y), ro, voff, soff, 0);
         else
-          static_cast<float*>(out)[row * N + col] = y;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ro, voff, soff, 0);
       }
     }
+  }
 }
 
 template <bool kBf16, bool kAligned>

@@ -274,6 +274,7 @@ def gm(**kw):
     (dict(dtype=2), 2), (dict(dtype=-1), 2),
     (dict(m=0), 3), (dict(n=-4), 3), (dict(k=0), 3), (dict(k=40), 3),
     (dict(k=(1 << 24) + 16), 3), (dict(m=1 << 40, n=1 << 10), 3), (dict(m=1 << 31, k=1 << 16), 3),
+    (dict(n=(1 << 24) + 1, m=1), 3),
     (dict(pa=ctypes.c_void_p(0x10002)), 4), (dict(pb=ctypes.c_void_p(0x40001)), 4),
     (dict(ga=ctypes.c_void_p(0x30002)), 4), (dict(out=ctypes.c_void_p(0x70002)), 4),
     (dict(out=ctypes.c_void_p(0x70001), dtype=nv.OUT_BF16), 4),
@@ -282,7 +283,7 @@ def gm(**kw):
 ])
 def test_gemm_rejects(kw, status):
     """nvfp4_gemm: nulls, out_dtype, shape (positive extents, k a multiple of
-    16 up to 2^24, products of extents up to 2^46), alignment (codes and
+    16 up to 2^24, n up to 2^24, products of extents up to 2^46), alignment (codes and
     scalars 4 bytes, out its element size) and an output overlapping any
     input."""
     assert gm(**kw) == status
