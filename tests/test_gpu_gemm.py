@@ -95,6 +95,20 @@ def test_random_operands_within_the_bound(M, N, K, out_dtype):
     assert_within(got, want, gabs, K, extra, f"{M}x{N}x{K}")
 
 
+def test_bf16_output_at_a_two_byte_offset():
+    banner("bf16 output not 4-byte aligned")
+    M, N, K = 70, 64, 96
+    pa, sa = random_nvfp4(43, M, K)
+    pb, sb = random_nvfp4(44, N, K)
+    big = torch.zeros(M * N + 1, dtype=torch.bfloat16, device="cuda")
+    out = big[1:]  # data pointer 2 bytes past an aligned one
+    nv.gemm(dev_operand(pa, sa, 0.5), dev_operand(pb, sb, 0.25), torch.bfloat16, out=out)
+    ref = gpu_gemm(pa, sa, 0.5, pb, sb, 0.25, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert big[0].item() == 0.0
+    np.testing.assert_array_equal(out.float().cpu().numpy().astype(np.float64).reshape(M, N), ref)
+
+
 def test_bf16_output_is_the_rounded_fp32_output():
     banner("bf16 = RNE(fp32)")
     M, N, K = 300, 270, 336
