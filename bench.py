@@ -213,7 +213,7 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     del ro, absmax_c, perm, fo, fo2, wgt
     # The quantize kernel on the other workloads' shapes and modes.
     for cid in (2, 3, 5):
-        cfg = testkit.CONFIGS[cid]
+        cfg = testkit.WORKLOADS[cid]
         xc = torch.from_numpy(testkit.make(cid).view(np.int16)).to(dev).view(torch.bfloat16)
         oc = nv.quantize(xc, cfg.block_axis, cfg.mode, cfg.rule)
         gc = oc["gscale"]
@@ -256,8 +256,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path's "
-              "multi-GPU sharding is described in DESIGN.md and not run here.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); sharding the path "
+              "over several GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -265,7 +265,7 @@ def main():
     import nvfp4_block_scaled_wave64_amd as nv
     import testkit
 
-    cfg = testkit.CONFIGS[4]
+    cfg = testkit.WORKLOADS[4]
     rows, cols = cfg.rows, cfg.cols
     numel = rows * cols
     log(f"generating config 4 input {rows}x{cols}")

@@ -126,7 +126,7 @@ class Config:
         return self.rows * self.cols
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Config(1, "std_256x1024_roundtrip", 256, 1024, MODE_STD, RULE_MSE, AXIS_COLS,
               "N(0,1); round(0.5% of N) = 1311 distinct seeded positions x50"),
     2: Config(2, "4over6_mse_4096x5120_act", 4096, 5120, MODE_4OVER6, RULE_MSE, AXIS_COLS,
@@ -148,7 +148,7 @@ def seeds(cid):
 def make(cid, rows=None, cols=None, threads=None):
     """The bf16 tensor of workload `cid` (optionally at another shape with the
     same recipe: outlier counts scale with the element count)."""
-    cfg = CONFIGS[cid]
+    cfg = WORKLOADS[cid]
     rows = rows or cfg.rows
     cols = cols or cfg.cols
     n = rows * cols

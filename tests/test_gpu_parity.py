@@ -3,7 +3,7 @@ element on the same seeded inputs.  Codes, scale bytes, global scale and the
 selection bitmap must be bit-exact; the per-tensor error sum must agree to
 1e-6 relative (binary64 sums in a different order).
 
-Workloads follow the five benchmark configurations (testkit.CONFIGS): full
+Workloads follow the five benchmark workloads (testkit.WORKLOADS): full
 size, and reduced/ragged shapes that span several tiles and leave a partial
 tail."""
 import numpy as np
@@ -31,7 +31,7 @@ def banner(msg):
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_config_full_size(cid):
-    cfg = testkit.CONFIGS[cid]
+    cfg = testkit.WORKLOADS[cid]
     banner(f"config {cid} {cfg.name} {cfg.rows}x{cfg.cols}")
     x = testkit.make(cid)
     check_against_oracle(x, cfg.block_axis, cfg.mode, cfg.rule, what=f"config {cid}")
@@ -278,7 +278,7 @@ def test_dequantize_tiny_scales_and_ragged(axis, dtype):
 def test_dequantize_full_size(axis, cid, dtype):
     """Dequantize the full column-blocked gradient workload (and a row-wise
     one) against the oracle's reconstruction, bit for bit."""
-    cfg = testkit.CONFIGS[cid]
+    cfg = testkit.WORKLOADS[cid]
     banner(f"dequantize full {cfg.rows}x{cfg.cols} axis={axis} {dtype}")
     x = testkit.make(cid)
     ref = oracle.quantize(x, axis, cfg.mode, cfg.rule, want_err=False)
