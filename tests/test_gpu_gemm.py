@@ -182,6 +182,21 @@ def test_full_size_prefill_product_sampled():
     assert np.isfinite(got).all()
 
 
+def test_long_k_errors_are_far_inside_the_bound():
+    # 512 stages of the K loop.  The bound is a worst case (every rounding
+    # in the same direction); random-sign sums grow like sqrt(K), so the
+    # typical error must sit well inside it.
+    M, N, K = 48, 32, 65536
+    banner(f"long K {M}x{N}x{K}")
+    pa, sa = random_nvfp4(91, M, K, 0x30, 0x48)
+    pb, sb = random_nvfp4(92, N, K, 0x30, 0x48)
+    got = gpu_gemm(pa, sa, 0.125, pb, sb, 0.5)
+    want, gabs = oracle.gemm(pa, sa, 0.125, pb, sb, 0.5, M, N, K, want_abs=True)
+    assert_within(got, want, gabs, K)
+    ratio = np.abs(got - want) / bound(K, gabs)
+    assert ratio.mean() < 0.01 and ratio.max() < 0.1, (ratio.mean(), ratio.max())
+
+
 def test_deterministic_and_exact_scalings():
     banner("determinism, g scaling, zero g")
     M, N, K = 257, 255, 1040
