@@ -27,13 +27,13 @@
 //
 // Data path.  A workgroup computes a 256 x 256 tile with four waves of
 // 128 x 128 (the accumulators fill the 256 AGPRs).  K is walked in stages of
-// 128 (eight blocks): the workgroup copies the stage's codes (256 rows x 64
-// bytes per operand, four lanes per row so that every request is one
-// contiguous 64-byte piece) and scale bytes into LDS, three stages deep, so
-// the loads of stage c + 2 are in flight while the matrix cores work on
-// stage c.  In LDS the 16-byte pieces of a row are XOR-swizzled by bits 2-3
-// of the row, which makes both the 16-byte writes and the fragment reads
-// (16 lanes on 16 consecutive rows) free of bank conflicts.
+// 128 (eight blocks): the stage's codes (256 rows x 64 bytes per operand,
+// four lanes per row so that every request is one contiguous 64-byte piece)
+// and scale bytes go from memory straight into a four-deep LDS ring, three
+// stages ahead of the stage the matrix cores work on.  In LDS the 16-byte
+// pieces of a row are XOR-swizzled by bits 2-3 of the row, which makes both
+// the 16-byte writes and the fragment reads (16 lanes on 16 consecutive
+// rows) free of bank conflicts.
 #include <type_traits>
 
 #include "nvfp4_device.h"
