@@ -97,3 +97,45 @@ def test_graph_capture_and_replay(axis):
         assert torch.equal(got_xhat.view(torch.int16), eager_xhat.view(torch.int16)), i
         ref = oracle.quantize(x, axis, F46, MSE, want_err=False)
         np.testing.assert_array_equal(got["scales"].cpu().numpy().reshape(-1), ref["scales"])
+
+
+def test_outlier_channels_and_w4a4_product_in_a_graph():
+    """The augmented layer (residual quantize of the activations, then the
+    W4A4 product with the duplicated weight) captured once and replayed on
+    new activations; each replay equals the eager calls bit for bit."""
+    banner("graph capture: residual quantize + W4A4 product")
+    rows, cols, n_out, nres = 512, 1024, 384, 64
+    w = to_device(testkit.fill((n_out, cols), testkit.NORMAL, 0.02, 7))
+    calib = to_device(testkit.fill((rows, cols), testkit.STUDENT_T3, 0.5, 8))
+    _, perm = nv.channel_order(calib)
+    qw = nv.quantize_residual(w, perm, nres, F46, MSE, duplicate=True)
+    inputs = [testkit.fill((rows, cols), testkit.STUDENT_T3, s, 200 + i)
+              for i, s in enumerate((0.5, 4.0, 0.02))]
+    static_x = to_device(inputs[0])
+    qa = nv.quantize_residual(static_x, perm, nres, F46, MSE)
+    y = torch.empty((rows, n_out), dtype=torch.bfloat16, device="cuda")
+
+    def layer():
+        nv.quantize_residual(static_x, perm, nres, F46, MSE, out=qa)
+        nv.gemm(qa, qw, torch.bfloat16, out=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    torch.cuda.synchronize()
+    for i, x in enumerate(inputs + inputs[:1]):
+        static_x.copy_(to_device(x))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        ea = nv.quantize_residual(to_device(x), perm, nres, F46, MSE)
+        ey = nv.gemm(ea, qw, torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(qa["packed"], ea["packed"]) and torch.equal(qa["scales"], ea["scales"]), i
+        assert torch.equal(got.view(torch.int16), ey.view(torch.int16)), i
