@@ -8,7 +8,8 @@ One 65600 x 16384 bf16 tensor (2^30 + 2^20 elements, 2 GiB) covers:
   * the amax pass's split at 2^27 16-byte vectors (element 2^30),
 and a 16384 x 65600 view of the same bytes exercises the column-blocked
 kernel's 64-bit addressing on a tensor larger than 2^31 bytes.  A 140000 x
-8192 tensor (2.3 GB) does the same for the outlier-channel calls.
+8192 tensor (2.3 GB) does the same for the outlier-channel calls, and a
+1.1M-row activation operand (2.25 GB of codes) for the W4A4 product.
 """
 import numpy as np
 import pytest
@@ -147,3 +148,31 @@ def test_large_residual_sampled_rows(big_res):
     np.testing.assert_array_equal(r["packed"][idx].cpu().numpy(), ref["packed"])
     np.testing.assert_array_equal(r["scales"][idx].cpu().numpy(), ref["scales"])
     del r
+
+
+def test_large_w4a4_product_sampled_rows():
+    """An activation operand of 2.25 GB of codes: the tiles' base addresses
+    pass 2^31 bytes (64-bit per-tile bases, 32-bit offsets within a tile);
+    sampled rows (first and last tiles among them) against the oracle."""
+    M, N, K = 1_100_000, 48, 4096
+    banner(f"W4A4 product {M}x{N}x{K}")
+    rng = np.random.default_rng(0xA4)
+    pa = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    sa = rng.integers(0x30, 0x48, (M, K // 16), dtype=np.uint8)
+    pb = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    sb = rng.integers(0x30, 0x48, (N, K // 16), dtype=np.uint8)
+    ga, gb = np.float32(0.01), np.float32(0.02)
+    a = {"packed": torch.from_numpy(pa).cuda(), "scales": torch.from_numpy(sa).cuda(),
+         "gscale": torch.tensor([float(ga)], device="cuda")}
+    b = {"packed": torch.from_numpy(pb).cuda(), "scales": torch.from_numpy(sb).cuda(),
+         "gscale": torch.tensor([float(gb)], device="cuda")}
+    y = nv.gemm(a, b)
+    torch.cuda.synchronize()
+    rows = np.concatenate([[0, 255, 256, M // 2, M - 257, M - 1],
+                           rng.choice(M, 42, replace=False)])
+    got = y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    want, gabs = oracle.gemm(pa[rows], sa[rows], ga, pb, sb, gb, len(rows), N, K, want_abs=True)
+    tol = (K + K // 16 + 2) * 2.0 ** -23 * gabs + 2.0 ** -126
+    assert np.all(np.abs(got - want) <= tol)
+    del a, b, y
+    torch.cuda.empty_cache()
