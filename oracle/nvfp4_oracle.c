@@ -19,14 +19,17 @@
  *        - "Implementation details": block scales are FP8 E4M3; under 4/6 the
  *          per-tensor scale is formed with 256 in place of 448.
  *  [MIN] "Why Gated DeltaNet in hybrid 27B LLMs withstands 4-bit quantization"
- *        (sns.style) - "Deep analysis": NVFP4 scales blocks of 16 elements.
+ *        (sns.style) - "Background": every linear layer in NVFP4 W4A4 (weights
+ *        and activations both 4-bit); "Deep analysis": NVFP4 scales blocks of
+ *        16 elements.
  *  [ARC] "ARCQuant" summary (gist.science, paper 2601.07475) - "Problem
  *        definition": NVFP4 requires block size 16; "Methodology": channels
  *        reordered by absolute maximum, the top-S outlier channels get a
  *        residual stage (original minus primary reconstruction) quantized as
  *        a second NVFP4 channel set appended along the reduction dimension;
  *        the authors fuse channel reordering, RMSNorm and both quantization
- *        stages into one kernel.
+ *        stages into one kernel; the matching weight channels are duplicated
+ *        and the whole layer runs as one GEMM over K_in + S.
  *
  * The pages fix the formats and the steps, not the floating-point operation
  * order.  This file fixes it, taking the plainest reading where the pages are
