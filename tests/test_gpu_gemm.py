@@ -213,3 +213,49 @@ def test_deterministic_and_exact_scalings():
     assert_within(t.T, want, gabs, K)
     z = gpu_gemm(pa, sa, 0.0, pb, sb, 0.5)
     assert (z == 0).all()
+
+
+def test_forward_and_backward_products_from_one_dual_quantization():
+    """4/6 on weights and gradients: one nvfp4_quantize_dual call on a
+    weight W [N][K] gives the row-blocked operand of the forward product
+    Y = X W^T (reduction over K) and the column-blocked one, the layout of
+    W^T [K][N] blocked along N, of the backward product dX = dY W
+    (reduction over N).  Both products against the oracle on the same
+    operands, within the bound."""
+    banner("forward and backward products from one dual quantization")
+    M, N, K = 192, 160, 320
+    w = testkit.fill((N, K), testkit.NORMAL, 0.02, 101)
+    x = testkit.fill((M, K), testkit.STUDENT_T3, 0.5, 102)
+    dy = testkit.fill((M, N), testkit.NORMAL, 1e-3, 103)
+    qd = nv.quantize_dual(to_device(w), F46, MSE)
+    qx = nv.quantize(to_device(x), nv.AXIS_COLS, F46, MSE)
+    qdy = nv.quantize(to_device(dy), nv.AXIS_COLS, F46, MSE)
+    g = qd["gscale"]
+    w_rows = {"packed": qd["rows"]["packed"].view(N, K // 2),
+              "scales": qd["rows"]["scales"].view(N, K // 16), "gscale": g}
+    w_cols = {"packed": qd["cols"]["packed"].view(K, N // 2),
+              "scales": qd["cols"]["scales"].view(K, N // 16), "gscale": g}
+    a_x = {"packed": qx["packed"].view(M, K // 2), "scales": qx["scales"].view(M, K // 16),
+           "gscale": qx["gscale"]}
+    a_dy = {"packed": qdy["packed"].view(M, N // 2), "scales": qdy["scales"].view(M, N // 16),
+            "gscale": qdy["gscale"]}
+    y = nv.gemm(a_x, w_rows).cpu().numpy().astype(np.float64)
+    dx = nv.gemm(a_dy, w_cols).cpu().numpy().astype(np.float64)
+    # The oracle's own quantizations of the same tensors (both layouts of W).
+    ow = oracle.quantize(w, nv.AXIS_COLS, F46, MSE, want_selmap=False, want_err=False)
+    owt = oracle.quantize(w, nv.AXIS_ROWS, F46, MSE, want_selmap=False, want_err=False)
+    ox = oracle.quantize(x, nv.AXIS_COLS, F46, MSE, want_selmap=False, want_err=False)
+    ody = oracle.quantize(dy, nv.AXIS_COLS, F46, MSE, want_selmap=False, want_err=False)
+    assert owt["gscale"] == ow["gscale"] == np.float32(g.item())
+    want_y, gy = oracle.gemm(ox["packed"], ox["scales"], ox["gscale"], ow["packed"], ow["scales"],
+                             ow["gscale"], M, N, K, want_abs=True)
+    want_dx, gdx = oracle.gemm(ody["packed"], ody["scales"], ody["gscale"], owt["packed"],
+                               owt["scales"], owt["gscale"], M, K, N, want_abs=True)
+    assert_within(y, want_y, gy, K, what="forward")
+    assert_within(dx, want_dx, gdx, N, what="backward")
+    # And both approximate the bf16 products.
+    xf, wf = testkit.bf16_to_f32(x).astype(np.float64), testkit.bf16_to_f32(w).astype(np.float64)
+    dyf = testkit.bf16_to_f32(dy).astype(np.float64)
+    for got, exact in ((y, xf @ wf.T), (dx, dyf @ wf)):
+        rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
+        assert rel < 0.2, rel
