@@ -55,7 +55,8 @@ constexpr int kStages = 4;                        // LDS buffers
 constexpr int kAhead = 3;                         // stages in flight ahead of the one computed
 constexpr int kRowBytes = kStageBlocks * 8;       // code bytes per row and stage
 constexpr int kCodeBytes = kTile * kRowBytes;     // one operand's codes per stage
-constexpr int kScaleBytes = kTile * kStageBlocks; // one operand's scales per stage
+constexpr int kScaleSlot = 16;                    // LDS bytes per row for its 8 scale bytes
+constexpr int kScaleBytes = kTile * kScaleSlot;   // one operand's scales per stage
 constexpr int kStageBytes = 2 * kCodeBytes + 2 * kScaleBytes;
 constexpr int kGroupM = 4;                        // tile rows per group of the walk
 
@@ -77,20 +78,25 @@ __device__ __forceinline__ uint32_t code_slot(uint32_t row, uint32_t piece) {
 // The loads of one stage go out in parts spread over the MFMA steps of the
 // stage before (a burst of them would stall the in-order issue of the
 // MFMAs): part q < 4 is the q-th code load of each operand, part 4 the
-// scale loads of A, part 5 those of B.
+// scale load of A, part 5 that of B.
 //
 // Code loads go straight to LDS (buffer_load ... lds): lane l of load q
 // writes bytes 16l .. 16l + 15 of the 1 KiB that holds tile rows
 // 64w + 16q .. 64w + 16q + 15, which is physical piece l % 4 of row
 // 64w + 16q + l / 4, so the lane loads the row's logical piece
-// (l % 4) ^ ((row >> 2) & 3).  Scale bytes (eight per tile row) go to LDS
-// the same way when every row's start is 4-byte aligned (lane l of load k
-// writes word l % 2 of row 64w + 32k + l / 2); otherwise they come back in
-// registers, those of tile row `thread`.  Rows past the tile's valid rows
-// read 0 (resource range); blocks at or past the end of K get scale 0, so
-// their codes (whatever they read) contribute 0.  With `live` false (no
-// such stage) every load is out of range and writes zeros to a buffer that
-// is not read again.
+// (l % 4) ^ ((row >> 2) & 3).  Scale loads do the same with one 16-byte
+// window per row (lane l: row 64w + l): the 16 bytes from the 4-byte
+// boundary at or below the row's first scale byte of the stage, which
+// contain its 8 bytes at offset (d0 + row * nblk) % 4 whatever K is (d0:
+// the tile's first scale byte's offset above the 4-byte boundary below it,
+// where the scale resource starts; the resource ends at the 4-byte boundary
+// above the tile's last scale byte, because its range check drops whole
+// dwords -- the extra bytes share a dword, hence a page, with valid ones and
+// are never used).  Rows past the tile's valid rows read 0; blocks at or
+// past the end of K are masked to scale 0 by the reader, so their codes
+// (whatever they read) contribute 0.  With `live` false (no such stage)
+// every load is out of range and writes zeros to a buffer that is not read
+// again.
 constexpr uint32_t kOut = 0xFFFFFFF0u;  // past any resource range: reads 0
 
 __device__ __forceinline__ void issue_codes(__amdgpu_buffer_rsrc_t rc, uint8_t* codes_lds,
@@ -104,42 +110,28 @@ __device__ __forceinline__ void issue_codes(__amdgpu_buffer_rsrc_t rc, uint8_t* 
       live ? row * (nblk * 8u) + c * kRowBytes + 16u * piece : kOut, 0, 0, 0);
 }
 
-template <bool kAligned>
-__device__ __forceinline__ u32x2 issue_scales(__amdgpu_buffer_rsrc_t rs, uint8_t* scales_lds,
-                                              uint32_t c, bool live, uint32_t nblk,
-                                              uint32_t wave, uint32_t lane) {
-  const uint32_t b0 = c * kStageBlocks;
-  u32x2 sc = {0u, 0u};
-  if constexpr (kAligned) {
-    // nblk % 4 == 0: each 4-block word is either wholly inside K or past it.
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t first = 64u * wave + 32u * k;
-      const uint32_t srow = first + (lane >> 1), word = lane & 1u;
-      const bool valid = live && b0 + 4u * word + 4u <= nblk;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(scales_lds + first * kStageBlocks), 4,
-          valid ? srow * nblk + b0 + 4u * word : kOut, 0, 0, 0);
-    }
-  } else {
-    const uint32_t base = threadIdx.x * nblk + b0;
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(
-          rs, live && b0 + b < nblk ? base + (uint32_t)b : kOut, 0, 0);
-      w[b >> 2] |= v << (8 * (b & 3));
-    }
-    sc.x = w[0];
-    sc.y = w[1];
-  }
-  return sc;
+__device__ __forceinline__ void issue_scales(__amdgpu_buffer_rsrc_t rs, uint8_t* scales_lds,
+                                             uint32_t c, bool live, uint32_t nblk, uint32_t d0,
+                                             uint32_t wave, uint32_t lane) {
+  const uint32_t first = 64u * wave;
+  const uint32_t row = first + lane;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)(scales_lds + first * kScaleSlot), 16,
+      live ? (d0 + row * nblk + c * kStageBlocks) & ~3u : kOut, 0, 0, 0);
+}
+
+// Scale-byte resource of a tile's rows (see issue_scales): starts at the
+// 4-byte boundary at or below p, and ends at the one at or above p + bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scale_rsrc(const uint8_t* p, uint32_t bytes,
+                                                             uint32_t& d0) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  d0 = __builtin_amdgcn_readfirstlane((uint32_t)(a & 3u));
+  return uniform_rsrc(reinterpret_cast<const uint8_t*>(a - d0), (d0 + bytes + 3u) & ~3u);
 }
 
 // Vector-memory operations one thread issues per stage (both operands):
-// four code loads and the scale loads.
-template <bool kAligned>
-constexpr int kLoadsPerStage = 2 * (4 + (kAligned ? 2 : 8));
+// four code loads and one scale load each.
+constexpr int kLoadsPerStage = 2 * (4 + 1);
 
 // Waits until at most N of this wave's vector-memory operations are
 // outstanding (they complete in issue order).
@@ -160,11 +152,24 @@ __device__ __forceinline__ u32x4 read_codes(const uint8_t* codes, uint32_t row, 
   return *reinterpret_cast<const u32x4*>(codes + code_slot(row, piece));
 }
 
-// dec(S) of the four blocks of lane half h as f16 (E4M3 -> f16 is exact):
-// lo = blocks 4h, 4h + 1 (steps 0-3), hi = blocks 4h + 2, 4h + 3 (steps 4-7).
+// dec(S) of the four blocks of lane half h in stage c as f16 (E4M3 -> f16
+// is exact): lo = blocks 4h, 4h + 1 (steps 0-3), hi = blocks 4h + 2, 4h + 3
+// (steps 4-7).  The row's bytes sit at offset (d0 + row * nblk) % 4 of its slot
+// (0 when d0 = 0 and nblk % 4 == 0); blocks at or past nblk read scale 0.
+template <bool kAligned>
 __device__ __forceinline__ void read_scales(const uint8_t* scales, uint32_t row, uint32_t h,
-                                            f16x2& lo, f16x2& hi) {
-  const uint32_t s = *reinterpret_cast<const uint32_t*>(scales + row * kStageBlocks + 4u * h);
+                                            uint32_t c, uint32_t nblk, uint32_t d0, f16x2& lo,
+                                            f16x2& hi) {
+  const uint32_t* slot = reinterpret_cast<const uint32_t*>(scales + row * kScaleSlot);
+  uint32_t s;
+  if constexpr (kAligned) {
+    s = slot[h];
+  } else {
+    const uint32_t b = ((d0 + row * nblk) & 3u) + 4u * h;
+    s = __builtin_amdgcn_alignbyte(slot[(b >> 2) + 1], slot[b >> 2], b & 3u);
+  }
+  const int32_t valid = (int32_t)nblk - (int32_t)(c * kStageBlocks + 4u * h);
+  if (valid < 4) s = valid <= 0 ? 0u : s & (0xFFFFFFFFu >> (8 * (4 - valid)));
   lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false);
   hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true);
 }
@@ -220,9 +225,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   const uint32_t rows_a = (uint32_t)min<int64_t>(kTile, M - m0);
   const uint32_t rows_b = (uint32_t)min<int64_t>(kTile, N - n0);
   const __amdgpu_buffer_rsrc_t rca = uniform_rsrc(pa + m0 * (K / 2), rows_a * nblk * 8u);
-  const __amdgpu_buffer_rsrc_t rsa = uniform_rsrc(sa + m0 * (K / 16), rows_a * nblk);
+  uint32_t da = 0, db = 0;  // scale resources' offsets below their tiles' first bytes
+  const __amdgpu_buffer_rsrc_t rsa = scale_rsrc(sa + m0 * (K / 16), rows_a * nblk, da);
   const __amdgpu_buffer_rsrc_t rcb = uniform_rsrc(pb + n0 * (K / 2), rows_b * nblk * 8u);
-  const __amdgpu_buffer_rsrc_t rsb = uniform_rsrc(sb + n0 * (K / 16), rows_b * nblk);
+  const __amdgpu_buffer_rsrc_t rsb = scale_rsrc(sb + n0 * (K / 16), rows_b * nblk, db);
 
   f32x16 acc[kFrags][kFrags];
 #pragma unroll
@@ -232,47 +238,35 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 
   auto stage_ptr = [&](uint32_t c) { return lds + (c % kStages) * kStageBytes; };
   // Part q (0..5) of the loads of stage c (see issue_codes).
-  auto issue_part = [&](uint32_t c, int q, bool live, u32x2& qa, u32x2& qb) {
+  auto issue_part = [&](uint32_t c, int q, bool live) {
     uint8_t* st = stage_ptr(c);
     if (q < 4) {
       issue_codes(rca, st, c, q, live, nblk, wave, lane);
       issue_codes(rcb, st + kCodeBytes, c, q, live, nblk, wave, lane);
     } else if (q == 4) {
-      qa = issue_scales<kAligned>(rsa, st + 2 * kCodeBytes, c, live, nblk, wave, lane);
+      issue_scales(rsa, st + 2 * kCodeBytes, c, live, nblk, da, wave, lane);
     } else {
-      qb = issue_scales<kAligned>(rsb, st + 2 * kCodeBytes + kScaleBytes, c, live, nblk, wave,
-                                  lane);
+      issue_scales(rsb, st + 2 * kCodeBytes + kScaleBytes, c, live, nblk, db, wave, lane);
     }
   };
-  auto issue = [&](uint32_t c, u32x2& qa, u32x2& qb) {
+  auto issue = [&](uint32_t c) {
 #pragma unroll
-    for (int q = 0; q < 6; ++q) issue_part(c, q, true, qa, qb);
-  };
-  auto put_scales = [&](uint32_t c, u32x2 qa, u32x2 qb) {
-    uint8_t* sc = stage_ptr(c) + 2 * kCodeBytes + threadIdx.x * kStageBlocks;
-    *reinterpret_cast<u32x2*>(sc) = qa;
-    *reinterpret_cast<u32x2*>(sc + kScaleBytes) = qb;
+    for (int q = 0; q < 6; ++q) issue_part(c, q, true);
   };
 
   // Pipeline: stage c is computed while the loads of stages c + 1 .. c + 3
   // are in flight; at the end of stage c this wave waits for its loads of
-  // stage c + 2 (only stage c + 3's may stay outstanding), writes that
-  // stage's scale bytes, and the barrier publishes it.  So during stage c,
-  // stages c and c + 1 are complete in LDS; buffer (c + 3) % 4 receives
-  // stage c + 3 and buffer (c + 2) % 4 the scales of stage c + 2, neither
-  // read by anyone during stage c.
-  u32x2 s0a = {}, s0b = {}, s1a = {}, s1b = {}, pa2 = {}, pb2 = {};
-  issue(0, s0a, s0b);
-  if (nstages > 1) issue(1, s1a, s1b);
+  // stage c + 2 (only stage c + 3's may stay outstanding) and the barrier
+  // publishes them.  So during stage c, stages c and c + 1 are complete in
+  // LDS, and buffer (c + 3) % 4, which receives stage c + 3, is read by
+  // nobody.
+  issue(0);
+  if (nstages > 1) issue(1);
   if (nstages > 2) {
-    issue(2, pa2, pb2);
-    wait_vm<kLoadsPerStage<kAligned>>();
+    issue(2);
+    wait_vm<kLoadsPerStage>();
   } else {
     wait_vm<0>();
-  }
-  if constexpr (!kAligned) {
-    put_scales(0, s0a, s0b);
-    if (nstages > 1) put_scales(1, s1a, s1b);
   }
   lds_barrier();
 
@@ -298,7 +292,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
     for (int r = 0; r < kOps; ++r) {
       lo[r] = read_codes(codes_of(st, r), op_row(r), 2u * h);
-      read_scales(scales_of(st, r), op_row(r), h, dlo[r], dhi[r]);
+      read_scales<kAligned>(scales_of(st, r), op_row(r), h, 0u, nblk, r < kFrags ? da : db,
+                            dlo[r], dhi[r]);
     }
 #pragma unroll
     for (int r = 0; r < kOps; ++r) op[0][r] = decode8(lo[r][0], dlo[r][0]);
@@ -323,14 +318,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 
   for (uint32_t c = 0; c < nstages; ++c) {
     const bool more = c + kAhead < nstages;
-    u32x2 qa = {}, qb = {};
     const uint8_t* st = stage_ptr(c);
 #pragma unroll
     for (int r = 0; r < kOps; ++r) hi[r] = read_codes(codes_of(st, r), op_row(r), 2u * h + 1u);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int cur = t & 1, nxt = cur ^ 1;
-      issue_part(c + kAhead, t, more, qa, qb);
+      issue_part(c + kAhead, t, more);
 #pragma unroll
       for (int r = 0; r < kOps; ++r)
         op[nxt][r] = t < 3 ? decode8(lo[r][t + 1], dlo[r][(t + 1) >> 1])
@@ -343,18 +337,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
     for (int r = 0; r < kOps; ++r) {
       lo[r] = read_codes(codes_of(sn, r), op_row(r), 2u * h);
-      read_scales(scales_of(sn, r), op_row(r), h, ndlo[r], ndhi[r]);
+      read_scales<kAligned>(scales_of(sn, r), op_row(r), h, c + 1u, nblk, r < kFrags ? da : db,
+                            ndlo[r], ndhi[r]);
     }
 #pragma unroll
     for (int t = 4; t < 8; ++t) {
       const int cur = t & 1, nxt = cur ^ 1;
-      if (t < 6) issue_part(c + kAhead, t, more, qa, qb);
+      if (t < 6) issue_part(c + kAhead, t, more);
 #pragma unroll
       for (int r = 0; r < kOps; ++r)
         op[nxt][r] = t < 7 ? decode8(hi[r][t - 3], dhi[r][(t - 3) >> 1])
                            : decode8(lo[r][0], ndlo[r][0]);
       if (t < 6)
-        mfma_step(cur, std::integral_constant<int, kAligned ? 2 : 8>{});
+        mfma_step(cur, std::integral_constant<int, 1>{});
       else
         mfma_step(cur, std::integral_constant<int, 0>{});
     }
@@ -365,18 +360,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     }
     // This stage's loads of stage c + 3 (issued even past the last stage,
     // then out of range) may stay in flight; stage c + 2's are complete.
-    wait_vm<kLoadsPerStage<kAligned>>();
-    if constexpr (!kAligned) {
-      // Scale bytes through registers (rows not 4-byte aligned): the copy
-      // below waits for this stage's loads, so this variant keeps fewer
-      // loads in flight.
-      if (c + 2 < nstages) put_scales(c + 2, pa2, pb2);
-    }
+    wait_vm<kLoadsPerStage>();
     lds_barrier();
-    if constexpr (!kAligned) {
-      pa2 = qa;
-      pb2 = qb;
-    }
   }
 
   wait_vm<0>();
@@ -429,8 +414,9 @@ hipError_t launch_gemm_v(const uint8_t* pa, const uint8_t* sa, const float* ga, 
 hipError_t launch_gemm(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
                        const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
                        int out_bf16, void* out, hipStream_t s, Events ev) {
-  // Scale rows start 4-byte aligned when K / 16 is a multiple of 4 (and the
-  // scale pointers are): then each stage's scales load as two words.
+  // Every scale row starts 4-byte aligned when K / 16 is a multiple of 4 and
+  // the scale pointers are; otherwise the reader shifts each row's bytes
+  // into place (scale windows start at the 4-byte boundary below them).
   const bool aligned = (K / 16) % 4 == 0 && (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
                        (reinterpret_cast<uintptr_t>(sb) & 3u) == 0;
   if (out_bf16)

@@ -95,6 +95,30 @@ def test_random_operands_within_the_bound(M, N, K, out_dtype):
     assert_within(got, want, gabs, K, extra, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,off_a,off_b", [(70, 90, 320, 1, 3), (257, 33, 336, 2, 1),
+                                                (31, 300, 1040, 3, 0)])
+def test_scale_tensors_not_four_byte_aligned(M, N, K, off_a, off_b):
+    """Scale bytes may start anywhere: each tile's scale window is read from
+    the 4-byte boundary below its first byte."""
+    banner(f"scale pointers offset by {off_a}, {off_b} bytes ({M}x{N}x{K})")
+    pa, sa = random_nvfp4(M + K + off_a, M, K)
+    pb, sb = random_nvfp4(N + K + off_b, N, K)
+
+    def shifted(scales, off):
+        big = torch.full((scales.size + off,), 0x7E, dtype=torch.uint8, device="cuda")
+        t = big[off:]
+        t.copy_(torch.from_numpy(scales.reshape(-1)).cuda())
+        return t.view(scales.shape)
+
+    a = dev_operand(pa, sa, 0.5)
+    b = dev_operand(pb, sb, 0.25)
+    a["scales"] = shifted(sa, off_a)
+    b["scales"] = shifted(sb, off_b)
+    got = nv.gemm(a, b).cpu().numpy().astype(np.float64)
+    want, gabs = oracle.gemm(pa, sa, 0.5, pb, sb, 0.25, M, N, K, want_abs=True)
+    assert_within(got, want, gabs, K)
+
+
 def test_bf16_output_at_a_two_byte_offset():
     banner("bf16 output not 4-byte aligned")
     M, N, K = 70, 64, 96
