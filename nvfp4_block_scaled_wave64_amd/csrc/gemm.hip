@@ -26,7 +26,9 @@
 // partners.
 //
 // Data path.  A workgroup computes a 256 x 256 tile with four waves of
-// 128 x 128 (the accumulators fill the 256 AGPRs).  K is walked in stages of
+// 128 x 128 (the accumulators fill the 256 AGPRs), or, where that fills the
+// compute units' rounds of tiles better (small products), a 256 x 128 tile
+// with waves of 128 x 64.  K is walked in stages of
 // 128 (eight blocks): the stage's codes (256 rows x 64 bytes per operand,
 // four lanes per row so that every request is one contiguous 64-byte piece)
 // and scale bytes go from memory straight into a four-deep LDS ring, three
@@ -47,17 +49,18 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmThreads = 256;                 // 4 waves as 2 x 2
-constexpr int kTile = 256;                        // workgroup tile, rows of A and of B
-constexpr int kWaveTile = 128;                    // wave tile
-constexpr int kFrags = kWaveTile / 32;            // 32 x 32 MFMA tiles per wave and side
+constexpr int kTile = 256;                        // workgroup tile rows of A (and of B when wide)
+constexpr int kWaveTile = 128;                    // wave tile rows of A
+constexpr int kFrags = kWaveTile / 32;            // 32 x 32 MFMA tiles per wave along A
 constexpr int kStageBlocks = 8;                   // blocks of K per stage (K = 128)
 constexpr int kStages = 4;                        // LDS buffers
 constexpr int kAhead = 3;                         // stages in flight ahead of the one computed
 constexpr int kRowBytes = kStageBlocks * 8;       // code bytes per row and stage
-constexpr int kCodeBytes = kTile * kRowBytes;     // one operand's codes per stage
 constexpr int kScaleSlot = 16;                    // LDS bytes per row for its 8 scale bytes
-constexpr int kScaleBytes = kTile * kScaleSlot;   // one operand's scales per stage
-constexpr int kStageBytes = 2 * kCodeBytes + 2 * kScaleBytes;
+// Per stage: A codes [256][64], B codes [kTileN][64], A scale slots [256][16],
+// B scale slots [kTileN][16].
+template <int kTileN>
+constexpr int kStageBytes = (kTile + kTileN) * (kRowBytes + kScaleSlot);
 constexpr int kGroupM = 4;                        // tile rows per group of the walk
 
 // Buffer resource from values the compiler may hold in vector registers but
@@ -99,10 +102,13 @@ __device__ __forceinline__ uint32_t code_slot(uint32_t row, uint32_t piece) {
 // again.
 constexpr uint32_t kOut = 0xFFFFFFF0u;  // past any resource range: reads 0
 
+// kRows: the operand's tile rows (256, or 128 for a narrow B tile), split
+// evenly over the four waves.
+template <int kRows>
 __device__ __forceinline__ void issue_codes(__amdgpu_buffer_rsrc_t rc, uint8_t* codes_lds,
                                             uint32_t c, int q, bool live, uint32_t nblk,
                                             uint32_t wave, uint32_t lane) {
-  const uint32_t first = 64u * wave + 16u * (uint32_t)q;
+  const uint32_t first = (uint32_t)(kRows / 4) * wave + 16u * (uint32_t)q;
   const uint32_t row = first + (lane >> 2);
   const uint32_t piece = (lane & 3u) ^ ((row >> 2) & 3u);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -110,13 +116,13 @@ __device__ __forceinline__ void issue_codes(__amdgpu_buffer_rsrc_t rc, uint8_t* 
       live ? row * (nblk * 8u) + c * kRowBytes + 16u * piece : kOut, 0, 0, 0);
 }
 
-__device__ __forceinline__ void issue_scales(__amdgpu_buffer_rsrc_t rs, uint8_t* scales_lds,
-                                             uint32_t c, bool live, uint32_t nblk, uint32_t d0,
-                                             uint32_t wave, uint32_t lane) {
-  const uint32_t first = 64u * wave;
+// One load covers the 64 rows from `first` and writes their slots at dst.
+__device__ __forceinline__ void issue_scales(__amdgpu_buffer_rsrc_t rs, uint8_t* dst,
+                                             uint32_t first, uint32_t c, bool live, uint32_t nblk,
+                                             uint32_t d0, uint32_t lane) {
   const uint32_t row = first + lane;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rs, (__attribute__((address_space(3))) void*)(scales_lds + first * kScaleSlot), 16,
+      rs, (__attribute__((address_space(3))) void*)dst, 16,
       live ? (d0 + row * nblk + c * kStageBlocks) & ~3u : kOut, 0, 0, 0);
 }
 
@@ -129,9 +135,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scale_rsrc(const uint8_t* p, u
   return uniform_rsrc(reinterpret_cast<const uint8_t*>(a - d0), (d0 + bytes + 3u) & ~3u);
 }
 
-// Vector-memory operations one thread issues per stage (both operands):
-// four code loads and one scale load each.
-constexpr int kLoadsPerStage = 2 * (4 + 1);
+// Vector-memory operations a wave issues per stage: its code loads of A (4)
+// and B (kTileN / 64) and one scale load per operand.  With a narrow B tile
+// only waves 0 and 1 have B scale rows to load; waves 2 and 3 issue an
+// out-of-range load into a spare 1 KiB of LDS that nobody reads, so every
+// wave waits for the same count.
+template <int kTileN>
+constexpr int kLoadsPerStage = 4 + kTileN / 64 + 2;
+constexpr int kSpareBytes = 64 * kScaleSlot;
 
 // Waits until at most N of this wave's vector-memory operations are
 // outstanding (they complete in issue order).
@@ -192,17 +203,22 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return (uint16_t)__builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
 }
 
-// One workgroup per 256 x 256 output tile; tiles are walked in groups of
+// One workgroup per 256 x kTileN output tile; tiles are walked in groups of
 // kGroupM tile rows (the workgroups running together share A and B panels
 // in L2), and consecutive tiles of the walk go to one XCD (workgroups are
 // dealt round-robin over the 8 XCDs).
-template <bool kBf16, bool kAligned>
+template <bool kBf16, bool kAligned, int kTileN>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const uint8_t* __restrict__ pa, const uint8_t* __restrict__ sa, const float* __restrict__ ga,
     const uint8_t* __restrict__ pb, const uint8_t* __restrict__ sb, const float* __restrict__ gb,
     int64_t M, int64_t N, int64_t K, uint32_t tiles_m, uint32_t tiles_n, uint32_t per_xcd,
     void* __restrict__ out) {
-  __shared__ __align__(16) uint8_t lds[kStages * kStageBytes];
+  constexpr int kStage = kStageBytes<kTileN>;
+  constexpr int kCodesA = kTile * kRowBytes, kCodesB = kTileN * kRowBytes;
+  constexpr int kScalesA = kTile * kScaleSlot;
+  constexpr int kWaveTileN = kTileN / 2;       // wave tile columns (rows of B)
+  constexpr int kFragsB = kWaveTileN / 32;     // 32 x 32 MFMA tiles per wave along B
+  __shared__ __align__(16) uint8_t lds[kStages * kStage + (kTileN < kTile ? kSpareBytes : 0)];
   const uint32_t total = tiles_m * tiles_n;
   const uint32_t L = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
   if (L >= total) return;
@@ -221,32 +237,39 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   const uint32_t nstages = (nblk + kStageBlocks - 1) / kStageBlocks;
 
   // Resources over this tile's rows of A and B (rows past M or N read 0).
-  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTileN;
   const uint32_t rows_a = (uint32_t)min<int64_t>(kTile, M - m0);
-  const uint32_t rows_b = (uint32_t)min<int64_t>(kTile, N - n0);
+  const uint32_t rows_b = (uint32_t)min<int64_t>(kTileN, N - n0);
+  // Whether this wave loads B scale rows (64 from row 64 * wave).
+  const bool b_scales = kTileN == kTile || wave < (uint32_t)(kTileN / 64);
   const __amdgpu_buffer_rsrc_t rca = uniform_rsrc(pa + m0 * (K / 2), rows_a * nblk * 8u);
   uint32_t da = 0, db = 0;  // scale resources' offsets below their tiles' first bytes
   const __amdgpu_buffer_rsrc_t rsa = scale_rsrc(sa + m0 * (K / 16), rows_a * nblk, da);
   const __amdgpu_buffer_rsrc_t rcb = uniform_rsrc(pb + n0 * (K / 2), rows_b * nblk * 8u);
   const __amdgpu_buffer_rsrc_t rsb = scale_rsrc(sb + n0 * (K / 16), rows_b * nblk, db);
 
-  f32x16 acc[kFrags][kFrags];
+  f32x16 acc[kFrags][kFragsB];
 #pragma unroll
   for (int i = 0; i < kFrags; ++i)
 #pragma unroll
-    for (int j = 0; j < kFrags; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < kFragsB; ++j) acc[i][j] = f32x16{};
 
-  auto stage_ptr = [&](uint32_t c) { return lds + (c % kStages) * kStageBytes; };
-  // Part q (0..5) of the loads of stage c (see issue_codes).
+  auto stage_ptr = [&](uint32_t c) { return lds + (c % kStages) * kStage; };
+  // Part q (0..5) of the loads of stage c (see issue_codes): the q-th code
+  // load of A and of B (B has kTileN / 64 of them), then A's scale load,
+  // then B's.
   auto issue_part = [&](uint32_t c, int q, bool live) {
     uint8_t* st = stage_ptr(c);
     if (q < 4) {
-      issue_codes(rca, st, c, q, live, nblk, wave, lane);
-      issue_codes(rcb, st + kCodeBytes, c, q, live, nblk, wave, lane);
+      issue_codes<kTile>(rca, st, c, q, live, nblk, wave, lane);
+      if (q < kTileN / 64) issue_codes<kTileN>(rcb, st + kCodesA, c, q, live, nblk, wave, lane);
     } else if (q == 4) {
-      issue_scales(rsa, st + 2 * kCodeBytes, c, live, nblk, da, wave, lane);
+      issue_scales(rsa, st + kCodesA + kCodesB + 64u * wave * kScaleSlot, 64u * wave, c, live,
+                   nblk, da, lane);
     } else {
-      issue_scales(rsb, st + 2 * kCodeBytes + kScaleBytes, c, live, nblk, db, wave, lane);
+      uint8_t* dst = b_scales ? st + kCodesA + kCodesB + kScalesA + 64u * wave * kScaleSlot
+                              : lds + kStages * kStage;
+      issue_scales(rsb, dst, 64u * wave, c, live && b_scales, nblk, db, lane);
     }
   };
   auto issue = [&](uint32_t c) {
@@ -264,25 +287,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   if (nstages > 1) issue(1);
   if (nstages > 2) {
     issue(2);
-    wait_vm<kLoadsPerStage>();
+    wait_vm<kLoadsPerStage<kTileN>>();
   } else {
     wait_vm<0>();
   }
   lds_barrier();
 
   // Operand r < kFrags is A fragment r (tile row wm*128 + 32r + l32), the
-  // others B fragments.  Software pipeline across stages: the codes of
+  // others B fragments (tile row wn * kWaveTileN + 32(r - kFrags) + l32).
+  // Software pipeline across stages: the codes of
   // steps 4-7 are read from LDS while steps 0-3 run, those of the next
   // stage's steps 0-3 (already in LDS: written before the previous barrier)
   // while steps 4-7 run, and each step's operands are decoded while the
   // matrix cores work on the step before.
-  constexpr int kOps = 2 * kFrags;
+  constexpr int kOps = kFrags + kFragsB;
   auto op_row = [&](int r) {
-    return (r < kFrags ? wm : wn) * kWaveTile + 32u * (uint32_t)(r % kFrags) + l32;
+    return r < kFrags ? wm * kWaveTile + 32u * (uint32_t)r + l32
+                      : wn * kWaveTileN + 32u * (uint32_t)(r - kFrags) + l32;
   };
-  auto codes_of = [&](const uint8_t* st, int r) { return st + (r < kFrags ? 0 : kCodeBytes); };
+  auto codes_of = [&](const uint8_t* st, int r) { return st + (r < kFrags ? 0 : kCodesA); };
   auto scales_of = [&](const uint8_t* st, int r) {
-    return st + 2 * kCodeBytes + (r < kFrags ? 0 : kScaleBytes);
+    return st + kCodesA + kCodesB + (r < kFrags ? 0 : kScalesA);
   };
   u32x4 lo[kOps], hi[kOps];
   f16x2 dlo[kOps], dhi[kOps], ndlo[kOps], ndhi[kOps];
@@ -298,19 +323,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
     for (int r = 0; r < kOps; ++r) op[0][r] = decode8(lo[r][0], dlo[r][0]);
   }
-  // vm: vector-memory instructions to place among this step's MFMAs.
+  // vm: vector-memory instructions to place among this step's MFMAs; the
+  // next step's decode (8 VALU per operand) is spread evenly over them.
+  constexpr int kValuPerMfma = 8 * kOps / (kFrags * kFragsB);
   auto mfma_step = [&](int cur, auto vm_c) {
     constexpr int vm = decltype(vm_c)::value;
 #pragma unroll
     for (int i = 0; i < kFrags; ++i)
 #pragma unroll
-      for (int j = 0; j < kFrags; ++j)
+      for (int j = 0; j < kFragsB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][i], op[cur][kFrags + j],
                                                            acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int k = 0; k < kFrags * kFrags; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+    for (int k = 0; k < kFrags * kFragsB; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // decode
       if constexpr (vm > 0)
         if (k == 2) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // loads
     }
@@ -329,7 +356,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
       for (int r = 0; r < kOps; ++r)
         op[nxt][r] = t < 3 ? decode8(lo[r][t + 1], dlo[r][(t + 1) >> 1])
                            : decode8(hi[r][0], dhi[r][0]);
-      mfma_step(cur, std::integral_constant<int, 2>{});
+      if (t < kTileN / 64)
+        mfma_step(cur, std::integral_constant<int, 2>{});
+      else
+        mfma_step(cur, std::integral_constant<int, 1>{});
     }
     // The next stage's first codes and scales (stage c + 1 is in LDS; on the
     // last stage this reads a stale buffer whose values are never used).
@@ -360,7 +390,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     }
     // This stage's loads of stage c + 3 (issued even past the last stage,
     // then out of range) may stay in flight; stage c + 2's are complete.
-    wait_vm<kLoadsPerStage>();
+    wait_vm<kLoadsPerStage<kTileN>>();
     lds_barrier();
   }
 
@@ -370,7 +400,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   // row offset of accumulator element r a scalar (N <= 2^24 keeps a slice's
   // byte offsets in 32 bits).
   const float gab = (*ga) * (*gb);
-  const int64_t mw = m0 + wm * kWaveTile, nw = n0 + wn * kWaveTile;
+  const int64_t mw = m0 + wm * kWaveTile, nw = n0 + wn * kWaveTileN;
   constexpr uint32_t kEsz = kBf16 ? 2u : 4u;
   const uint32_t row_bytes = (uint32_t)N * kEsz;
 #pragma unroll
@@ -380,7 +410,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const __amdgpu_buffer_rsrc_t ro =
         uniform_rsrc(static_cast<uint8_t*>(out) + r0 * (int64_t)row_bytes, rows * row_bytes);
 #pragma unroll
-    for (int j = 0; j < kFrags; ++j) {
+    for (int j = 0; j < kFragsB; ++j) {
       const int64_t col = nw + 32 * j + l32;
       if (col >= N) continue;
       const uint32_t voff = 4u * h * row_bytes + (uint32_t)col * kEsz;
@@ -397,16 +427,34 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   }
 }
 
-template <bool kBf16, bool kAligned>
+template <bool kBf16, bool kAligned, int kTileN>
 hipError_t launch_gemm_v(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
                          const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
                          void* out, hipStream_t s, Events ev) {
   const uint32_t tiles_m = (uint32_t)((M + kTile - 1) / kTile);
-  const uint32_t tiles_n = (uint32_t)((N + kTile - 1) / kTile);
+  const uint32_t tiles_n = (uint32_t)((N + kTileN - 1) / kTileN);
   const uint32_t per_xcd = (tiles_m * tiles_n + 7u) / 8u;
-  return launch_with_events(gemm_kernel<kBf16, kAligned>, dim3(per_xcd * 8u),
+  return launch_with_events(gemm_kernel<kBf16, kAligned, kTileN>, dim3(per_xcd * 8u),
                             dim3(kGemmThreads), s, ev, pa, sa, ga, pb, sb, gb, M, N, K, tiles_m,
                             tiles_n, per_xcd, out);
+}
+
+template <bool kBf16, bool kAligned>
+hipError_t launch_gemm_t(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
+                         const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
+                         void* out, hipStream_t s, Events ev) {
+  // Tiles run in rounds of one per compute unit.  A 256 x 128 tile takes
+  // about 0.65 of the time of a 256 x 256 one (its decode costs 6 VALU
+  // instructions per MFMA instead of 4), so the narrow tiles are chosen only
+  // where they need fewer than 20/13 as many rounds: products with at most
+  // half a round of wide tiles, or a little over one round of them.
+  const int64_t cus = device_cu_count();
+  const int64_t tiles_m = (M + kTile - 1) / kTile;
+  const int64_t rounds_wide = (tiles_m * ((N + 255) / 256) + cus - 1) / cus;
+  const int64_t rounds_narrow = (tiles_m * ((N + 127) / 128) + cus - 1) / cus;
+  if (13 * rounds_narrow < 20 * rounds_wide)
+    return launch_gemm_v<kBf16, kAligned, 128>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
+  return launch_gemm_v<kBf16, kAligned, 256>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
 }
 
 }  // namespace
@@ -420,10 +468,10 @@ hipError_t launch_gemm(const uint8_t* pa, const uint8_t* sa, const float* ga, co
   const bool aligned = (K / 16) % 4 == 0 && (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
                        (reinterpret_cast<uintptr_t>(sb) & 3u) == 0;
   if (out_bf16)
-    return aligned ? launch_gemm_v<true, true>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev)
-                   : launch_gemm_v<true, false>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
-  return aligned ? launch_gemm_v<false, true>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev)
-                 : launch_gemm_v<false, false>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
+    return aligned ? launch_gemm_t<true, true>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev)
+                   : launch_gemm_t<true, false>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
+  return aligned ? launch_gemm_t<false, true>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev)
+                 : launch_gemm_t<false, false>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
 }
 
 }  // namespace nvfp4

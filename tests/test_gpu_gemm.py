@@ -9,8 +9,10 @@ the final scaling.  The tests use the bound the header states,
 |out - exact| <= (K + K/16 + 2) * 2^-23 * ga * gb * sum |a b|, and are
 bit-exact where every partial sum is representable (unit scales, g = 1).
 Shapes cover ragged tile edges in M and N, K tails that are not a multiple
-of the 64-wide chunk, one block, and the 32768 x 5120 x 5120 prefill product
-at full size (sampled rows and columns against the oracle)."""
+of the 128-wide stage, one block, both tile widths (256 x 128 for small
+products, 256 x 256 for large ones), and the
+32768 x 5120 x 5120 prefill product at full size (sampled rows and columns
+against the oracle)."""
 import numpy as np
 import pytest
 import torch
@@ -51,6 +53,15 @@ def gpu_gemm(pa, sa, ga, pb, sb, gb, out_dtype=torch.float32):
     torch.cuda.synchronize()
     buf.check()
     return buf.view.float().cpu().numpy().astype(np.float64).reshape(M, N)
+
+
+def shifted(scales, off):
+    """Device copy of a scale tensor starting `off` bytes past an allocation's
+    start (the bytes before it hold 0x7E)."""
+    big = torch.full((scales.size + off,), 0x7E, dtype=torch.uint8, device="cuda")
+    t = big[off:]
+    t.copy_(torch.from_numpy(np.ascontiguousarray(scales).reshape(-1)).cuda())
+    return t.view(scales.shape)
 
 
 def bound(K, gabs):
@@ -103,13 +114,6 @@ def test_scale_tensors_not_four_byte_aligned(M, N, K, off_a, off_b):
     banner(f"scale pointers offset by {off_a}, {off_b} bytes ({M}x{N}x{K})")
     pa, sa = random_nvfp4(M + K + off_a, M, K)
     pb, sb = random_nvfp4(N + K + off_b, N, K)
-
-    def shifted(scales, off):
-        big = torch.full((scales.size + off,), 0x7E, dtype=torch.uint8, device="cuda")
-        t = big[off:]
-        t.copy_(torch.from_numpy(scales.reshape(-1)).cuda())
-        return t.view(scales.shape)
-
     a = dev_operand(pa, sa, 0.5)
     b = dev_operand(pb, sb, 0.25)
     a["scales"] = shifted(sa, off_a)
@@ -203,6 +207,38 @@ def test_full_size_prefill_product_sampled():
     want, gabs = oracle.gemm(pa[rows], sa[rows], ga, pb[cols], sb[cols], gb, len(rows), len(cols),
                              K, want_abs=True)
     assert_within(got[np.ix_(rows, cols)], want, gabs, K, what="sampled")
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("K,off", [(592, 0), (640, 1)])
+def test_wide_tiles_with_ragged_edges(K, off):
+    # The tile width follows from how many rounds of tiles (one per compute
+    # unit) each width needs; the small shapes elsewhere in this file take
+    # 256 x 128 tiles.  This one takes 256 x 256 tiles on any device (just
+    # over two rounds of them, where the narrow tiles need five), with M and
+    # N ending mid-tile and K ending mid-stage (592) or scale tensors off the
+    # 4-byte grid (640 with an offset): all rows of the last tile row and a
+    # sample of the others, against the oracle over every column.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles_n = 17
+    tiles_m = -(-2 * cus // tiles_n) + 1
+    M, N = 256 * tiles_m - 37, 256 * tiles_n - 100
+    banner(f"wide tiles {M}x{N}x{K} scale offset {off}")
+    pa, sa = random_nvfp4(131 + K, M, K, 0x28, 0x50)
+    pb, sb = random_nvfp4(132 + K, N, K, 0x28, 0x50)
+    ga, gb = np.float32(3.0e-2), np.float32(7.0e-4)
+    a, b = dev_operand(pa, sa, ga), dev_operand(pb, sb, gb)
+    a["scales"], b["scales"] = shifted(sa, off), shifted(sb, off)
+    buf = Guarded(M * N * 4, torch.float32)
+    nv.gemm(a, b, torch.float32, out=buf.view)
+    torch.cuda.synchronize()
+    buf.check()
+    got = buf.view.cpu().numpy().astype(np.float64).reshape(M, N)
+    rng = np.random.default_rng(133)
+    rows = np.unique(np.concatenate([np.arange(256 * (tiles_m - 1), M), [0, 127, 128, 255, 256],
+                                     rng.choice(M, 24, replace=False)]))
+    want, gabs = oracle.gemm(pa[rows], sa[rows], ga, pb, sb, gb, len(rows), N, K, want_abs=True)
+    assert_within(got[rows], want, gabs, K, what="wide tiles")
     assert np.isfinite(got).all()
 
 
