@@ -28,11 +28,11 @@
 // Data path.  A workgroup computes a 256 x 256 tile with four waves of
 // 128 x 128 (the accumulators fill the 256 AGPRs), or, where that fills the
 // compute units' rounds of tiles better (small products), a 256 x 128 tile
-// with waves of 128 x 64.  K is walked in stages of
-// 128 (eight blocks): the stage's codes (256 rows x 64 bytes per operand,
-// four lanes per row so that every request is one contiguous 64-byte piece)
-// and scale bytes go from memory straight into a four-deep LDS ring, three
-// stages ahead of the stage the matrix cores work on.  In LDS the 16-byte
+// with waves of 128 x 64.  K is walked in stages of 128 (eight blocks): the
+// stage's codes (64 bytes per tile row of either operand, four lanes per
+// row so that every request is one contiguous 64-byte piece) and scale
+// bytes go from memory straight into a four-deep LDS ring, three stages
+// ahead of the stage the matrix cores work on.  In LDS the 16-byte
 // pieces of a row are XOR-swizzled by bits 2-3 of the row, which makes both
 // the 16-byte writes and the fragment reads (16 lanes on 16 consecutive
 // rows) free of bank conflicts.
