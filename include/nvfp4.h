@@ -293,8 +293,10 @@ nvfp4_status nvfp4_rmsnorm_quantize_residual(const uint16_t* in_bf16, int64_t ro
  * fp32 (matrix cores, fp32 accumulation); the sum runs in fp32 in an order
  * the library chooses, then is multiplied by RN(ga * gb).  So
  *   |out - exact| <= (k + k/16 + 2) * 2^-23 * ga * gb * sum_k |a b|
- * (plus the bf16 rounding with NVFP4_OUT_BF16); results are deterministic
- * for a given library build and shape.
+ * (plus the bf16 rounding with NVFP4_OUT_BF16).  For a given library
+ * build every output is summed in an order fixed by k alone: results are
+ * deterministic and do not depend on m, n or the device's compute-unit
+ * count (which choose the tile shape).
  *   k: a positive multiple of 16, at most 2^24; n positive, at most 2^24;
  *     m positive; each of m*n, m*k and n*k at most 2^46.
  *   Alignment: packed codes 4 bytes, scalars 4 bytes, out 4 (fp32) or 2

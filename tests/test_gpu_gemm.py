@@ -242,6 +242,32 @@ def test_wide_tiles_with_ragged_edges(K, off):
     assert np.isfinite(got).all()
 
 
+def test_tile_width_does_not_change_results():
+    # Both tile widths give every output the same summation order (the same
+    # stages and MFMA steps, in order), so the first 256 rows of a product
+    # small enough for 256 x 128 tiles equal, bit for bit, those rows of a
+    # product large enough for 256 x 256 tiles.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K = 5120, 1040
+
+    def rounds(M, width):
+        return -(-((M + 255) // 256) * (-(-N // width)) // cus)
+
+    def narrow(M):
+        return 13 * rounds(M, 128) < 20 * rounds(M, 256)
+
+    M_big = 256 * -(-4 * cus // 20)
+    assert narrow(256) and not narrow(M_big), (cus, M_big)
+    banner(f"tile widths agree: 256 vs {M_big} rows, {N}x{K}")
+    pa, sa = random_nvfp4(141, M_big, K, 0x28, 0x50)
+    pb, sb = random_nvfp4(142, N, K, 0x28, 0x50)
+    small = gpu_gemm(pa[:256], sa[:256], 0.75, pb, sb, 1.0e-3)
+    big = gpu_gemm(pa, sa, 0.75, pb, sb, 1.0e-3)
+    np.testing.assert_array_equal(small, big[:256])
+    want, gabs = oracle.gemm(pa[:256], sa[:256], 0.75, pb, sb, 1.0e-3, 256, N, K, want_abs=True)
+    assert_within(small, want, gabs, K)
+
+
 def test_long_k_errors_are_far_inside_the_bound():
     # 512 stages of the K loop.  The bound is a worst case (every rounding
     # in the same direction); random-sign sums grow like sqrt(K), so the
