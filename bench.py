@@ -249,8 +249,8 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the full-tensor oracle run; gate on sampled rows instead")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
@@ -333,13 +333,17 @@ def main():
     log("parity ok")
 
     # ---- timed region ----
-    for _ in range(args.warmup):
-        step()
+    # The events are created before the warm-up so that the warm-up runs
+    # straight into the timed steps: after an idle gap of ten or so
+    # milliseconds the first ~250 steps run slower while the device's clocks
+    # ramp back up.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    for a, b in evs:  # create the events before the clock starts
+    for a, b in evs:
         a.record(stream)
         b.record(stream)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
