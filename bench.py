@@ -67,12 +67,27 @@ def measured_traffic(numel):
     return int(kv["bytes_per_launch"])
 
 
+def warm(fn, torch, seconds=0.04):
+    """Repeat fn until about `seconds` of back-to-back calls have run (at
+    least 5): after an idle gap the device's clocks take about 30 ms of load
+    to settle, and a measurement taken during that time is slower."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < 5 or time.perf_counter() - t0 < seconds:
+        for _ in range(5):
+            fn()
+        n += 5
+        torch.cuda.synchronize()
+
+
 def kernel_times(fn, torch, reps, between=None):
     """Per-launch kernel times (s) from events bound to the kernel itself."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
-    for _ in range(3):
-        fn(None)
+    for a, b in evs:
+        a.record()
+        b.record()
+    warm(lambda: fn(None), torch)
     for e in evs:
         if between is not None:
             between()
@@ -83,10 +98,10 @@ def kernel_times(fn, torch, reps, between=None):
 
 def call_time(fn, torch, stream, reps=50):
     """Mean time (s) of back-to-back calls between one pair of stream events."""
-    for _ in range(5):
-        fn()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    a.record(stream)
+    b.record(stream)
+    warm(fn, torch)
     a.record(stream)
     for _ in range(reps):
         fn()
