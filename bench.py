@@ -224,7 +224,18 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     t_aug = call_time(lambda: nv.gemm(ro, qwa, torch.bfloat16, out=y), torch, stream, 20)
     res["gemm_augmented_k5376_bf16_us"] = round(t_aug * 1e6, 1)
     res["gemm_augmented_tflops"] = round(2.0 * rows * cols * (cols + nres) / t_aug / 1e12, 1)
-    del w_bf, qw, qa, y, qwa
+    # A decode-sized product (the first 128 rows), whole and split along K.
+    qd = {"packed": qa["packed"][:128], "scales": qa["scales"][:128], "gscale": g}
+    yd = torch.empty((128, cols), dtype=torch.bfloat16, device=dev)
+    sd = nv.gemm_splits_hint(128, cols, cols)
+    wsd = torch.empty(max(1, sd) * 128 * cols, dtype=torch.float32, device=dev)
+    t_d1 = call_time(lambda: nv.gemm(qd, qw, torch.bfloat16, out=yd), torch, stream, 50)
+    t_ds = call_time(lambda: nv.gemm(qd, qw, torch.bfloat16, out=yd, splits=sd, workspace=wsd),
+                     torch, stream, 50)
+    res["gemm_w4a4_128x5120x5120_bf16_us"] = round(t_d1 * 1e6, 1)
+    res["gemm_w4a4_128x5120x5120_splitk_us"] = round(t_ds * 1e6, 1)
+    res["gemm_w4a4_128x5120x5120_splits"] = sd
+    del w_bf, qw, qa, y, qwa, qd, yd, wsd
     del ro, absmax_c, perm, fo, fo2, wgt
     # The quantize kernel on the other workloads' shapes and modes.
     for cid in (2, 3, 5):

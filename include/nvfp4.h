@@ -305,6 +305,34 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_packed, const uint8_t* a_scales, const 
                         const uint8_t* b_packed, const uint8_t* b_scales, const float* b_gscale,
                         int64_t m, int64_t n, int64_t k, int out_dtype, void* out, void* stream);
 
+/* The product of nvfp4_gemm with the reduction axis split into `splits`
+ * contiguous ranges of whole 128-wide chunks of k, computed side by side
+ * (products with few output tiles, e.g. decode-sized m, would otherwise
+ * leave most compute units idle while a few walk all of k), then added.
+ *   workspace: caller-owned device memory of workspace_floats fp32 values,
+ *     at least splits * m * n, 4-byte aligned, overlapping no input or the
+ *     output; its contents on entry do not matter and on return are the
+ *     per-range sums (unscaled).  The library allocates nothing.
+ *   splits: 1 .. min(64, ceil(k / 128)) (NVFP4_ERR_SHAPE otherwise); see
+ *     nvfp4_gemm_splits_hint.
+ *   Other arguments, layouts, checks and the error bound as nvfp4_gemm.
+ * Each range is summed in fp32 as nvfp4_gemm sums all of k, the range sums
+ * are then added in order in fp32 and multiplied by RN(ga * gb): results
+ * are deterministic for a given split count, and with splits = 1 equal
+ * nvfp4_gemm's bit for bit. */
+nvfp4_status nvfp4_gemm_splitk(const uint8_t* a_packed, const uint8_t* a_scales,
+                               const float* a_gscale, const uint8_t* b_packed,
+                               const uint8_t* b_scales, const float* b_gscale, int64_t m,
+                               int64_t n, int64_t k, int splits, int out_dtype, void* out,
+                               float* workspace, int64_t workspace_floats, void* stream);
+
+/* Split count suggested for an m x n x k nvfp4_gemm_splitk on the current
+ * device: enough to give about one unit of work per compute unit, each range
+ * keeping at least four 128-wide chunks of k; 1 where splitting does not
+ * help (then nvfp4_gemm is the faster call).  Host only; returns 0 for
+ * shapes nvfp4_gemm rejects. */
+int nvfp4_gemm_splits_hint(int64_t m, int64_t n, int64_t k);
+
 /* Static description of a status code. */
 const char* nvfp4_status_string(nvfp4_status s);
 

@@ -51,6 +51,9 @@ SIGNATURES = {
     "nvfp4_rmsnorm_quantize_residual": ([_P, _I64, _I64, _P, ctypes.c_float, _P, _I64, _I, _I,
                                          _U32, _P, _P, _P, _P, _P], _I),
     "nvfp4_gemm": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P], _I),
+    "nvfp4_gemm_splitk": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, _P, _I64, _P],
+                          _I),
+    "nvfp4_gemm_splits_hint": ([_I64, _I64, _I64], _I),
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
     "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _P, _P], _I),
     "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _P, _P], _I),
@@ -408,13 +411,23 @@ def dequantize(packed, scales, gscale, rows, cols, block_axis=AXIS_COLS, out_dty
     return out
 
 
-def gemm(a, b, out_dtype=torch.float32, out=None, stream=None):
+def gemm_splits_hint(M, N, K):
+    """Split count nvfp4_gemm_splits_hint suggests for an M x N x K product
+    on the current device (1: splitting does not help)."""
+    return int(lib().nvfp4_gemm_splits_hint(M, N, K))
+
+
+def gemm(a, b, out_dtype=torch.float32, out=None, stream=None, splits=None, workspace=None):
     """W4A4 product out [M][N] = ga * gb * sum_k a(m,k) b(n,k) (nvfp4_gemm):
     Y = X W^T for NVFP4 activations X [M][K] and weights W [N][K], both
     blocked along K.  a, b: dicts with "packed" ([rows][K/2] uint8),
     "scales" ([rows][K/16] uint8) and "gscale" (1-element float32), e.g. the
     results of quantize (AXIS_COLS) or quantize_residual.  Returns out, float32
-    or bfloat16."""
+    or bfloat16.
+    splits: None (nvfp4_gemm), an int (nvfp4_gemm_splitk with that many
+    ranges of K) or "auto" (the library's hint; nvfp4_gemm when it is 1).
+    workspace: float32 device tensor of at least splits * M * N elements for
+    the split product; allocated here when not given."""
     code = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
     pa, pb = a["packed"], b["packed"]
     if pa.dim() != 2 or pb.dim() != 2 or pa.shape[1] != pb.shape[1]:
@@ -428,9 +441,25 @@ def gemm(a, b, out_dtype=torch.float32, out=None, stream=None):
     sb = _need(b["scales"], N * K // 16, torch.uint8, dev, "b['scales']")
     gb = _need(b["gscale"], 1, torch.float32, dev, "b['gscale']")
     out = _out({"out": out}, "out", (M, N), out_dtype, dev)
-    st = lib().nvfp4_gemm(_ptr(pa), _ptr(sa), _ptr(ga), _ptr(pb), _ptr(sb), _ptr(gb), M, N, K,
-                          code, _ptr(out), _stream(stream))
-    _check(st, "nvfp4_gemm")
+    if splits == "auto":
+        splits = gemm_splits_hint(M, N, K)
+        if splits <= 1:
+            splits = None
+    if splits is None:
+        st = lib().nvfp4_gemm(_ptr(pa), _ptr(sa), _ptr(ga), _ptr(pb), _ptr(sb), _ptr(gb), M, N,
+                              K, code, _ptr(out), _stream(stream))
+        _check(st, "nvfp4_gemm")
+        return out
+    splits = int(splits)
+    if workspace is None:
+        workspace = torch.empty(max(1, splits) * M * N, dtype=torch.float32, device=dev)
+    elif (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.float32
+          or workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous float32 tensor on the operands' device")
+    st = lib().nvfp4_gemm_splitk(_ptr(pa), _ptr(sa), _ptr(ga), _ptr(pb), _ptr(sb), _ptr(gb), M,
+                                 N, K, splits, code, _ptr(out), _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
+    _check(st, "nvfp4_gemm_splitk")
     return out
 
 

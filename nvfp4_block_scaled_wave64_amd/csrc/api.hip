@@ -407,6 +407,12 @@ nvfp4_status nvfp4_rmsnorm_quantize_residual(const uint16_t* in_bf16, int64_t ro
 
 extern "C" {
 
+static bool gemm_shape_ok(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || k > (int64_t(1) << 24)) return false;
+  if (n > (int64_t(1) << 24)) return false;
+  return !(m > kMaxNumel / n || m > kMaxNumel / k || n > kMaxNumel / k);
+}
+
 nvfp4_status nvfp4_gemm(const uint8_t* a_packed, const uint8_t* a_scales, const float* a_gscale,
                         const uint8_t* b_packed, const uint8_t* b_scales, const float* b_gscale,
                         int64_t m, int64_t n, int64_t k, int out_dtype, void* out,
@@ -414,10 +420,7 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_packed, const uint8_t* a_scales, const 
   if (!a_packed || !a_scales || !a_gscale || !b_packed || !b_scales || !b_gscale || !out)
     return NVFP4_ERR_NULL;
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_ENUM;
-  if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || k > (int64_t(1) << 24))
-    return NVFP4_ERR_SHAPE;
-  if (n > (int64_t(1) << 24)) return NVFP4_ERR_SHAPE;
-  if (m > kMaxNumel / n || m > kMaxNumel / k || n > kMaxNumel / k) return NVFP4_ERR_SHAPE;
+  if (!gemm_shape_ok(m, n, k)) return NVFP4_ERR_SHAPE;
   const int64_t esz = out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
   if (!aligned(a_packed, 4) || !aligned(b_packed, 4) || !aligned(a_gscale, 4) ||
       !aligned(b_gscale, 4) || !aligned(out, (uintptr_t)esz))
@@ -430,6 +433,42 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_packed, const uint8_t* a_scales, const 
   return hip_status(nvfp4::launch_gemm(a_packed, a_scales, a_gscale, b_packed, b_scales,
                                        b_gscale, m, n, k, out_dtype == NVFP4_OUT_BF16, out,
                                        static_cast<hipStream_t>(stream), nvfp4::Events{}));
+}
+
+nvfp4_status nvfp4_gemm_splitk(const uint8_t* a_packed, const uint8_t* a_scales,
+                               const float* a_gscale, const uint8_t* b_packed,
+                               const uint8_t* b_scales, const float* b_gscale, int64_t m,
+                               int64_t n, int64_t k, int splits, int out_dtype, void* out,
+                               float* workspace, int64_t workspace_floats, void* stream) {
+  if (!a_packed || !a_scales || !a_gscale || !b_packed || !b_scales || !b_gscale || !out ||
+      !workspace)
+    return NVFP4_ERR_NULL;
+  if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_ENUM;
+  if (!gemm_shape_ok(m, n, k)) return NVFP4_ERR_SHAPE;
+  const int64_t nchunks = (k + 127) / 128;
+  if (splits < 1 || splits > nvfp4::kGemmMaxSplits || splits > nchunks) return NVFP4_ERR_SHAPE;
+  const int64_t ws_floats = (int64_t)splits * m * n;
+  if (workspace_floats < ws_floats) return NVFP4_ERR_SHAPE;
+  const int64_t esz = out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
+  if (!aligned(a_packed, 4) || !aligned(b_packed, 4) || !aligned(a_gscale, 4) ||
+      !aligned(b_gscale, 4) || !aligned(out, (uintptr_t)esz) || !aligned(workspace, 4))
+    return NVFP4_ERR_ALIGN;
+  const int64_t out_bytes = m * n * esz;
+  const void* ins[7] = {a_packed, a_scales, a_gscale, b_packed, b_scales, b_gscale, out};
+  const int64_t in_bytes[7] = {m * k / 2, m * k / 16, 4, n * k / 2, n * k / 16, 4, out_bytes};
+  for (int i = 0; i < 7; ++i) {
+    if (i < 6 && overlap(out, out_bytes, ins[i], in_bytes[i])) return NVFP4_ERR_ALIAS;
+    if (overlap(workspace, ws_floats * 4, ins[i], in_bytes[i])) return NVFP4_ERR_ALIAS;
+  }
+  return hip_status(nvfp4::launch_gemm_splitk(a_packed, a_scales, a_gscale, b_packed, b_scales,
+                                              b_gscale, m, n, k, (uint32_t)splits,
+                                              out_dtype == NVFP4_OUT_BF16, out, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int nvfp4_gemm_splits_hint(int64_t m, int64_t n, int64_t k) {
+  if (!gemm_shape_ok(m, n, k)) return 0;
+  return nvfp4::gemm_splits_hint(m, n, k);
 }
 
 }  // extern "C"

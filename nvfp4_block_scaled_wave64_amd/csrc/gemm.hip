@@ -203,25 +203,31 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return (uint16_t)__builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
 }
 
-// One workgroup per 256 x kTileN output tile; tiles are walked in groups of
-// kGroupM tile rows (the workgroups running together share A and B panels
-// in L2), and consecutive tiles of the walk go to one XCD (workgroups are
-// dealt round-robin over the 8 XCDs).
-template <bool kBf16, bool kAligned, int kTileN>
+// One workgroup per 256 x kTileN output tile and split of K; tiles are
+// walked in groups of kGroupM tile rows (the workgroups running together
+// share A and B panels in L2), and consecutive units of the walk go to one
+// XCD (workgroups are dealt round-robin over the 8 XCDs).  With kSplit the
+// stages of K are divided into `splits` contiguous ranges; unit u covers
+// range u / tiles of tile u % tiles and stores its raw fp32 sums in slice
+// u / tiles of ws ([splits][M][N], passed as out); splitk_reduce_kernel then
+// adds the slices.  Without kSplit, splits is 1 and the unit writes out.
+template <bool kBf16, bool kAligned, int kTileN, bool kSplit>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const uint8_t* __restrict__ pa, const uint8_t* __restrict__ sa, const float* __restrict__ ga,
     const uint8_t* __restrict__ pb, const uint8_t* __restrict__ sb, const float* __restrict__ gb,
     int64_t M, int64_t N, int64_t K, uint32_t tiles_m, uint32_t tiles_n, uint32_t per_xcd,
-    void* __restrict__ out) {
+    uint32_t splits, void* __restrict__ out) {
   constexpr int kStage = kStageBytes<kTileN>;
   constexpr int kCodesA = kTile * kRowBytes, kCodesB = kTileN * kRowBytes;
   constexpr int kScalesA = kTile * kScaleSlot;
   constexpr int kWaveTileN = kTileN / 2;       // wave tile columns (rows of B)
   constexpr int kFragsB = kWaveTileN / 32;     // 32 x 32 MFMA tiles per wave along B
   __shared__ __align__(16) uint8_t lds[kStages * kStage + (kTileN < kTile ? kSpareBytes : 0)];
-  const uint32_t total = tiles_m * tiles_n;
-  const uint32_t L = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
-  if (L >= total) return;
+  const uint32_t tiles = tiles_m * tiles_n;
+  const uint32_t U = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
+  if (U >= tiles * splits) return;
+  const uint32_t split = U / tiles;
+  const uint32_t L = U - split * tiles;
   const uint32_t group = L / (kGroupM * tiles_n);
   const uint32_t first_m = group * kGroupM;
   const uint32_t gm = min((uint32_t)kGroupM, tiles_m - first_m);
@@ -235,6 +241,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   const uint32_t h = lane >> 5, l32 = lane & 31u;
   const uint32_t nblk = (uint32_t)(K / 16);
   const uint32_t nstages = (nblk + kStageBlocks - 1) / kStageBlocks;
+  // This unit's stages c_begin .. c_end - 1 (all of them without kSplit;
+  // splits <= nstages, so no range is empty).
+  const uint32_t c_begin = (uint32_t)((uint64_t)split * nstages / splits);
+  const uint32_t c_end = (uint32_t)((uint64_t)(split + 1u) * nstages / splits);
+  const uint32_t nst = c_end - c_begin;
 
   // Resources over this tile's rows of A and B (rows past M or N read 0).
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTileN;
@@ -283,10 +294,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   // publishes them.  So during stage c, stages c and c + 1 are complete in
   // LDS, and buffer (c + 3) % 4, which receives stage c + 3, is read by
   // nobody.
-  issue(0);
-  if (nstages > 1) issue(1);
-  if (nstages > 2) {
-    issue(2);
+  issue(c_begin);
+  if (nst > 1) issue(c_begin + 1u);
+  if (nst > 2) {
+    issue(c_begin + 2u);
     wait_vm<kLoadsPerStage<kTileN>>();
   } else {
     wait_vm<0>();
@@ -313,12 +324,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   f16x2 dlo[kOps], dhi[kOps], ndlo[kOps], ndhi[kOps];
   f16x8 op[2][kOps];
   {
-    const uint8_t* st = stage_ptr(0);
+    const uint8_t* st = stage_ptr(c_begin);
 #pragma unroll
     for (int r = 0; r < kOps; ++r) {
       lo[r] = read_codes(codes_of(st, r), op_row(r), 2u * h);
-      read_scales<kAligned>(scales_of(st, r), op_row(r), h, 0u, nblk, r < kFrags ? da : db,
-                            dlo[r], dhi[r]);
+      read_scales<kAligned>(scales_of(st, r), op_row(r), h, c_begin, nblk,
+                            r < kFrags ? da : db, dlo[r], dhi[r]);
     }
 #pragma unroll
     for (int r = 0; r < kOps; ++r) op[0][r] = decode8(lo[r][0], dlo[r][0]);
@@ -343,8 +354,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     }
   };
 
-  for (uint32_t c = 0; c < nstages; ++c) {
-    const bool more = c + kAhead < nstages;
+  for (uint32_t c = c_begin; c < c_end; ++c) {
+    const bool more = c + kAhead < c_end;
     const uint8_t* st = stage_ptr(c);
 #pragma unroll
     for (int r = 0; r < kOps; ++r) hi[r] = read_codes(codes_of(st, r), op_row(r), 2u * h + 1u);
@@ -388,18 +399,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
       dlo[r] = ndlo[r];
       dhi[r] = ndhi[r];
     }
-    // This stage's loads of stage c + 3 (issued even past the last stage,
-    // then out of range) may stay in flight; stage c + 2's are complete.
+    // This stage's loads of stage c + 3 (issued even past the unit's last
+    // stage, then out of range) may stay in flight; stage c + 2's are
+    // complete.
     wait_vm<kLoadsPerStage<kTileN>>();
     lds_barrier();
   }
 
   wait_vm<0>();
-  // Epilogue: out = acc * RN(ga * gb).  One buffer resource per 32-row slice
-  // (its range drops rows past M); a lane's column offset is per lane, the
-  // row offset of accumulator element r a scalar (N <= 2^24 keeps a slice's
-  // byte offsets in 32 bits).
-  const float gab = (*ga) * (*gb);
+  // Epilogue: out = acc * RN(ga * gb), or with kSplit the raw sums into the
+  // unit's slice (a multiply by 1 is exact).  One buffer resource per 32-row
+  // slice (its range drops rows past M); a lane's column offset is per lane,
+  // the row offset of accumulator element r a scalar (N <= 2^24 keeps a
+  // slice's byte offsets in 32 bits).
+  static_assert(!(kSplit && kBf16), "split units store fp32 sums");
+  const float gab = kSplit ? 1.0f : (*ga) * (*gb);
+  if constexpr (kSplit) out = static_cast<float*>(out) + (int64_t)split * M * N;
   const int64_t mw = m0 + wm * kWaveTile, nw = n0 + wn * kWaveTileN;
   constexpr uint32_t kEsz = kBf16 ? 2u : 4u;
   const uint32_t row_bytes = (uint32_t)N * kEsz;
@@ -427,22 +442,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   }
 }
 
-template <bool kBf16, bool kAligned, int kTileN>
+template <bool kBf16, bool kAligned, int kTileN, bool kSplit>
 hipError_t launch_gemm_v(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
                          const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
-                         void* out, hipStream_t s, Events ev) {
+                         uint32_t splits, void* out, hipStream_t s, Events ev) {
   const uint32_t tiles_m = (uint32_t)((M + kTile - 1) / kTile);
   const uint32_t tiles_n = (uint32_t)((N + kTileN - 1) / kTileN);
-  const uint32_t per_xcd = (tiles_m * tiles_n + 7u) / 8u;
-  return launch_with_events(gemm_kernel<kBf16, kAligned, kTileN>, dim3(per_xcd * 8u),
+  const uint32_t per_xcd = (tiles_m * tiles_n * splits + 7u) / 8u;
+  return launch_with_events(gemm_kernel<kBf16, kAligned, kTileN, kSplit>, dim3(per_xcd * 8u),
                             dim3(kGemmThreads), s, ev, pa, sa, ga, pb, sb, gb, M, N, K, tiles_m,
-                            tiles_n, per_xcd, out);
+                            tiles_n, per_xcd, splits, out);
 }
 
-template <bool kBf16, bool kAligned>
-hipError_t launch_gemm_t(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
-                         const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
-                         void* out, hipStream_t s, Events ev) {
+// Whether 256 x 128 tiles beat 256 x 256 ones with `splits` units per tile.
+bool narrow_tiles(int64_t M, int64_t N, int64_t splits) {
   // Tiles run in rounds of one per compute unit.  A 256 x 128 tile takes
   // about 0.65 of the time of a 256 x 256 one (its decode costs 6 VALU
   // instructions per MFMA instead of 4), so the narrow tiles are chosen only
@@ -450,11 +463,53 @@ hipError_t launch_gemm_t(const uint8_t* pa, const uint8_t* sa, const float* ga, 
   // half a round of wide tiles, or a little over one round of them.
   const int64_t cus = device_cu_count();
   const int64_t tiles_m = (M + kTile - 1) / kTile;
-  const int64_t rounds_wide = (tiles_m * ((N + 255) / 256) + cus - 1) / cus;
-  const int64_t rounds_narrow = (tiles_m * ((N + 127) / 128) + cus - 1) / cus;
-  if (13 * rounds_narrow < 20 * rounds_wide)
-    return launch_gemm_v<kBf16, kAligned, 128>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
-  return launch_gemm_v<kBf16, kAligned, 256>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
+  const int64_t rounds_wide = (tiles_m * ((N + 255) / 256) * splits + cus - 1) / cus;
+  const int64_t rounds_narrow = (tiles_m * ((N + 127) / 128) * splits + cus - 1) / cus;
+  return 13 * rounds_narrow < 20 * rounds_wide;
+}
+
+template <bool kBf16, bool kAligned>
+hipError_t launch_gemm_t(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
+                         const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
+                         void* out, hipStream_t s, Events ev) {
+  if (narrow_tiles(M, N, 1))
+    return launch_gemm_v<kBf16, kAligned, 128, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u, out, s,
+                                                      ev);
+  return launch_gemm_v<kBf16, kAligned, 256, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u, out, s,
+                                                    ev);
+}
+
+// out[i] = (ws[0][i] + ws[1][i] + ... + ws[splits-1][i]) * RN(ga * gb), the
+// slices added in order in fp32 (so one split reproduces the unsplit
+// product bit for bit), over the mn elements of the product.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
+                                                            int64_t mn, uint32_t splits,
+                                                            const float* __restrict__ ga,
+                                                            const float* __restrict__ gb,
+                                                            void* __restrict__ out) {
+  const float gab = (*ga) * (*gb);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
+    float t = ws[i];
+    for (uint32_t q = 1; q < splits; ++q) t = t + ws[(int64_t)q * mn + i];
+    const float y = t * gab;
+    if constexpr (kBf16)
+      static_cast<uint16_t*>(out)[i] = to_bf16_bits(y);
+    else
+      static_cast<float*>(out)[i] = y;
+  }
+}
+
+template <bool kAligned>
+hipError_t launch_gemm_split_t(const uint8_t* pa, const uint8_t* sa, const float* ga,
+                               const uint8_t* pb, const uint8_t* sb, const float* gb, int64_t M,
+                               int64_t N, int64_t K, uint32_t splits, float* ws, hipStream_t s) {
+  if (narrow_tiles(M, N, splits))
+    return launch_gemm_v<false, kAligned, 128, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits, ws,
+                                                     s, Events{});
+  return launch_gemm_v<false, kAligned, 256, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits, ws, s,
+                                                   Events{});
 }
 
 }  // namespace
@@ -472,6 +527,39 @@ hipError_t launch_gemm(const uint8_t* pa, const uint8_t* sa, const float* ga, co
                    : launch_gemm_t<true, false>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
   return aligned ? launch_gemm_t<false, true>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev)
                  : launch_gemm_t<false, false>(pa, sa, ga, pb, sb, gb, M, N, K, out, s, ev);
+}
+
+hipError_t launch_gemm_splitk(const uint8_t* pa, const uint8_t* sa, const float* ga,
+                              const uint8_t* pb, const uint8_t* sb, const float* gb, int64_t M,
+                              int64_t N, int64_t K, uint32_t splits, int out_bf16, void* out,
+                              float* ws, hipStream_t s) {
+  const bool aligned = (K / 16) % 4 == 0 && (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(sb) & 3u) == 0;
+  const hipError_t e =
+      aligned ? launch_gemm_split_t<true>(pa, sa, ga, pb, sb, gb, M, N, K, splits, ws, s)
+              : launch_gemm_split_t<false>(pa, sa, ga, pb, sb, gb, M, N, K, splits, ws, s);
+  if (e != hipSuccess) return e;
+  const int64_t mn = M * N;
+  int64_t groups = (mn + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (groups > cap) groups = cap;
+  if (out_bf16)
+    splitk_reduce_kernel<true><<<(unsigned)groups, 256, 0, s>>>(ws, mn, splits, ga, gb, out);
+  else
+    splitk_reduce_kernel<false><<<(unsigned)groups, 256, 0, s>>>(ws, mn, splits, ga, gb, out);
+  return hipGetLastError();
+}
+
+int gemm_splits_hint(int64_t M, int64_t N, int64_t K) {
+  // Enough splits to bring a product with few tiles up to about one round
+  // of the compute units, each split keeping at least four stages of K.
+  const int64_t cus = device_cu_count();
+  const int64_t nstages = (K / 16 + kStageBlocks - 1) / kStageBlocks;
+  const int64_t tiles = ((M + kTile - 1) / kTile) * ((N + 127) / 128);
+  int64_t splits = cus / tiles;
+  if (splits > nstages / 4) splits = nstages / 4;
+  if (splits > kGemmMaxSplits) splits = kGemmMaxSplits;
+  return splits < 1 ? 1 : (int)splits;
 }
 
 }  // namespace nvfp4

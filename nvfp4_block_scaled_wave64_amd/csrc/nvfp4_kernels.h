@@ -143,6 +143,16 @@ hipError_t launch_rms_quantize_residual(const uint16_t* in, int64_t rows, int64_
 hipError_t launch_gemm(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
                        const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
                        int out_bf16, void* out, hipStream_t s, Events ev);
+// The same with K split into `splits` (1 .. min(kGemmMaxSplits, K/128
+// rounded up)) contiguous ranges: raw fp32 sums into ws [splits][M][N], then
+// one pass adds the slices in order and scales them.
+constexpr int kGemmMaxSplits = 64;
+hipError_t launch_gemm_splitk(const uint8_t* pa, const uint8_t* sa, const float* ga,
+                              const uint8_t* pb, const uint8_t* sb, const float* gb, int64_t M,
+                              int64_t N, int64_t K, uint32_t splits, int out_bf16, void* out,
+                              float* ws, hipStream_t s);
+// Suggested split count for an M x N x K product on the current device.
+int gemm_splits_hint(int64_t M, int64_t N, int64_t K);
 
 // Atomic max of RN(max |y| / six_m) into *acc (fp32 bits; the caller zeroes it).
 hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const RmsArgs& ra,

@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
@@ -287,3 +287,42 @@ def test_gemm_rejects(kw, status):
     scalars 4 bytes, out its element size) and an output overlapping any
     input."""
     assert gm(**kw) == status
+
+
+W = ctypes.c_void_p(0x90000)
+
+
+def gs(**kw):
+    args = dict(pa=A, sa=B, ga=C, pb=D, sb=E, gb=F, m=32, n=32, k=256, splits=2,
+                dtype=nv.OUT_F32, out=G, ws=W, nws=2048)
+    args.update(kw)
+    return nv.lib().nvfp4_gemm_splitk(args["pa"], args["sa"], args["ga"], args["pb"], args["sb"],
+                                      args["gb"], args["m"], args["n"], args["k"], args["splits"],
+                                      args["dtype"], args["out"], args["ws"], args["nws"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), 1), (dict(pa=None), 1), (dict(out=None), 1),
+    (dict(dtype=3), 2),
+    (dict(m=0), 3), (dict(k=40), 3), (dict(splits=0), 3), (dict(splits=-1), 3),
+    (dict(splits=3), 3), (dict(splits=65, k=64 * 128), 3), (dict(nws=2047), 3),
+    (dict(k=64, splits=2, nws=1 << 20), 3),
+    (dict(ws=ctypes.c_void_p(0x90002)), 4), (dict(out=ctypes.c_void_p(0x70002)), 4),
+    (dict(ws=ctypes.c_void_p(0x70800)), 6), (dict(ws=ctypes.c_void_p(0x6FF00)), 6),
+    (dict(ws=ctypes.c_void_p(0x10400)), 6), (dict(ws=ctypes.c_void_p(0x3FFF8), nws=4096), 6),
+    (dict(out=D), 6),
+])
+def test_gemm_splitk_rejects(kw, status):
+    """nvfp4_gemm_splitk: nvfp4_gemm's checks plus a workspace that is null,
+    too small (fewer than splits * m * n floats), not 4-byte aligned or
+    overlapping an input or the output, and a split count outside
+    1 .. min(64, ceil(k / 128))."""
+    assert gs(**kw) == status
+
+
+def test_gemm_splits_hint_rejects_bad_shapes():
+    """The hint returns 0, before any HIP call, for shapes nvfp4_gemm rejects."""
+    L = nv.lib()
+    assert L.nvfp4_gemm_splits_hint(0, 16, 16) == 0
+    assert L.nvfp4_gemm_splits_hint(16, 16, 40) == 0
+    assert L.nvfp4_gemm_splits_hint(16, (1 << 24) + 1, 16) == 0

@@ -345,3 +345,91 @@ def test_forward_and_backward_products_from_one_dual_quantization():
     for got, exact in ((y, xf @ wf.T), (dx, dyf @ wf)):
         rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
         assert rel < 0.2, rel
+
+
+# ---- nvfp4_gemm_splitk: the same product with K split into ranges ----
+
+def gpu_gemm_split(pa, sa, ga, pb, sb, gb, splits, out_dtype=torch.float32, ws=None):
+    """Split product through the C ABI with guarded output and workspace."""
+    M, N = pa.shape[0], pb.shape[0]
+    esz = 4 if out_dtype == torch.float32 else 2
+    buf = Guarded(M * N * esz, out_dtype)
+    wsb = ws if ws is not None else Guarded(splits * M * N * 4, torch.float32)
+    nv.gemm(dev_operand(pa, sa, ga), dev_operand(pb, sb, gb), out_dtype, out=buf.view,
+            splits=splits, workspace=wsb.view)
+    torch.cuda.synchronize()
+    buf.check()
+    wsb.check()
+    return buf.view.float().cpu().numpy().astype(np.float64).reshape(M, N)
+
+
+SPLIT_SHAPES = [(31, 17, 272), (256, 300, 1040), (257, 129, 5120), (128, 640, 5376)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_one_split_equals_the_unsplit_product(M, N, K, out_dtype):
+    banner(f"split 1 vs unsplit {M}x{N}x{K} {out_dtype}")
+    pa, sa = random_nvfp4(M + 7 * K, M, K)
+    pb, sb = random_nvfp4(N + 9 * K, N, K)
+    got = gpu_gemm_split(pa, sa, 0.37, pb, sb, 1.9e-3, 1, out_dtype)
+    want = gpu_gemm(pa, sa, 0.37, pb, sb, 1.9e-3, out_dtype)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_split_products_within_the_bound(M, N, K):
+    nchunks = -(-K // 128)
+    pa, sa = random_nvfp4(M + 11 * K, M, K)
+    pb, sb = random_nvfp4(N + 13 * K, N, K)
+    ga, gb = np.float32(0.37), np.float32(1.9e-3)
+    want, gabs = oracle.gemm(pa, sa, ga, pb, sb, gb, M, N, K, want_abs=True)
+    for splits in sorted({2, 3, 7, nchunks} & set(range(1, min(64, nchunks) + 1))):
+        banner(f"{splits} splits {M}x{N}x{K}")
+        got = gpu_gemm_split(pa, sa, ga, pb, sb, gb, splits)
+        assert_within(got, want, gabs, K, what=f"{splits} splits")
+        again = gpu_gemm_split(pa, sa, ga, pb, sb, gb, splits)
+        np.testing.assert_array_equal(got, again)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_split_unit_scales_are_bit_exact(splits):
+    M, N, K = 200, 96, 1296  # 11 chunks of K, the last one partial
+    banner(f"unit scales, {splits} splits {M}x{N}x{K}")
+    pa, _ = random_nvfp4(301, M, K)
+    pb, _ = random_nvfp4(302, N, K)
+    sa = np.full((M, K // 16), 0x38, np.uint8)
+    sb = np.full((N, K // 16), 0x38, np.uint8)
+    got = gpu_gemm_split(pa, sa, 1.0, pb, sb, 1.0, splits)
+    np.testing.assert_array_equal(got, oracle.gemm(pa, sa, 1.0, pb, sb, 1.0, M, N, K))
+
+
+def test_split_workspace_reused_by_a_smaller_product():
+    # The workspace holds the previous call's sums on entry; a second,
+    # smaller call with the same workspace must not depend on them.
+    ws = Guarded(4 * 300 * 200 * 4, torch.float32)
+    for (M, N, K, splits) in [(300, 200, 2048, 4), (70, 90, 640, 3)]:
+        banner(f"workspace reuse {M}x{N}x{K}, {splits} splits")
+        pa, sa = random_nvfp4(M + K, M, K)
+        pb, sb = random_nvfp4(N + K, N, K)
+        got = gpu_gemm_split(pa, sa, 0.5, pb, sb, 0.25, splits, ws=ws)
+        want, gabs = oracle.gemm(pa, sa, 0.5, pb, sb, 0.25, M, N, K, want_abs=True)
+        assert_within(got, want, gabs, K)
+
+
+def test_decode_sized_product_with_the_hinted_split():
+    M, N, K = 128, 5120, 5120
+    hint = nv.gemm_splits_hint(M, N, K)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert hint == max(1, min(cus // ((M + 255) // 256 * (N // 128)), K // 128 // 4, 64))
+    banner(f"decode-sized {M}x{N}x{K}, hint {hint}")
+    pa, sa = random_nvfp4(401, M, K, 0x28, 0x50)
+    pb, sb = random_nvfp4(402, N, K, 0x28, 0x50)
+    ga, gb = np.float32(2.5e-3), np.float32(4.0e-5)
+    a, b = dev_operand(pa, sa, ga), dev_operand(pb, sb, gb)
+    got = nv.gemm(a, b, torch.float32, splits="auto").cpu().numpy().astype(np.float64)
+    cols = np.concatenate([[0, 127, 128, N - 1], np.random.default_rng(403).choice(N, 60, False)])
+    want, gabs = oracle.gemm(pa, sa, ga, pb[cols], sb[cols], gb, M, len(cols), K, want_abs=True)
+    assert_within(got[:, cols], want, gabs, K)
+    assert nv.gemm_splits_hint(32768, 5120, 5120) == 1
+    assert nv.gemm_splits_hint(128, 5120, 256) == 1
