@@ -49,18 +49,16 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmThreads = 256;                 // 4 waves as 2 x 2
-constexpr int kTile = 256;                        // workgroup tile rows of A (and of B when wide)
-constexpr int kWaveTile = 128;                    // wave tile rows of A
-constexpr int kFrags = kWaveTile / 32;            // 32 x 32 MFMA tiles per wave along A
+constexpr int kTile = 256;                        // workgroup tile rows, at most
 constexpr int kStageBlocks = 8;                   // blocks of K per stage (K = 128)
 constexpr int kStages = 4;                        // LDS buffers
 constexpr int kAhead = 3;                         // stages in flight ahead of the one computed
 constexpr int kRowBytes = kStageBlocks * 8;       // code bytes per row and stage
 constexpr int kScaleSlot = 16;                    // LDS bytes per row for its 8 scale bytes
-// Per stage: A codes [256][64], B codes [kTileN][64], A scale slots [256][16],
-// B scale slots [kTileN][16].
-template <int kTileN>
-constexpr int kStageBytes = (kTile + kTileN) * (kRowBytes + kScaleSlot);
+// Per stage: A codes [kTileM][64], B codes [kTileN][64], A scale slots
+// [kTileM][16], B scale slots [kTileN][16].
+template <int kTileM, int kTileN>
+constexpr int kStageBytes = (kTileM + kTileN) * (kRowBytes + kScaleSlot);
 constexpr int kGroupM = 4;                        // tile rows per group of the walk
 
 // Buffer resource from values the compiler may hold in vector registers but
@@ -135,13 +133,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scale_rsrc(const uint8_t* p, u
   return uniform_rsrc(reinterpret_cast<const uint8_t*>(a - d0), (d0 + bytes + 3u) & ~3u);
 }
 
-// Vector-memory operations a wave issues per stage: its code loads of A (4)
-// and B (kTileN / 64) and one scale load per operand.  With a narrow B tile
-// only waves 0 and 1 have B scale rows to load; waves 2 and 3 issue an
-// out-of-range load into a spare 1 KiB of LDS that nobody reads, so every
-// wave waits for the same count.
-template <int kTileN>
-constexpr int kLoadsPerStage = 4 + kTileN / 64 + 2;
+// Vector-memory operations a wave issues per stage: its code loads of A
+// (kTileM / 64) and B (kTileN / 64) and one scale load per operand.  With a
+// 128-row tile of an operand only waves 0 and 1 have scale rows of it to
+// load; waves 2 and 3 issue an out-of-range load into a spare 1 KiB of LDS
+// that nobody reads, so every wave waits for the same count.
+template <int kTileM, int kTileN>
+constexpr int kLoadsPerStage = kTileM / 64 + kTileN / 64 + 2;
 constexpr int kSpareBytes = 64 * kScaleSlot;
 
 // Waits until at most N of this wave's vector-memory operations are
@@ -211,18 +209,21 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
 // range u / tiles of tile u % tiles and stores its raw fp32 sums in slice
 // u / tiles of ws ([splits][M][N], passed as out); splitk_reduce_kernel then
 // adds the slices.  Without kSplit, splits is 1 and the unit writes out.
-template <bool kBf16, bool kAligned, int kTileN, bool kSplit>
+template <bool kBf16, bool kAligned, int kTileM, int kTileN, bool kSplit>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const uint8_t* __restrict__ pa, const uint8_t* __restrict__ sa, const float* __restrict__ ga,
     const uint8_t* __restrict__ pb, const uint8_t* __restrict__ sb, const float* __restrict__ gb,
     int64_t M, int64_t N, int64_t K, uint32_t tiles_m, uint32_t tiles_n, uint32_t per_xcd,
     uint32_t splits, void* __restrict__ out) {
-  constexpr int kStage = kStageBytes<kTileN>;
-  constexpr int kCodesA = kTile * kRowBytes, kCodesB = kTileN * kRowBytes;
-  constexpr int kScalesA = kTile * kScaleSlot;
+  constexpr int kStage = kStageBytes<kTileM, kTileN>;
+  constexpr int kCodesA = kTileM * kRowBytes, kCodesB = kTileN * kRowBytes;
+  constexpr int kScalesA = kTileM * kScaleSlot;
+  constexpr int kWaveTileM = kTileM / 2;       // wave tile rows (rows of A)
+  constexpr int kFragsA = kWaveTileM / 32;     // 32 x 32 MFMA tiles per wave along A
   constexpr int kWaveTileN = kTileN / 2;       // wave tile columns (rows of B)
   constexpr int kFragsB = kWaveTileN / 32;     // 32 x 32 MFMA tiles per wave along B
-  __shared__ __align__(16) uint8_t lds[kStages * kStage + (kTileN < kTile ? kSpareBytes : 0)];
+  constexpr bool kSpare = kTileM < kTile || kTileN < kTile;
+  __shared__ __align__(16) uint8_t lds[kStages * kStage + (kSpare ? kSpareBytes : 0)];
   const uint32_t tiles = tiles_m * tiles_n;
   const uint32_t U = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
   if (U >= tiles * splits) return;
@@ -248,35 +249,37 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   const uint32_t nst = c_end - c_begin;
 
   // Resources over this tile's rows of A and B (rows past M or N read 0).
-  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTileN;
-  const uint32_t rows_a = (uint32_t)min<int64_t>(kTile, M - m0);
+  const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
+  const uint32_t rows_a = (uint32_t)min<int64_t>(kTileM, M - m0);
   const uint32_t rows_b = (uint32_t)min<int64_t>(kTileN, N - n0);
-  // Whether this wave loads B scale rows (64 from row 64 * wave).
-  const bool b_scales = kTileN == kTile || wave < (uint32_t)(kTileN / 64);
+  // Whether this wave loads scale rows of A and of B (64 from row 64 * wave).
+  const bool a_scales = kTileM >= kTile || wave < (uint32_t)(kTileM / 64);
+  const bool b_scales = kTileN >= kTile || wave < (uint32_t)(kTileN / 64);
   const __amdgpu_buffer_rsrc_t rca = uniform_rsrc(pa + m0 * (K / 2), rows_a * nblk * 8u);
   uint32_t da = 0, db = 0;  // scale resources' offsets below their tiles' first bytes
   const __amdgpu_buffer_rsrc_t rsa = scale_rsrc(sa + m0 * (K / 16), rows_a * nblk, da);
   const __amdgpu_buffer_rsrc_t rcb = uniform_rsrc(pb + n0 * (K / 2), rows_b * nblk * 8u);
   const __amdgpu_buffer_rsrc_t rsb = scale_rsrc(sb + n0 * (K / 16), rows_b * nblk, db);
 
-  f32x16 acc[kFrags][kFragsB];
+  f32x16 acc[kFragsA][kFragsB];
 #pragma unroll
-  for (int i = 0; i < kFrags; ++i)
+  for (int i = 0; i < kFragsA; ++i)
 #pragma unroll
     for (int j = 0; j < kFragsB; ++j) acc[i][j] = f32x16{};
 
   auto stage_ptr = [&](uint32_t c) { return lds + (c % kStages) * kStage; };
   // Part q (0..5) of the loads of stage c (see issue_codes): the q-th code
-  // load of A and of B (B has kTileN / 64 of them), then A's scale load,
-  // then B's.
+  // load of A and of B (they have kTileM / 64 and kTileN / 64 of them), then
+  // A's scale load, then B's.
   auto issue_part = [&](uint32_t c, int q, bool live) {
     uint8_t* st = stage_ptr(c);
     if (q < 4) {
-      issue_codes<kTile>(rca, st, c, q, live, nblk, wave, lane);
+      if (q < kTileM / 64) issue_codes<kTileM>(rca, st, c, q, live, nblk, wave, lane);
       if (q < kTileN / 64) issue_codes<kTileN>(rcb, st + kCodesA, c, q, live, nblk, wave, lane);
     } else if (q == 4) {
-      issue_scales(rsa, st + kCodesA + kCodesB + 64u * wave * kScaleSlot, 64u * wave, c, live,
-                   nblk, da, lane);
+      uint8_t* dst = a_scales ? st + kCodesA + kCodesB + 64u * wave * kScaleSlot
+                              : lds + kStages * kStage;
+      issue_scales(rsa, dst, 64u * wave, c, live && a_scales, nblk, da, lane);
     } else {
       uint8_t* dst = b_scales ? st + kCodesA + kCodesB + kScalesA + 64u * wave * kScaleSlot
                               : lds + kStages * kStage;
@@ -298,27 +301,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   if (nst > 1) issue(c_begin + 1u);
   if (nst > 2) {
     issue(c_begin + 2u);
-    wait_vm<kLoadsPerStage<kTileN>>();
+    wait_vm<kLoadsPerStage<kTileM, kTileN>>();
   } else {
     wait_vm<0>();
   }
   lds_barrier();
 
-  // Operand r < kFrags is A fragment r (tile row wm*128 + 32r + l32), the
-  // others B fragments (tile row wn * kWaveTileN + 32(r - kFrags) + l32).
+  // Operand r < kFragsA is A fragment r (tile row wm * kWaveTileM + 32r + l32), the
+  // others B fragments (tile row wn * kWaveTileN + 32(r - kFragsA) + l32).
   // Software pipeline across stages: the codes of
   // steps 4-7 are read from LDS while steps 0-3 run, those of the next
   // stage's steps 0-3 (already in LDS: written before the previous barrier)
   // while steps 4-7 run, and each step's operands are decoded while the
   // matrix cores work on the step before.
-  constexpr int kOps = kFrags + kFragsB;
+  constexpr int kOps = kFragsA + kFragsB;
   auto op_row = [&](int r) {
-    return r < kFrags ? wm * kWaveTile + 32u * (uint32_t)r + l32
-                      : wn * kWaveTileN + 32u * (uint32_t)(r - kFrags) + l32;
+    return r < kFragsA ? wm * kWaveTileM + 32u * (uint32_t)r + l32
+                      : wn * kWaveTileN + 32u * (uint32_t)(r - kFragsA) + l32;
   };
-  auto codes_of = [&](const uint8_t* st, int r) { return st + (r < kFrags ? 0 : kCodesA); };
+  auto codes_of = [&](const uint8_t* st, int r) { return st + (r < kFragsA ? 0 : kCodesA); };
   auto scales_of = [&](const uint8_t* st, int r) {
-    return st + kCodesA + kCodesB + (r < kFrags ? 0 : kScalesA);
+    return st + kCodesA + kCodesB + (r < kFragsA ? 0 : kScalesA);
   };
   u32x4 lo[kOps], hi[kOps];
   f16x2 dlo[kOps], dhi[kOps], ndlo[kOps], ndhi[kOps];
@@ -329,24 +332,24 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     for (int r = 0; r < kOps; ++r) {
       lo[r] = read_codes(codes_of(st, r), op_row(r), 2u * h);
       read_scales<kAligned>(scales_of(st, r), op_row(r), h, c_begin, nblk,
-                            r < kFrags ? da : db, dlo[r], dhi[r]);
+                            r < kFragsA ? da : db, dlo[r], dhi[r]);
     }
 #pragma unroll
     for (int r = 0; r < kOps; ++r) op[0][r] = decode8(lo[r][0], dlo[r][0]);
   }
   // vm: vector-memory instructions to place among this step's MFMAs; the
   // next step's decode (8 VALU per operand) is spread evenly over them.
-  constexpr int kValuPerMfma = 8 * kOps / (kFrags * kFragsB);
+  constexpr int kValuPerMfma = 8 * kOps / (kFragsA * kFragsB);
   auto mfma_step = [&](int cur, auto vm_c) {
     constexpr int vm = decltype(vm_c)::value;
 #pragma unroll
-    for (int i = 0; i < kFrags; ++i)
+    for (int i = 0; i < kFragsA; ++i)
 #pragma unroll
       for (int j = 0; j < kFragsB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][i], op[cur][kFrags + j],
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[cur][i], op[cur][kFragsA + j],
                                                            acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int k = 0; k < kFrags * kFragsB; ++k) {
+    for (int k = 0; k < kFragsA * kFragsB; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // decode
       if constexpr (vm > 0)
@@ -367,10 +370,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
       for (int r = 0; r < kOps; ++r)
         op[nxt][r] = t < 3 ? decode8(lo[r][t + 1], dlo[r][(t + 1) >> 1])
                            : decode8(hi[r][0], dhi[r][0]);
-      if (t < kTileN / 64)
+      const int nvm = (t < kTileM / 64 ? 1 : 0) + (t < kTileN / 64 ? 1 : 0);
+      if (nvm == 2)
         mfma_step(cur, std::integral_constant<int, 2>{});
-      else
+      else if (nvm == 1)
         mfma_step(cur, std::integral_constant<int, 1>{});
+      else
+        mfma_step(cur, std::integral_constant<int, 0>{});
     }
     // The next stage's first codes and scales (stage c + 1 is in LDS; on the
     // last stage this reads a stale buffer whose values are never used).
@@ -378,7 +384,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
     for (int r = 0; r < kOps; ++r) {
       lo[r] = read_codes(codes_of(sn, r), op_row(r), 2u * h);
-      read_scales<kAligned>(scales_of(sn, r), op_row(r), h, c + 1u, nblk, r < kFrags ? da : db,
+      read_scales<kAligned>(scales_of(sn, r), op_row(r), h, c + 1u, nblk, r < kFragsA ? da : db,
                             ndlo[r], ndhi[r]);
     }
 #pragma unroll
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     // This stage's loads of stage c + 3 (issued even past the unit's last
     // stage, then out of range) may stay in flight; stage c + 2's are
     // complete.
-    wait_vm<kLoadsPerStage<kTileN>>();
+    wait_vm<kLoadsPerStage<kTileM, kTileN>>();
     lds_barrier();
   }
 
@@ -415,11 +421,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   static_assert(!(kSplit && kBf16), "split units store fp32 sums");
   const float gab = kSplit ? 1.0f : (*ga) * (*gb);
   if constexpr (kSplit) out = static_cast<float*>(out) + (int64_t)split * M * N;
-  const int64_t mw = m0 + wm * kWaveTile, nw = n0 + wn * kWaveTileN;
+  const int64_t mw = m0 + wm * kWaveTileM, nw = n0 + wn * kWaveTileN;
   constexpr uint32_t kEsz = kBf16 ? 2u : 4u;
   const uint32_t row_bytes = (uint32_t)N * kEsz;
 #pragma unroll
-  for (int i = 0; i < kFrags; ++i) {
+  for (int i = 0; i < kFragsA; ++i) {
     const int64_t r0 = mw + 32 * i;
     const uint32_t rows = (uint32_t)max<int64_t>(0, min<int64_t>(32, M - r0));
     const __amdgpu_buffer_rsrc_t ro =
@@ -442,14 +448,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   }
 }
 
-template <bool kBf16, bool kAligned, int kTileN, bool kSplit>
+template <bool kBf16, bool kAligned, int kTileM, int kTileN, bool kSplit>
 hipError_t launch_gemm_v(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
                          const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
                          uint32_t splits, void* out, hipStream_t s, Events ev) {
-  const uint32_t tiles_m = (uint32_t)((M + kTile - 1) / kTile);
+  const uint32_t tiles_m = (uint32_t)((M + kTileM - 1) / kTileM);
   const uint32_t tiles_n = (uint32_t)((N + kTileN - 1) / kTileN);
   const uint32_t per_xcd = (tiles_m * tiles_n * splits + 7u) / 8u;
-  return launch_with_events(gemm_kernel<kBf16, kAligned, kTileN, kSplit>, dim3(per_xcd * 8u),
+  return launch_with_events(gemm_kernel<kBf16, kAligned, kTileM, kTileN, kSplit>,
+                            dim3(per_xcd * 8u),
                             dim3(kGemmThreads), s, ev, pa, sa, ga, pb, sb, gb, M, N, K, tiles_m,
                             tiles_n, per_xcd, splits, out);
 }
@@ -472,11 +479,16 @@ template <bool kBf16, bool kAligned>
 hipError_t launch_gemm_t(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
                          const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
                          void* out, hipStream_t s, Events ev) {
+  // At most 128 rows of A: 128 x 128 tiles, as many as 256 x 128 ones but
+  // without MFMAs on rows past M.
+  if (M <= 128)
+    return launch_gemm_v<kBf16, kAligned, 128, 128, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u,
+                                                           out, s, ev);
   if (narrow_tiles(M, N, 1))
-    return launch_gemm_v<kBf16, kAligned, 128, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u, out, s,
-                                                      ev);
-  return launch_gemm_v<kBf16, kAligned, 256, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u, out, s,
-                                                    ev);
+    return launch_gemm_v<kBf16, kAligned, 256, 128, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u,
+                                                           out, s, ev);
+  return launch_gemm_v<kBf16, kAligned, 256, 256, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u,
+                                                         out, s, ev);
 }
 
 // out[i] = (ws[0][i] + ws[1][i] + ... + ws[splits-1][i]) * RN(ga * gb), the
@@ -505,11 +517,14 @@ template <bool kAligned>
 hipError_t launch_gemm_split_t(const uint8_t* pa, const uint8_t* sa, const float* ga,
                                const uint8_t* pb, const uint8_t* sb, const float* gb, int64_t M,
                                int64_t N, int64_t K, uint32_t splits, float* ws, hipStream_t s) {
+  if (M <= 128)
+    return launch_gemm_v<false, kAligned, 128, 128, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits,
+                                                          ws, s, Events{});
   if (narrow_tiles(M, N, splits))
-    return launch_gemm_v<false, kAligned, 128, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits, ws,
-                                                     s, Events{});
-  return launch_gemm_v<false, kAligned, 256, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits, ws, s,
-                                                   Events{});
+    return launch_gemm_v<false, kAligned, 256, 128, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits,
+                                                          ws, s, Events{});
+  return launch_gemm_v<false, kAligned, 256, 256, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits,
+                                                        ws, s, Events{});
 }
 
 }  // namespace

@@ -243,10 +243,10 @@ def test_wide_tiles_with_ragged_edges(K, off):
 
 
 def test_tile_width_does_not_change_results():
-    # Both tile widths give every output the same summation order (the same
-    # stages and MFMA steps, in order), so the first 256 rows of a product
-    # small enough for 256 x 128 tiles equal, bit for bit, those rows of a
-    # product large enough for 256 x 256 tiles.
+    # Every tile shape gives every output the same summation order (the same
+    # stages and MFMA steps, in order), so the first 128 rows (128 x 128
+    # tiles) and the first 256 rows (256 x 128 tiles) of a product equal, bit
+    # for bit, those rows of a product large enough for 256 x 256 tiles.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     N, K = 5120, 1040
 
@@ -262,8 +262,10 @@ def test_tile_width_does_not_change_results():
     pa, sa = random_nvfp4(141, M_big, K, 0x28, 0x50)
     pb, sb = random_nvfp4(142, N, K, 0x28, 0x50)
     small = gpu_gemm(pa[:256], sa[:256], 0.75, pb, sb, 1.0e-3)
+    tiny = gpu_gemm(pa[:128], sa[:128], 0.75, pb, sb, 1.0e-3)
     big = gpu_gemm(pa, sa, 0.75, pb, sb, 1.0e-3)
     np.testing.assert_array_equal(small, big[:256])
+    np.testing.assert_array_equal(tiny, big[:128])
     want, gabs = oracle.gemm(pa[:256], sa[:256], 0.75, pb, sb, 1.0e-3, 256, N, K, want_abs=True)
     assert_within(small, want, gabs, K)
 
