@@ -493,8 +493,10 @@ hipError_t launch_gemm_t(const uint8_t* pa, const uint8_t* sa, const float* ga, 
 
 // out[i] = (ws[0][i] + ws[1][i] + ... + ws[splits-1][i]) * RN(ga * gb), the
 // slices added in order in fp32 (so one split reproduces the unsplit
-// product bit for bit), over the mn elements of the product.
-template <bool kBf16>
+// product bit for bit), over the mn elements of the product.  With kVec
+// (mn a multiple of 4, ws 16-byte and out 4-element aligned) each thread
+// takes 4 consecutive elements per step, with 16-byte loads.
+template <bool kBf16, bool kVec>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
                                                             int64_t mn, uint32_t splits,
                                                             const float* __restrict__ ga,
@@ -502,14 +504,39 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             void* __restrict__ out) {
   const float gab = (*ga) * (*gb);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
-    float t = ws[i];
-    for (uint32_t q = 1; q < splits; ++q) t = t + ws[(int64_t)q * mn + i];
-    const float y = t * gab;
-    if constexpr (kBf16)
-      static_cast<uint16_t*>(out)[i] = to_bf16_bits(y);
-    else
-      static_cast<float*>(out)[i] = y;
+  if constexpr (kVec) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int64_t n4 = mn / 4;
+    const f32x4* w4 = reinterpret_cast<const f32x4*>(ws);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+      f32x4 t = w4[i];
+      for (uint32_t q = 1; q < splits; ++q) {
+        const f32x4 u = w4[(int64_t)q * n4 + i];
+        t.x = t.x + u.x;
+        t.y = t.y + u.y;
+        t.z = t.z + u.z;
+        t.w = t.w + u.w;
+      }
+      const float y0 = t.x * gab, y1 = t.y * gab, y2 = t.z * gab, y3 = t.w * gab;
+      if constexpr (kBf16) {
+        u32x2 o;
+        o.x = (uint32_t)to_bf16_bits(y0) | ((uint32_t)to_bf16_bits(y1) << 16);
+        o.y = (uint32_t)to_bf16_bits(y2) | ((uint32_t)to_bf16_bits(y3) << 16);
+        static_cast<u32x2*>(out)[i] = o;
+      } else {
+        static_cast<f32x4*>(out)[i] = f32x4{y0, y1, y2, y3};
+      }
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
+      float t = ws[i];
+      for (uint32_t q = 1; q < splits; ++q) t = t + ws[(int64_t)q * mn + i];
+      const float y = t * gab;
+      if constexpr (kBf16)
+        static_cast<uint16_t*>(out)[i] = to_bf16_bits(y);
+      else
+        static_cast<float*>(out)[i] = y;
+    }
   }
 }
 
@@ -555,13 +582,15 @@ hipError_t launch_gemm_splitk(const uint8_t* pa, const uint8_t* sa, const float*
               : launch_gemm_split_t<false>(pa, sa, ga, pb, sb, gb, M, N, K, splits, ws, s);
   if (e != hipSuccess) return e;
   const int64_t mn = M * N;
-  int64_t groups = (mn + 255) / 256;
+  const uintptr_t out_align = out_bf16 ? 8u : 16u;
+  const bool vec = mn % 4 == 0 && (reinterpret_cast<uintptr_t>(ws) & 15u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(out) & (out_align - 1u)) == 0;
+  int64_t groups = ((vec ? mn / 4 : mn) + 255) / 256;
   const int64_t cap = (int64_t)device_cu_count() * 8;
   if (groups > cap) groups = cap;
-  if (out_bf16)
-    splitk_reduce_kernel<true><<<(unsigned)groups, 256, 0, s>>>(ws, mn, splits, ga, gb, out);
-  else
-    splitk_reduce_kernel<false><<<(unsigned)groups, 256, 0, s>>>(ws, mn, splits, ga, gb, out);
+  auto* k = out_bf16 ? (vec ? splitk_reduce_kernel<true, true> : splitk_reduce_kernel<true, false>)
+                     : (vec ? splitk_reduce_kernel<false, true> : splitk_reduce_kernel<false, false>);
+  k<<<(unsigned)groups, 256, 0, s>>>(ws, mn, splits, ga, gb, out);
   return hipGetLastError();
 }
 

@@ -435,3 +435,21 @@ def test_decode_sized_product_with_the_hinted_split():
     assert_within(got[:, cols], want, gabs, K)
     assert nv.gemm_splits_hint(32768, 5120, 5120) == 1
     assert nv.gemm_splits_hint(128, 5120, 256) == 1
+
+
+def test_split_reduce_vector_and_scalar_paths_agree():
+    # mn a multiple of 4 with aligned buffers takes the 16-byte reduce; a
+    # bf16 output 2 bytes off its allocation takes the element-wise one.
+    # Same split count, same sums: the outputs agree bit for bit.
+    M, N, K, splits = 256, 300, 1040, 3
+    banner(f"split reduce paths {M}x{N}x{K}, {splits} splits")
+    pa, sa = random_nvfp4(501, M, K)
+    pb, sb = random_nvfp4(502, N, K)
+    a, b = dev_operand(pa, sa, 0.37), dev_operand(pb, sb, 1.9e-3)
+    aligned = nv.gemm(a, b, torch.bfloat16, splits=splits)
+    raw = torch.full((M * N + 1,), 7, dtype=torch.bfloat16, device="cuda")
+    shifted_out = raw[1:].view(M, N)
+    nv.gemm(a, b, torch.bfloat16, out=shifted_out, splits=splits)
+    torch.cuda.synchronize()
+    assert raw[0].item() == 7
+    np.testing.assert_array_equal(aligned.float().cpu().numpy(), shifted_out.float().cpu().numpy())
