@@ -27,8 +27,8 @@
 //
 // Data path.  A workgroup computes a 256 x 256 tile with four waves of
 // 128 x 128 (the accumulators fill the 256 AGPRs), or, where that fills the
-// compute units' rounds of tiles better (small products), a 256 x 128 tile
-// with waves of 128 x 64.  K is walked in stages of 128 (eight blocks): the
+// compute units' rounds of tiles better (smaller products), a 256 x 128 or
+// 128 x 128 tile with waves of 128 x 64 or 64 x 64.  K is walked in stages of 128 (eight blocks): the
 // stage's codes (64 bytes per tile row of either operand, four lanes per
 // row so that every request is one contiguous 64-byte piece) and scale
 // bytes go from memory straight into a four-deep LDS ring, three stages
@@ -461,30 +461,34 @@ hipError_t launch_gemm_v(const uint8_t* pa, const uint8_t* sa, const float* ga, 
                             tiles_n, per_xcd, splits, out);
 }
 
-// Whether 256 x 128 tiles beat 256 x 256 ones with `splits` units per tile.
-bool narrow_tiles(int64_t M, int64_t N, int64_t splits) {
-  // Tiles run in rounds of one per compute unit.  A 256 x 128 tile takes
-  // about 0.65 of the time of a 256 x 256 one (its decode costs 6 VALU
-  // instructions per MFMA instead of 4), so the narrow tiles are chosen only
-  // where they need fewer than 20/13 as many rounds: products with at most
-  // half a round of wide tiles, or a little over one round of them.
+// Tile shape for an M x N product with `splits` units per tile.  Tiles run
+// in rounds of one per compute unit; measured at full load, a 128 x 128
+// tile takes about 0.43 and a 256 x 128 tile about 0.61 of the time of a
+// 256 x 256 one (smaller tiles decode more per MFMA: 8 and 6 VALU
+// instructions against 4), so each shape costs its rounds times that
+// weight and the cheapest wins (ties to the larger tile).
+enum class TileShape { k128x128, k256x128, k256x256 };
+TileShape pick_tile(int64_t M, int64_t N, int64_t splits) {
   const int64_t cus = device_cu_count();
-  const int64_t tiles_m = (M + kTile - 1) / kTile;
-  const int64_t rounds_wide = (tiles_m * ((N + 255) / 256) * splits + cus - 1) / cus;
-  const int64_t rounds_narrow = (tiles_m * ((N + 127) / 128) * splits + cus - 1) / cus;
-  return 13 * rounds_narrow < 20 * rounds_wide;
+  auto cost = [&](int64_t tm, int64_t tn, int64_t weight) {
+    const int64_t units = ((M + tm - 1) / tm) * ((N + tn - 1) / tn) * splits;
+    return (units + cus - 1) / cus * weight;
+  };
+  const int64_t c_wide = cost(256, 256, 100), c_narrow = cost(256, 128, 61);
+  const int64_t c_small = cost(128, 128, 43);
+  if (c_small < c_narrow && c_small < c_wide) return TileShape::k128x128;
+  return c_narrow < c_wide ? TileShape::k256x128 : TileShape::k256x256;
 }
 
 template <bool kBf16, bool kAligned>
 hipError_t launch_gemm_t(const uint8_t* pa, const uint8_t* sa, const float* ga, const uint8_t* pb,
                          const uint8_t* sb, const float* gb, int64_t M, int64_t N, int64_t K,
                          void* out, hipStream_t s, Events ev) {
-  // At most 128 rows of A: 128 x 128 tiles, as many as 256 x 128 ones but
-  // without MFMAs on rows past M.
-  if (M <= 128)
+  const TileShape t = pick_tile(M, N, 1);
+  if (t == TileShape::k128x128)
     return launch_gemm_v<kBf16, kAligned, 128, 128, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u,
                                                            out, s, ev);
-  if (narrow_tiles(M, N, 1))
+  if (t == TileShape::k256x128)
     return launch_gemm_v<kBf16, kAligned, 256, 128, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u,
                                                            out, s, ev);
   return launch_gemm_v<kBf16, kAligned, 256, 256, false>(pa, sa, ga, pb, sb, gb, M, N, K, 1u,
@@ -544,10 +548,11 @@ template <bool kAligned>
 hipError_t launch_gemm_split_t(const uint8_t* pa, const uint8_t* sa, const float* ga,
                                const uint8_t* pb, const uint8_t* sb, const float* gb, int64_t M,
                                int64_t N, int64_t K, uint32_t splits, float* ws, hipStream_t s) {
-  if (M <= 128)
+  const TileShape t = pick_tile(M, N, splits);
+  if (t == TileShape::k128x128)
     return launch_gemm_v<false, kAligned, 128, 128, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits,
                                                           ws, s, Events{});
-  if (narrow_tiles(M, N, splits))
+  if (t == TileShape::k256x128)
     return launch_gemm_v<false, kAligned, 256, 128, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits,
                                                           ws, s, Events{});
   return launch_gemm_v<false, kAligned, 256, 256, true>(pa, sa, ga, pb, sb, gb, M, N, K, splits,

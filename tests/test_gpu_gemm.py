@@ -64,6 +64,22 @@ def shifted(scales, off):
     return t.view(scales.shape)
 
 
+def tile_shape(M, N, splits=1):
+    """The tile shape the library picks (its documented rule): rounds of
+    tiles, one per compute unit, times 43, 61 or 100 for 128 x 128, 256 x 128
+    and 256 x 256 tiles; the cheapest wins, ties to the larger tile."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def cost(tm, tn, w):
+        units = -(-M // tm) * -(-N // tn) * splits
+        return -(-units // cus) * w
+
+    small, narrow, wide = cost(128, 128, 43), cost(256, 128, 61), cost(256, 256, 100)
+    if small < narrow and small < wide:
+        return "128x128"
+    return "256x128" if narrow < wide else "256x256"
+
+
 def bound(K, gabs):
     return (K + K // 16 + 2) * 2.0 ** -23 * gabs + 2.0 ** -126
 
@@ -210,20 +226,27 @@ def test_full_size_prefill_product_sampled():
     assert np.isfinite(got).all()
 
 
+@pytest.mark.parametrize("shape", ["256x256", "256x128"])
 @pytest.mark.parametrize("K,off", [(592, 0), (640, 1)])
-def test_wide_tiles_with_ragged_edges(K, off):
-    # The tile width follows from how many rounds of tiles (one per compute
-    # unit) each width needs; the small shapes elsewhere in this file take
-    # 256 x 128 tiles.  This one takes 256 x 256 tiles on any device (just
-    # over two rounds of them, where the narrow tiles need five), with M and
-    # N ending mid-tile and K ending mid-stage (592) or scale tensors off the
-    # 4-byte grid (640 with an offset): all rows of the last tile row and a
-    # sample of the others, against the oracle over every column.
+def test_large_tiles_with_ragged_edges(K, off, shape):
+    # The tile shape follows from how many rounds of tiles (one per compute
+    # unit) each shape needs; the small shapes elsewhere in this file take
+    # 128 x 128 tiles.  These take 256 x 256 tiles (one round of them, where
+    # 256 x 128 tiles need two) or 256 x 128 tiles (one round, where 128 x 128
+    # ones need two) on any device, with M and N ending mid-tile and K ending
+    # mid-stage (592) or scale tensors off the 4-byte grid (640 with an
+    # offset): all rows of the last tile row and a sample of the others,
+    # against the oracle over every column.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tiles_n = 17
-    tiles_m = -(-2 * cus // tiles_n) + 1
-    M, N = 256 * tiles_m - 37, 256 * tiles_n - 100
-    banner(f"wide tiles {M}x{N}x{K} scale offset {off}")
+    if shape == "256x256":
+        tiles_n = 17
+        tiles_m = cus // tiles_n
+        M, N = 256 * tiles_m - 37, 256 * tiles_n - 100
+    else:
+        tiles_m = max(1, cus // 40)
+        M, N = 256 * tiles_m - 37, 128 * 40 - 100
+    assert tile_shape(M, N) == shape, (M, N, cus)
+    banner(f"{shape} tiles {M}x{N}x{K} scale offset {off}")
     pa, sa = random_nvfp4(131 + K, M, K, 0x28, 0x50)
     pb, sb = random_nvfp4(132 + K, N, K, 0x28, 0x50)
     ga, gb = np.float32(3.0e-2), np.float32(7.0e-4)
@@ -244,30 +267,26 @@ def test_wide_tiles_with_ragged_edges(K, off):
 
 def test_tile_width_does_not_change_results():
     # Every tile shape gives every output the same summation order (the same
-    # stages and MFMA steps, in order), so the first 128 rows (128 x 128
-    # tiles) and the first 256 rows (256 x 128 tiles) of a product equal, bit
-    # for bit, those rows of a product large enough for 256 x 256 tiles.
+    # stages and MFMA steps, in order), so the first rows of products that
+    # take 128 x 128 and 256 x 128 tiles equal, bit for bit, those rows of a
+    # product large enough for 256 x 256 tiles.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     N, K = 5120, 1040
-
-    def rounds(M, width):
-        return -(-((M + 255) // 256) * (-(-N // width)) // cus)
-
-    def narrow(M):
-        return 13 * rounds(M, 128) < 20 * rounds(M, 256)
-
+    M_narrow = 256 * max(1, cus // 64)
     M_big = 256 * -(-4 * cus // 20)
-    assert narrow(256) and not narrow(M_big), (cus, M_big)
-    banner(f"tile widths agree: 256 vs {M_big} rows, {N}x{K}")
+    assert tile_shape(128, N) == "128x128", cus
+    assert tile_shape(M_narrow, N) == "256x128", (cus, M_narrow)
+    assert tile_shape(M_big, N) == "256x256", (cus, M_big)
+    banner(f"tile shapes agree: 128, {M_narrow} vs {M_big} rows, {N}x{K}")
     pa, sa = random_nvfp4(141, M_big, K, 0x28, 0x50)
     pb, sb = random_nvfp4(142, N, K, 0x28, 0x50)
-    small = gpu_gemm(pa[:256], sa[:256], 0.75, pb, sb, 1.0e-3)
+    small = gpu_gemm(pa[:M_narrow], sa[:M_narrow], 0.75, pb, sb, 1.0e-3)
     tiny = gpu_gemm(pa[:128], sa[:128], 0.75, pb, sb, 1.0e-3)
     big = gpu_gemm(pa, sa, 0.75, pb, sb, 1.0e-3)
-    np.testing.assert_array_equal(small, big[:256])
+    np.testing.assert_array_equal(small, big[:M_narrow])
     np.testing.assert_array_equal(tiny, big[:128])
-    want, gabs = oracle.gemm(pa[:256], sa[:256], 0.75, pb, sb, 1.0e-3, 256, N, K, want_abs=True)
-    assert_within(small, want, gabs, K)
+    want, gabs = oracle.gemm(pa[:128], sa[:128], 0.75, pb, sb, 1.0e-3, 128, N, K, want_abs=True)
+    assert_within(tiny, want, gabs, K)
 
 
 def test_long_k_errors_are_far_inside_the_bound():
