@@ -28,11 +28,11 @@
 // Data path.  A workgroup computes a 256 x 256 tile with four waves of
 // 128 x 128 (the accumulators fill the 256 AGPRs), or, where that fills the
 // compute units' rounds of tiles better (smaller products), a 256 x 128 or
-// 128 x 128 tile with waves of 128 x 64 or 64 x 64.  K is walked in stages of 128 (eight blocks): the
-// stage's codes (64 bytes per tile row of either operand, four lanes per
-// row so that every request is one contiguous 64-byte piece) and scale
-// bytes go from memory straight into a four-deep LDS ring, three stages
-// ahead of the stage the matrix cores work on.  In LDS the 16-byte
+// 128 x 128 tile with waves of 128 x 64 or 64 x 64.  K is walked in stages
+// of 128 (eight blocks): the stage's codes (64 bytes per tile row of either
+// operand, four lanes per row so that every request is one contiguous
+// 64-byte piece) and scale bytes go from memory straight into a four-deep
+// LDS ring, three stages ahead of the stage the matrix cores work on.  In LDS the 16-byte
 // pieces of a row are XOR-swizzled by bits 2-3 of the row, which makes both
 // the 16-byte writes and the fragment reads (16 lanes on 16 consecutive
 // rows) free of bank conflicts.
@@ -78,15 +78,16 @@ __device__ __forceinline__ uint32_t code_slot(uint32_t row, uint32_t piece) {
 
 // The loads of one stage go out in parts spread over the MFMA steps of the
 // stage before (a burst of them would stall the in-order issue of the
-// MFMAs): part q < 4 is the q-th code load of each operand, part 4 the
-// scale load of A, part 5 that of B.
+// MFMAs): part q < 4 is the q-th code load of each operand (an operand with
+// a 128-row tile has two), part 4 the scale load of A, part 5 that of B.
 //
 // Code loads go straight to LDS (buffer_load ... lds): lane l of load q
 // writes bytes 16l .. 16l + 15 of the 1 KiB that holds tile rows
-// 64w + 16q .. 64w + 16q + 15, which is physical piece l % 4 of row
-// 64w + 16q + l / 4, so the lane loads the row's logical piece
-// (l % 4) ^ ((row >> 2) & 3).  Scale loads do the same with one 16-byte
-// window per row (lane l: row 64w + l): the 16 bytes from the 4-byte
+// R w + 16q .. R w + 16q + 15 (R = tile rows / 4 per wave), which is
+// physical piece l % 4 of row R w + 16q + l / 4, so the lane loads the
+// row's logical piece (l % 4) ^ ((row >> 2) & 3).  Scale loads do the same
+// with one 16-byte window per row (lane l: row 64w + l, waves with no such
+// rows loading into a spare buffer): the 16 bytes from the 4-byte
 // boundary at or below the row's first scale byte of the stage, which
 // contain its 8 bytes at offset (d0 + row * nblk) % 4 whatever K is (d0:
 // the tile's first scale byte's offset above the 4-byte boundary below it,
