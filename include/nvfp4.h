@@ -327,10 +327,12 @@ nvfp4_status nvfp4_gemm_splitk(const uint8_t* a_packed, const uint8_t* a_scales,
                                float* workspace, int64_t workspace_floats, void* stream);
 
 /* Split count suggested for an m x n x k nvfp4_gemm_splitk on the current
- * device: enough to give about one unit of work per compute unit, each range
- * keeping at least four 128-wide chunks of k; 1 where splitting does not
- * help (then nvfp4_gemm is the faster call).  Host only; returns 0 for
- * shapes nvfp4_gemm rejects. */
+ * device: the count with the lowest time under a model of the launch
+ * (rounds of units over the compute units, the per-chunk cost of the tile
+ * shape used, the extra pass over the workspace), each range keeping at
+ * least four 128-wide chunks of k; 1 where splitting does not help (then
+ * nvfp4_gemm is the faster call).  Host only; returns 0 for shapes
+ * nvfp4_gemm rejects. */
 int nvfp4_gemm_splits_hint(int64_t m, int64_t n, int64_t k);
 
 /* Static description of a status code. */

@@ -601,15 +601,38 @@ hipError_t launch_gemm_splitk(const uint8_t* pa, const uint8_t* sa, const float*
 }
 
 int gemm_splits_hint(int64_t M, int64_t N, int64_t K) {
-  // Enough splits to bring a product with few tiles up to about one round
-  // of the compute units, each split keeping at least four stages of K.
+  // The split count with the lowest modelled time, each split keeping at
+  // least four stages of K.  Model (fitted to measurements on MI355X at
+  // full load): a unit of S splits runs ceil(nstages / S) stages at 1.075,
+  // 1.525 or 2.5 us per stage for the 128 x 128, 256 x 128 or 256 x 256 tile
+  // the launch picks, plus 2 us of prologue and epilogue; units run in
+  // rounds of one per compute unit; with S > 1 the reduce pass adds 3 us
+  // plus 1.6 us per split and 2^20 outputs.
   const int64_t cus = device_cu_count();
   const int64_t nstages = (K / 16 + kStageBlocks - 1) / kStageBlocks;
-  const int64_t tiles = ((M + kTile - 1) / kTile) * ((N + 127) / 128);
-  int64_t splits = cus / tiles;
-  if (splits > nstages / 4) splits = nstages / 4;
-  if (splits > kGemmMaxSplits) splits = kGemmMaxSplits;
-  return splits < 1 ? 1 : (int)splits;
+  int64_t cap = nstages / 4;
+  if (cap > kGemmMaxSplits) cap = kGemmMaxSplits;
+  const double mn_mi = (double)M * (double)N / 1048576.0;
+  int best_s = 1;
+  double best = 0.0;
+  for (int64_t S = 1; S <= (cap < 1 ? 1 : cap); ++S) {
+    const TileShape t = pick_tile(M, N, S);
+    const int64_t tm = t == TileShape::k128x128 ? 128 : 256;
+    const int64_t tn = t == TileShape::k256x256 ? 256 : 128;
+    const double per_stage = t == TileShape::k128x128   ? 1.075
+                             : t == TileShape::k256x128 ? 1.525
+                                                        : 2.5;
+    const int64_t units = ((M + tm - 1) / tm) * ((N + tn - 1) / tn) * S;
+    const int64_t rounds = (units + cus - 1) / cus;
+    const int64_t stages = (nstages + S - 1) / S;
+    double time = (double)rounds * ((double)stages * per_stage + 2.0);
+    if (S > 1) time += 3.0 + 1.6 * (double)S * mn_mi;
+    if (S == 1 || time < best) {
+      best = time;
+      best_s = (int)S;
+    }
+  }
+  return best_s;
 }
 
 }  // namespace nvfp4

@@ -441,8 +441,7 @@ def test_split_workspace_reused_by_a_smaller_product():
 def test_decode_sized_product_with_the_hinted_split():
     M, N, K = 128, 5120, 5120
     hint = nv.gemm_splits_hint(M, N, K)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert hint == max(1, min(cus // ((M + 255) // 256 * (N // 128)), K // 128 // 4, 64))
+    assert 2 <= hint <= K // 128 // 4, hint
     banner(f"decode-sized {M}x{N}x{K}, hint {hint}")
     pa, sa = random_nvfp4(401, M, K, 0x28, 0x50)
     pb, sb = random_nvfp4(402, N, K, 0x28, 0x50)
