@@ -281,7 +281,8 @@ def main():
                     help="skip the full-tensor oracle run; gate on sampled rows instead")
     ap.add_argument("--no-extra", action="store_true", help="skip the side measurements")
     ap.add_argument("--event-every", type=int, default=8,
-                    help="bind the kernel-timing events to every N-th timed step")
+                    help="bind the kernel-timing events to every N-th timed step (fewer "
+                         "when that would leave under 100 timed samples)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); sharding the path "
@@ -366,8 +367,9 @@ def main():
     # milliseconds the first ~250 steps run slower while the device's clocks
     # ramp back up.
     # Binding the events to a dispatch costs about 8 us of step time, so
-    # they go on every N-th step only (evenly spread over the timed region).
-    every = max(1, args.event_every)
+    # they go on every N-th step only (evenly spread over the timed region),
+    # N lowered where needed to keep at least about 100 samples.
+    every = max(1, min(args.event_every, args.steps // 100))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range((args.steps + every - 1) // every)]
     for a, b in evs:
