@@ -40,9 +40,12 @@ def lib():
     """Load the oracle library, compiling it first only if it is not built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        path = os.environ.get("NVFP4_ORACLE_LIB")  # e.g. the sanitizer build
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64 = ctypes.c_int64
         L.nvfp4o_bf16_to_f32.argtypes = [ctypes.c_uint16]
