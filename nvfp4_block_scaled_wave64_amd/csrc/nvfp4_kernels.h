@@ -67,6 +67,7 @@ enum : uint32_t {
   kVarMax = 16u,         // minimum-maximum-error selection rule instead of MSE
   kVarSelmap = 4u,       // write the selection bitmap
   kVarErr = 8u,          // accumulate the per-tensor error sum
+  kVarAmax = 32u,        // also fold the tensor's max |x| into amax_out (row kernel)
 };
 
 // ---- amax.hip ----

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
                                         : kRuleMse;
   constexpr bool kSel = (V & kVarSelmap) != 0;
   constexpr bool kErr = (V & kVarErr) != 0;
+  constexpr bool kAmax = (V & kVarAmax) != 0;
   constexpr bool kNeedErr = k46 || kErr;
 
   __shared__ float2 tab[128];
@@ -60,29 +61,47 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
   __syncthreads();
 
   const uint32_t nb = (uint32_t)nblocks;  // <= 2^26 per launch
-  const __amdgpu_buffer_rsrc_t r_in = make_rsrc(in, nb * 32u);
-  const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed, nb * 8u);
-  const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales, nb);
-  const __amdgpu_buffer_rsrc_t r_sel = make_rsrc(selmap, (nb + 7u) / 8u);
-
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t off_in = (lane & 31u) * 32u + (lane >> 5) * 16u;  // within a 1 KiB half
-  const uint32_t off_sel = lane < 8u ? lane : 0x80000000u;
+  const uint32_t off_sel = lane < 8u ? lane : 0x80000000u;          // lanes 0-7 store
   const uint32_t nchunks = (nb + 63u) / 64u;
   const uint32_t nwaves = gridDim.x * kRowsWaves;
-  const uint32_t first = blockIdx.x * kRowsWaves + (threadIdx.x >> 6);
+  // The chunk a wave works on is wave-uniform: it lives in scalar registers,
+  // and so do the per-chunk buffer resources below (no per-lane address
+  // arithmetic in the loop).
+  const uint32_t first =
+      blockIdx.x * kRowsWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   double acc = 0.0;
   float bmax = 0.0f;  // running block max for amax_out (blocks past the end are 0)
 
-  // Chunks past the end read as zeros (range-checked buffer loads); ch stays
-  // below nchunks + 2 * nwaves, so ch * 2048 cannot wrap.
+  // Resource over the bytes [off, total) of chunk ch's part of a stream p,
+  // based at p + off; empty for a chunk past the end (the prefetch of a
+  // wave's last step).  For a chunk that exists, off < total holds for every
+  // stream (its first input byte, code byte, scale byte and bitmap byte all
+  // lie inside the tensor's), so the count needs no clamp; selecting it on
+  // ch < nchunks keeps it scalar arithmetic (the compiler turns a clamp on
+  // off < total into a vector instruction, and the resource would then look
+  // divergent).  Range-checked accesses past the end read 0 or are dropped,
+  // so the ragged last chunk needs no branches either.
+  auto part = [&](const void* p, uint32_t ch, uint32_t off, uint32_t total) {
+    return make_rsrc(static_cast<const uint8_t*>(p) + off, ch < nchunks ? total - off : 0u);
+  };
   struct Two {
     u32x4 a, b;
   };
   auto load = [&](uint32_t ch) -> Two {
+    const __amdgpu_buffer_rsrc_t r = part(in, ch, ch * 2048u, nb * 32u);
     Two t;
-    t.a = __builtin_amdgcn_raw_buffer_load_b128(r_in, ch * 2048u + off_in, 0, kStreamLoad);
-    t.b = __builtin_amdgcn_raw_buffer_load_b128(r_in, ch * 2048u + 1024u + off_in, 0, kStreamLoad);
+    t.a = __builtin_amdgcn_raw_buffer_load_b128(r, off_in, 0, kStreamLoad);
+    t.b = __builtin_amdgcn_raw_buffer_load_b128(r, off_in + 1024u, 0, kStreamLoad);
+    return t;
+  };
+  // The next chunk's loads are issued at raised wave priority so that they
+  // leave as soon as the wave is scheduled, ahead of other waves' arithmetic.
+  auto prefetch = [&](uint32_t ch) -> Two {
+    __builtin_amdgcn_s_setprio(3);
+    const Two t = load(ch);
+    __builtin_amdgcn_s_setprio(0);
     return t;
   };
 
@@ -97,29 +116,23 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
       wd[4 + j] = p[1];
     }
     const Block16 q = quantize_block16<k46, kRule, kNeedErr>(wd, ts.k6, ts.k4, tab);
-    bmax = __builtin_elementwise_maximum(bmax, q.b);
+    if (kAmax) bmax = __builtin_elementwise_maximum(bmax, q.b);
     u32x2 codes;
     codes.x = q.lo;
     codes.y = q.hi;
-    __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, ch * 512u + lane * 8u, 0, kStreamStore);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q.S, r_scales, ch * 64u + lane, 0, kMergedStore);
+    __builtin_amdgcn_raw_buffer_store_b64(codes, part(packed, ch, ch * 512u, nb * 8u), lane * 8u, 0,
+                                          kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q.S, part(scales, ch, ch * 64u, nb), lane, 0,
+                                         kMergedStore);
     if (kSel) {
       // Lane l decides block l: the ballot is the chunk's 64 selection bits;
       // lanes 0-7 store its 8 bytes.
       const uint64_t bits = __ballot(q.pick4);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(bits >> (8u * (lane & 7u))), r_sel,
-                                           ch * 8u + off_sel, 0, kMergedStore);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(bits >> (8u * (lane & 7u))),
+                                           part(selmap, ch, ch * 8u, (nb + 7u) / 8u), off_sel, 0,
+                                           kMergedStore);
     }
     if (kErr) acc += (double)q.err;  // blocks past the end contribute 0
-  };
-
-  // The next chunk's loads are issued at raised wave priority so that they
-  // leave as soon as the wave is scheduled, ahead of other waves' arithmetic.
-  auto prefetch = [&](uint32_t ch) -> Two {
-    __builtin_amdgcn_s_setprio(3);
-    const Two t = load(ch);
-    __builtin_amdgcn_s_setprio(0);
-    return t;
   };
 
   // Every wave runs the same number of steps (a chunk index past the end is
@@ -127,26 +140,39 @@ __global__ __launch_bounds__(kRowsThreads) void quantize_rows_kernel(
   // kRowsSyncEvery steps.  Measured on MI355X: without it the 16 waves of a
   // compute unit drift apart over the tensor and their loads spread over
   // more DRAM pages; with it the kernel runs about 10% faster.
-  const uint32_t steps = (nchunks + nwaves - 1) / nwaves;
-  Two buf = load(first);
-  for (uint32_t k = 0; k < steps; ++k) {
-    const uint32_t ch = first + k * nwaves;
-    const Two w = buf;
-    buf = prefetch(ch + nwaves);
-    if (ch < nchunks) process(ch, w);
+  // The loop is unrolled twice with two load buffers used in turn, so the
+  // prefetched registers are never copied.
+  auto after_step = [&](uint32_t k) {
     if constexpr (kRowsSyncEvery > 0) {
       if (k % kRowsSyncEvery == kRowsSyncEvery - 1) __syncthreads();
     }
+  };
+  const uint32_t steps = (nchunks + nwaves - 1) / nwaves;
+  Two bufa = load(first);
+  uint32_t k = 0;
+  for (; k + 1 < steps; k += 2) {
+    const uint32_t ch = first + k * nwaves;
+    const Two bufb = prefetch(ch + nwaves);
+    if (ch < nchunks) process(ch, bufa);
+    after_step(k);
+    bufa = prefetch(ch + 2u * nwaves);
+    if (ch + nwaves < nchunks) process(ch + nwaves, bufb);
+    after_step(k + 1);
+  }
+  if (k < steps) {
+    const uint32_t ch = first + k * nwaves;
+    if (ch < nchunks) process(ch, bufa);
+    after_step(k);
   }
 
-  if (amax_out) group_max_to<kRowsWaves>(amax_out, bmax, wmax);  // uniform branch
+  if (kAmax) group_max_to<kRowsWaves>(amax_out, bmax, wmax);
   if (kErr) {
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (lane == 0) wsum[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
       double t = wsum[0];
-      for (int k = 1; k < kRowsWaves; ++k) t += wsum[k];
+      for (int k2 = 1; k2 < kRowsWaves; ++k2) t += wsum[k2];
       unsafeAtomicAdd(err_sum, t);
     }
   }
@@ -184,9 +210,14 @@ hipError_t launch_quantize_rows(const uint16_t* in, int64_t nblocks, const float
                                 uint32_t variant, uint8_t* packed, uint8_t* scales,
                                 uint8_t* selmap, double* err_sum, uint32_t* amax_out,
                                 hipStream_t s, Events ev) {
-#define NVFP4_ROWS_CASE(v) \
-  case v:                  \
-    return launch_rows_v<v>(in, nblocks, gscale, packed, scales, selmap, err_sum, amax_out, s, ev);
+  if (amax_out) variant |= kVarAmax;
+#define NVFP4_ROWS_CASE(v)                                                                       \
+  case v:                                                                                        \
+    return launch_rows_v<v>(in, nblocks, gscale, packed, scales, selmap, err_sum, amax_out, s,  \
+                            ev);                                                                 \
+  case v | kVarAmax:                                                                             \
+    return launch_rows_v<v | kVarAmax>(in, nblocks, gscale, packed, scales, selmap, err_sum,     \
+                                       amax_out, s, ev);
   switch (variant) {
     NVFP4_ROWS_CASE(0)
     NVFP4_ROWS_CASE(1)

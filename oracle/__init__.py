@@ -76,6 +76,9 @@ def lib():
         L.nvfp4o_quantize.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, P, P, P, P, P]
         L.nvfp4o_quantize.restype = ctypes.c_int
+        L.nvfp4o_quantize_mt.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, P, P, P, P, P]
+        L.nvfp4o_quantize_mt.restype = ctypes.c_int
         L.nvfp4o_dequantize.argtypes = [P, P, ctypes.c_float, i64, i64, ctypes.c_int,
                                         ctypes.c_int, P]
         L.nvfp4o_dequantize.restype = ctypes.c_int
@@ -205,6 +208,30 @@ def quantize(x_bf16, block_axis, mode, rule, gscale=None, want_selmap=True, want
         "selmap": selmap,
         "err_sum": float(err[0]) if want_err else None,
     }
+
+
+def quantize_mt(x_bf16, mode, rule, threads, gscale=None):
+    """quantize(x, AXIS_COLS, ...) run on `threads` host threads (the CPU
+    baseline's driver); bit-identical outputs."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    n_packed, n_scales, n_sel = output_shapes(rows, cols, AXIS_COLS)
+    packed = np.zeros(n_packed, np.uint8)
+    scales = np.zeros(n_scales, np.uint8)
+    selmap = np.zeros(n_sel, np.uint8)
+    err = np.zeros(1, np.float64)
+    g = np.zeros(1, np.float32)
+    given = 0
+    if gscale is not None:
+        g[0] = np.float32(gscale)
+        given = 1
+    st = lib().nvfp4o_quantize_mt(_ptr(x), rows, cols, int(mode), int(rule), int(threads),
+                                  given, _ptr(g), _ptr(packed), _ptr(scales), _ptr(selmap),
+                                  _ptr(err))
+    if st != 0:
+        raise ValueError(f"oracle quantize_mt failed with status {st}")
+    return {"packed": packed, "scales": scales, "gscale": np.float32(g[0]), "selmap": selmap,
+            "err_sum": float(err[0])}
 
 
 def dequantize(packed, scales, gscale, rows, cols, block_axis, out_bf16=False):

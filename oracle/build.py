@@ -8,6 +8,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "nvfp4_oracle.c")
+# The multi-threaded driver of the CPU baseline (calls the oracle's functions).
+SRC_MT = os.path.join(HERE, "nvfp4_oracle_mt.c")
 LIB = os.path.join(HERE, "libnvfp4_oracle.so")
 
 CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-Wall", "-Wextra"]
@@ -20,7 +22,7 @@ SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefin
 
 def build(extra_flags=(), out=LIB):
     """Compile the oracle into a shared library; returns its path."""
-    cmd = ["gcc", *CFLAGS, *extra_flags, "-shared", "-o", out, SRC, "-lm"]
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-pthread", "-shared", "-o", out, SRC, SRC_MT, "-lm"]
     subprocess.run(cmd, check=True, cwd=HERE)
     return out
 

@@ -57,6 +57,13 @@ void nvfp4o_quantize_block(const float x[16], float g, int mode, int rule, nvfp4
 int nvfp4o_quantize(const uint16_t* x, int64_t rows, int64_t cols, int block_axis, int mode,
                     int rule, int gscale_given, float* gscale, uint8_t* packed, uint8_t* scales,
                     uint8_t* selmap, double* err_sum);
+/* nvfp4o_quantize (blocks along rows, AXIS_COLS) on `threads` host threads:
+ * amax reduced over slices first, then rows split into ranges of a multiple
+ * of 8 rows.  Bit-identical outputs; err_sum adds the ranges in order.
+ * (nvfp4_oracle_mt.c, for the CPU baseline.) */
+int nvfp4o_quantize_mt(const uint16_t* x, int64_t rows, int64_t cols, int mode, int rule,
+                       int threads, int gscale_given, float* gscale, uint8_t* packed,
+                       uint8_t* scales, uint8_t* selmap, double* err_sum);
 int nvfp4o_dequantize(const uint8_t* packed, const uint8_t* scales, float g, int64_t rows,
                       int64_t cols, int block_axis, int out_bf16, void* out);
 void nvfp4o_channel_absmax(const uint16_t* x, int64_t rows, int64_t cols, float* absmax);
