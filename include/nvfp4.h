@@ -35,7 +35,9 @@
  *
  * Conventions shared by every call:
  *   - Every pointer is caller-owned DEVICE memory (e.g. torch tensors); the
- *     library allocates nothing and keeps no pointer after returning.
+ *     library allocates nothing and keeps no pointer after returning.  One
+ *     exception: nvfp4_gemm_splitk_noalloc uses a fixed scratch array the
+ *     library holds on each device it runs on.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued on it; no call synchronizes the host.
  *   - Arguments are checked before any HIP call, in the order null pointers,
@@ -44,7 +46,9 @@
  *     faults surface at the caller's next synchronization.
  *   - Tensors are row-major [rows][cols] bf16 bit patterns.  Non-finite
  *     inputs are outside the contract.
- *   - Calls on different streams may run concurrently; they share no state.
+ *   - Calls on different streams may run concurrently; they share no state
+ *     (nvfp4_gemm_splitk_noalloc aside: its calls share the device's
+ *     scratch, so calls of it that overlap in time on one device race).
  *   - Alignment: bf16 inputs and dequantized outputs 16 bytes; packed codes
  *     and the selection bitmap 4 bytes; err_sum 8 bytes; scalars 4 bytes.
  *
@@ -73,7 +77,8 @@ typedef enum nvfp4_status {
   NVFP4_ERR_SHAPE = 3, /* non-positive extent, or block-axis extent % 16 != 0 */
   NVFP4_ERR_ALIGN = 4, /* a pointer violates the alignment listed above      */
   NVFP4_ERR_HIP = 5,   /* a kernel launch failed                            */
-  NVFP4_ERR_ALIAS = 6  /* an output aliases an input it must not overwrite  */
+  NVFP4_ERR_ALIAS = 6, /* an output aliases an input it must not overwrite  */
+  NVFP4_ERR_SCRATCH = 7 /* more scratch needed than the library's fixed buffer */
 } nvfp4_status;
 
 enum { NVFP4_AXIS_ROWS = 0, NVFP4_AXIS_COLS = 1 };
@@ -325,6 +330,31 @@ nvfp4_status nvfp4_gemm_splitk(const uint8_t* a_packed, const uint8_t* a_scales,
                                const uint8_t* b_scales, const float* b_gscale, int64_t m,
                                int64_t n, int64_t k, int splits, int out_dtype, void* out,
                                float* workspace, int64_t workspace_floats, void* stream);
+
+/* nvfp4_gemm_splitk for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same product, kernels and result -- bit for bit that of
+ * nvfp4_gemm_splitk with the same split count -- with the per-range sums
+ * kept in a scratch buffer the library owns instead of a caller workspace.
+ *   The scratch is a fixed device array of 2^23 fp32 values (32 MiB) that
+ *     every device the library runs on holds until the process ends; its
+ *     address on a device is looked up on the first call made with that
+ *     device current.  splits * m * n must be at most 2^23
+ *     (NVFP4_ERR_SCRATCH otherwise, before any HIP call).  The call itself
+ *     allocates nothing.
+ *   Every call on a device uses that device's one array, and the array
+ *     keeps the last call's sums (each call overwrites every value it reads,
+ *     so nothing needs clearing).  Calls that overlap in time on one device
+ *     -- on different streams, or from different host threads without
+ *     ordering -- race on it and give wrong results; order them on one
+ *     stream, or use nvfp4_gemm_splitk with separate workspaces.
+ *   Other arguments, checks (those of the workspace aside), layouts and the
+ *   error bound: as nvfp4_gemm_splitk. */
+nvfp4_status nvfp4_gemm_splitk_noalloc(const uint8_t* a_packed, const uint8_t* a_scales,
+                                       const float* a_gscale, const uint8_t* b_packed,
+                                       const uint8_t* b_scales, const float* b_gscale, int64_t m,
+                                       int64_t n, int64_t k, int splits, int out_dtype,
+                                       void* out, void* stream);
 
 /* Split count suggested for an m x n x k nvfp4_gemm_splitk on the current
  * device: the count with the lowest time under a model of the launch

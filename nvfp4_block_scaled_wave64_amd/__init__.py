@@ -30,7 +30,9 @@ FLAG_STATS_ACCUMULATE = 4
 FLAG_RESIDUAL_DUPLICATE = 8
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_ENUM", 3: "NVFP4_ERR_SHAPE",
-          4: "NVFP4_ERR_ALIGN", 5: "NVFP4_ERR_HIP", 6: "NVFP4_ERR_ALIAS"}
+          4: "NVFP4_ERR_ALIGN", 5: "NVFP4_ERR_HIP", 6: "NVFP4_ERR_ALIAS", 7: "NVFP4_ERR_SCRATCH"}
+# Largest splits * M * N of nvfp4_gemm_splitk_noalloc (its fixed scratch).
+NOALLOC_SCRATCH_FLOATS = 1 << 23
 
 # Every symbol the public headers declare, with its ctypes signature.
 _P, _I64, _I, _U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
@@ -53,6 +55,8 @@ SIGNATURES = {
     "nvfp4_gemm": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P], _I),
     "nvfp4_gemm_splitk": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, _P, _I64, _P],
                           _I),
+    "nvfp4_gemm_splitk_noalloc": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, _P],
+                                  _I),
     "nvfp4_gemm_splits_hint": ([_I64, _I64, _I64], _I),
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
     "nvfp4v_e2m1_encode_sweep": ([_U32, _I64, _P, _P], _I),
@@ -460,6 +464,35 @@ def gemm(a, b, out_dtype=torch.float32, out=None, stream=None, splits=None, work
                                  N, K, splits, code, _ptr(out), _ptr(workspace),
                                  workspace.numel(), _stream(stream))
     _check(st, "nvfp4_gemm_splitk")
+    return out
+
+
+def gemm_splitk_noalloc(a, b, splits, out, stream=None):
+    """The split product of gemm(a, b, splits=splits) through
+    nvfp4_gemm_splitk_noalloc, whose per-range sums live in the library's
+    fixed device scratch (at most NOALLOC_SCRATCH_FLOATS = splits * M * N):
+    no workspace, and the call allocates nothing.  `out` ([M][N] float32 or
+    bfloat16, preallocated) is written and returned.  Calls that overlap in
+    time on one device race on the scratch."""
+    pa, pb = a["packed"], b["packed"]
+    if pa.dim() != 2 or pb.dim() != 2 or pa.shape[1] != pb.shape[1]:
+        raise ValueError("operands must be [rows][K/2] with the same K")
+    M, N, K = pa.shape[0], pb.shape[0], pa.shape[1] * 2
+    dev = pa.device
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out must be a preallocated float32 or bfloat16 tensor")
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    pa = _need(pa, M * K // 2, torch.uint8, dev, "a['packed']")
+    sa = _need(a["scales"], M * K // 16, torch.uint8, dev, "a['scales']")
+    ga = _need(a["gscale"], 1, torch.float32, dev, "a['gscale']")
+    pb = _need(pb, N * K // 2, torch.uint8, dev, "b['packed']")
+    sb = _need(b["scales"], N * K // 16, torch.uint8, dev, "b['scales']")
+    gb = _need(b["gscale"], 1, torch.float32, dev, "b['gscale']")
+    out = _need(out, M * N, out.dtype, dev, "out")
+    st = lib().nvfp4_gemm_splitk_noalloc(_ptr(pa), _ptr(sa), _ptr(ga), _ptr(pb), _ptr(sb),
+                                         _ptr(gb), M, N, K, int(splits), code, _ptr(out),
+                                         _stream(stream))
+    _check(st, "nvfp4_gemm_splitk_noalloc")
     return out
 
 

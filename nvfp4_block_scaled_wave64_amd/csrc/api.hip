@@ -1,6 +1,7 @@
 // api.hip -- the C ABI (include/nvfp4.h): argument checks, then kernel
 // launches on the caller's stream.  No allocation, no host synchronization.
 #include <atomic>
+#include <mutex>
 
 #include "nvfp4.h"
 #include "nvfp4_kernels.h"
@@ -60,6 +61,8 @@ const char* nvfp4_status_string(nvfp4_status s) {
     case NVFP4_ERR_ALIGN: return "misaligned pointer";
     case NVFP4_ERR_HIP: return "HIP kernel launch failed";
     case NVFP4_ERR_ALIAS: return "an output aliases an input it must not overwrite";
+    case NVFP4_ERR_SCRATCH:
+      return "the product needs more than the library's fixed scratch (splits * m * n > 2^23)";
   }
   return "unknown status";
 }
@@ -435,34 +438,110 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_packed, const uint8_t* a_scales, const 
                                        static_cast<hipStream_t>(stream), nvfp4::Events{}));
 }
 
-nvfp4_status nvfp4_gemm_splitk(const uint8_t* a_packed, const uint8_t* a_scales,
+}  // extern "C"
+
+namespace {
+
+// Checks of nvfp4_gemm_splitk, in the header's order: null pointers, enums,
+// shape, alignment, aliasing.  With workspace == nullptr and
+// caller_workspace false (the allocation-free variant, whose scratch is the
+// library's own) the workspace checks are skipped.
+nvfp4_status check_gemm_splitk(const uint8_t* a_packed, const uint8_t* a_scales,
                                const float* a_gscale, const uint8_t* b_packed,
                                const uint8_t* b_scales, const float* b_gscale, int64_t m,
                                int64_t n, int64_t k, int splits, int out_dtype, void* out,
-                               float* workspace, int64_t workspace_floats, void* stream) {
+                               const float* workspace, int64_t workspace_floats,
+                               bool caller_workspace) {
   if (!a_packed || !a_scales || !a_gscale || !b_packed || !b_scales || !b_gscale || !out ||
-      !workspace)
+      (caller_workspace && !workspace))
     return NVFP4_ERR_NULL;
   if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_ENUM;
   if (!gemm_shape_ok(m, n, k)) return NVFP4_ERR_SHAPE;
   const int64_t nchunks = (k + 127) / 128;
   if (splits < 1 || splits > nvfp4::kGemmMaxSplits || splits > nchunks) return NVFP4_ERR_SHAPE;
   const int64_t ws_floats = (int64_t)splits * m * n;
-  if (workspace_floats < ws_floats) return NVFP4_ERR_SHAPE;
+  if (caller_workspace && workspace_floats < ws_floats) return NVFP4_ERR_SHAPE;
   const int64_t esz = out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
   if (!aligned(a_packed, 4) || !aligned(b_packed, 4) || !aligned(a_gscale, 4) ||
-      !aligned(b_gscale, 4) || !aligned(out, (uintptr_t)esz) || !aligned(workspace, 4))
+      !aligned(b_gscale, 4) || !aligned(out, (uintptr_t)esz) ||
+      (caller_workspace && !aligned(workspace, 4)))
     return NVFP4_ERR_ALIGN;
   const int64_t out_bytes = m * n * esz;
   const void* ins[7] = {a_packed, a_scales, a_gscale, b_packed, b_scales, b_gscale, out};
   const int64_t in_bytes[7] = {m * k / 2, m * k / 16, 4, n * k / 2, n * k / 16, 4, out_bytes};
   for (int i = 0; i < 7; ++i) {
     if (i < 6 && overlap(out, out_bytes, ins[i], in_bytes[i])) return NVFP4_ERR_ALIAS;
-    if (overlap(workspace, ws_floats * 4, ins[i], in_bytes[i])) return NVFP4_ERR_ALIAS;
+    if (caller_workspace && overlap(workspace, ws_floats * 4, ins[i], in_bytes[i]))
+      return NVFP4_ERR_ALIAS;
   }
+  return NVFP4_OK;
+}
+
+// Fixed scratch of nvfp4_gemm_splitk_noalloc: the per-range fp32 sums of
+// one product, at most kScratchFloats of them (32 MiB), held by every device
+// the library runs on until the process ends.  In host code `scratch` only
+// names the variable; its device address (one per device) comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr int64_t kScratchFloats = int64_t(8) << 20;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call for that device).
+nvfp4_status scratch_on_current_device(float** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NVFP4_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_gemm_splitk(const uint8_t* a_packed, const uint8_t* a_scales,
+                               const float* a_gscale, const uint8_t* b_packed,
+                               const uint8_t* b_scales, const float* b_gscale, int64_t m,
+                               int64_t n, int64_t k, int splits, int out_dtype, void* out,
+                               float* workspace, int64_t workspace_floats, void* stream) {
+  const nvfp4_status st =
+      check_gemm_splitk(a_packed, a_scales, a_gscale, b_packed, b_scales, b_gscale, m, n, k,
+                        splits, out_dtype, out, workspace, workspace_floats, true);
+  if (st != NVFP4_OK) return st;
   return hip_status(nvfp4::launch_gemm_splitk(a_packed, a_scales, a_gscale, b_packed, b_scales,
                                               b_gscale, m, n, k, (uint32_t)splits,
                                               out_dtype == NVFP4_OUT_BF16, out, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_gemm_splitk_noalloc(const uint8_t* a_packed, const uint8_t* a_scales,
+                                       const float* a_gscale, const uint8_t* b_packed,
+                                       const uint8_t* b_scales, const float* b_gscale, int64_t m,
+                                       int64_t n, int64_t k, int splits, int out_dtype,
+                                       void* out, void* stream) {
+  // The checks of nvfp4_gemm_splitk without the workspace ones (the
+  // library's scratch cannot overlap caller memory), then the size limit,
+  // all before any HIP call.
+  nvfp4_status st =
+      check_gemm_splitk(a_packed, a_scales, a_gscale, b_packed, b_scales, b_gscale, m, n, k,
+                        splits, out_dtype, out, nullptr, 0, false);
+  if (st != NVFP4_OK) return st;
+  if ((int64_t)splits * m * n > kScratchFloats) return NVFP4_ERR_SCRATCH;
+  float* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != NVFP4_OK) return st;
+  return hip_status(nvfp4::launch_gemm_splitk(a_packed, a_scales, a_gscale, b_packed, b_scales,
+                                              b_gscale, m, n, k, (uint32_t)splits,
+                                              out_dtype == NVFP4_OUT_BF16, out, ws,
                                               static_cast<hipStream_t>(stream)));
 }
 

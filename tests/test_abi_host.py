@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
@@ -39,9 +39,10 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = nv.lib()
-    for s in range(7):
+    for s in range(8):
         assert L.nvfp4_status_string(s)
     assert b"alias" in L.nvfp4_status_string(6)
+    assert b"scratch" in L.nvfp4_status_string(7)
     assert b"unknown" in L.nvfp4_status_string(99)
 
 
@@ -326,3 +327,36 @@ def test_gemm_splits_hint_rejects_bad_shapes():
     assert L.nvfp4_gemm_splits_hint(0, 16, 16) == 0
     assert L.nvfp4_gemm_splits_hint(16, 16, 40) == 0
     assert L.nvfp4_gemm_splits_hint(16, (1 << 24) + 1, 16) == 0
+
+
+FAR = {name: ctypes.c_void_p((i + 1) << 32)
+       for i, name in enumerate(("pa", "sa", "ga", "pb", "sb", "gb", "out"))}
+
+
+def gn(**kw):
+    args = dict(pa=A, sa=B, ga=C, pb=D, sb=E, gb=F, m=32, n=32, k=256, splits=2,
+                dtype=nv.OUT_F32, out=G)
+    args.update(kw)
+    return nv.lib().nvfp4_gemm_splitk_noalloc(args["pa"], args["sa"], args["ga"], args["pb"],
+                                              args["sb"], args["gb"], args["m"], args["n"],
+                                              args["k"], args["splits"], args["dtype"],
+                                              args["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pa=None), 1), (dict(gb=None), 1), (dict(out=None), 1),
+    (dict(dtype=3), 2),
+    (dict(m=0), 3), (dict(k=40), 3), (dict(splits=0), 3), (dict(splits=3), 3),
+    (dict(splits=65, k=64 * 128), 3),
+    (dict(out=ctypes.c_void_p(0x70002)), 4), (dict(pb=ctypes.c_void_p(0x40001)), 4),
+    (dict(out=D), 6), (dict(out=A), 6),
+    # splits * m * n above the fixed scratch of 2^23 floats, checked before any
+    # HIP call (operands placed 4 GiB apart so that they do not overlap)
+    (dict(FAR, m=4097, n=1024, k=1024, splits=2), 7),
+    (dict(FAR, m=1, n=1 << 22, k=512, splits=3), 7),
+])
+def test_gemm_splitk_noalloc_rejects(kw, status):
+    """nvfp4_gemm_splitk_noalloc: nvfp4_gemm_splitk's checks without the
+    workspace ones, plus the scratch limit (NVFP4_ERR_SCRATCH when
+    splits * m * n > 2^23), all before any HIP call."""
+    assert gn(**kw) == status
