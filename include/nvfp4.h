@@ -130,7 +130,10 @@ nvfp4_status nvfp4_quantize(const uint16_t* in_bf16, int64_t rows, int64_t cols,
  *     in which case the sum is added to its current value (e.g. a total over
  *     several tensors, or a value the caller zeroed on the same stream).
  *     Divide by rows*cols for the per-tensor MSE / MAE (by the number of
- *     blocks for the mean block maximum error). */
+ *     blocks for the mean block maximum error).
+ *   Outputs -- packed_out, scales_out, gscale_inout, selmap_out,
+ *   err_sum_out -- must not overlap the input or each other
+ *   (NVFP4_ERR_ALIAS). */
 nvfp4_status nvfp4_quantize_ex(const uint16_t* in_bf16, int64_t rows, int64_t cols,
                                int block_axis, int mode, int rule, uint32_t flags,
                                uint8_t* packed_out, uint8_t* scales_out, float* gscale_inout,
@@ -165,7 +168,8 @@ nvfp4_status nvfp4_quantize_ex_timed(const uint16_t* in_bf16, int64_t rows, int6
  *   selmap_r / selmap_c and err_sum_r / err_sum_c: both or neither
  *     (NVFP4_ERR_NULL otherwise); the error sums are zeroed first unless
  *     flags has NVFP4_FLAG_ERR_ACCUMULATE.
- *   flags, gscale_inout, mode, rule, alignment: as nvfp4_quantize_ex. */
+ *   flags, gscale_inout, mode, rule, alignment: as nvfp4_quantize_ex.
+ *   No output may overlap the input or another output (NVFP4_ERR_ALIAS). */
 nvfp4_status nvfp4_quantize_dual(const uint16_t* in_bf16, int64_t rows, int64_t cols, int mode,
                                  int rule, uint32_t flags, uint8_t* packed_r, uint8_t* scales_r,
                                  uint8_t* packed_c, uint8_t* scales_c, float* gscale_inout,
@@ -197,7 +201,9 @@ nvfp4_status nvfp4_quantize_delayed(const uint16_t* in_bf16, int64_t rows, int64
  * out_dtype NVFP4_OUT_F32 writes float, NVFP4_OUT_BF16 writes the bf16
  * (round to nearest even) of it.  `out` is [rows][cols] in the caller's
  * layout for either block axis; packed/scales are laid out as produced by
- * nvfp4_quantize with the same block_axis. */
+ * nvfp4_quantize with the same block_axis.  A scale byte 0x7F (the E4M3
+ * NaN code, never written by the quantizers themselves) decodes to NaN.
+ * out must not overlap packed, scales or gscale (NVFP4_ERR_ALIAS). */
 nvfp4_status nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, const float* gscale,
                               int64_t rows, int64_t cols, int block_axis, int out_dtype,
                               void* out, void* stream);
@@ -219,6 +225,17 @@ nvfp4_status nvfp4_channel_order(const uint16_t* in_bf16, int64_t rows, int64_t 
                                  uint32_t flags, float* absmax_inout, int32_t* perm_out,
                                  void* stream);
 
+/* Whether a channel order is a permutation of [0, cols): writes to *bad_out
+ * (device uint32) the number of entries that keep it from being one, i.e.
+ * cols minus the number of distinct values of perm inside [0, cols) -- 0
+ * for a valid order.  The orders of the "ARCQuant" summary (gist.science
+ * 2601.07475, "Methodology") reorder the channels, so an order given to
+ * nvfp4_quantize_residual is expected to be a permutation.
+ *   perm: cols int32 (device); cols in [1, 32768].
+ *   bad_out must not overlap perm (NVFP4_ERR_ALIAS). */
+nvfp4_status nvfp4_check_order(const int32_t* perm, int64_t cols, uint32_t* bad_out,
+                               void* stream);
+
 /* Outlier channels, step 2 (per step): two-stage quantization with
  * reordered channels ("ARCQuant" summary, gist.science 2601.07475,
  * "Methodology": the leading channels get a residual stage, x minus its
@@ -232,9 +249,15 @@ nvfp4_status nvfp4_channel_order(const uint16_t* in_bf16, int64_t rows, int64_t 
  *   packed_out [rows][W/2] and scales_out [rows][W/16], layouts as
  *   nvfp4_quantize; dequantizing them as a [rows][W] tensor and adding
  *   column cols + k to column k (k < nres) reconstructs the reordered x.
- *   perm: cols int32 (device), normally nvfp4_channel_order's; any entry is
- *     allowed (a gather), and entries outside [0, cols) read channel
- *     cols - 1.
+ *   perm: cols int32 (device), normally nvfp4_channel_order's, i.e. a
+ *     permutation of the channels ("Methodology": channels are reordered).
+ *     Entries inside [0, cols) are gathered as given (a repeated channel is
+ *     read twice; nvfp4_check_order tells whether perm is a permutation).
+ *     If any entry lies outside [0, cols), the call fails on the device:
+ *     every output scale byte is written as 0x7F (the E4M3 NaN code) and
+ *     every code as 0, so that nvfp4_dequantize of the result, and any
+ *     product over it, is NaN rather than plausible numbers (the host call
+ *     cannot see device data; check perm first where that matters).
  *   nres: residual channels, a multiple of 16 in [0, cols].
  *   cols: a positive multiple of 16, at most 32768.
  *   flags: 0 (g computed from the tensor amax as nvfp4_quantize does and

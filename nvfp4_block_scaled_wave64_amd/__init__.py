@@ -49,6 +49,7 @@ SIGNATURES = {
                             _I),
     "nvfp4_dequantize": ([_P, _P, _P, _I64, _I64, _I, _I, _P, _P], _I),
     "nvfp4_channel_order": ([_P, _I64, _I64, _U32, _P, _P, _P], _I),
+    "nvfp4_check_order": ([_P, _I64, _P, _P], _I),
     "nvfp4_quantize_residual": ([_P, _I64, _I64, _P, _I64, _I, _I, _U32, _P, _P, _P, _P], _I),
     "nvfp4_rmsnorm_quantize_residual": ([_P, _I64, _I64, _P, ctypes.c_float, _P, _I64, _I, _I,
                                          _U32, _P, _P, _P, _P, _P], _I),
@@ -326,6 +327,20 @@ def channel_order(x, absmax=None, accumulate=False, perm=None, stream=None):
     _check(lib().nvfp4_channel_order(_ptr(x), rows, cols, flags, _ptr(absmax), _ptr(perm),
                                      _stream(stream)), "nvfp4_channel_order")
     return absmax, perm
+
+
+def check_order(perm, stream=None):
+    """nvfp4_check_order: the number of entries keeping the int32 device
+    tensor `perm` from being a permutation of [0, len(perm)) (0: a valid
+    channel order), as a 1-element int32 device tensor holding the call's
+    uint32 count (read it after a synchronization)."""
+    if not isinstance(perm, torch.Tensor) or perm.dim() != 1:
+        raise ValueError("perm must be a 1-D int32 device tensor")
+    perm = _need(perm, perm.numel(), torch.int32, perm.device, "perm")
+    bad = torch.empty(1, dtype=torch.int32, device=perm.device)
+    _check(lib().nvfp4_check_order(_ptr(perm), perm.numel(), _ptr(bad), _stream(stream)),
+           "nvfp4_check_order")
+    return bad
 
 
 def quantize_residual(x, perm, nres, mode=MODE_4OVER6, rule=RULE_MSE, gscale=None, out=None,

@@ -1,6 +1,7 @@
 // api.hip -- the C ABI (include/nvfp4.h): argument checks, then kernel
 // launches on the caller's stream.  No allocation, no host synchronization.
 #include <atomic>
+#include <initializer_list>
 #include <mutex>
 
 #include "nvfp4.h"
@@ -34,6 +35,27 @@ nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP
 bool overlap(const void* a, int64_t an, const void* b, int64_t bn) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + (uintptr_t)bn && y < x + (uintptr_t)an;
+}
+
+// A byte range of an argument (a null pointer or an empty range overlaps
+// nothing).
+struct Span {
+  const void* p;
+  int64_t bytes;
+};
+
+// Whether any output range overlaps an input range or another output range.
+// Everything a call writes, or reads while other workgroups write (a tensor
+// scale, an accumulator), counts as an output here.
+bool outputs_overlap(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    if (!o->p || o->bytes <= 0) continue;
+    for (const Span& i : ins)
+      if (i.p && i.bytes > 0 && overlap(o->p, o->bytes, i.p, i.bytes)) return true;
+    for (auto q = o + 1; q != outs.end(); ++q)
+      if (q->p && q->bytes > 0 && overlap(o->p, o->bytes, q->p, q->bytes)) return true;
+  }
+  return false;
 }
 
 // Largest supported element count: keeps every byte offset and the bitmap
@@ -108,8 +130,13 @@ nvfp4_status quantize_impl(const uint16_t* in_bf16, int64_t rows, int64_t cols, 
   if (!aligned(in_bf16, 16) || !aligned(packed_out, 4) || !aligned(gscale_inout, 4) ||
       !aligned(selmap_out, 4) || !aligned(err_sum_out, 8) || !aligned(amax_out, 4))
     return NVFP4_ERR_ALIGN;
-  if (amax_out && reinterpret_cast<void*>(amax_out) == reinterpret_cast<void*>(gscale_inout))
-    return NVFP4_ERR_ALIAS;
+  {
+    const int64_t n = rows * cols, nb = n / 16;
+    if (outputs_overlap({{packed_out, n / 2}, {scales_out, nb}, {gscale_inout, 4},
+                         {selmap_out, (nb + 7) / 8}, {err_sum_out, 8}, {amax_out, 4}},
+                        {{in_bf16, n * 2}}))
+      return NVFP4_ERR_ALIAS;
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool given = (flags & NVFP4_FLAG_GSCALE_GIVEN) != 0;
@@ -180,6 +207,14 @@ nvfp4_status nvfp4_quantize_dual(const uint16_t* in_bf16, int64_t rows, int64_t 
       !aligned(gscale_inout, 4) || !aligned(selmap_r, 4) || !aligned(selmap_c, 4) ||
       !aligned(err_sum_r, 8) || !aligned(err_sum_c, 8))
     return NVFP4_ERR_ALIGN;
+  {
+    const int64_t n = rows * cols, nb = n / 16;
+    if (outputs_overlap({{packed_r, n / 2}, {scales_r, nb}, {packed_c, n / 2}, {scales_c, nb},
+                         {gscale_inout, 4}, {selmap_r, (nb + 7) / 8}, {selmap_c, (nb + 7) / 8},
+                         {err_sum_r, 8}, {err_sum_c, 8}},
+                        {{in_bf16, n * 2}}))
+      return NVFP4_ERR_ALIAS;
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool given = (flags & NVFP4_FLAG_GSCALE_GIVEN) != 0;
@@ -259,6 +294,12 @@ nvfp4_status nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, cons
   const nvfp4_status shape = check_shape(rows, cols, block_axis);
   if (shape != NVFP4_OK) return shape;
   if (!aligned(packed, 4) || !aligned(gscale, 4) || !aligned(out, 16)) return NVFP4_ERR_ALIGN;
+  {
+    const int64_t n = rows * cols;
+    const int64_t esz = out_dtype == NVFP4_OUT_BF16 ? 2 : 4;
+    if (outputs_overlap({{out, n * esz}}, {{packed, n / 2}, {scales, n / 16}, {gscale, 4}}))
+      return NVFP4_ERR_ALIAS;
+  }
   return hip_status(nvfp4::launch_dequantize(packed, scales, gscale, rows, cols, block_axis,
                                              out_dtype == NVFP4_OUT_BF16, out,
                                              static_cast<hipStream_t>(stream)));
@@ -267,6 +308,16 @@ nvfp4_status nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, cons
 }  // extern "C"
 
 extern "C" {
+
+nvfp4_status nvfp4_check_order(const int32_t* perm, int64_t cols, uint32_t* bad_out,
+                               void* stream) {
+  if (!perm || !bad_out) return NVFP4_ERR_NULL;
+  if (cols <= 0 || cols > nvfp4::kResidualMaxCols) return NVFP4_ERR_SHAPE;
+  if (!aligned(perm, 4) || !aligned(bad_out, 4)) return NVFP4_ERR_ALIGN;
+  if (overlap(bad_out, 4, perm, cols * 4)) return NVFP4_ERR_ALIAS;
+  return hip_status(nvfp4::launch_check_order(perm, cols, bad_out,
+                                              static_cast<hipStream_t>(stream)));
+}
 
 nvfp4_status nvfp4_channel_order(const uint16_t* in_bf16, int64_t rows, int64_t cols,
                                  uint32_t flags, float* absmax_inout, int32_t* perm_out,

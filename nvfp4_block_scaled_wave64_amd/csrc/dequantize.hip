@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kRowsThreads) void dequantize_rows_kernel(
   for (uint32_t ch = first; ch < nchunks; ch += nwaves) {
     const In cur = nxt;
     nxt = load(ch + nwaves);
-    const float d = e4m3_decode(cur.s & 0xFFu) * g;
+    const float d = block_decode_scale(cur.s & 0xFFu, g);
     float v[16];
     e2m1_decode8(cur.c.x, v);
     e2m1_decode8(cur.c.y, v + 8);
@@ -206,8 +206,8 @@ __global__ __launch_bounds__(kDtThreads) void dequantize_cols_kernel(
       const int cp = t & 31, b = t >> 5;
       float v0[16], v1[16];
       const int ca = 2 * cp, cb = 2 * cp + 1;
-      const float da = e4m3_decode((sc[ca][b >> 2] >> (8 * (b & 3))) & 0xFFu) * g;
-      const float db = e4m3_decode((sc[cb][b >> 2] >> (8 * (b & 3))) & 0xFFu) * g;
+      const float da = block_decode_scale((sc[ca][b >> 2] >> (8 * (b & 3))) & 0xFFu, g);
+      const float db = block_decode_scale((sc[cb][b >> 2] >> (8 * (b & 3))) & 0xFFu, g);
       e2m1_decode8(cw[ca][2 * b], v0);
       e2m1_decode8(cw[ca][2 * b + 1], v0 + 8);
       e2m1_decode8(cw[cb][2 * b], v1);

@@ -56,6 +56,14 @@ __device__ __forceinline__ float e4m3_decode(uint32_t S) {
   return __uint_as_float(S << 20) * 0x1p120f;
 }
 
+// Decode multiplier dec(S) * g of a stored scale byte S (0x00..0x7E as the
+// quantizers write them).  0x7F, the E4M3FN NaN code, gives NaN: the
+// outlier-channel path writes it for an invalid channel order, and the
+// result must not read as numbers.
+__device__ __forceinline__ float block_decode_scale(uint32_t S, float g) {
+  return S == 0x7Fu ? __builtin_nanf("") : e4m3_decode(S) * g;
+}
+
 // E4M3 bytes of two block scales s0, s1 (s0 in bits 0-7, s1 in bits 8-15):
 // round to nearest even, saturating at 448; NaN and non-positive inputs give
 // 0.  Clamping to [0, 448] first makes the gfx950 conversion

@@ -114,6 +114,9 @@ hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, const
 // tensors).
 hipError_t launch_channel_absmax(const uint16_t* in, int64_t rows, int64_t cols,
                                  uint32_t* absmax_bits, hipStream_t s);
+// *bad = the number of entries keeping perm from being a permutation of
+// [0, cols) (cols - distinct in-range values); cols <= kResidualMaxCols.
+hipError_t launch_check_order(const int32_t* perm, int64_t cols, uint32_t* bad, hipStream_t s);
 // perm[k] = the channel of rank k (largest max first, ties by index).
 hipError_t launch_channel_rank(const uint32_t* absmax_bits, int64_t cols, int32_t* perm,
                                hipStream_t s);

@@ -134,6 +134,52 @@ __global__ __launch_bounds__(kRankThreads) void channel_rank_kernel(
   }
 }
 
+// ----------------------------------------------------------- check order --
+
+// *bad = cols - (number of distinct values of perm inside [0, cols)): 0
+// exactly when perm is a permutation of the channels.  One workgroup; an LDS
+// bitmap marks the values seen.
+constexpr int kCheckThreads = 1024;
+
+__global__ __launch_bounds__(kCheckThreads) void check_order_kernel(
+    const int32_t* __restrict__ perm, uint32_t cols, uint32_t* __restrict__ bad) {
+  __shared__ uint32_t seen[32768 / 32];
+  __shared__ uint32_t part[kCheckThreads / 64];
+  const uint32_t words = (cols + 31u) / 32u;
+  for (uint32_t w = threadIdx.x; w < words; w += kCheckThreads) seen[w] = 0u;
+  __syncthreads();
+  for (uint32_t c = threadIdx.x; c < cols; c += kCheckThreads) {
+    const uint32_t v = (uint32_t)perm[c];
+    if (v < cols) atomicOr(&seen[v >> 5], 1u << (v & 31u));
+  }
+  __syncthreads();
+  uint32_t n = 0u;
+  for (uint32_t w = threadIdx.x; w < words; w += kCheckThreads) n += __popc(seen[w]);
+  for (int off = 32; off > 0; off >>= 1) n += (uint32_t)__shfl_xor((int)n, off);
+  if ((threadIdx.x & 63u) == 0u) part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0u;
+    for (int k = 0; k < kCheckThreads / 64; ++k) t += part[k];
+    *bad = cols - t;
+  }
+}
+
+// Output rows of a call whose order has an entry outside [0, cols): every
+// scale byte is 0x7F (the E4M3 NaN code) and every code 0, so that
+// dequantizing the result, or a product over it, gives NaN instead of
+// plausible numbers.  Rows row0, row0 + stride, ... of bout blocks; the
+// threads of `team` (tid = 0 .. team - 1) share each row.
+__device__ void poison_rows(int64_t row0, int64_t stride, int64_t rows, uint32_t bout,
+                            uint32_t tid, uint32_t team, uint8_t* packed, uint8_t* scales) {
+  for (int64_t r = row0; r < rows; r += stride) {
+    for (uint32_t b = tid; b < bout; b += team) {
+      scales[r * bout + b] = 0x7Fu;
+      *reinterpret_cast<u32x2*>(packed + (r * bout + b) * 8) = u32x2{0u, 0u};
+    }
+  }
+}
+
 // -------------------------------------------------------------- quantize --
 
 // Output block j of one staged row xr (bf16 in LDS): gathers the channels
@@ -218,13 +264,24 @@ __global__ __launch_bounds__(kResThreads) void quantize_residual_kernel(
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
   // Byte offsets of the channels in a row; indices are clamped into the
-  // row, so no entry can read outside it.
-  for (uint32_t c = threadIdx.x; c < cols; c += kResThreads)
-    pm[c] = (uint16_t)(2u * std::min((uint32_t)perm[c], cols - 1u));
+  // row, so no entry can read outside it, and an order with an entry
+  // outside [0, cols) poisons the whole output (poison_rows).
+  int bad = 0;
+  for (uint32_t c = threadIdx.x; c < cols; c += kResThreads) {
+    const uint32_t v = (uint32_t)perm[c];
+    bad |= v >= cols;
+    pm[c] = (uint16_t)(2u * std::min(v, cols - 1u));
+  }
 
   const uint32_t nb = cols >> 4, nrb = nres >> 4, bout = nb + nrb;
   const uint32_t vrow = cols >> 3;
   const int64_t niter = (rows + R - 1) / R;
+  if (__syncthreads_or(bad)) {
+    for (int64_t it = blockIdx.x; it < niter; it += gridDim.x)
+      poison_rows(it * R, 1, std::min<int64_t>(rows, it * R + R), bout, threadIdx.x,
+                  kResThreads, packed, scales);
+    return;
+  }
 
   auto rows_at = [&](int64_t it) -> uint32_t {
     return (uint32_t)std::min<int64_t>((int64_t)R, rows - it * R);
@@ -483,15 +540,23 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
 
   const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
-  for (uint32_t c = threadIdx.x; c < cols; c += blockDim.x)
-    pm[c] = (uint16_t)(2u * std::min((uint32_t)perm[c], cols - 1u));
+  // Clamped byte offsets; an entry outside [0, cols) poisons the output.
+  int bad = 0;
+  for (uint32_t c = threadIdx.x; c < cols; c += blockDim.x) {
+    const uint32_t v = (uint32_t)perm[c];
+    bad |= v >= cols;
+    pm[c] = (uint16_t)(2u * std::min(v, cols - 1u));
+  }
   const uint32_t vrow = cols >> 3;
   if constexpr (kRms) stage_weight<kVpl>(w4, ra.weight, vrow);
-  __syncthreads();
 
   const uint32_t nb = cols >> 4, nrb = nres >> 4, bout = nb + nrb;
   const int64_t first = (int64_t)blockIdx.x * nwaves_g + wave;
   const int64_t stride = (int64_t)gridDim.x * nwaves_g;
+  if (__syncthreads_or(bad)) {
+    poison_rows(first, stride, rows, bout, lane, 64u, packed, scales);
+    return;
+  }
   uint32_t ymax = 0u;  // packed bf16 max |y| (kRms)
 
   auto load = [&](int64_t row, u32x4 (&buf)[kVpl]) {
@@ -573,6 +638,11 @@ hipError_t launch_channel_absmax(const uint16_t* in, int64_t rows, int64_t cols,
   splits = (rows + per - 1) / per;
   channel_absmax_kernel<<<(unsigned)(ctiles * splits), kAbsThreads, 0, s>>>(
       in, rows, (uint32_t)cols, (uint32_t)ctiles, per, absmax_bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_order(const int32_t* perm, int64_t cols, uint32_t* bad, hipStream_t s) {
+  check_order_kernel<<<1, kCheckThreads, 0, s>>>(perm, (uint32_t)cols, bad);
   return hipGetLastError();
 }
 

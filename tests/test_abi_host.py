@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
@@ -360,3 +360,64 @@ def test_gemm_splitk_noalloc_rejects(kw, status):
     workspace ones, plus the scratch limit (NVFP4_ERR_SCRATCH when
     splits * m * n > 2^23), all before any HIP call."""
     assert gn(**kw) == status
+
+
+def P(gib, off=0):
+    """A fake device address `gib` GiB up (plus off bytes), never touched."""
+    return ctypes.c_void_p((gib << 30) + off)
+
+
+# 32 x 64 tensor: input 4096 B, codes 1024 B, scales 128 B, bitmap 16 B.
+QX = dict(in_=P(1), packed=P(2), scales=P(3), g=P(4), sel=P(5), err=P(6))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(packed=P(1, 4092)), dict(scales=P(1)), dict(g=P(1, 100)), dict(sel=P(1, 4080)),
+    dict(err=P(1, 8)), dict(scales=P(2, 1020)), dict(g=P(3, 124)), dict(sel=P(2)),
+    dict(err=P(4)), dict(err=P(5, 8)),
+])
+def test_quantize_rejects_overlapping_outputs(kw):
+    """nvfp4_quantize_ex: no output (codes, scales, g, bitmap, error sum) may
+    overlap the input or another output."""
+    args = dict(QX)
+    args.update(kw)
+    assert q(**args) == 6
+
+
+def test_quantize_accepts_adjacent_outputs():
+    """Ranges that only touch are not overlaps: the checks stop at the HIP
+    launch, which a host without a GPU reports as a launch failure, not an
+    aliasing error."""
+    assert q(**dict(QX, packed=P(1, 4096), scales=P(1, 4096 + 1024))) not in (1, 2, 3, 4, 6)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(pr=P(1, 100)), dict(pc=P(2, 1000)), dict(sc=P(3, 64)), dict(g=P(5)),
+    dict(selc=P(5, 8)), dict(errr=P(10)), dict(errc=P(4)),
+])
+def test_dual_rejects_overlapping_outputs(kw):
+    args = dict(in_=P(1), pr=P(2), sr=P(3), pc=P(4), sc=P(5), g=P(6), selr=P(7), selc=P(8),
+                errr=P(9), errc=P(10))
+    args.update(kw)
+    assert du(**args) == 6
+
+
+@pytest.mark.parametrize("out,dtype,g", [(P(1, 992), 0, P(3)), (P(2, 64), 1, P(3)),
+                                         (P(3), 0, P(3)), (P(4), 0, P(4, 8188)),
+                                         (P(4), 1, P(4, 4092))])
+def test_dequantize_rejects_overlap(out, dtype, g):
+    """out (32 x 64: fp32 8192 B, bf16 4096 B) may not overlap the codes
+    (1 GiB up, 1024 B), scales (2 GiB up, 128 B) or g it reads."""
+    L = nv.lib()
+    assert L.nvfp4_dequantize(P(1), P(2), g, 32, 64, nv.AXIS_COLS, dtype, out, None) == 6
+
+
+def test_check_order_rejects():
+    L = nv.lib()
+    assert L.nvfp4_check_order(None, 16, A, None) == 1
+    assert L.nvfp4_check_order(A, 16, None, None) == 1
+    assert L.nvfp4_check_order(A, 0, B, None) == 3
+    assert L.nvfp4_check_order(A, 32769, B, None) == 3
+    assert L.nvfp4_check_order(MIS, 16, B, None) == 4
+    assert L.nvfp4_check_order(A, 16, ctypes.c_void_p(0x10002), None) == 4
+    assert L.nvfp4_check_order(A, 16, ctypes.c_void_p(0x10000 + 60), None) == 6

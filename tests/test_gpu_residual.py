@@ -147,18 +147,18 @@ def test_quantize_residual_matches_oracle(rows, cols, nres, mode, rule):
 
 
 def test_quantize_residual_given_scale_and_any_index_vector():
-    """A given tensor scale, and an index vector that is not a permutation
-    (repeated channels, entries out of range read the last channel)."""
+    """A given tensor scale, and an in-range index vector that is not a
+    permutation (repeated and missing channels): gathered as given.
+    (Entries out of range poison the output: see below.)"""
     banner("residual given scale, general index vector")
     rows, cols, nres = 50, 640, 64
     x = outlier_tensor(31, rows, cols)
     rng = np.random.default_rng(9)
     idx = rng.integers(0, cols, cols).astype(np.int32)
-    idx[:5] = [-1, cols, cols + 7, 2 ** 31 - 1, -(2 ** 31)]
-    clamped = np.where((idx < 0) | (idx >= cols), cols - 1, idx).astype(np.int32)
+    idx[:5] = [0, 0, cols - 1, cols - 1, 3]
     g = np.float32(0.0123)
     got = gpu_residual(x, idx, nres, F46, MSE, gscale=g)
-    ref = oracle.quantize_residual(x, clamped, nres, F46, MSE, gscale=g)
+    ref = oracle.quantize_residual(x, idx, nres, F46, MSE, gscale=g)
     assert_residual_same(got, ref, "index vector")
 
 
@@ -298,3 +298,77 @@ def test_rmsnorm_residual_full_size_prefill():
     ref = oracle.quantize_residual(y[pick], perm, nres, F46, MSE, gscale=g_ref)
     sub = {"packed": got["packed"][pick], "scales": got["scales"][pick], "gscale": got["gscale"]}
     assert_residual_same(sub, ref, "full size sampled rows")
+
+
+# ------------------------------------------------- invalid channel orders ----
+
+@pytest.mark.parametrize("cols", [16, 80, 5120, 8208, 32768])
+def test_check_order_counts_what_breaks_a_permutation(cols):
+    """nvfp4_check_order: 0 for permutations; out-of-range entries and
+    repeats counted as cols - (distinct in-range values)."""
+    banner(f"check_order cols={cols}")
+    rng = np.random.default_rng(cols)
+    perm = rng.permutation(cols).astype(np.int32)
+    cases = [(perm, 0), (perm[::-1].copy(), 0)]
+    p1 = perm.copy(); p1[cols // 2] = cols; cases.append((p1, 1))
+    p2 = perm.copy(); p2[0] = -1; p2[-1] = 1 << 30; cases.append((p2, 2))
+    if cols > 1:
+        p3 = perm.copy(); p3[1] = p3[0]; cases.append((p3, 1))
+    cases.append((np.zeros(cols, np.int32), cols - 1))
+    for p, want in cases:
+        bad = nv.check_order(torch.from_numpy(p).cuda())
+        torch.cuda.synchronize()
+        assert int(bad.cpu().numpy()[0]) == want
+
+
+@pytest.mark.parametrize("rows,cols,nres,rms", [
+    (37, 80, 16, False), (300, 5120, 256, False), (20, 9216, 512, False),  # both kernel shapes
+    (37, 80, 16, True), (300, 5120, 256, True),  # fused RMSNorm (rows of at most 8192)
+])
+def test_out_of_range_order_poisons_the_output(rows, cols, nres, rms):
+    """An order entry outside [0, cols) makes nvfp4_quantize_residual (and
+    the fused RMSNorm call) write 0x7F (E4M3 NaN) into every scale byte and
+    0 into every code; dequantizing gives NaN everywhere, and so does a
+    W4A4 product over it.  The same call with a valid order is checked
+    against the oracle first, so the outputs are known to be overwritten."""
+    banner(f"poisoned output {rows}x{cols}, nres={nres}, rms={rms}")
+    x = outlier_tensor(7 + cols, rows, cols)
+    xd = to_device(x)
+    perm = oracle.channel_order(oracle.channel_absmax(x))
+    width = cols + nres
+    out = {"packed": torch.empty(rows * width // 2, dtype=torch.uint8, device="cuda"),
+           "scales": torch.empty(rows * width // 16, dtype=torch.uint8, device="cuda"),
+           "gscale": torch.empty(1, dtype=torch.float32, device="cuda")}
+
+    def call(p):
+        pd = torch.from_numpy(p.astype(np.int32)).cuda()
+        if rms:
+            nv.rmsnorm_quantize_residual(xd, pd, nres, out=out)
+        else:
+            nv.quantize_residual(xd, pd, nres, out=out)
+        torch.cuda.synchronize()
+        return out["packed"].cpu().numpy(), out["scales"].cpu().numpy()
+
+    good_p, good_s = call(perm)
+    if not rms:
+        ref = oracle.quantize_residual(x, perm, nres, F46, MSE)
+        np.testing.assert_array_equal(good_s, ref["scales"].reshape(-1))
+        np.testing.assert_array_equal(good_p, ref["packed"].reshape(-1))
+    assert (good_s != 0x7F).all()
+    for bad_value in (cols, -5):
+        p = perm.copy()
+        p[cols // 3] = bad_value
+        assert int(nv.check_order(torch.from_numpy(p.astype(np.int32)).cuda()).cpu()[0]) == 1
+        pk, sc = call(p)
+        assert (sc == 0x7F).all(), "every scale byte must carry the NaN code"
+        assert (pk == 0).all()
+        deq = nv.dequantize(out["packed"], out["scales"], out["gscale"], rows, width,
+                            nv.AXIS_COLS)
+        assert torch.isnan(deq).all().item()
+    w = testkit.fill((24, width), testkit.NORMAL, 0.02, 3)
+    qw = nv.quantize(to_device(w), nv.AXIS_COLS, F46, MSE)
+    a = {"packed": out["packed"].view(rows, width // 2), "scales": out["scales"].view(rows, width // 16),
+         "gscale": out["gscale"]}
+    b = {"packed": qw["packed"].view(24, width // 2), "scales": qw["scales"].view(24, width // 16),
+         "gscale": qw["gscale"]}
+    assert torch.isnan(nv.gemm(a, b)).all().item()
