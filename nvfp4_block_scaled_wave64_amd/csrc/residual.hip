@@ -341,31 +341,44 @@ __global__ __launch_bounds__(kResThreads) void quantize_residual_kernel(
 constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
 
 // Pairwise sum over the 64 lanes, levels in the order of the lane index
-// bits (lane l and l ^ 2^k at level k): ds_swizzle exchanges within 32
-// lanes, then the two halves' (uniform) values.  Every lane gets the sum.
-__device__ __forceinline__ float wave_pair_sum(float t) {
-  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (1 << 10)));
-  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (2 << 10)));
-  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (4 << 10)));
-  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (8 << 10)));
-  t = t + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(t), 0x1F | (16 << 10)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 0)) +
-         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 32));
+// bits: level k adds the values of lanes l and l ^ 2^k.  DPP moves within the
+// VALU (no LDS round trips): quad permutations for partners l ^ 1 and l ^ 2,
+// row shifts by 4 and 8 (lane l takes l - 4 or l - 8 in its row of 16), then
+// the row broadcasts of lanes 15 and 31.  A shift reaches the partner only
+// in lanes whose bit k is set, so only some lanes carry the tree's pairs;
+// lane 63, whose bits are all set, does at every level (its partners 62, 61,
+// 59, 55, 47 and 31 did too at the levels before), and every pair is added in
+// some order of its two operands (the same value).  Returns lane 63's sum.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_tree_sum(float t) {
+  t = t + dpp_f32<0xB1>(t);   // quad_perm [1,0,3,2]: lane l ^ 1
+  t = t + dpp_f32<0x4E>(t);   // quad_perm [2,3,0,1]: lane l ^ 2
+  t = t + dpp_f32<0x114>(t);  // row_shr:4
+  t = t + dpp_f32<0x118>(t);  // row_shr:8
+  t = t + dpp_f32<0x142>(t);  // row_bcast:15 (lane 15 of each row to the next row)
+  t = t + dpp_f32<0x143>(t);  // row_bcast:31 (lane 31 to rows 2 and 3)
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 63));
 }
 
 // Sum of squares of the row a wave holds as kVpl 16-byte vectors per lane
 // (vector v = lane + 64 m covers elements 8v .. 8v+7; vectors past the row
-// were loaded as zeros).  Lane xor-shuffles add the pairs of the tree's
-// first six levels, the vectors of one lane the rest; every lane ends with
-// the same value.
+// were loaded as zeros).  The chunk sums of one vector index m go through
+// the lane tree (the first six levels of the pairwise tree over v), the
+// per-m sums through the rest.  Vector indices m with no vector of the row
+// (64 m >= vrow) hold zeros only: their sums are exactly 0 and are not
+// computed.
 template <int kVpl>
-__device__ __forceinline__ float row_sumsq(const u32x4 (&buf)[kVpl]) {
+__device__ __forceinline__ float row_sumsq(const u32x4 (&buf)[kVpl], uint32_t vrow) {
   constexpr int kM = pow2_at_least(kVpl);
   float a[kM];
 #pragma unroll
   for (int m = 0; m < kM; ++m) {
     a[m] = 0.0f;
-    if (m < kVpl) {
+    if (m < kVpl && 64u * m < vrow) {
       float t = 0.0f;
       t = __builtin_fmaf(bf16_lo(buf[m].x), bf16_lo(buf[m].x), t);
       t = __builtin_fmaf(bf16_hi(buf[m].x), bf16_hi(buf[m].x), t);
@@ -375,9 +388,8 @@ __device__ __forceinline__ float row_sumsq(const u32x4 (&buf)[kVpl]) {
       t = __builtin_fmaf(bf16_hi(buf[m].z), bf16_hi(buf[m].z), t);
       t = __builtin_fmaf(bf16_lo(buf[m].w), bf16_lo(buf[m].w), t);
       t = __builtin_fmaf(bf16_hi(buf[m].w), bf16_hi(buf[m].w), t);
-      a[m] = wave_pair_sum(t);
+      a[m] = wave_tree_sum(t);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int n = kM; n > 1; n >>= 1) {
@@ -402,14 +414,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
 }
 
-// One bf16 pair of y: bf16(x * rstd), then bf16(w * y).  Without a weight
-// vector w is 1, which leaves y unchanged (the product is exact).
-// ymax keeps the two halves' running max |y| as bf16 bit patterns
-// (non-negative bf16 values order like their patterns).
-__device__ __forceinline__ uint32_t rms_pair(uint32_t x, uint32_t w, float rstd, uint32_t& ymax) {
+// One bf16 pair of y: bf16(x * rstd), then bf16(w * y) with the weights
+// (wl, wh) as fp32 values (1 without a weight vector, which leaves y
+// unchanged: the product of two bf16 values is exact).  With kMax, ymax
+// keeps the two halves' running max |y| as bf16 bit patterns (non-negative
+// bf16 values order like their patterns).
+template <bool kMax>
+__device__ __forceinline__ uint32_t rms_pair(uint32_t x, float wl, float wh, float rstd,
+                                             uint32_t& ymax) {
   uint32_t y = pack_bf16(bf16_lo(x) * rstd, bf16_hi(x) * rstd);
-  y = pack_bf16(bf16_lo(w) * bf16_lo(y), bf16_hi(w) * bf16_hi(y));
-  ymax = max_u16x2(ymax, y & 0x7FFF7FFFu);
+  y = pack_bf16(wl * bf16_lo(y), wh * bf16_hi(y));
+  if (kMax) ymax = max_u16x2(ymax, y & 0x7FFF7FFFu);
   return y;
 }
 
@@ -418,37 +433,33 @@ __device__ __forceinline__ float bf16_pair_max(uint32_t m) {
   return __uint_as_float(max(m & 0xFFFFu, m >> 16) << 16);
 }
 
-// Replaces the row held in buf by y = RMSNorm(x) (bf16) and folds max |y|
-// into ymax.  w4: the weight vector in LDS (ones without one), zero-padded
-// to 64 * kVpl 16-byte vectors.  Vectors past the row hold zeros and stay
-// zero.
-template <int kVpl>
-__device__ __forceinline__ void rms_apply(u32x4 (&buf)[kVpl], const u32x4* w4, uint32_t lane,
-                                          float rstd, uint32_t& ymax) {
-  // The widened values of the sum of squares are not reused here: an empty
-  // register constraint makes the compiler re-read the packed words, rather
-  // than keep 8 fp32 values per vector alive across the reduction.
-#pragma unroll
-  for (int m = 0; m < kVpl; ++m)
-    asm volatile("" : "+v"(buf[m].x), "+v"(buf[m].y), "+v"(buf[m].z), "+v"(buf[m].w));
+// Replaces the row held in buf (kVpl 16-byte vectors per lane, vector
+// lane + 64 m) by y = RMSNorm(x), bf16 pairs.  wf: the weights in LDS as
+// fp32, 8 per row vector (32 bytes).  Vectors past the row are loaded as
+// zeros and are left unchanged (they are never stored); vector indices m
+// past the row are skipped.
+template <int kVpl, bool kMax>
+__device__ __forceinline__ void rms_apply(u32x4 (&buf)[kVpl], const float* wf, uint32_t lane,
+                                          uint32_t vrow, float rstd, uint32_t& ymax) {
 #pragma unroll
   for (int m = 0; m < kVpl; ++m) {
-    const u32x4 w = w4[lane + 64u * m];
-    buf[m].x = rms_pair(buf[m].x, w.x, rstd, ymax);
-    buf[m].y = rms_pair(buf[m].y, w.y, rstd, ymax);
-    buf[m].z = rms_pair(buf[m].z, w.z, rstd, ymax);
-    buf[m].w = rms_pair(buf[m].w, w.w, rstd, ymax);
+    const uint32_t v = lane + 64u * m;
+    if (64u * m < vrow && v < vrow) {
+      const float4 w0 = reinterpret_cast<const float4*>(wf)[2 * v];
+      const float4 w1 = reinterpret_cast<const float4*>(wf)[2 * v + 1];
+      buf[m].x = rms_pair<kMax>(buf[m].x, w0.x, w0.y, rstd, ymax);
+      buf[m].y = rms_pair<kMax>(buf[m].y, w0.z, w0.w, rstd, ymax);
+      buf[m].z = rms_pair<kMax>(buf[m].z, w1.x, w1.y, rstd, ymax);
+      buf[m].w = rms_pair<kMax>(buf[m].w, w1.z, w1.w, rstd, ymax);
+    }
   }
 }
 
-// Stages the weight vector in LDS as 64 * kVpl 16-byte vectors: the weights
-// (bf16 ones without a weight vector), then zeros.
-template <int kVpl>
-__device__ __forceinline__ void stage_weight(u32x4* w4, const uint16_t* weight, uint32_t vrow) {
-  const u32x4* wg = reinterpret_cast<const u32x4*>(weight);
-  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  for (uint32_t v = threadIdx.x; v < 64u * kVpl; v += blockDim.x)
-    w4[v] = v < vrow ? (weight ? wg[v] : ones) : u32x4{0u, 0u, 0u, 0u};
+// Stages the weight vector in LDS as fp32 (8 per row vector, vrow vectors):
+// the weights widened exactly, or ones without a weight vector.
+__device__ __forceinline__ void stage_weight(float* wf, const uint16_t* weight, uint32_t cols) {
+  for (uint32_t c = threadIdx.x; c < cols; c += blockDim.x)
+    wf[c] = weight ? __uint_as_float((uint32_t)weight[c] << 16) : 1.0f;
 }
 
 // Wave maximum of a non-negative float, then one atomic max per wave on its
@@ -477,11 +488,11 @@ __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint1
                                                         RmsArgs ra, float six_m,
                                                         uint32_t* __restrict__ acc) {
   extern __shared__ __align__(16) uint8_t lds[];
-  u32x4* w4 = reinterpret_cast<u32x4*>(lds);
+  float* wf = reinterpret_cast<float*>(lds);
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t vrow = cols >> 3;
-  stage_weight<kVpl>(w4, ra.weight, vrow);
+  stage_weight(wf, ra.weight, cols);
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * (blockDim.x >> 6);
   uint32_t ymax = 0u;
@@ -500,8 +511,8 @@ __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint1
 #pragma unroll
     for (int m = 0; m < kVpl; ++m) buf[m] = nxt[m];
     if (row + stride < rows) load(row + stride, nxt);
-    const float rstd = rms_rstd(row_sumsq<kVpl>(buf), cols, ra.eps);
-    rms_apply<kVpl>(buf, w4, lane, rstd, ymax);
+    const float rstd = rms_rstd(row_sumsq<kVpl>(buf, vrow), cols, ra.eps);
+    rms_apply<kVpl, true>(buf, wf, lane, vrow, rstd, ymax);
   }
   wave_max_to(acc, bf16_pair_max(ymax), six_m);
 }
@@ -511,9 +522,9 @@ __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint1
 // (kVpl 16-byte vectors per lane) are in flight while the wave quantizes the
 // current one; lane l handles the row's blocks l, l + 64, ...  The workgroup
 // shares the scale table, the channel order and (kRms) the weight vector.
-// With kRms the staged row is normalized in LDS (RMSNorm above; its sum of
-// squares comes from the row's registers), so the gathers, both stages and
-// the residual see y.
+// With kRms the row is normalized in its registers before it is staged
+// (RMSNorm above), so the gathers, both stages and the residual see y; with
+// kVarAmax in V the kernel also folds max |y| into ra.amax_out.
 template <uint32_t V, int kVpl, bool kRms>
 __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_residual_wave_kernel(
     const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
@@ -524,18 +535,19 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
                         : (V & kVarMax) ? kRuleMax
                         : (V & kVarMae) ? kRuleMae
                                         : kRuleMse;
+  constexpr bool kMax = kRms && (V & kVarAmax) != 0;
   // LDS: scale table (1 KiB), channel order (cols 16-bit byte offsets),
-  // with kRms the zero-padded weight vector, one row per wave.
+  // with kRms the weights as fp32 (cols * 4 bytes), one row per wave.
   extern __shared__ __align__(16) uint8_t lds[];
   float2* tab = reinterpret_cast<float2*>(lds);
   uint16_t* pm = reinterpret_cast<uint16_t*>(lds + 1024);
-  u32x4* w4 = reinterpret_cast<u32x4*>(pm + cols);
+  float* wf = reinterpret_cast<float*>(pm + cols);
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t nwaves_g = blockDim.x >> 6;
-  // cols * 2 bytes is a multiple of 32; the weight area is 64 * kVpl
-  // 16-byte vectors.
-  uint16_t* xr = pm + cols + (kRms ? 512u * kVpl : 0u) + cols * wave;
+  // cols * 2 bytes is a multiple of 32, so every row buffer is 16-byte
+  // aligned.
+  uint16_t* xr = pm + cols + (kRms ? 2u * cols : 0u) + cols * wave;
   u32x4* xr4 = reinterpret_cast<u32x4*>(xr);
 
   const TensorScales ts = tensor_scales(*gscale);
@@ -548,7 +560,7 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
     pm[c] = (uint16_t)(2u * std::min(v, cols - 1u));
   }
   const uint32_t vrow = cols >> 3;
-  if constexpr (kRms) stage_weight<kVpl>(w4, ra.weight, vrow);
+  if constexpr (kRms) stage_weight(wf, ra.weight, cols);
 
   const uint32_t nb = cols >> 4, nrb = nres >> 4, bout = nb + nrb;
   const int64_t first = (int64_t)blockIdx.x * nwaves_g + wave;
@@ -569,8 +581,11 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
   u32x4 buf[kVpl];
   if (first < rows) load(first, buf);
   for (int64_t row = first; row < rows; row += stride) {
-    float rstd = 0.0f;
-    if constexpr (kRms) rstd = rms_rstd(row_sumsq<kVpl>(buf), cols, ra.eps);
+    if constexpr (kRms) {
+      // Normalize the row in its registers (each lane its own vectors).
+      const float rstd = rms_rstd(row_sumsq<kVpl>(buf, vrow), cols, ra.eps);
+      rms_apply<kVpl, kMax>(buf, wf, lane, vrow, rstd, ymax);
+    }
     // LDS operations of one wave complete in order: the previous row's
     // gathers are done before these writes, and the writes before the
     // gathers below.
@@ -586,17 +601,6 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
       load(row + stride, buf);
       __builtin_amdgcn_s_setprio(0);
     }
-    if constexpr (kRms) {
-      // Normalize the staged row in place, each lane its own vectors, while
-      // the next row's loads are in flight (its registers are taken).
-#pragma unroll 1
-      for (uint32_t v = lane; v < vrow; v += 64u) {
-        const u32x4 x = xr4[v], w = w4[v];
-        xr4[v] = u32x4{rms_pair(x.x, w.x, rstd, ymax), rms_pair(x.y, w.y, rstd, ymax),
-                       rms_pair(x.z, w.z, rstd, ymax), rms_pair(x.w, w.w, rstd, ymax)};
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
     const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed + row * bout * 8, bout * 8u);
     const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + row * bout, bout);
 #pragma unroll 1
@@ -604,7 +608,7 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
       residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts,
                                  tab);
   }
-  if (kRms && ra.amax_out) wave_max_to(ra.amax_out, bf16_pair_max(ymax), 0.0f);
+  if (kMax) wave_max_to(ra.amax_out, bf16_pair_max(ymax), 0.0f);
 }
 
 // ------------------------------------------------------------- launchers --
@@ -686,7 +690,7 @@ static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t
   // As many waves per compute unit as their row buffers fit in LDS (at most
   // 16), one workgroup per compute unit.
   const int64_t row_bytes = cols * 2;
-  const int64_t shared = 1024 + row_bytes + (kRms ? 1024 * kVpl : 0);
+  const int64_t shared = 1024 + row_bytes + (kRms ? cols * 4 : 0);
   int64_t waves = (163840 - shared) / row_bytes;
   const int64_t max_waves = (kRms ? rms_threads(kVpl) : 1024) / 64;
   if (waves > max_waves) waves = max_waves;
@@ -747,13 +751,23 @@ hipError_t launch_rms_quantize_residual(const uint16_t* in, int64_t rows, int64_
                                         const int32_t* perm, int64_t nres, const float* gscale,
                                         uint32_t variant, uint8_t* packed, uint8_t* scales,
                                         const RmsArgs& ra, hipStream_t s) {
+  // max |y| is tracked only when asked for (kVarAmax).
+  if (ra.amax_out) variant |= kVarAmax;
+#define NVFP4_RMS_CASE(v) \
+  case v:                 \
+    return launch_rms_residual_v<v>(in, rows, cols, perm, nres, gscale, packed, scales, ra, s);
   switch (variant) {
-    case 0: return launch_rms_residual_v<0>(in, rows, cols, perm, nres, gscale, packed, scales, ra, s);
-    case 1: return launch_rms_residual_v<1>(in, rows, cols, perm, nres, gscale, packed, scales, ra, s);
-    case 3: return launch_rms_residual_v<3>(in, rows, cols, perm, nres, gscale, packed, scales, ra, s);
-    case 17: return launch_rms_residual_v<17>(in, rows, cols, perm, nres, gscale, packed, scales, ra, s);
+    NVFP4_RMS_CASE(0)
+    NVFP4_RMS_CASE(1)
+    NVFP4_RMS_CASE(3)
+    NVFP4_RMS_CASE(17)
+    NVFP4_RMS_CASE(0 | kVarAmax)
+    NVFP4_RMS_CASE(1 | kVarAmax)
+    NVFP4_RMS_CASE(3 | kVarAmax)
+    NVFP4_RMS_CASE(17 | kVarAmax)
     default: return hipErrorInvalidValue;
   }
+#undef NVFP4_RMS_CASE
 }
 
 template <int kVpl>
@@ -763,7 +777,7 @@ static hipError_t launch_rms_amax_v(const uint16_t* in, int64_t rows, int64_t co
   const int64_t waves = rms_threads(kVpl) / 64;
   int64_t groups = (rows + waves - 1) / waves;
   if (groups > device_cu_count()) groups = device_cu_count();
-  const size_t lds = (size_t)1024 * kVpl;
+  const size_t lds = (size_t)cols * 4;
   rms_amax_kernel<kVpl><<<(unsigned)groups, (unsigned)(waves * 64), lds, s>>>(
       in, rows, (uint32_t)cols, ra, six_m, acc);
   return hipGetLastError();
