@@ -186,13 +186,19 @@ __device__ void poison_rows(int64_t row0, int64_t stride, int64_t rows, uint32_t
 // pm[16j .. 16j+15], quantizes them, stores codes and scale as block ob of
 // the output, and with `res` also block ob + nb: the residual block, or with
 // `dup` (the weight side of the augmented product) a copy of block ob.
+//   stash (nullable): instead of quantizing the residual block here, store
+//   its 16 values x - v*d to stash[q * plane] (q = 0..3, float4 each) for a
+//   later pass that quantizes up to 64 of them at once (stash_quantize).
+//   The stash is four planes of float4 (values 4q .. 4q+3 of every block in
+//   plane q), so that consecutive lanes access consecutive 16-byte slots.
 template <bool k46, int kRule>
 __device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_t* pm,
                                                uint32_t j, uint32_t ob, uint32_t nb, bool res,
                                                bool dup,
                                                __amdgpu_buffer_rsrc_t r_packed,
                                                __amdgpu_buffer_rsrc_t r_scales,
-                                               const TensorScales& ts, const float2* tab) {
+                                               const TensorScales& ts, const float2* tab,
+                                               float4* stash = nullptr, uint32_t plane = 0) {
   constexpr bool kNeedErr = k46;
   // pm holds byte offsets into the row, two per dword; each gathered bf16
   // becomes its fp32 value by a 16-bit shift.
@@ -225,6 +231,12 @@ __device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_
     const float d = tab[q.S].x;
 #pragma unroll
     for (int k = 0; k < 16; ++k) rx[k] = __builtin_fmaf(-v[k], d, x[k]);
+    if (stash) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        stash[plane * k] = float4{rx[4 * k], rx[4 * k + 1], rx[4 * k + 2], rx[4 * k + 3]};
+      return;
+    }
     const Block16 qr = quantize_block16f<k46, kRule, kNeedErr>(rx, ts.k6, ts.k4, tab);
     u32x2 rc;
     rc.x = qr.lo;
@@ -232,6 +244,27 @@ __device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_
     __builtin_amdgcn_raw_buffer_store_b64(rc, r_packed, (ob + nb) * 8u, 0, kStreamStore);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)qr.S, r_scales, ob + nb, 0, kMergedStore);
   }
+}
+
+// Quantizes one stashed residual block (its 16 values at stash[q * plane],
+// q = 0..3) and stores it as block ob of `packed` / `scales` (global
+// pointers: the stashed blocks of one pass belong to several rows).
+template <bool k46, int kRule>
+__device__ __forceinline__ void stash_quantize(const float4* stash, uint32_t plane, int64_t ob,
+                                               uint8_t* packed, uint8_t* scales,
+                                               const TensorScales& ts, const float2* tab) {
+  float rx[16];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 t = stash[plane * k];
+    rx[4 * k] = t.x;
+    rx[4 * k + 1] = t.y;
+    rx[4 * k + 2] = t.z;
+    rx[4 * k + 3] = t.w;
+  }
+  const Block16 qr = quantize_block16f<k46, kRule, k46>(rx, ts.k6, ts.k4, tab);
+  *reinterpret_cast<u32x2*>(packed + ob * 8) = u32x2{qr.lo, qr.hi};
+  scales[ob] = (uint8_t)qr.S;
 }
 
 // Wide rows (cols > 8192): a workgroup of 1024 threads stages R rows in LDS
@@ -529,7 +562,7 @@ template <uint32_t V, int kVpl, bool kRms>
 __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_residual_wave_kernel(
     const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
     uint32_t nres, const float* __restrict__ gscale, uint8_t* __restrict__ packed,
-    uint8_t* __restrict__ scales, RmsArgs ra, uint32_t dup) {
+    uint8_t* __restrict__ scales, RmsArgs ra, uint32_t dup, uint32_t stash_items) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr int kRule = !k46 ? kRuleMse
                         : (V & kVarMax) ? kRuleMax
@@ -547,7 +580,18 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
   const uint32_t nwaves_g = blockDim.x >> 6;
   // cols * 2 bytes is a multiple of 32, so every row buffer is 16-byte
   // aligned.
-  uint16_t* xr = pm + cols + (kRms ? 2u * cols : 0u) + cols * wave;
+  // Residual blocks (nres > 0, not dup): when the launch gives a stash of
+  // stash_items (32 or 64) blocks per wave and a row has at most that many,
+  // each row's are stashed (x - v*d, 64 bytes each) and quantized in passes
+  // of batch = stash_items / nrb rows, so that the second stage runs on
+  // (nearly) full waves instead of a few lanes per row.
+  const uint32_t nrb_ = nres >> 4;
+  const uint32_t batch = stash_items ? stash_items / nrb_ : 0u;
+  const uint32_t stash_bytes = stash_items * 64u;
+  uint8_t* wave_area = reinterpret_cast<uint8_t*>(pm + cols + (kRms ? 2u * cols : 0u)) +
+                       (size_t)(cols * 2u + stash_bytes) * wave;
+  uint16_t* xr = reinterpret_cast<uint16_t*>(wave_area);
+  float4* stash = reinterpret_cast<float4*>(wave_area + cols * 2u);
   u32x4* xr4 = reinterpret_cast<u32x4*>(xr);
 
   const TensorScales ts = tensor_scales(*gscale);
@@ -578,8 +622,13 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
       buf[m] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + 64u * m) * 16u, 0, kStreamLoad);
   };
 
+  // Stashed block i = slot * nrb + j (slot = the row's place in its batch)
+  // is lane i's in the pass: its row and block are fixed per lane.
+  const uint32_t my_slot = batch ? lane / nrb_ : 0u, my_j = batch ? lane % nrb_ : 0u;
   u32x4 buf[kVpl];
   if (first < rows) load(first, buf);
+  uint32_t slot = 0;
+  int64_t batch_row0 = first;
   for (int64_t row = first; row < rows; row += stride) {
     if constexpr (kRms) {
       // Normalize the row in its registers (each lane its own vectors).
@@ -603,10 +652,30 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
     }
     const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed + row * bout * 8, bout * 8u);
     const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + row * bout, bout);
+    if (batch) {
 #pragma unroll 1
-    for (uint32_t j = lane; j < nb; j += 64u)
-      residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts,
-                                 tab);
+      for (uint32_t j = lane; j < nb; j += 64u)
+        residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, false, r_packed, r_scales, ts, tab,
+                                   stash + slot * nrb + j, stash_items);
+      // A full batch, or the wave's last row: quantize the stashed blocks
+      // (LDS operations of one wave complete in order).
+      if (++slot == batch || row + stride >= rows) {
+        __builtin_amdgcn_wave_barrier();
+        if (lane < slot * nrb) {
+          const int64_t r = batch_row0 + (int64_t)my_slot * stride;
+          stash_quantize<k46, kRule>(stash + lane, stash_items, r * bout + nb + my_j, packed,
+                                     scales, ts, tab);
+        }
+        __builtin_amdgcn_wave_barrier();
+        slot = 0;
+        batch_row0 = row + stride;
+      }
+    } else {
+#pragma unroll 1
+      for (uint32_t j = lane; j < nb; j += 64u)
+        residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts,
+                                   tab);
+    }
   }
   if (kMax) wave_max_to(ra.amax_out, bf16_pair_max(ymax), 0.0f);
 }
@@ -687,12 +756,35 @@ static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t
                                        const int32_t* perm, int64_t nres, const float* gscale,
                                        uint8_t* packed, uint8_t* scales, const RmsArgs& ra,
                                        bool dup, hipStream_t s) {
-  // As many waves per compute unit as their row buffers fit in LDS (at most
-  // 16), one workgroup per compute unit.
-  const int64_t row_bytes = cols * 2;
-  const int64_t shared = 1024 + row_bytes + (kRms ? cols * 4 : 0);
-  int64_t waves = (163840 - shared) / row_bytes;
+  // Stash capacity (blocks per wave; 0 = the residual blocks are quantized
+  // where they are formed).  The stash shares LDS with the row buffers, and
+  // these kernels slow down sharply below about 12 waves per compute unit
+  // (measured on 32768 x 5120, nres = 256: the plain kernel 105 us without a
+  // stash at 14 waves, 95 us with 32 blocks at 12 waves, 99 us with 64 at
+  // 10; the fused RMSNorm kernel 130 us without at 12 waves, 148 and 161 us
+  // with 32 and 64 at 10 and 9), so the smallest capacity that holds a
+  // row's residual blocks is taken only if it leaves at least
+  // min(12, the waves without a stash).
+  const int64_t nrb = nres / 16;
+  const int64_t fixed = 1024 + cols * 2 + (kRms ? cols * 4 : 0);
   const int64_t max_waves = (kRms ? rms_threads(kVpl) : 1024) / 64;
+  auto waves_with = [&](int64_t items) {
+    return std::min<int64_t>(max_waves, (163840 - fixed) / (cols * 2 + items * 64));
+  };
+  int64_t stash_items = 0;
+  if (!dup && nrb > 0) {
+    const int64_t need = std::min<int64_t>(12, waves_with(0));
+    for (int64_t cap : {32, 64})
+      if (nrb <= cap && waves_with(cap) >= need) {
+        stash_items = cap;
+        break;
+      }
+  }
+  // As many waves per compute unit as their row buffers (and stashes) fit
+  // in LDS, at most max_waves; one workgroup per compute unit.
+  const int64_t row_bytes = cols * 2 + stash_items * 64;
+  const int64_t shared = fixed;
+  int64_t waves = (163840 - shared) / row_bytes;
   if (waves > max_waves) waves = max_waves;
   if (waves < 1) waves = 1;
   int64_t groups = (rows + waves - 1) / waves;
@@ -703,7 +795,7 @@ static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t
   quantize_residual_wave_kernel<V, kVpl, kRms>
       <<<(unsigned)groups, (unsigned)(waves * 64), lds, s>>>(
           in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, ra,
-          (uint32_t)dup);
+          (uint32_t)dup, (uint32_t)stash_items);
   return hipGetLastError();
 }
 

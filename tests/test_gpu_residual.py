@@ -372,3 +372,28 @@ def test_out_of_range_order_poisons_the_output(rows, cols, nres, rms):
     b = {"packed": qw["packed"].view(24, width // 2), "scales": qw["scales"].view(24, width // 16),
          "gscale": qw["gscale"]}
     assert torch.isnan(nv.gemm(a, b)).all().item()
+
+
+# ------------------------------------------- stashed residual passes ----
+
+STASH_SHAPES = [
+    # (rows, cols, nres): residual blocks per row nrb = nres / 16 and rows per
+    # wave chosen to cover every stash mode of the one-row-per-wave kernel --
+    # passes of 32 blocks over 16 rows (nrb = 2, full and partial batches),
+    # over 2 rows (nrb = 16: the 32768 x 5120 configuration's mode, several
+    # batches per wave), one row per pass (nrb = 17 and 32), the 64-block
+    # stash (nrb = 48), no stash (nrb = 80) -- and ragged per-wave row counts.
+    (70001, 80, 32), (9221, 80, 32), (15367, 5120, 256), (7000, 1040, 272), (6000, 512, 512),
+    (5000, 2048, 768), (4000, 2048, 1280),
+]
+
+
+@pytest.mark.parametrize("rows,cols,nres", STASH_SHAPES)
+@pytest.mark.parametrize("mode,rule", [(F46, MSE), (F46, MAE)])
+def test_quantize_residual_stash_batches(rows, cols, nres, mode, rule):
+    banner(f"residual stash passes {rows}x{cols} nres={nres} rule={rule}")
+    x = outlier_tensor(5000 + cols + nres, rows, cols)
+    perm = oracle.channel_order(oracle.channel_absmax(x))
+    got = gpu_residual(x, perm, nres, mode, rule)
+    ref = oracle.quantize_residual(x, perm, nres, mode, rule)
+    assert_residual_same(got, ref, f"stash {rows}x{cols} nres={nres}")
