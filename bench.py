@@ -180,6 +180,8 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     t_deq = call_time(lambda: nv.dequantize(packed, scales, g, rows, cols, nv.AXIS_COLS,
                                             torch.bfloat16, out=deq), torch, stream)
     res["dequantize_bf16_gbps"] = gb(t_deq, 0.5 + 1 / 16 + 2)
+    res["dequantize_bf16_frac_of_hbm_peak"] = round(
+        numel * (2.5625) / t_deq / 1e9 / HBM_PEAK_GBPS, 4)
     del deq
     # Outlier channels with a residual stage on the same activations:
     # calibration (channel maxima + order) and the per-step two-stage
@@ -207,6 +209,7 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
                      torch, stream)
     res["rmsnorm_residual_given_g_us"] = round(t_f1 * 1e6, 2)
     res["rmsnorm_residual_given_g_gbps"] = round(res_bytes / t_f1 / 1e9, 1)
+    res["rmsnorm_residual_given_g_frac_of_hbm_peak"] = round(res_bytes / t_f1 / 1e9 / HBM_PEAK_GBPS, 4)
     res["rmsnorm_residual_two_pass_us"] = round(t_f2 * 1e6, 2)
     # W4A4 product on the matrix cores: these activations (as quantized by
     # the step) times a 5120 x 5120 weight, and the augmented product over
@@ -252,7 +255,21 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
         tm = float(np.median(t))
         res[f"workload{cid}_{cfg.rows}x{cfg.cols}_kernel_us_median"] = round(tm * 1e6, 2)
         res[f"workload{cid}_gbps"] = gb(tm, n=cfg.rows * cfg.cols)
+        res[f"workload{cid}_frac_of_hbm_peak"] = round(
+            cfg.rows * cfg.cols * BYTES_PER_ELEM / tm / 1e9 / HBM_PEAK_GBPS, 4)
         if cid == 5:
+            # Dequantize of the column-blocked output back to [rows][cols]
+            # (0.5625 B read, 2 or 4 B written per element).
+            n5 = cfg.rows * cfg.cols
+            for dt, name, bpe in ((torch.bfloat16, "bf16", 2), (torch.float32, "f32", 4)):
+                dq = torch.empty((cfg.rows, cfg.cols), dtype=dt, device=dev)
+                t_dq = call_time(lambda: nv.dequantize(oc["packed"], oc["scales"], gc, cfg.rows,
+                                                       cfg.cols, nv.AXIS_ROWS, dt, out=dq),
+                                 torch, stream)
+                res[f"dequantize_cols_{name}_8192x5120_gbps"] = gb(t_dq, 0.5625 + bpe, n5)
+                res[f"dequantize_cols_{name}_frac_of_hbm_peak"] = round(
+                    n5 * (0.5625 + bpe) / t_dq / 1e9 / HBM_PEAK_GBPS, 4)
+                del dq
             # Both layouts from one read (given g) against the two single-layout calls.
             n5 = cfg.rows * cfg.cols
             od = nv.quantize_dual(xc, cfg.mode, cfg.rule, gscale=gc)

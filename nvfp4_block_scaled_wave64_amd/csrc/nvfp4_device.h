@@ -129,6 +129,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            0x00020000);
 }
 
+// p, which the caller knows to be the same in every lane of the wave, made
+// visibly uniform to the compiler (two readfirstlane): a buffer resource
+// built from it then stays in scalar registers, where the compiler could
+// otherwise wrap every access in a loop over distinct lane values.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Per-launch scale constants derived from g ("Implementation details": the
 // tensor scale; the encode side uses its reciprocal).
 struct TensorScales {

@@ -468,9 +468,10 @@ __device__ __forceinline__ float bf16_pair_max(uint32_t m) {
 
 // Replaces the row held in buf (kVpl 16-byte vectors per lane, vector
 // lane + 64 m) by y = RMSNorm(x), bf16 pairs.  wf: the weights in LDS as
-// fp32, 8 per row vector (32 bytes).  Vectors past the row are loaded as
-// zeros and are left unchanged (they are never stored); vector indices m
-// past the row are skipped.
+// fp32 in two planes of vrow float4 (the first and the last four weights of
+// every row vector), so that consecutive lanes read consecutive 16-byte
+// slots.  Vectors past the row are loaded as zeros and are left unchanged
+// (they are never stored); vector indices m past the row are skipped.
 template <int kVpl, bool kMax>
 __device__ __forceinline__ void rms_apply(u32x4 (&buf)[kVpl], const float* wf, uint32_t lane,
                                           uint32_t vrow, float rstd, uint32_t& ymax) {
@@ -478,8 +479,8 @@ __device__ __forceinline__ void rms_apply(u32x4 (&buf)[kVpl], const float* wf, u
   for (int m = 0; m < kVpl; ++m) {
     const uint32_t v = lane + 64u * m;
     if (64u * m < vrow && v < vrow) {
-      const float4 w0 = reinterpret_cast<const float4*>(wf)[2 * v];
-      const float4 w1 = reinterpret_cast<const float4*>(wf)[2 * v + 1];
+      const float4 w0 = reinterpret_cast<const float4*>(wf)[v];
+      const float4 w1 = reinterpret_cast<const float4*>(wf)[vrow + v];
       buf[m].x = rms_pair<kMax>(buf[m].x, w0.x, w0.y, rstd, ymax);
       buf[m].y = rms_pair<kMax>(buf[m].y, w0.z, w0.w, rstd, ymax);
       buf[m].z = rms_pair<kMax>(buf[m].z, w1.x, w1.y, rstd, ymax);
@@ -488,11 +489,17 @@ __device__ __forceinline__ void rms_apply(u32x4 (&buf)[kVpl], const float* wf, u
   }
 }
 
-// Stages the weight vector in LDS as fp32 (8 per row vector, vrow vectors):
-// the weights widened exactly, or ones without a weight vector.
+// Stages the weight vector in LDS as fp32 in the two planes rms_apply
+// reads: weight c (row vector v = c / 8, place i = c % 8) at plane i / 4,
+// slot v, element i % 4; the weights widened exactly, or ones without a
+// weight vector.
 __device__ __forceinline__ void stage_weight(float* wf, const uint16_t* weight, uint32_t cols) {
-  for (uint32_t c = threadIdx.x; c < cols; c += blockDim.x)
-    wf[c] = weight ? __uint_as_float((uint32_t)weight[c] << 16) : 1.0f;
+  const uint32_t vrow = cols >> 3;
+  for (uint32_t c = threadIdx.x; c < cols; c += blockDim.x) {
+    const uint32_t v = c >> 3, i = c & 7u;
+    wf[((i >> 2) * vrow + v) * 4u + (i & 3u)] =
+        weight ? __uint_as_float((uint32_t)weight[c] << 16) : 1.0f;
+  }
 }
 
 // Wave maximum of a non-negative float, then one atomic max per wave on its
@@ -530,7 +537,7 @@ __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint1
   const int64_t stride = (int64_t)gridDim.x * (blockDim.x >> 6);
   uint32_t ymax = 0u;
   auto load = [&](int64_t row, u32x4 (&buf)[kVpl]) {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(in + row * cols, vrow * 16u);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(in + row * cols), vrow * 16u);
 #pragma unroll
     for (int m = 0; m < kVpl; ++m)
       buf[m] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + 64u * m) * 16u, 0, kStreamLoad);
