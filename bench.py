@@ -258,6 +258,19 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
         res[f"workload{cid}_frac_of_hbm_peak"] = round(
             cfg.rows * cfg.cols * BYTES_PER_ELEM / tm / 1e9 / HBM_PEAK_GBPS, 4)
         if cid == 5:
+            # The same access pattern without the block arithmetic (the
+            # attainable ceiling for this kernel): global traffic alone, and
+            # with the LDS transpose, staging and barriers; back-to-back calls
+            # of each and of the quantize call itself.
+            pk = torch.empty(cfg.rows * cfg.cols // 2, dtype=torch.uint8, device=dev)
+            sk = torch.empty(cfg.rows * cfg.cols // 16, dtype=torch.uint8, device=dev)
+            res["workload5_call_us"] = round(call_time(
+                lambda: nv.quantize(xc, cfg.block_axis, cfg.mode, cfg.rule, gscale=gc, out=oc),
+                torch, stream) * 1e6, 2)
+            for lds, name in ((False, "memory"), (True, "lds")):
+                res[f"workload5_pattern_{name}_call_us"] = round(call_time(
+                    lambda: nv.stream_pattern_cols(xc, pk, sk, lds), torch, stream) * 1e6, 2)
+            del pk, sk
             # Dequantize of the column-blocked output back to [rows][cols]
             # (0.5625 B read, 2 or 4 B written per element).
             n5 = cfg.rows * cfg.cols

@@ -54,6 +54,22 @@ nvfp4_status nvfp4v_decode_tables(float g, float* e2m1_out, float* e4m3_out, flo
 nvfp4_status nvfp4v_stream_pattern(const uint16_t* in_bf16, int64_t nblocks, uint8_t* packed_out,
                                    uint8_t* scales_out, void* stream);
 
+/* The column-blocked quantizer's (NVFP4_AXIS_ROWS) access pattern without
+ * its block arithmetic, as the attainable-bandwidth reference for that
+ * kernel: same launch shape, tile walk (256 rows x 64 columns), loads and
+ * output stores (codes [cols][rows/2], scales [cols][rows/16]).
+ *   with_lds = 1: also the kernel's LDS transpose, code staging and
+ *     barriers, with the block quantizer replaced by a fold of each block's
+ *     words (the codes are the XOR of words 0-3 and 4-7, the scale byte the
+ *     low 7 bits of their XOR);
+ *   with_lds = 0: the global memory traffic alone (each lane stores a fold
+ *     of its loaded words where the kernel stores codes and scales).
+ * The bytes written are not NVFP4 codes.  rows a multiple of 256, cols of
+ * 64; in_bf16, packed_out and scales_out 16-byte aligned. */
+nvfp4_status nvfp4v_stream_pattern_cols(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                        int with_lds, uint8_t* packed_out, uint8_t* scales_out,
+                                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,7 @@ SIGNATURES = {
     "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _P, _P], _I),
     "nvfp4v_decode_tables": ([ctypes.c_float, _P, _P, _P, _P, _P], _I),
     "nvfp4v_stream_pattern": ([_P, _I64, _P, _P, _P], _I),
+    "nvfp4v_stream_pattern_cols": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
 }
 
 
@@ -509,6 +510,19 @@ def gemm_splitk_noalloc(a, b, splits, out, stream=None):
                                          _stream(stream))
     _check(st, "nvfp4_gemm_splitk_noalloc")
     return out
+
+
+def stream_pattern_cols(x, packed, scales, with_lds, stream=None):
+    """The column-blocked quantizer's access pattern without its arithmetic
+    (nvfp4v_stream_pattern_cols) on a [rows][cols] bf16 tensor: with_lds
+    keeps its LDS transpose, staging and barriers.  Measurement only."""
+    x = _bf16_input(x)
+    rows, cols = x.shape
+    packed = _need(packed, x.numel() // 2, torch.uint8, x.device, "packed")
+    scales = _need(scales, x.numel() // 16, torch.uint8, x.device, "scales")
+    _check(lib().nvfp4v_stream_pattern_cols(_ptr(x), rows, cols, int(bool(with_lds)), _ptr(packed),
+                                            _ptr(scales), _stream(stream)),
+           "nvfp4v_stream_pattern_cols")
 
 
 def stream_pattern(x, packed, scales, stream=None):

@@ -17,6 +17,8 @@
 // Blocks along the column (stored as the transpose): tiles of 64 columns x
 // 256 rows are decoded into a row-major LDS tile and leave as 16-byte row
 // segments (see dequantize_cols_kernel).
+#include <type_traits>
+
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -143,119 +145,150 @@ __global__ __launch_bounds__(kDtThreads) void dequantize_cols_kernel(
   const int64_t rb_col = rows / 16;
   const bool scales16 = (reinterpret_cast<uintptr_t>(scales) % 16 == 0) && (rb_col % 16 == 0);
 
-  // A tile's inputs in registers: lane t holds blocks t and t + 512 of the
-  // 64 x 16 (column, block) grid (8 code bytes each); lanes t < 64 also hold
-  // column t's 16 scale bytes.  Loaded one tile ahead.
+  // Waves split by role: the first half loads the next tile's codes and
+  // scale bytes, the second half stores the output rows, and all decode.  A
+  // wave's memory counter then covers only its own kind of access, so the
+  // loading waves wait for their loads alone (issued a tile ahead) and never
+  // for the previous tile's stores, which drain while the next tile is
+  // staged and decoded.
+  constexpr int kHalf = kDtThreads / 2;
+  const bool loader_wave = __builtin_amdgcn_readfirstlane(t) < kHalf;  // wave-uniform
+
+  // A tile's inputs in registers of the loading waves: lane u holds blocks
+  // u + 256 h (h = 0..3) of the 64 x 16 (column, block) grid (8 code bytes
+  // each); lanes u < 64 also hold column u's 16 scale bytes.  Loaded one tile
+  // ahead.
+  constexpr int kLoadH = kDtCols * 16 / kHalf;
   struct In {
-    uint32_t c[4];
+    uint32_t c[2 * kLoadH];
     uint32_t s[4];
   };
-  auto load = [&](int64_t tt) -> In {
-    In in = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    if (tt >= ntiles) return in;
-    const int64_t strip = tt / nrt, rt = tt % nrt;
-    const int64_t c0 = strip * kDtCols, r0 = rt * kDtRows;
-    const int nrb = (int)((rows - r0) / 16 < 16 ? (rows - r0) / 16 : 16);
-    const int ncol = (int)(cols - c0 < kDtCols ? cols - c0 : kDtCols);
+  // Each role runs its own copy of the tile loop (the same barriers in the
+  // same order), so that neither copy holds the other's memory operations.
+  auto run = [&](auto role) {
+    constexpr bool loader = decltype(role)::value;
+    const int u = loader ? t : t - kHalf;  // index within the role
+    auto load = [&](int64_t tt) -> In {
+      In in;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = t + h * kDtThreads, c = k >> 4, b = k & 15;
-      if (c < ncol && b < nrb) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(
-            packed + (c0 + c) * (rows / 2) + (r0 / 16 + b) * 8);
-        in.c[2 * h] = __builtin_nontemporal_load(src);
-        in.c[2 * h + 1] = __builtin_nontemporal_load(src + 1);
-      }
-    }
-    if (t < ncol) {
-      const uint8_t* src = scales + (c0 + t) * rb_col + r0 / 16;
-      if (scales16 && nrb == 16) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(src);
-        in.s[0] = w.x; in.s[1] = w.y; in.s[2] = w.z; in.s[3] = w.w;
-      } else {
-        for (int b = 0; b < nrb; ++b) in.s[b >> 2] |= (uint32_t)src[b] << (8 * (b & 3));
-      }
-    }
-    return in;
-  };
-
-  In nxt = load(blockIdx.x);
-  for (int64_t tt = blockIdx.x; tt < ntiles; tt += gridDim.x) {
-    const int64_t strip = tt / nrt, rt = tt % nrt;
-    const int64_t c0 = strip * kDtCols, r0 = rt * kDtRows;
-    const int nrb = (int)((rows - r0) / 16 < 16 ? (rows - r0) / 16 : 16);
-    const In cur = nxt;
-    __syncthreads();  // the previous tile has been written out
-    // 1. stage the codes and scale bytes in LDS.
+      for (int i = 0; i < 2 * kLoadH; ++i) in.c[i] = 0u;
+      in.s[0] = in.s[1] = in.s[2] = in.s[3] = 0u;
+      if (tt >= ntiles || !loader) return in;  // the storing waves load nothing
+      const int64_t strip = tt / nrt, rt = tt % nrt;
+      const int64_t c0 = strip * kDtCols, r0 = rt * kDtRows;
+      const int nrb = (int)((rows - r0) / 16 < 16 ? (rows - r0) / 16 : 16);
+      const int ncol = (int)(cols - c0 < kDtCols ? cols - c0 : kDtCols);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = t + h * kDtThreads, c = k >> 4, b = k & 15;
-      cw[c][2 * b] = cur.c[2 * h];
-      cw[c][2 * b + 1] = cur.c[2 * h + 1];
-    }
-    if (t < kDtCols) {
-      sc[t][0] = cur.s[0];
-      sc[t][1] = cur.s[1];
-      sc[t][2] = cur.s[2];
-      sc[t][3] = cur.s[3];
-    }
-    __syncthreads();
-    nxt = load(tt + gridDim.x);  // in flight during the decode and the stores
-    // 2. lane t decodes block b = t / 32 of the column pair cp = t % 32.
-    {
-      const int cp = t & 31, b = t >> 5;
-      float v0[16], v1[16];
-      const int ca = 2 * cp, cb = 2 * cp + 1;
-      const float da = block_decode_scale((sc[ca][b >> 2] >> (8 * (b & 3))) & 0xFFu, g);
-      const float db = block_decode_scale((sc[cb][b >> 2] >> (8 * (b & 3))) & 0xFFu, g);
-      e2m1_decode8(cw[ca][2 * b], v0);
-      e2m1_decode8(cw[ca][2 * b + 1], v0 + 8);
-      e2m1_decode8(cw[cb][2 * b], v1);
-      e2m1_decode8(cw[cb][2 * b + 1], v1 + 8);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float xa = v0[i] * da, xb = v1[i] * db;
-        uint8_t* dst = &tile[(b * 16 + i) * kPitch + ca * kEl];
-        if (kBf16) {
-          const f32x2 p = {xa, xb};
-          *reinterpret_cast<uint32_t*>(dst) = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
-        } else {
-          *reinterpret_cast<u32x2*>(dst) = u32x2{__float_as_uint(xa), __float_as_uint(xb)};
+      for (int h = 0; h < kLoadH; ++h) {
+        const int k = u + h * kHalf, c = k >> 4, b = k & 15;
+        if (c < ncol && b < nrb) {
+          const uint32_t* src = reinterpret_cast<const uint32_t*>(
+              packed + (c0 + c) * (rows / 2) + (r0 / 16 + b) * 8);
+          in.c[2 * h] = __builtin_nontemporal_load(src);
+          in.c[2 * h + 1] = __builtin_nontemporal_load(src + 1);
         }
       }
-    }
-    __syncthreads();
-    // 3. rows of x: 256 rows x (64 * kEl) bytes, 16 bytes per lane and step.
-    constexpr int kSegs = kDtCols * kEl / 16;  // 8 (bf16) or 16 (fp32) per row
-    for (int k = t; k < kDtRows * kSegs; k += kDtThreads) {
-      const int r = k / kSegs, sg = k % kSegs;
-      const int64_t gr = r0 + r;
-      const int64_t gc = c0 + sg * (16 / kEl);
-      if (gr < r0 + nrb * 16 && gc < cols) {
-        const uint8_t* src = &tile[r * kPitch + sg * 16];
-        const u32x2 a = *reinterpret_cast<const u32x2*>(src);
-        const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
-        uint8_t* dst = static_cast<uint8_t*>(out) + (gr * cols + gc) * kEl;
-        if (gc + 16 / kEl <= cols && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
-          // Measured: non-temporal stores are faster for the bf16 rows
-          // (128 bytes per row and tile), the default policy for fp32 (256).
-          if (kBf16)
-            __builtin_nontemporal_store(u32x4{a.x, a.y, b.x, b.y}, reinterpret_cast<u32x4*>(dst));
-          else
-            *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b.x, b.y};
+      if (u < ncol) {
+        const uint8_t* src = scales + (c0 + u) * rb_col + r0 / 16;
+        if (scales16 && nrb == 16) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+          in.s[0] = w.x; in.s[1] = w.y; in.s[2] = w.z; in.s[3] = w.w;
         } else {
-          const uint32_t w[4] = {a.x, a.y, b.x, b.y};
-          const int n = (int)((cols - gc) < 16 / kEl ? (cols - gc) : 16 / kEl);
-          for (int e = 0; e < n; ++e) {
-            if (kBf16)
-              reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-            else
-              reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+          for (int b = 0; b < nrb; ++b) in.s[b >> 2] |= (uint32_t)src[b] << (8 * (b & 3));
+        }
+      }
+      return in;
+    };
+
+    In nxt = load(blockIdx.x);
+    for (int64_t tt = blockIdx.x; tt < ntiles; tt += gridDim.x) {
+      const int64_t strip = tt / nrt, rt = tt % nrt;
+      const int64_t c0 = strip * kDtCols, r0 = rt * kDtRows;
+      const int nrb = (int)((rows - r0) / 16 < 16 ? (rows - r0) / 16 : 16);
+      __syncthreads();  // the previous tile's LDS contents have been read
+      // 1. stage the codes and scale bytes in LDS (loading waves).
+      if (loader) {
+        const In cur = nxt;
+#pragma unroll
+        for (int h = 0; h < kLoadH; ++h) {
+          const int k = u + h * kHalf, c = k >> 4, b = k & 15;
+          cw[c][2 * b] = cur.c[2 * h];
+          cw[c][2 * b + 1] = cur.c[2 * h + 1];
+        }
+        if (u < kDtCols) {
+          sc[u][0] = cur.s[0];
+          sc[u][1] = cur.s[1];
+          sc[u][2] = cur.s[2];
+          sc[u][3] = cur.s[3];
+        }
+      }
+      __syncthreads();
+      nxt = load(tt + gridDim.x);  // in flight during the decode and the stores
+      // 2. lane t decodes block b = t / 32 of the column pair cp = t % 32.
+      {
+        const int cp = t & 31, b = t >> 5;
+        float v0[16], v1[16];
+        const int ca = 2 * cp, cb = 2 * cp + 1;
+        const float da = block_decode_scale((sc[ca][b >> 2] >> (8 * (b & 3))) & 0xFFu, g);
+        const float db = block_decode_scale((sc[cb][b >> 2] >> (8 * (b & 3))) & 0xFFu, g);
+        e2m1_decode8(cw[ca][2 * b], v0);
+        e2m1_decode8(cw[ca][2 * b + 1], v0 + 8);
+        e2m1_decode8(cw[cb][2 * b], v1);
+        e2m1_decode8(cw[cb][2 * b + 1], v1 + 8);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float xa = v0[i] * da, xb = v1[i] * db;
+          uint8_t* dst = &tile[(b * 16 + i) * kPitch + ca * kEl];
+          if (kBf16) {
+            const f32x2 p = {xa, xb};
+            *reinterpret_cast<uint32_t*>(dst) =
+                __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+          } else {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{__float_as_uint(xa), __float_as_uint(xb)};
+          }
+        }
+      }
+      __syncthreads();
+      // 3. rows of x (storing waves): 256 rows x (64 * kEl) bytes, 16 bytes per
+      // lane and step.
+      constexpr int kSegs = kDtCols * kEl / 16;  // 8 (bf16) or 16 (fp32) per row
+      if (!loader) {
+        for (int k = u; k < kDtRows * kSegs; k += kHalf) {
+          const int r = k / kSegs, sg = k % kSegs;
+          const int64_t gr = r0 + r;
+          const int64_t gc = c0 + sg * (16 / kEl);
+          if (gr < r0 + nrb * 16 && gc < cols) {
+            const uint8_t* src = &tile[r * kPitch + sg * 16];
+            const u32x2 a = *reinterpret_cast<const u32x2*>(src);
+            const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
+            uint8_t* dst = static_cast<uint8_t*>(out) + (gr * cols + gc) * kEl;
+            if (gc + 16 / kEl <= cols && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+              // Measured: non-temporal stores are faster for the bf16 rows
+              // (128 bytes per row and tile), the default policy for fp32 (256).
+              if (kBf16)
+                __builtin_nontemporal_store(u32x4{a.x, a.y, b.x, b.y},
+                                            reinterpret_cast<u32x4*>(dst));
+              else
+                *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b.x, b.y};
+            } else {
+              const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+              const int n = (int)((cols - gc) < 16 / kEl ? (cols - gc) : 16 / kEl);
+              for (int e = 0; e < n; ++e) {
+                if (kBf16)
+                  reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                else
+                  reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+              }
+            }
           }
         }
       }
     }
-  }
+  };
+  if (loader_wave)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, const float* gscale,

@@ -162,6 +162,13 @@ int gemm_splits_hint(int64_t M, int64_t N, int64_t K);
 hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const RmsArgs& ra,
                            float six_m, uint32_t* acc, hipStream_t s);
 
+// The column quantizer's structure without its arithmetic (with_lds: loads,
+// LDS transpose and staging, barriers and stores, the block quantizer
+// replaced by a fold) or its global memory traffic alone (with_lds = 0).
+hipError_t launch_stream_pattern_cols(const uint16_t* in, int64_t rows, int64_t cols,
+                                     uint8_t* packed, uint8_t* scales, int with_lds,
+                                     hipStream_t s);
+
 // ---- verify.hip: the row quantizer's memory traffic without its arithmetic ----
 hipError_t launch_stream_pattern(const uint16_t* in, int64_t nblocks, uint8_t* packed,
                                  uint8_t* scales, hipStream_t s);

@@ -6,18 +6,19 @@
 // [cols][rows/2], scales [cols][rows/16], bitmap bit c*(rows/16) + rb.
 //
 // Tiles of 256 rows x 64 columns.  Per tile a workgroup of 8 waves
-//   1. has the tile's 256 row segments of 128 contiguous bytes in registers
-//      (4 x 16-byte loads per lane, issued one tile ahead so they are in
-//      flight while the previous tile is computed) and writes them row-major
-//      into LDS (row pitch 136 bytes, see the pitches below);
+//   1. has the tile's 256 row segments of 128 contiguous bytes in the
+//      registers of its four loading waves (8 x 16-byte loads per lane,
+//      issued one tile ahead so they are in flight while the previous tile
+//      is computed), which write them row-major into LDS (row pitch 136
+//      bytes, see the pitches below);
 //   2. lets every lane read a column pair over 16 rows (16 x 4-byte LDS
 //      reads, consecutive banks across each half-wave), which are two whole
 //      blocks; the lane repacks them and runs the same whole-block quantizer
 //      as the row-wise kernel on each;
 //   3. stages the codes (8 bytes per block), the scale bytes and the
-//      selection flags per column in LDS, so that each column's 128 bytes of
-//      codes and 16 scale bytes leave as 16-byte stores (whole 128-byte
-//      lines of codes per column and tile).
+//      selection flags per column in LDS, so that the four storing waves
+//      send each column's 128 bytes of codes and 16 scale bytes out as
+//      16-byte stores (whole 128-byte lines of codes per column and tile).
 // The grid is persistent (a few workgroups per compute unit) and walks the
 // tiles row-tile-major within each 64-column strip.  Workgroups are
 // renumbered so that consecutive tiles run on one XCD: the 8 row tiles that
@@ -28,6 +29,8 @@
 // row-direction blocks, read from the LDS tile (32 contiguous bytes each),
 // quantized by the same block quantizer and written in the row-blocked
 // layout; such a call walks strips fastest instead.
+#include <type_traits>
+
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -71,11 +74,29 @@ constexpr int kPasses = 512 / kColsThreads;        // column-pair tasks per lane
 static_assert(kColsThreads == 256 || kColsThreads == 512, "tile mapping");
 
 
+// Stand-in for the block quantizer in the measurement kernel (kPat 1): a
+// fold of the block's eight words.
+__device__ __forceinline__ Block16 fold_block(const uint32_t w[8]) {
+  Block16 q;
+  q.lo = w[0] ^ w[1] ^ w[2] ^ w[3];
+  q.hi = w[4] ^ w[5] ^ w[6] ^ w[7];
+  q.S = (q.lo ^ q.hi) & 0x7Fu;
+  q.b = 0.0f;
+  q.pick4 = false;
+  q.err = 0.0f;
+  return q;
+}
+
 // kDual: also quantize the tile's row-direction blocks (16 contiguous
 // elements of a row) into the row-blocked outputs packed_r / scales_r (scale
 // bit 7 marks the kept max->4 candidate for the bitmap pass) and err_r.
 // order: 0 walks row tiles fastest within a strip, 1 strips fastest.
-template <uint32_t V, bool kDual>
+// kPat (measurement only): 0 quantizes; 1 keeps everything but the block
+// quantizer, which a fold of the block's words replaces (the loads, the LDS
+// transpose and staging, the barriers, the stores); 2 keeps only the global
+// memory traffic (each lane folds its loaded words into the 16 bytes it
+// would store, with no LDS and no barrier).
+template <uint32_t V, bool kDual, int kPat = 0>
 __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     const uint16_t* __restrict__ in, int64_t rows, int64_t cols, const float* __restrict__ gscale,
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
@@ -98,7 +119,7 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
   __shared__ double wsum_r[kColsWaves];
   __shared__ uint32_t wmax[kColsWaves];
 
-  const TensorScales ts = tensor_scales(*gscale);
+  const TensorScales ts = tensor_scales(kPat ? 1.0f : *gscale);  // no scale in the probes
   build_scale_table(tab, ts);
 
   const int t = threadIdx.x;
@@ -123,9 +144,23 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
   const uint32_t wg =
       (nwg % 8u == 0u) ? (blockIdx.x % 8u) * (nwg / 8u) + blockIdx.x / 8u : blockIdx.x;
 
-  // Load k of lane t covers tile row k * kLoadRows + t/8, columns
-  // (t%8)*8 .. +7.
-  const int lrow = t >> 3, lseg = t & 7;
+  // Waves split by role (kSplit): the first half loads the tiles (one
+  // tile ahead), the second half stores the codes, scale and bitmap bytes,
+  // and all quantize.  A wave's memory counter then covers only its own
+  // kind of access: the loading waves wait for their loads alone, never for
+  // the previous tile's stores, which drain while the next tile is staged
+  // and quantized.  The dual call (whose row-direction blocks are stored by
+  // every lane) and the memory-only probe keep one role.
+  constexpr bool kSplit = !kDual && kPat != 2;
+  constexpr int kHalf = kColsThreads / 2;
+  constexpr int kLoadLanes = kSplit ? kHalf : kColsThreads;
+  constexpr int kLPL = kTileRows * kTileCols * 2 / (kLoadLanes * 16);  // loads per lane
+  constexpr int kLR = kLoadLanes / 8;  // tile rows covered by one load
+  const bool loader_wave = !kSplit || __builtin_amdgcn_readfirstlane(t) < kHalf;
+  const int u = (kSplit && !loader_wave) ? t - kHalf : t;  // index within the role
+  // Load k of a loading lane u covers tile row k * kLR + u/8, columns
+  // (u%8)*8 .. +7.
+  const int lrow = u >> 3, lseg = u & 7;
   auto tile_of = [&](int64_t tt, int64_t& strip, int64_t& rt) {
     if (order == 0) {
       strip = tt / nrt;
@@ -140,8 +175,8 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     tile_of(tt, strip, rt);
     const int64_t r0 = rt * kTileRows, c = strip * kTileCols + lseg * 8;
 #pragma unroll
-    for (int k = 0; k < kLoadsPerLane; ++k) {
-      const int64_t r = r0 + k * kLoadRows + lrow;
+    for (int k = 0; k < kLPL; ++k) {
+      const int64_t r = r0 + k * kLR + lrow;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (tt < ntiles && r < rows) {
         const uint16_t* src = in + r * cols + c;
@@ -162,23 +197,45 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
   const bool codes_r16 =
       kDual && (reinterpret_cast<uintptr_t>(packed_r) % 16 == 0) && ((cols / 2) % 16 == 0);
   // Quantizes tile tt from the registers w, then refills w with tile
-  // tt + nwg.
-  auto process = [&](int64_t tt, u32x4* w) {
+  // tt + nwg.  kLoad / kStore: this copy of the loop loads and stages the
+  // tiles / stores the outputs (both without kSplit).
+  auto process = [&](int64_t tt, u32x4* w, auto load_role) {
+    constexpr bool kLoad = decltype(load_role)::value || !kSplit;
+    constexpr bool kStore = !decltype(load_role)::value || !kSplit;
     int64_t strip, rt;
     tile_of(tt, strip, rt);
     const int64_t r0 = rt * kTileRows, c0 = strip * kTileCols;
     const int nrb = (int)((rows - r0) / 16 < kRowBlocks ? (rows - r0) / 16 : kRowBlocks);
     const int ncol = (int)(cols - c0 < kTileCols ? cols - c0 : kTileCols);
 
-    __syncthreads();  // the previous tile's staging has been stored (and tab built)
+    if constexpr (kPat == 2) {
+      // Global traffic only: the bytes this lane would store, from its loads.
+      u32x4 f = w[0];
 #pragma unroll
-    for (int k = 0; k < kLoadsPerLane; ++k) {
-      u32x2* dst = reinterpret_cast<u32x2*>(&tile[(k * kLoadRows + lrow) * kInPitch + lseg * 16]);
-      dst[0] = u32x2{w[k].x, w[k].y};
-      dst[1] = u32x2{w[k].z, w[k].w};
+      for (int k = 1; k < kLPL; ++k) f ^= w[k];
+      load_tile(tt + nwg, w);
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const int c = p * kLoadRows + (t >> 3), seg = t & 7;
+        if (c < ncol && 2 * seg + 1 < nrb && codes16)
+          __builtin_nontemporal_store(f, reinterpret_cast<u32x4*>(
+                                             packed + (c0 + c) * (rows / 2) + r0 / 2 + seg * 16));
+      }
+      if (t < ncol && scales16 && nrb == kRowBlocks)
+        *reinterpret_cast<u32x4*>(scales + (c0 + t) * rb_col + r0 / 16) = f;
+      return;
+    }
+    __syncthreads();  // the previous tile's staging has been stored (and tab built)
+    if constexpr (kLoad) {
+#pragma unroll
+      for (int k = 0; k < kLPL; ++k) {
+        u32x2* dst = reinterpret_cast<u32x2*>(&tile[(k * kLR + lrow) * kInPitch + lseg * 16]);
+        dst[0] = u32x2{w[k].x, w[k].y};
+        dst[1] = u32x2{w[k].z, w[k].w};
+      }
     }
     __syncthreads();
-    load_tile(tt + nwg, w);  // in flight during this tile's compute
+    if constexpr (kLoad) load_tile(tt + nwg, w);  // in flight during this tile's compute
 
     // 16 row blocks x 32 column pairs = 512 lane tasks, kPasses per lane:
     // in pass p, wave w takes row block (p * kColsWaves + w) * 2 + lane/32
@@ -197,8 +254,14 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
         wa[j] = (v[2 * j] & 0xFFFFu) | (v[2 * j + 1] << 16);
         wb[j] = (v[2 * j] >> 16) | (v[2 * j + 1] & 0xFFFF0000u);
       }
-      const Block16 qa = quantize_block16<k46, kRule, kNeedErr>(wa, ts.k6, ts.k4, tab);
-      const Block16 qb = quantize_block16<k46, kRule, kNeedErr>(wb, ts.k6, ts.k4, tab);
+      Block16 qa, qb;
+      if constexpr (kPat == 1) {
+        qa = fold_block(wa);
+        qb = fold_block(wb);
+      } else {
+        qa = quantize_block16<k46, kRule, kNeedErr>(wa, ts.k6, ts.k4, tab);
+        qb = quantize_block16<k46, kRule, kNeedErr>(wb, ts.k6, ts.k4, tab);
+      }
       bmax = __builtin_elementwise_maximum(bmax, __builtin_elementwise_maximum(qa.b, qb.b));
       const int ca = 2 * cp, cb = 2 * cp + 1;
       u32x2 pa, pb;
@@ -221,11 +284,13 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     }
     __syncthreads();
 
-    // Codes: column c's nrb * 8 bytes go to packed[c][r0/2 ..]; in each pass
-    // lane t stores 16 bytes (two row blocks) of column p * kLoadRows + t/8.
+    // Codes: column c's nrb * 8 bytes go to packed[c][r0/2 ..]; each storing
+    // lane stores 16-byte pieces (two row blocks each) of columns.
+    constexpr int kStoreLanes = kSplit ? kHalf : kColsThreads;
+    constexpr int kPieces = kTileCols * 8 / kStoreLanes;  // 16-byte pieces per lane
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int c = p * kLoadRows + (t >> 3), seg = t & 7;
+    for (int p = 0; p < (kStore ? kPieces : 0); ++p) {
+      const int piece = p * kStoreLanes + u, c = piece >> 3, seg = piece & 7;
       if (c < ncol && 2 * seg < nrb) {
         const uint32_t* src = reinterpret_cast<const uint32_t*>(&codes[c * kCodePitch + seg * 16]);
         const u32x4 cw = {src[0], src[1], src[2], src[3]};
@@ -244,8 +309,9 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
         }
       }
     }
-    // Scale bytes (and bitmap bytes): lane t < 64 handles column t.
-    if (t < ncol) {
+    // Scale bytes (and bitmap bytes): storing lane u < 64 handles column u.
+    if (kStore && u < ncol) {
+      const int t = u;  // the column
       const uint32_t* sw = reinterpret_cast<const uint32_t*>(&sbytes[t * kSPitch]);
       uint32_t s[4] = {sw[0], sw[1], sw[2], sw[3]};
       uint32_t bits = 0u;
@@ -317,9 +383,17 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     }
   };
 
-  u32x4 w[kLoadsPerLane];
-  load_tile(wg, w);
-  for (int64_t tt = wg; tt < ntiles; tt += nwg) process(tt, w);
+  // Each role runs its own copy of the tile loop (the same barriers in the
+  // same order), so that neither copy holds the other's memory operations.
+  auto run = [&](auto load_role) {
+    u32x4 w[kLPL];
+    if (decltype(load_role)::value) load_tile(wg, w);
+    for (int64_t tt = wg; tt < ntiles; tt += nwg) process(tt, w, load_role);
+  };
+  if (loader_wave)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   if (amax_out) group_max_to<kColsWaves>(amax_out, bmax, wmax);  // uniform branch
   if (kErr) {
@@ -401,6 +475,25 @@ static hipError_t launch_cols_v(const uint16_t* in, int64_t rows, int64_t cols,
   if (pass_c) e = bitmap_pass(scales, rows / 16 * cols, selmap, !pass_r);
   if (e == hipSuccess && pass_r) e = bitmap_pass(dual->scales_r, rows * cols / 16, dual->selmap_r, true);
   return e;
+}
+
+hipError_t launch_stream_pattern_cols(const uint16_t* in, int64_t rows, int64_t cols,
+                                     uint8_t* packed, uint8_t* scales, int with_lds,
+                                     hipStream_t s) {
+  const int64_t ntiles =
+      ((cols + kTileCols - 1) / kTileCols) * ((rows + kTileRows - 1) / kTileRows);
+  int64_t groups = (int64_t)device_cu_count() * kColsGroupsPerCu;
+  if (groups > ntiles) groups = ntiles;
+  if (groups < 1) groups = 1;
+  if (with_lds)
+    quantize_cols_kernel<0, false, 1><<<(unsigned)groups, kColsThreads, 0, s>>>(
+        in, rows, cols, nullptr, packed, scales, nullptr, nullptr, nullptr, nullptr, nullptr,
+        nullptr, 0);
+  else
+    quantize_cols_kernel<0, false, 2><<<(unsigned)groups, kColsThreads, 0, s>>>(
+        in, rows, cols, nullptr, packed, scales, nullptr, nullptr, nullptr, nullptr, nullptr,
+        nullptr, 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_cols(const uint16_t* in, int64_t rows, int64_t cols,

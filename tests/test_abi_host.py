@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(nv.SIGNATURES)
