@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace nvfp4 {
 
 constexpr float kFltMax = 3.40282346638528859812e+38f;
@@ -228,9 +230,17 @@ __device__ __forceinline__ float block_error(float lo, float hi) {
 // the two partial sums then added (or, for the maximum-error rule, the
 // largest single difference).
 //   `scales(S)` gives the (d, r) pair of scale byte S.
-template <bool k46, int kRule, bool kNeedErr, typename Scales>
+//   `mid()` (optional) runs right after both pairs are requested, before
+//   they are used: a caller's slot for independent work, e.g. issuing the
+//   next block's LDS reads behind the table reads.
+struct NoMid {
+  __device__ void operator()() const {}
+};
+template <bool k46, int kRule, bool kNeedErr, typename Scales, typename Mid = NoMid>
 __device__ __forceinline__ Block16 quantize_block16_with(const float x[16], float k6, float k4,
-                                                         const Scales& scales) {
+                                                         const Scales& scales,
+                                                         const Mid& mid = Mid{}) {
+  constexpr bool kMid = !std::is_same<Mid, NoMid>::value;
   const float b = __builtin_elementwise_maximum(
       absmax3(absmax3(x[0], x[1], x[2]), absmax3(x[3], x[4], x[5]), absmax3(x[6], x[7], x[8])),
       absmax3(absmax3(x[9], x[10], x[11]), absmax3(x[12], x[13], x[14]), x[15]));
@@ -238,6 +248,11 @@ __device__ __forceinline__ Block16 quantize_block16_with(const float x[16], floa
   const uint32_t S2 = e4m3_encode2(b * k6, k46 ? b * k4 : 0.0f);
   const uint32_t S6 = S2 & 0xFFu, S4 = (S2 >> 8) & 0xFFu;
   const float2 t6 = scales(S6);  // (d, r)
+  float2 t4 = {0.0f, 0.0f};
+  if constexpr (kMid) {
+    if (k46) t4 = scales(S4);
+    mid();
+  }
 
   float y[8];
 #pragma unroll
@@ -258,7 +273,7 @@ __device__ __forceinline__ Block16 quantize_block16_with(const float x[16], floa
   r.pick4 = false;
   r.err = e6;
   if (k46) {
-    const float2 t4 = scales(S4);
+    if constexpr (!kMid) t4 = scales(S4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = x[i] * t4.y;
     const uint32_t c4lo = e2m1_encode8(y);
@@ -277,11 +292,11 @@ __device__ __forceinline__ Block16 quantize_block16_with(const float x[16], floa
 }
 
 // The same with the (d, r) pairs read from a table tab[S] (LDS).
-template <bool k46, int kRule, bool kNeedErr>
+template <bool k46, int kRule, bool kNeedErr, typename Mid = NoMid>
 __device__ __forceinline__ Block16 quantize_block16f(const float x[16], float k6, float k4,
-                                                     const float2* tab) {
-  return quantize_block16_with<k46, kRule, kNeedErr>(x, k6, k4,
-                                                     [tab](uint32_t S) { return tab[S]; });
+                                                     const float2* tab, const Mid& mid = Mid{}) {
+  return quantize_block16_with<k46, kRule, kNeedErr>(
+      x, k6, k4, [tab](uint32_t S) { return tab[S]; }, mid);
 }
 
 // The same for a block of 16 bf16 values: wd[0..7] hold them in pairs

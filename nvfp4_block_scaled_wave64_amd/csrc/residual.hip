@@ -46,6 +46,12 @@
 
 namespace nvfp4 {
 
+// Cache policy of the code stores (8 bytes per block, scattered over the
+// rows of a batch): non-temporal.  Measured on 32768 x 5120, nres 256: 1.6 us
+// of 93 faster than sc1 (the row-wise quantizer's choice), 3 us faster than
+// the default policy.
+constexpr int kResCodeStore = 2;
+
 // ---------------------------------------------------------------- absmax --
 
 constexpr int kAbsThreads = 512;
@@ -182,46 +188,60 @@ __device__ void poison_rows(int64_t row0, int64_t stride, int64_t rows, uint32_t
 
 // -------------------------------------------------------------- quantize --
 
-// Output block j of one staged row xr (bf16 in LDS): gathers the channels
-// pm[16j .. 16j+15], quantizes them, stores codes and scale as block ob of
-// the output, and with `res` also block ob + nb: the residual block, or with
-// `dup` (the weight side of the augmented product) a copy of block ob.
+// Channel offsets of output block j: pm[16j .. 16j+15], byte offsets into
+// a staged row, two per dword.
+struct BlockIdx {
+  u32x4 a, b;
+};
+__device__ __forceinline__ BlockIdx read_block_idx(const uint16_t* pm, uint32_t j) {
+  const u32x4* p4 = reinterpret_cast<const u32x4*>(pm + j * 16u);
+  return BlockIdx{p4[0], p4[1]};
+}
+
+// Gathers the 16 channels of a block from the staged row xr (bf16 in LDS):
+// w[k] = the bf16 pattern of element k in the low 16 bits.
+__device__ __forceinline__ void gather_block(const uint16_t* xr, const BlockIdx& ix,
+                                             uint32_t (&w)[16]) {
+  const uint32_t o[8] = {ix.a.x, ix.a.y, ix.a.z, ix.a.w, ix.b.x, ix.b.y, ix.b.z, ix.b.w};
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(xr);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    w[2 * k] = *reinterpret_cast<const uint16_t*>(xb + (o[k] & 0xFFFFu));
+    w[2 * k + 1] = *reinterpret_cast<const uint16_t*>(xb + (o[k] >> 16));
+  }
+}
+
+// Output block ob from its gathered channels w (gather_block): quantizes
+// them, stores codes and scale as block ob of the output, and with `res`
+// also block ob + nb: the residual block, or with `dup` (the weight side of
+// the augmented product) a copy of block ob.
 //   stash (nullable): instead of quantizing the residual block here, store
 //   its 16 values x - v*d to stash[q * plane] (q = 0..3, float4 each) for a
 //   later pass that quantizes up to 64 of them at once (stash_quantize).
 //   The stash is four planes of float4 (values 4q .. 4q+3 of every block in
 //   plane q), so that consecutive lanes access consecutive 16-byte slots.
-template <bool k46, int kRule>
-__device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_t* pm,
-                                               uint32_t j, uint32_t ob, uint32_t nb, bool res,
-                                               bool dup,
-                                               __amdgpu_buffer_rsrc_t r_packed,
-                                               __amdgpu_buffer_rsrc_t r_scales,
-                                               const TensorScales& ts, const float2* tab,
-                                               float4* stash = nullptr, uint32_t plane = 0) {
+//   mid: run inside the block quantizer once its scale-table reads are
+//   issued (quantize_block16_with).
+template <bool k46, int kRule, typename Mid = NoMid>
+__device__ __forceinline__ void residual_tail(const uint32_t (&w)[16], uint32_t ob, uint32_t nb,
+                                              bool res, bool dup,
+                                              __amdgpu_buffer_rsrc_t r_packed,
+                                              __amdgpu_buffer_rsrc_t r_scales,
+                                              const TensorScales& ts, const float2* tab,
+                                              float4* stash = nullptr, uint32_t plane = 0,
+                                              const Mid& mid = Mid{}) {
   constexpr bool kNeedErr = k46;
-  // pm holds byte offsets into the row, two per dword; each gathered bf16
-  // becomes its fp32 value by a 16-bit shift.
-  const u32x4* p4 = reinterpret_cast<const u32x4*>(pm + j * 16u);
-  const u32x4 i0 = p4[0], i1 = p4[1];
-  const uint32_t ix[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-  const uint8_t* xb = reinterpret_cast<const uint8_t*>(xr);
   float x[16];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    x[2 * k] = __uint_as_float(
-        (uint32_t)*reinterpret_cast<const uint16_t*>(xb + (ix[k] & 0xFFFFu)) << 16);
-    x[2 * k + 1] =
-        __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(xb + (ix[k] >> 16)) << 16);
-  }
-  const Block16 q = quantize_block16f<k46, kRule, kNeedErr>(x, ts.k6, ts.k4, tab);
+  for (int k = 0; k < 16; ++k) x[k] = bf16_lo(w[k]);
+  const Block16 q = quantize_block16f<k46, kRule, kNeedErr>(x, ts.k6, ts.k4, tab, mid);
   u32x2 codes;
   codes.x = q.lo;
   codes.y = q.hi;
-  __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, ob * 8u, 0, kStreamStore);
+  __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, ob * 8u, 0, kResCodeStore);
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q.S, r_scales, ob, 0, kMergedStore);
   if (res && dup) {
-    __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, (ob + nb) * 8u, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, (ob + nb) * 8u, 0, kResCodeStore);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)q.S, r_scales, ob + nb, 0, kMergedStore);
   } else if (res) {
     // Residual of the kept candidate, x - v*d rounded once.
@@ -241,9 +261,21 @@ __device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_
     u32x2 rc;
     rc.x = qr.lo;
     rc.y = qr.hi;
-    __builtin_amdgcn_raw_buffer_store_b64(rc, r_packed, (ob + nb) * 8u, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b64(rc, r_packed, (ob + nb) * 8u, 0, kResCodeStore);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)qr.S, r_scales, ob + nb, 0, kMergedStore);
   }
+}
+
+// Output block j of one staged row xr: gather_block, then residual_tail.
+template <bool k46, int kRule>
+__device__ __forceinline__ void residual_block(const uint16_t* xr, const uint16_t* pm,
+                                               uint32_t j, uint32_t ob, uint32_t nb, bool res,
+                                               bool dup, __amdgpu_buffer_rsrc_t r_packed,
+                                               __amdgpu_buffer_rsrc_t r_scales,
+                                               const TensorScales& ts, const float2* tab) {
+  uint32_t w[16];
+  gather_block(xr, read_block_idx(pm, j), w);
+  residual_tail<k46, kRule>(w, ob, nb, res, dup, r_packed, r_scales, ts, tab);
 }
 
 // Quantizes one stashed residual block (its 16 values at stash[q * plane],
@@ -557,6 +589,14 @@ __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint1
   wave_max_to(acc, bf16_pair_max(ymax), six_m);
 }
 
+// Workgroup size bound of the narrow-row kernel: 12 waves where the row (in
+// registers), the normalization and two blocks in flight need more than 128
+// VGPRs.  Rows of 12 or more vectors per lane fit at most 12 waves per
+// compute unit in LDS anyway.
+constexpr int wave_threads(bool kRms, int kVpl) {
+  return (kVpl >= 12 || (kRms && kVpl >= 8)) ? 768 : 1024;
+}
+
 // Narrow rows (cols <= 8192): every wave owns one LDS row buffer and
 // streams its own rows with no workgroup barrier.  The next row's loads
 // (kVpl 16-byte vectors per lane) are in flight while the wave quantizes the
@@ -566,7 +606,7 @@ __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint1
 // (RMSNorm above), so the gathers, both stages and the residual see y; with
 // kVarAmax in V the kernel also folds max |y| into ra.amax_out.
 template <uint32_t V, int kVpl, bool kRms>
-__global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_residual_wave_kernel(
+__global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wave_kernel(
     const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
     uint32_t nres, const float* __restrict__ gscale, uint8_t* __restrict__ packed,
     uint8_t* __restrict__ scales, RmsArgs ra, uint32_t dup, uint32_t stash_items) {
@@ -629,6 +669,45 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
       buf[m] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + 64u * m) * 16u, 0, kStreamLoad);
   };
 
+  // The staged row's blocks j = lane, lane + 64, ... < nb, two in flight:
+  // the next block's channels are gathered (and the offsets of the one
+  // after it read) while the current block is quantized, right behind its
+  // scale-table reads, so that their LDS latency hides behind that work.
+  // Indices past the row are clamped to its last block (gathered and never
+  // used).
+  auto each_block = [&](auto&& tail) {
+    if (lane >= nb) return;
+    if constexpr (kRms && kVpl >= 16) {
+      // Rows of 16 vectors per lane with the normalization leave no
+      // registers for a second block: one at a time.
+#pragma unroll 1
+      for (uint32_t j = lane; j < nb; j += 64u) {
+        uint32_t w[16];
+        gather_block(xr, read_block_idx(pm, j), w);
+        tail(w, j, NoMid{});
+      }
+      return;
+    }
+    const uint32_t last = nb - 1u;
+    uint32_t wa[16], wb[16];
+    gather_block(xr, read_block_idx(pm, lane), wa);
+    BlockIdx ib = read_block_idx(pm, std::min(lane + 64u, last));
+    BlockIdx ia;
+#pragma unroll 1
+    for (uint32_t j = lane;; j += 128u) {
+      tail(wa, j, [&] {
+        gather_block(xr, ib, wb);
+        ia = read_block_idx(pm, std::min(j + 128u, last));
+      });
+      if (j + 64u >= nb) break;
+      tail(wb, j + 64u, [&] {
+        gather_block(xr, ia, wa);
+        ib = read_block_idx(pm, std::min(j + 192u, last));
+      });
+      if (j + 128u >= nb) break;
+    }
+  };
+
   // Stashed block i = slot * nrb + j (slot = the row's place in its batch)
   // is lane i's in the pass: its row and block are fixed per lane.
   const uint32_t my_slot = batch ? lane / nrb_ : 0u, my_j = batch ? lane % nrb_ : 0u;
@@ -660,10 +739,10 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
     const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed + row * bout * 8, bout * 8u);
     const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + row * bout, bout);
     if (batch) {
-#pragma unroll 1
-      for (uint32_t j = lane; j < nb; j += 64u)
-        residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, false, r_packed, r_scales, ts, tab,
-                                   stash + slot * nrb + j, stash_items);
+      each_block([&](const uint32_t(&w)[16], uint32_t j, const auto& mid) {
+        residual_tail<k46, kRule>(w, j, nb, j < nrb, false, r_packed, r_scales, ts, tab,
+                                  stash + slot * nrb + j, stash_items, mid);
+      });
       // A full batch, or the wave's last row: quantize the stashed blocks
       // (LDS operations of one wave complete in order).
       if (++slot == batch || row + stride >= rows) {
@@ -678,10 +757,10 @@ __global__ __launch_bounds__(kRms ? rms_threads(kVpl) : 1024) void quantize_resi
         batch_row0 = row + stride;
       }
     } else {
-#pragma unroll 1
-      for (uint32_t j = lane; j < nb; j += 64u)
-        residual_block<k46, kRule>(xr, pm, j, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts,
-                                   tab);
+      each_block([&](const uint32_t(&w)[16], uint32_t j, const auto& mid) {
+        residual_tail<k46, kRule>(w, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts, tab,
+                                  nullptr, 0u, mid);
+      });
     }
   }
   if (kMax) wave_max_to(ra.amax_out, bf16_pair_max(ymax), 0.0f);
@@ -774,7 +853,7 @@ static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t
   // min(12, the waves without a stash).
   const int64_t nrb = nres / 16;
   const int64_t fixed = 1024 + cols * 2 + (kRms ? cols * 4 : 0);
-  const int64_t max_waves = (kRms ? rms_threads(kVpl) : 1024) / 64;
+  const int64_t max_waves = wave_threads(kRms, kVpl) / 64;
   auto waves_with = [&](int64_t items) {
     return std::min<int64_t>(max_waves, (163840 - fixed) / (cols * 2 + items * 64));
   };
