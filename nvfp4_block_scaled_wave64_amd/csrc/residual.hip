@@ -549,10 +549,11 @@ __device__ __forceinline__ void wave_max_to(uint32_t* dst, float m, float six_m)
 // First pass of the fused path when g is not given: max |y| over the
 // normalized tensor, folded into *acc as RN(max / six_m) = g.  One row per
 // wave, the weight vector in LDS.
-// Workgroup size of the kernels that normalize rows of kVpl >= 12 vectors
-// per lane: 12 waves, which leaves each wave room for its row, the
-// normalization and (fused) the block quantizer in registers.
-constexpr int rms_threads(int kVpl) { return kVpl >= 12 ? 768 : 1024; }
+// Workgroup size of the kernels that normalize rows of kVpl >= 10 vectors
+// per lane: 12 waves, which leaves each wave room for its row (two, in the
+// first pass), the normalization and (fused) the block quantizer in
+// registers.
+constexpr int rms_threads(int kVpl) { return kVpl >= 10 ? 768 : 1024; }
 
 template <int kVpl>
 __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint16_t* __restrict__ in,
@@ -574,15 +575,24 @@ __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint1
     for (int m = 0; m < kVpl; ++m)
       buf[m] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + 64u * m) * 16u, 0, kStreamLoad);
   };
-  // The next row's loads are in flight while the current row is reduced.
+  // The next row's loads are in flight while the current row is reduced,
+  // where two rows fit in registers (up to 10 vectors per lane); wider rows
+  // load one row at a time and rely on the other waves.
   const int64_t first = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  constexpr bool kAhead = kVpl <= 10;
   u32x4 nxt[kVpl];
-  if (first < rows) load(first, nxt);
+  if constexpr (kAhead) {
+    if (first < rows) load(first, nxt);
+  }
   for (int64_t row = first; row < rows; row += stride) {
     u32x4 buf[kVpl];
+    if constexpr (kAhead) {
 #pragma unroll
-    for (int m = 0; m < kVpl; ++m) buf[m] = nxt[m];
-    if (row + stride < rows) load(row + stride, nxt);
+      for (int m = 0; m < kVpl; ++m) buf[m] = nxt[m];
+      if (row + stride < rows) load(row + stride, nxt);
+    } else {
+      load(row, buf);
+    }
     const float rstd = rms_rstd(row_sumsq<kVpl>(buf, vrow), cols, ra.eps);
     rms_apply<kVpl, true>(buf, wf, lane, vrow, rstd, ymax);
   }
@@ -594,7 +604,7 @@ __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint1
 // VGPRs.  Rows of 12 or more vectors per lane fit at most 12 waves per
 // compute unit in LDS anyway.
 constexpr int wave_threads(bool kRms, int kVpl) {
-  return (kVpl >= 12 || (kRms && kVpl >= 8)) ? 768 : 1024;
+  return (kVpl >= 10 || (kRms && kVpl >= 8)) ? 768 : 1024;
 }
 
 // Narrow rows (cols <= 8192): every wave owns one LDS row buffer and
@@ -898,6 +908,9 @@ static hipError_t launch_residual_v(const uint16_t* in, int64_t rows, int64_t co
   if (cols <= 4096)
     return launch_residual_wave<V, 8, false>(in, rows, cols, perm, nres, gscale, packed, scales,
                                            RmsArgs{}, dup, s);
+  if (cols <= 5120)
+    return launch_residual_wave<V, 10, false>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                           RmsArgs{}, dup, s);
   if (cols <= 6144)
     return launch_residual_wave<V, 12, false>(in, rows, cols, perm, nres, gscale, packed, scales,
                                            RmsArgs{}, dup, s);
@@ -917,6 +930,9 @@ static hipError_t launch_rms_residual_v(const uint16_t* in, int64_t rows, int64_
                                             ra, false, s);
   if (cols <= 4096)
     return launch_residual_wave<V, 8, true>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                            ra, false, s);
+  if (cols <= 5120)
+    return launch_residual_wave<V, 10, true>(in, rows, cols, perm, nres, gscale, packed, scales,
                                             ra, false, s);
   if (cols <= 6144)
     return launch_residual_wave<V, 12, true>(in, rows, cols, perm, nres, gscale, packed, scales,
@@ -965,6 +981,7 @@ hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const
                            float six_m, uint32_t* acc, hipStream_t s) {
   if (cols <= 2048) return launch_rms_amax_v<4>(in, rows, cols, ra, six_m, acc, s);
   if (cols <= 4096) return launch_rms_amax_v<8>(in, rows, cols, ra, six_m, acc, s);
+  if (cols <= 5120) return launch_rms_amax_v<10>(in, rows, cols, ra, six_m, acc, s);
   if (cols <= 6144) return launch_rms_amax_v<12>(in, rows, cols, ra, six_m, acc, s);
   return launch_rms_amax_v<16>(in, rows, cols, ra, six_m, acc, s);
 }

@@ -227,7 +227,7 @@ RMS_SHAPES = [
     # (rows, cols, nres): every row-buffer size class of the fused kernel,
     # fewer rows than waves, ragged row counts, nres = 0 and nres = cols
     (1, 16, 16), (7, 48, 0), (100, 1040, 64), (33, 2048, 256), (65, 2064, 128), (40, 4096, 512),
-    (19, 5120, 256), (25, 6144, 96), (13, 6160, 1024), (9, 8192, 8192),
+    (11, 4112, 32), (19, 5120, 256), (25, 6144, 96), (13, 6160, 1024), (9, 8192, 8192),
 ]
 
 
