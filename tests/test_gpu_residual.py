@@ -131,7 +131,7 @@ RES_SHAPES = [
     # two and three rows per step, ragged last step), nres = 0 and nres = cols
     (1, 16, 16), (5, 48, 16), (37, 64, 0), (1000, 80, 32), (129, 1040, 112), (33, 5120, 256),
     (16, 8192, 512), (20, 8208, 1024), (3, 32768, 2048), (7, 256, 256), (37, 12288, 512),
-    (300, 16384, 1024), (500, 4112, 64),
+    (300, 16384, 1024), (500, 4112, 64), (9, 4096, 128), (11, 5136, 48),
 ]
 
 
@@ -227,7 +227,8 @@ RMS_SHAPES = [
     # (rows, cols, nres): every row-buffer size class of the fused kernel,
     # fewer rows than waves, ragged row counts, nres = 0 and nres = cols
     (1, 16, 16), (7, 48, 0), (100, 1040, 64), (33, 2048, 256), (65, 2064, 128), (40, 4096, 512),
-    (11, 4112, 32), (19, 5120, 256), (25, 6144, 96), (13, 6160, 1024), (9, 8192, 8192),
+    (11, 4112, 32), (19, 5120, 256), (5, 5136, 16), (25, 6144, 96), (13, 6160, 1024),
+    (9, 8192, 8192),
 ]
 
 
