@@ -49,7 +49,7 @@ constexpr int kWavesPerGroup = kThreads / 64;
 #define NVFP4_ROWS_THREADS 1024
 #endif
 #ifndef NVFP4_ROWS_SYNC_EVERY
-#define NVFP4_ROWS_SYNC_EVERY 2
+#define NVFP4_ROWS_SYNC_EVERY 1
 #endif
 constexpr int kRowsSyncEvery = NVFP4_ROWS_SYNC_EVERY;
 // One workgroup of 16 waves per compute unit: the 16 consecutive chunks a
