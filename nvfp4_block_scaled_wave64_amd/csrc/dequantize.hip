@@ -202,7 +202,10 @@ __global__ __launch_bounds__(kDtThreads) void dequantize_cols_kernel(
           const u32x4 w = *reinterpret_cast<const u32x4*>(src);
           in.s[0] = w.x; in.s[1] = w.y; in.s[2] = w.z; in.s[3] = w.w;
         } else {
-          for (int b = 0; b < nrb; ++b) in.s[b >> 2] |= (uint32_t)src[b] << (8 * (b & 3));
+          // Unrolled with constant word indices, so that in.s stays in registers.
+#pragma unroll
+          for (int b = 0; b < 16; ++b)
+            if (b < nrb) in.s[b >> 2] |= (uint32_t)src[b] << (8 * (b & 3));
         }
       }
       return in;
@@ -281,7 +284,9 @@ __global__ __launch_bounds__(kDtThreads) void dequantize_cols_kernel(
             } else {
               const uint32_t w[4] = {a.x, a.y, b.x, b.y};
               const int n = (int)((cols - gc) < 16 / kEl ? (cols - gc) : 16 / kEl);
-              for (int e = 0; e < n; ++e) {
+#pragma unroll
+              for (int e = 0; e < 16 / kEl; ++e) {
+                if (e >= n) break;
                 if (kBf16)
                   reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
                 else
