@@ -197,6 +197,12 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     res["residual_quantize_256ch_us"] = round(t_res * 1e6, 2)
     res["residual_quantize_256ch_gbps"] = round(res_bytes / t_res / 1e9, 1)
     res["residual_quantize_256ch_frac_of_hbm_peak"] = round(res_bytes / t_res / 1e9 / HBM_PEAK_GBPS, 4)
+    # The same kernel structure without the block arithmetic (loads, LDS
+    # staging, channel gathers, stores): the attainable time for it.
+    pk, sk = torch.empty_like(ro["packed"]), torch.empty_like(ro["scales"])
+    res["residual_pattern_call_us"] = round(call_time(
+        lambda: nv.stream_pattern_residual(xd, perm, nres, pk, sk), torch, stream) * 1e6, 2)
+    del pk, sk
     # RMSNorm in front (the fused path): one pass with a given g, and with g
     # computed from max |y| by a first pass.
     wgt = torch.from_numpy(testkit.fill((cols,), testkit.NORMAL, 1.0, 99).view(np.int16)).to(

@@ -70,6 +70,25 @@ nvfp4_status nvfp4v_stream_pattern_cols(const uint16_t* in_bf16, int64_t rows, i
                                         int with_lds, uint8_t* packed_out, uint8_t* scales_out,
                                         void* stream);
 
+/* The narrow-row residual quantizer's structure (nvfp4_quantize_residual,
+ * cols <= 8192) without its block arithmetic, as the attainable-time
+ * reference for that kernel: the same launch shape, row loads, LDS staging,
+ * channel gathers through perm and output stores, with the block quantizer
+ * replaced by a fold.  For output block j < cols/16 of a row, with g_k the
+ * bf16 bit pattern of the row's channel perm[16j + k] (k = 0..15):
+ * packed_out[8j .. 8j+7] = (g_0^g_2^...^g_14, g_1^g_3^...^g_15) as two
+ * little-endian 32-bit words (zero-extended), scales_out[j] = the low 7 bits
+ * of their XOR; residual block j (< nres/16) at cols/16 + j gets the same
+ * bytes.  Row r's blocks start at (cols + nres)/16 * r.  The bytes are not
+ * NVFP4 codes.  An entry of perm outside [0, cols) gives the poisoned rows
+ * of nvfp4_quantize_residual.  cols a multiple of 16 up to 8192, nres a
+ * multiple of 16 up to cols; in_bf16 16-byte, perm and packed_out 4-byte
+ * aligned. */
+nvfp4_status nvfp4v_stream_pattern_residual(const uint16_t* in_bf16, int64_t rows, int64_t cols,
+                                            const int32_t* perm, int64_t nres,
+                                            uint8_t* packed_out, uint8_t* scales_out,
+                                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif
