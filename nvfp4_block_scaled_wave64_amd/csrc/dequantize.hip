@@ -159,6 +159,12 @@ __global__ __launch_bounds__(kDtThreads) void dequantize_cols_kernel(
   // loading waves wait for their loads alone (issued a tile ahead) and never
   // for the previous tile's stores, which drain while the next tile is
   // staged and decoded.
+  // Consecutive tiles on one XCD (workgroups are dispatched round-robin over
+  // the 8 XCDs): the 8 row tiles of a strip share each 128-byte line of a
+  // column's scale bytes, which one L2 then fetches once.
+  const uint32_t nwg = gridDim.x;
+  const uint32_t wg =
+      (nwg % 8u == 0u) ? (blockIdx.x % 8u) * (nwg / 8u) + blockIdx.x / 8u : blockIdx.x;
   constexpr int kHalf = kDtThreads / 2;
   const bool loader_wave = __builtin_amdgcn_readfirstlane(t) < kHalf;  // wave-uniform
 
@@ -213,8 +219,8 @@ __global__ __launch_bounds__(kDtThreads) void dequantize_cols_kernel(
       return in;
     };
 
-    In nxt = load(blockIdx.x);
-    for (int64_t tt = blockIdx.x; tt < ntiles; tt += gridDim.x) {
+    In nxt = load(wg);
+    for (int64_t tt = wg; tt < ntiles; tt += gridDim.x) {
       const int64_t strip = tt / nrt, rt = tt % nrt;
       const int64_t c0 = strip * kDtCols, r0 = rt * kDtRows;
       const int nrb = (int)((rows - r0) / 16 < 16 ? (rows - r0) / 16 : 16);
