@@ -508,8 +508,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 template <bool kMax>
 __device__ __forceinline__ uint32_t rms_pair(uint32_t x, float wl, float wh, float rstd,
                                              uint32_t& ymax) {
-  uint32_t y = pack_bf16(bf16_lo(x) * rstd, bf16_hi(x) * rstd);
-  y = pack_bf16(wl * bf16_lo(y), wh * bf16_hi(y));
+  // bf16(x * rstd) of each half straight as an fp32 value: converting the
+  // pair (0, v) puts bf16(v) in the high half over a zero low half.
+  const float yl = __uint_as_float(pack_bf16(0.0f, bf16_lo(x) * rstd));
+  const float yh = __uint_as_float(pack_bf16(0.0f, bf16_hi(x) * rstd));
+  const uint32_t y = pack_bf16(wl * yl, wh * yh);
   if (kMax) ymax = max_u16x2(ymax, y & 0x7FFF7FFFu);
   return y;
 }
