@@ -197,12 +197,6 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     res["residual_quantize_256ch_us"] = round(t_res * 1e6, 2)
     res["residual_quantize_256ch_gbps"] = round(res_bytes / t_res / 1e9, 1)
     res["residual_quantize_256ch_frac_of_hbm_peak"] = round(res_bytes / t_res / 1e9 / HBM_PEAK_GBPS, 4)
-    # The same kernel structure without the block arithmetic (loads, LDS
-    # staging, channel gathers, stores): the attainable time for it.
-    pk, sk = torch.empty_like(ro["packed"]), torch.empty_like(ro["scales"])
-    res["residual_pattern_call_us"] = round(call_time(
-        lambda: nv.stream_pattern_residual(xd, perm, nres, pk, sk), torch, stream) * 1e6, 2)
-    del pk, sk
     # RMSNorm in front (the fused path): one pass with a given g, and with g
     # computed from max |y| by a first pass.
     wgt = torch.from_numpy(testkit.fill((cols,), testkit.NORMAL, 1.0, 99).view(np.int16)).to(
@@ -264,19 +258,9 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
         res[f"workload{cid}_frac_of_hbm_peak"] = round(
             cfg.rows * cfg.cols * BYTES_PER_ELEM / tm / 1e9 / HBM_PEAK_GBPS, 4)
         if cid == 5:
-            # The same access pattern without the block arithmetic (the
-            # attainable ceiling for this kernel): global traffic alone, and
-            # with the LDS transpose, staging and barriers; back-to-back calls
-            # of each and of the quantize call itself.
-            pk = torch.empty(cfg.rows * cfg.cols // 2, dtype=torch.uint8, device=dev)
-            sk = torch.empty(cfg.rows * cfg.cols // 16, dtype=torch.uint8, device=dev)
             res["workload5_call_us"] = round(call_time(
                 lambda: nv.quantize(xc, cfg.block_axis, cfg.mode, cfg.rule, gscale=gc, out=oc),
                 torch, stream) * 1e6, 2)
-            for lds, name in ((False, "memory"), (True, "lds")):
-                res[f"workload5_pattern_{name}_call_us"] = round(call_time(
-                    lambda: nv.stream_pattern_cols(xc, pk, sk, lds), torch, stream) * 1e6, 2)
-            del pk, sk
             # Dequantize of the column-blocked output back to [rows][cols]
             # (0.5625 B read, 2 or 4 B written per element).
             n5 = cfg.rows * cfg.cols

@@ -54,41 +54,6 @@ nvfp4_status nvfp4v_decode_tables(float g, float* e2m1_out, float* e4m3_out, flo
 nvfp4_status nvfp4v_stream_pattern(const uint16_t* in_bf16, int64_t nblocks, uint8_t* packed_out,
                                    uint8_t* scales_out, void* stream);
 
-/* The column-blocked quantizer's (NVFP4_AXIS_ROWS) access pattern without
- * its block arithmetic, as the attainable-bandwidth reference for that
- * kernel: same launch shape, tile walk (256 rows x 64 columns), loads and
- * output stores (codes [cols][rows/2], scales [cols][rows/16]).
- *   with_lds = 1: also the kernel's LDS transpose, code staging and
- *     barriers, with the block quantizer replaced by a fold of each block's
- *     words (the codes are the XOR of words 0-3 and 4-7, the scale byte the
- *     low 7 bits of their XOR);
- *   with_lds = 0: the global memory traffic alone (each lane stores a fold
- *     of its loaded words where the kernel stores codes and scales).
- * The bytes written are not NVFP4 codes.  rows a multiple of 256, cols of
- * 64; in_bf16, packed_out and scales_out 16-byte aligned. */
-nvfp4_status nvfp4v_stream_pattern_cols(const uint16_t* in_bf16, int64_t rows, int64_t cols,
-                                        int with_lds, uint8_t* packed_out, uint8_t* scales_out,
-                                        void* stream);
-
-/* The narrow-row residual quantizer's structure (nvfp4_quantize_residual,
- * cols <= 8192) without its block arithmetic, as the attainable-time
- * reference for that kernel: the same launch shape, row loads, LDS staging,
- * channel gathers through perm and output stores, with the block quantizer
- * replaced by a fold.  For output block j < cols/16 of a row, with g_k the
- * bf16 bit pattern of the row's channel perm[16j + k] (k = 0..15):
- * packed_out[8j .. 8j+7] = (g_0^g_2^...^g_14, g_1^g_3^...^g_15) as two
- * little-endian 32-bit words (zero-extended), scales_out[j] = the low 7 bits
- * of their XOR; residual block j (< nres/16) at cols/16 + j gets the same
- * bytes.  Row r's blocks start at (cols + nres)/16 * r.  The bytes are not
- * NVFP4 codes.  An entry of perm outside [0, cols) gives the poisoned rows
- * of nvfp4_quantize_residual.  cols a multiple of 16 up to 8192, nres a
- * multiple of 16 up to cols; in_bf16 16-byte, perm and packed_out 4-byte
- * aligned. */
-nvfp4_status nvfp4v_stream_pattern_residual(const uint16_t* in_bf16, int64_t rows, int64_t cols,
-                                            const int32_t* perm, int64_t nres,
-                                            uint8_t* packed_out, uint8_t* scales_out,
-                                            void* stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -64,8 +64,6 @@ SIGNATURES = {
     "nvfp4v_e4m3_encode_sweep": ([_U32, _I64, _P, _P], _I),
     "nvfp4v_decode_tables": ([ctypes.c_float, _P, _P, _P, _P, _P], _I),
     "nvfp4v_stream_pattern": ([_P, _I64, _P, _P, _P], _I),
-    "nvfp4v_stream_pattern_cols": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
-    "nvfp4v_stream_pattern_residual": ([_P, _I64, _I64, _P, _I64, _P, _P, _P], _I),
 }
 
 
@@ -511,36 +509,6 @@ def gemm_splitk_noalloc(a, b, splits, out, stream=None):
                                          _stream(stream))
     _check(st, "nvfp4_gemm_splitk_noalloc")
     return out
-
-
-def stream_pattern_cols(x, packed, scales, with_lds, stream=None):
-    """The column-blocked quantizer's access pattern without its arithmetic
-    (nvfp4v_stream_pattern_cols) on a [rows][cols] bf16 tensor: with_lds
-    keeps its LDS transpose, staging and barriers.  Measurement only."""
-    x = _bf16_input(x)
-    rows, cols = x.shape
-    packed = _need(packed, x.numel() // 2, torch.uint8, x.device, "packed")
-    scales = _need(scales, x.numel() // 16, torch.uint8, x.device, "scales")
-    _check(lib().nvfp4v_stream_pattern_cols(_ptr(x), rows, cols, int(bool(with_lds)), _ptr(packed),
-                                            _ptr(scales), _stream(stream)),
-           "nvfp4v_stream_pattern_cols")
-
-
-def stream_pattern_residual(x, perm, nres, packed, scales, stream=None):
-    """The narrow-row residual quantizer's structure without its arithmetic
-    (nvfp4v_stream_pattern_residual) on a [rows][cols] bf16 tensor with a
-    channel order perm (int32, cols) and nres residual channels: same
-    launch shape, loads, gathers and stores.  Measurement only; the bytes
-    written are a fold of the gathered values, not NVFP4 codes."""
-    x = _bf16_input(x)
-    rows, cols = x.shape
-    perm = _need(perm, cols, torch.int32, x.device, "perm")
-    width = cols + int(nres)
-    packed = _need(packed, rows * width // 2, torch.uint8, x.device, "packed")
-    scales = _need(scales, rows * width // 16, torch.uint8, x.device, "scales")
-    _check(lib().nvfp4v_stream_pattern_residual(_ptr(x), rows, cols, _ptr(perm), int(nres),
-                                                _ptr(packed), _ptr(scales), _stream(stream)),
-           "nvfp4v_stream_pattern_residual")
 
 
 def stream_pattern(x, packed, scales, stream=None):

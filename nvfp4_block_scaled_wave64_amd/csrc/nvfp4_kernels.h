@@ -68,7 +68,6 @@ enum : uint32_t {
   kVarSelmap = 4u,       // write the selection bitmap
   kVarErr = 8u,          // accumulate the per-tensor error sum
   kVarAmax = 32u,        // also fold the tensor's max |x| into amax_out (row kernel)
-  kVarProbe = 64u,       // measurement probe: a fold in place of the block arithmetic
 };
 
 // ---- amax.hip ----
@@ -162,22 +161,6 @@ int gemm_splits_hint(int64_t M, int64_t N, int64_t K);
 // Atomic max of RN(max |y| / six_m) into *acc (fp32 bits; the caller zeroes it).
 hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const RmsArgs& ra,
                            float six_m, uint32_t* acc, hipStream_t s);
-
-// The column quantizer's structure without its arithmetic (with_lds: loads,
-// LDS transpose and staging, barriers and stores, the block quantizer
-// replaced by a fold) or its global memory traffic alone (with_lds = 0).
-hipError_t launch_stream_pattern_cols(const uint16_t* in, int64_t rows, int64_t cols,
-                                     uint8_t* packed, uint8_t* scales, int with_lds,
-                                     hipStream_t s);
-
-// The narrow-row residual kernel's structure without its arithmetic: the
-// same launch shape, row loads, LDS staging, channel gathers and stores,
-// with the block quantizer replaced by a fold of each block's gathered
-// values (residual blocks get their primary block's bytes); cols <=
-// kRmsMaxCols.
-hipError_t launch_stream_pattern_residual(const uint16_t* in, int64_t rows, int64_t cols,
-                                          const int32_t* perm, int64_t nres, uint8_t* packed,
-                                          uint8_t* scales, hipStream_t s);
 
 // ---- verify.hip: the row quantizer's memory traffic without its arithmetic ----
 hipError_t launch_stream_pattern(const uint16_t* in, int64_t nblocks, uint8_t* packed,

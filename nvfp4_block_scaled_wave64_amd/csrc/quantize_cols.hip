@@ -68,35 +68,15 @@ static_assert(kInPitch % 8 == 0 && kCodePitch % 4 == 0 && kSPitch % 4 == 0, "LDS
 #endif
 constexpr int kColsThreads = NVFP4_COLS_THREADS;
 constexpr int kColsWaves = kColsThreads / 64;
-constexpr int kLoadsPerLane = kTileRows * kTileCols * 2 / (kColsThreads * 16);
-constexpr int kLoadRows = kColsThreads / 8;        // tile rows covered by one load
 constexpr int kPasses = 512 / kColsThreads;        // column-pair tasks per lane
 static_assert(kColsThreads == 256 || kColsThreads == 512, "tile mapping");
 
-
-// Stand-in for the block quantizer in the measurement kernel (kPat 1): a
-// fold of the block's eight words.
-__device__ __forceinline__ Block16 fold_block(const uint32_t w[8]) {
-  Block16 q;
-  q.lo = w[0] ^ w[1] ^ w[2] ^ w[3];
-  q.hi = w[4] ^ w[5] ^ w[6] ^ w[7];
-  q.S = (q.lo ^ q.hi) & 0x7Fu;
-  q.b = 0.0f;
-  q.pick4 = false;
-  q.err = 0.0f;
-  return q;
-}
 
 // kDual: also quantize the tile's row-direction blocks (16 contiguous
 // elements of a row) into the row-blocked outputs packed_r / scales_r (scale
 // bit 7 marks the kept max->4 candidate for the bitmap pass) and err_r.
 // order: 0 walks row tiles fastest within a strip, 1 strips fastest.
-// kPat (measurement only): 0 quantizes; 1 keeps everything but the block
-// quantizer, which a fold of the block's words replaces (the loads, the LDS
-// transpose and staging, the barriers, the stores); 2 keeps only the global
-// memory traffic (each lane folds its loaded words into the 16 bytes it
-// would store, with no LDS and no barrier).
-template <uint32_t V, bool kDual, int kPat = 0>
+template <uint32_t V, bool kDual>
 __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     const uint16_t* __restrict__ in, int64_t rows, int64_t cols, const float* __restrict__ gscale,
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales, uint8_t* __restrict__ selmap,
@@ -119,7 +99,7 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
   __shared__ double wsum_r[kColsWaves];
   __shared__ uint32_t wmax[kColsWaves];
 
-  const TensorScales ts = tensor_scales(kPat ? 1.0f : *gscale);  // no scale in the probes
+  const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
 
   const int t = threadIdx.x;
@@ -150,8 +130,8 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
   // kind of access: the loading waves wait for their loads alone, never for
   // the previous tile's stores, which drain while the next tile is staged
   // and quantized.  The dual call (whose row-direction blocks are stored by
-  // every lane) and the memory-only probe keep one role.
-  constexpr bool kSplit = !kDual && kPat != 2;
+  // every lane) keeps one role.
+  constexpr bool kSplit = !kDual;
   constexpr int kHalf = kColsThreads / 2;
   constexpr int kLoadLanes = kSplit ? kHalf : kColsThreads;
   constexpr int kLPL = kTileRows * kTileCols * 2 / (kLoadLanes * 16);  // loads per lane
@@ -208,23 +188,6 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
     const int nrb = (int)((rows - r0) / 16 < kRowBlocks ? (rows - r0) / 16 : kRowBlocks);
     const int ncol = (int)(cols - c0 < kTileCols ? cols - c0 : kTileCols);
 
-    if constexpr (kPat == 2) {
-      // Global traffic only: the bytes this lane would store, from its loads.
-      u32x4 f = w[0];
-#pragma unroll
-      for (int k = 1; k < kLPL; ++k) f ^= w[k];
-      load_tile(tt + nwg, w);
-#pragma unroll
-      for (int p = 0; p < kPasses; ++p) {
-        const int c = p * kLoadRows + (t >> 3), seg = t & 7;
-        if (c < ncol && 2 * seg + 1 < nrb && codes16)
-          __builtin_nontemporal_store(f, reinterpret_cast<u32x4*>(
-                                             packed + (c0 + c) * (rows / 2) + r0 / 2 + seg * 16));
-      }
-      if (t < ncol && scales16 && nrb == kRowBlocks)
-        *reinterpret_cast<u32x4*>(scales + (c0 + t) * rb_col + r0 / 16) = f;
-      return;
-    }
     __syncthreads();  // the previous tile's staging has been stored (and tab built)
     if constexpr (kLoad) {
 #pragma unroll
@@ -254,14 +217,8 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(
         wa[j] = (v[2 * j] & 0xFFFFu) | (v[2 * j + 1] << 16);
         wb[j] = (v[2 * j] >> 16) | (v[2 * j + 1] & 0xFFFF0000u);
       }
-      Block16 qa, qb;
-      if constexpr (kPat == 1) {
-        qa = fold_block(wa);
-        qb = fold_block(wb);
-      } else {
-        qa = quantize_block16<k46, kRule, kNeedErr>(wa, ts.k6, ts.k4, tab);
-        qb = quantize_block16<k46, kRule, kNeedErr>(wb, ts.k6, ts.k4, tab);
-      }
+      const Block16 qa = quantize_block16<k46, kRule, kNeedErr>(wa, ts.k6, ts.k4, tab);
+      const Block16 qb = quantize_block16<k46, kRule, kNeedErr>(wb, ts.k6, ts.k4, tab);
       bmax = __builtin_elementwise_maximum(bmax, __builtin_elementwise_maximum(qa.b, qb.b));
       const int ca = 2 * cp, cb = 2 * cp + 1;
       u32x2 pa, pb;
@@ -475,25 +432,6 @@ static hipError_t launch_cols_v(const uint16_t* in, int64_t rows, int64_t cols,
   if (pass_c) e = bitmap_pass(scales, rows / 16 * cols, selmap, !pass_r);
   if (e == hipSuccess && pass_r) e = bitmap_pass(dual->scales_r, rows * cols / 16, dual->selmap_r, true);
   return e;
-}
-
-hipError_t launch_stream_pattern_cols(const uint16_t* in, int64_t rows, int64_t cols,
-                                     uint8_t* packed, uint8_t* scales, int with_lds,
-                                     hipStream_t s) {
-  const int64_t ntiles =
-      ((cols + kTileCols - 1) / kTileCols) * ((rows + kTileRows - 1) / kTileRows);
-  int64_t groups = (int64_t)device_cu_count() * kColsGroupsPerCu;
-  if (groups > ntiles) groups = ntiles;
-  if (groups < 1) groups = 1;
-  if (with_lds)
-    quantize_cols_kernel<0, false, 1><<<(unsigned)groups, kColsThreads, 0, s>>>(
-        in, rows, cols, nullptr, packed, scales, nullptr, nullptr, nullptr, nullptr, nullptr,
-        nullptr, 0);
-  else
-    quantize_cols_kernel<0, false, 2><<<(unsigned)groups, kColsThreads, 0, s>>>(
-        in, rows, cols, nullptr, packed, scales, nullptr, nullptr, nullptr, nullptr, nullptr,
-        nullptr, 0);
-  return hipGetLastError();
 }
 
 hipError_t launch_quantize_cols(const uint16_t* in, int64_t rows, int64_t cols,

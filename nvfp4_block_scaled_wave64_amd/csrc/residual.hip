@@ -222,10 +222,7 @@ __device__ __forceinline__ void gather_block(const uint16_t* xr, const BlockIdx&
 //   plane q), so that consecutive lanes access consecutive 16-byte slots.
 //   mid: run inside the block quantizer once its scale-table reads are
 //   issued (quantize_block16_with).
-//   kProbe: a measurement probe; the codes are the XOR of the even- and of
-//   the odd-numbered gathered values (two words), the scale byte the low 7
-//   bits of their XOR, and the residual block (res) gets the same bytes.
-template <bool k46, int kRule, bool kProbe = false, typename Mid = NoMid>
+template <bool k46, int kRule, typename Mid = NoMid>
 __device__ __forceinline__ void residual_tail(const uint32_t (&w)[16], uint32_t ob, uint32_t nb,
                                               bool res, bool dup,
                                               __amdgpu_buffer_rsrc_t r_packed,
@@ -233,24 +230,6 @@ __device__ __forceinline__ void residual_tail(const uint32_t (&w)[16], uint32_t 
                                               const TensorScales& ts, const float2* tab,
                                               float4* stash = nullptr, uint32_t plane = 0,
                                               const Mid& mid = Mid{}) {
-  if constexpr (kProbe) {
-    uint32_t f0 = 0u, f1 = 0u;
-#pragma unroll
-    for (int k = 0; k < 16; k += 2) {
-      f0 ^= w[k];
-      f1 ^= w[k + 1];
-    }
-    mid();
-    const u32x2 codes = {f0, f1};
-    const uint8_t S = (uint8_t)((f0 ^ f1) & 0x7Fu);
-    __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, ob * 8u, 0, kResCodeStore);
-    __builtin_amdgcn_raw_buffer_store_b8(S, r_scales, ob, 0, kMergedStore);
-    if (res) {
-      __builtin_amdgcn_raw_buffer_store_b64(codes, r_packed, (ob + nb) * 8u, 0, kResCodeStore);
-      __builtin_amdgcn_raw_buffer_store_b8(S, r_scales, ob + nb, 0, kMergedStore);
-    }
-    return;
-  }
   constexpr bool kNeedErr = k46;
   float x[16];
 #pragma unroll
@@ -650,7 +629,6 @@ __global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wa
                         : (V & kVarMae) ? kRuleMae
                                         : kRuleMse;
   constexpr bool kMax = kRms && (V & kVarAmax) != 0;
-  constexpr bool kProbe = (V & kVarProbe) != 0;  // measurement probe (residual_tail)
   // LDS: scale table (1 KiB), channel order (cols 16-bit byte offsets),
   // with kRms the weights as fp32 (cols * 4 bytes), one row per wave.
   extern __shared__ __align__(16) uint8_t lds[];
@@ -668,7 +646,7 @@ __global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wa
   // of batch = stash_items / nrb rows, so that the second stage runs on
   // (nearly) full waves instead of a few lanes per row.
   const uint32_t nrb_ = nres >> 4;
-  const uint32_t batch = (stash_items && !kProbe) ? stash_items / nrb_ : 0u;
+  const uint32_t batch = stash_items ? stash_items / nrb_ : 0u;
   const uint32_t stash_bytes = stash_items * 64u;
   uint8_t* wave_area = reinterpret_cast<uint8_t*>(pm + cols + (kRms ? 2u * cols : 0u)) +
                        (size_t)(cols * 2u + stash_bytes) * wave;
@@ -676,7 +654,7 @@ __global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wa
   float4* stash = reinterpret_cast<float4*>(wave_area + cols * 2u);
   u32x4* xr4 = reinterpret_cast<u32x4*>(xr);
 
-  const TensorScales ts = tensor_scales(kProbe ? 1.0f : *gscale);
+  const TensorScales ts = tensor_scales(*gscale);
   build_scale_table(tab, ts);
   // Clamped byte offsets; an entry outside [0, cols) poisons the output.
   int bad = 0;
@@ -775,7 +753,7 @@ __global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wa
     const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + row * bout, bout);
     if (batch) {
       each_block([&](const uint32_t(&w)[16], uint32_t j, const auto& mid) {
-        residual_tail<k46, kRule, kProbe>(w, j, nb, j < nrb, false, r_packed, r_scales, ts, tab,
+        residual_tail<k46, kRule>(w, j, nb, j < nrb, false, r_packed, r_scales, ts, tab,
                                           stash + slot * nrb + j, stash_items, mid);
       });
       // A full batch, or the wave's last row: quantize the stashed blocks
@@ -793,7 +771,7 @@ __global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wa
       }
     } else {
       each_block([&](const uint32_t(&w)[16], uint32_t j, const auto& mid) {
-        residual_tail<k46, kRule, kProbe>(w, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts,
+        residual_tail<k46, kRule>(w, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts,
                                           tab, nullptr, 0u, mid);
       });
     }
@@ -1009,31 +987,6 @@ hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const
   if (cols <= 5120) return launch_rms_amax_v<10>(in, rows, cols, ra, six_m, acc, s);
   if (cols <= 6144) return launch_rms_amax_v<12>(in, rows, cols, ra, six_m, acc, s);
   return launch_rms_amax_v<16>(in, rows, cols, ra, six_m, acc, s);
-}
-
-hipError_t launch_stream_pattern_residual(const uint16_t* in, int64_t rows, int64_t cols,
-                                          const int32_t* perm, int64_t nres, uint8_t* packed,
-                                          uint8_t* scales, hipStream_t s) {
-  // The launch of nvfp4_quantize_residual (4/6, MSE, not duplicated) for
-  // these sizes, with the probe bit.
-  constexpr uint32_t V = kVarFourOverSix | kVarProbe;
-  const RmsArgs none{};
-  if (cols <= 2048)
-    return launch_residual_wave<V, 4, false>(in, rows, cols, perm, nres, nullptr, packed, scales,
-                                             none, false, s);
-  if (cols <= 4096)
-    return launch_residual_wave<V, 8, false>(in, rows, cols, perm, nres, nullptr, packed, scales,
-                                             none, false, s);
-  if (cols <= 5120)
-    return launch_residual_wave<V, 10, false>(in, rows, cols, perm, nres, nullptr, packed, scales,
-                                              none, false, s);
-  if (cols <= 6144)
-    return launch_residual_wave<V, 12, false>(in, rows, cols, perm, nres, nullptr, packed, scales,
-                                              none, false, s);
-  if (cols <= kRmsMaxCols)
-    return launch_residual_wave<V, 16, false>(in, rows, cols, perm, nres, nullptr, packed, scales,
-                                              none, false, s);
-  return hipErrorInvalidValue;
 }
 
 hipError_t launch_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,

@@ -163,39 +163,4 @@ nvfp4_status nvfp4v_stream_pattern(const uint16_t* in_bf16, int64_t nblocks, uin
              : NVFP4_ERR_HIP;
 }
 
-nvfp4_status nvfp4v_stream_pattern_cols(const uint16_t* in_bf16, int64_t rows, int64_t cols,
-                                        int with_lds, uint8_t* packed_out, uint8_t* scales_out,
-                                        void* stream) {
-  if (!in_bf16 || !packed_out || !scales_out) return NVFP4_ERR_NULL;
-  if (with_lds != 0 && with_lds != 1) return NVFP4_ERR_ENUM;
-  if (rows <= 0 || cols <= 0 || rows % 256 != 0 || cols % 64 != 0 ||
-      rows > (int64_t(1) << 40) / cols)
-    return NVFP4_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(in_bf16) | reinterpret_cast<uintptr_t>(packed_out) |
-       reinterpret_cast<uintptr_t>(scales_out)) % 16 != 0)
-    return NVFP4_ERR_ALIGN;
-  return nvfp4::launch_stream_pattern_cols(in_bf16, rows, cols, packed_out, scales_out, with_lds,
-                                           static_cast<hipStream_t>(stream)) == hipSuccess
-             ? NVFP4_OK
-             : NVFP4_ERR_HIP;
-}
-
-nvfp4_status nvfp4v_stream_pattern_residual(const uint16_t* in_bf16, int64_t rows, int64_t cols,
-                                            const int32_t* perm, int64_t nres,
-                                            uint8_t* packed_out, uint8_t* scales_out,
-                                            void* stream) {
-  if (!in_bf16 || !perm || !packed_out || !scales_out) return NVFP4_ERR_NULL;
-  if (rows <= 0 || cols <= 0 || cols % 16 != 0 || cols > nvfp4::kRmsMaxCols || nres < 0 ||
-      nres > cols || nres % 16 != 0 || rows > (int64_t(1) << 40) / cols)
-    return NVFP4_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(in_bf16) & 15u) || (reinterpret_cast<uintptr_t>(perm) & 3u) ||
-      (reinterpret_cast<uintptr_t>(packed_out) & 3u))
-    return NVFP4_ERR_ALIGN;
-  return nvfp4::launch_stream_pattern_residual(in_bf16, rows, cols, perm, nres, packed_out,
-                                               scales_out, static_cast<hipStream_t>(stream)) ==
-                 hipSuccess
-             ? NVFP4_OK
-             : NVFP4_ERR_HIP;
-}
-
 }  // extern "C"

@@ -76,62 +76,3 @@ def test_stream_pattern_bytes(nblocks):
     np.testing.assert_array_equal(scales.cpu().numpy(), want_scales)
 
 
-def xor_fold(words, axis):
-    return np.bitwise_xor.reduce(words, axis=axis)
-
-
-@pytest.mark.parametrize("rows,cols", [(256, 64), (512, 320), (768, 5120)])
-def test_stream_pattern_cols_bytes(rows, cols):
-    """with_lds = 1: block (column c, row block b) folds its eight words
-    (rows 2i and 2i+1 of the column as one word) into codes at
-    packed[c][8b ..] and a scale byte at scales[c][b]; with_lds = 0 stays
-    inside the outputs."""
-    banner(f"stream pattern cols {rows}x{cols}")
-    x = testkit.fill((rows, cols), testkit.NORMAL, 1.0, rows + cols)
-    xd = to_device(x)
-    guard = 4096
-    packed = torch.full((rows * cols // 2 + guard,), 0xA5, dtype=torch.uint8, device="cuda")
-    scales = torch.full((rows * cols // 16 + guard,), 0x5A, dtype=torch.uint8, device="cuda")
-    nv.stream_pattern_cols(xd, packed, scales, True)
-    col = x.T.astype(np.uint32)                      # [cols][rows]
-    w = col[:, 0::2] | (col[:, 1::2] << 16)          # [cols][rows/2] words
-    w = w.reshape(cols, rows // 16, 8)
-    lo, hi = xor_fold(w[:, :, :4], 2), xor_fold(w[:, :, 4:], 2)
-    want_p = np.stack([lo, hi], axis=2).astype("<u4").view(np.uint8).reshape(-1)
-    want_s = ((lo ^ hi) & 0x7F).astype(np.uint8).reshape(-1)
-    got_p, got_s = packed.cpu().numpy(), scales.cpu().numpy()
-    np.testing.assert_array_equal(got_p[:want_p.size], want_p)
-    np.testing.assert_array_equal(got_s[:want_s.size], want_s)
-    assert (got_p[want_p.size:] == 0xA5).all() and (got_s[want_s.size:] == 0x5A).all()
-    packed.fill_(0xA5)
-    scales.fill_(0x5A)
-    nv.stream_pattern_cols(xd, packed, scales, False)
-    got_p, got_s = packed.cpu().numpy(), scales.cpu().numpy()
-    assert (got_p[want_p.size:] == 0xA5).all() and (got_s[want_s.size:] == 0x5A).all()
-
-
-@pytest.mark.parametrize("rows,cols,nres", [(64, 5120, 256), (37, 1040, 48), (19, 8192, 128),
-                                            (23, 4112, 16), (9, 6144, 0), (130, 2048, 2048)])
-def test_stream_pattern_residual_bytes(rows, cols, nres):
-    """Block j of row r folds the bf16 patterns of channels perm[16j ..
-    16j+15] (even and odd positions into two words); residual block j
-    repeats block j's bytes; nothing past the outputs is written."""
-    banner(f"stream pattern residual {rows}x{cols} nres={nres}")
-    x = testkit.fill((rows, cols), testkit.NORMAL, 1.0, 3 * rows + cols)
-    xd = to_device(x)
-    perm = np.random.default_rng(cols + nres).permutation(cols).astype(np.int32)
-    width = cols + nres
-    guard = 4096
-    packed = torch.full((rows * width // 2 + guard,), 0xA5, dtype=torch.uint8, device="cuda")
-    scales = torch.full((rows * width // 16 + guard,), 0x5A, dtype=torch.uint8, device="cuda")
-    nv.stream_pattern_residual(xd, torch.from_numpy(perm).cuda(), nres, packed, scales)
-    g = x[:, perm].astype(np.uint32).reshape(rows, cols // 16, 16)
-    f0, f1 = xor_fold(g[:, :, 0::2], 2), xor_fold(g[:, :, 1::2], 2)
-    f0 = np.concatenate([f0, f0[:, :nres // 16]], axis=1)
-    f1 = np.concatenate([f1, f1[:, :nres // 16]], axis=1)
-    want_p = np.stack([f0, f1], axis=2).astype("<u4").view(np.uint8).reshape(-1)
-    want_s = ((f0 ^ f1) & 0x7F).astype(np.uint8).reshape(-1)
-    got_p, got_s = packed.cpu().numpy(), scales.cpu().numpy()
-    np.testing.assert_array_equal(got_p[:want_p.size], want_p)
-    np.testing.assert_array_equal(got_s[:want_s.size], want_s)
-    assert (got_p[want_p.size:] == 0xA5).all() and (got_s[want_s.size:] == 0x5A).all()
