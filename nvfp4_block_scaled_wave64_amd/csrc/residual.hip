@@ -222,14 +222,15 @@ __device__ __forceinline__ void gather_block(const uint16_t* xr, const BlockIdx&
 //   plane q), so that consecutive lanes access consecutive 16-byte slots.
 //   mid: run inside the block quantizer once its scale-table reads are
 //   issued (quantize_block16_with).
+// Returns the primary block (codes and scale of block ob).
 template <bool k46, int kRule, typename Mid = NoMid>
-__device__ __forceinline__ void residual_tail(const uint32_t (&w)[16], uint32_t ob, uint32_t nb,
-                                              bool res, bool dup,
-                                              __amdgpu_buffer_rsrc_t r_packed,
-                                              __amdgpu_buffer_rsrc_t r_scales,
-                                              const TensorScales& ts, const float2* tab,
-                                              float4* stash = nullptr, uint32_t plane = 0,
-                                              const Mid& mid = Mid{}) {
+__device__ __forceinline__ Block16 residual_tail(const uint32_t (&w)[16], uint32_t ob,
+                                                 uint32_t nb, bool res, bool dup,
+                                                 __amdgpu_buffer_rsrc_t r_packed,
+                                                 __amdgpu_buffer_rsrc_t r_scales,
+                                                 const TensorScales& ts, const float2* tab,
+                                                 float4* stash = nullptr, uint32_t plane = 0,
+                                                 const Mid& mid = Mid{}) {
   constexpr bool kNeedErr = k46;
   float x[16];
 #pragma unroll
@@ -255,7 +256,7 @@ __device__ __forceinline__ void residual_tail(const uint32_t (&w)[16], uint32_t 
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         stash[plane * k] = float4{rx[4 * k], rx[4 * k + 1], rx[4 * k + 2], rx[4 * k + 3]};
-      return;
+      return q;
     }
     const Block16 qr = quantize_block16f<k46, kRule, kNeedErr>(rx, ts.k6, ts.k4, tab);
     u32x2 rc;
@@ -264,6 +265,7 @@ __device__ __forceinline__ void residual_tail(const uint32_t (&w)[16], uint32_t 
     __builtin_amdgcn_raw_buffer_store_b64(rc, r_packed, (ob + nb) * 8u, 0, kResCodeStore);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)qr.S, r_scales, ob + nb, 0, kMergedStore);
   }
+  return q;
 }
 
 // Output block j of one staged row xr: gather_block, then residual_tail.
@@ -427,6 +429,44 @@ __device__ __forceinline__ float wave_tree_sum(float t) {
   t = t + dpp_f32<0x142>(t);  // row_bcast:15 (lane 15 of each row to the next row)
   t = t + dpp_f32<0x143>(t);  // row_bcast:31 (lane 31 to rows 2 and 3)
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 63));
+}
+
+// One block held by a lane pair: lane 2b + h holds elements 8h .. 8h+7 of
+// block b.  The steps and roundings are those of quantize_block16_with: the
+// block max is the larger of the two halves' maxima (a maximum in any order),
+// each lane encodes its half under both candidates and sums its half's error
+// sequentially, and the block error joins the two halves (a sum or a
+// maximum: both commute, so the two lanes hold the same value and keep the
+// same candidate).  Returns this lane's 32-bit code word (its 8 codes) and
+// the kept scale byte.  Both lanes of every pair must be active.
+struct Half8 {
+  uint32_t w;
+  uint32_t S;
+};
+template <bool k46, int kRule>
+__device__ __forceinline__ Half8 quantize_half8(const float x[8], float k6, float k4,
+                                                const float2* tab) {
+  const float bh = __builtin_elementwise_maximum(
+      absmax3(x[0], x[1], x[2]), absmax3(absmax3(x[3], x[4], x[5]), x[6], x[7]));
+  const float b = __builtin_elementwise_maximum(bh, dpp_f32<0xB1>(bh));  // lane l ^ 1
+  const uint32_t S2 = e4m3_encode2(b * k6, k46 ? b * k4 : 0.0f);
+  const uint32_t S6 = S2 & 0xFFu, S4 = (S2 >> 8) & 0xFFu;
+  const float2 t6 = tab[S6];
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = x[i] * t6.y;
+  const uint32_t c6 = e2m1_encode8(y);
+  if constexpr (!k46) return Half8{c6, S6};
+  const float2 t4 = tab[S4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = x[i] * t4.y;
+  const uint32_t c4 = e2m1_encode8(y);
+  const float h6 = half_error<kRule>(x, c6, t6.x);
+  const float h4 = half_error<kRule>(x, c4, t4.x);
+  const float e6 = block_error<kRule>(h6, dpp_f32<0xB1>(h6));
+  const float e4 = block_error<kRule>(h4, dpp_f32<0xB1>(h4));
+  const bool pick4 = e4 < e6;  // ties and NaN keep max->6
+  return Half8{pick4 ? c4 : c6, pick4 ? S4 : S6};
 }
 
 // Sum of squares of the row a wave holds as kVpl 16-byte vectors per lane
@@ -610,6 +650,11 @@ constexpr int wave_threads(bool kRms, int kVpl) {
   return (kVpl >= 10 || (kRms && kVpl >= 8)) ? 768 : 1024;
 }
 
+// Instantiations that hold the two-lanes-per-block residual pass: the
+// plain kernels of 8 and 16 vectors per lane are at their register limit
+// already (the pass would spill there) and keep the stash.
+constexpr bool pair_res_fits(bool kRms, int kVpl) { return kRms || (kVpl != 8 && kVpl != 16); }
+
 // Narrow rows (cols <= 8192): every wave owns one LDS row buffer and
 // streams its own rows with no workgroup barrier.  The next row's loads
 // (kVpl 16-byte vectors per lane) are in flight while the wave quantizes the
@@ -622,7 +667,8 @@ template <uint32_t V, int kVpl, bool kRms>
 __global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wave_kernel(
     const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
     uint32_t nres, const float* __restrict__ gscale, uint8_t* __restrict__ packed,
-    uint8_t* __restrict__ scales, RmsArgs ra, uint32_t dup, uint32_t stash_items) {
+    uint8_t* __restrict__ scales, RmsArgs ra, uint32_t dup, uint32_t stash_items,
+    uint32_t pair_res) {
   constexpr bool k46 = (V & kVarFourOverSix) != 0;
   constexpr int kRule = !k46 ? kRuleMse
                         : (V & kVarMax) ? kRuleMax
@@ -724,6 +770,10 @@ __global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wa
   // Stashed block i = slot * nrb + j (slot = the row's place in its batch)
   // is lane i's in the pass: its row and block are fixed per lane.
   const uint32_t my_slot = batch ? lane / nrb_ : 0u, my_j = batch ? lane % nrb_ : 0u;
+  // pair_res (only where pair_res_fits): lane j < nrb keeps its primary
+  // block's codes and scale byte for the residual pass (pair_res implies
+  // nrb <= 32).
+  uint32_t keep_lo = 0u, keep_hi = 0u, keep_s = 0u;
   u32x4 buf[kVpl];
   if (first < rows) load(first, buf);
   uint32_t slot = 0;
@@ -751,10 +801,51 @@ __global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wa
     }
     const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed + row * bout * 8, bout * 8u);
     const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + row * bout, bout);
-    if (batch) {
+    if (pair_res_fits(kRms, kVpl) && pair_res) {
+      each_block([&](const uint32_t(&w)[16], uint32_t j, const auto& mid) {
+        const Block16 q = residual_tail<k46, kRule>(w, j, nb, false, false, r_packed, r_scales,
+                                                    ts, tab, nullptr, 0u, mid);
+        if (j < nrb) {
+          keep_lo = q.lo;
+          keep_hi = q.hi;
+          keep_s = q.S;
+        }
+      });
+      // Residual blocks, two lanes each (quantize_half8): lane 2b + h
+      // gathers elements 8h .. 8h+7 of block b again from the staged row,
+      // takes block b's codes and scale byte from lane b, and quantizes
+      // x - v*d (one fused multiply-add per element, as residual_tail).
+      // The exchanges run with every lane active.
+      const uint32_t src = lane >> 1;
+      const uint32_t p_lo = (uint32_t)__shfl((int)keep_lo, (int)src);
+      const uint32_t p_hi = (uint32_t)__shfl((int)keep_hi, (int)src);
+      const uint32_t p_s = (uint32_t)__shfl((int)keep_s, (int)src);
+      if (lane < 2u * nrb) {
+        const uint32_t b = lane >> 1, h = lane & 1u;
+        const u32x4 o = *reinterpret_cast<const u32x4*>(pm + 16u * b + 8u * h);
+        const uint32_t oo[4] = {o.x, o.y, o.z, o.w};
+        const uint8_t* xb = reinterpret_cast<const uint8_t*>(xr);
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = bf16_lo(*reinterpret_cast<const uint16_t*>(xb + (oo[k] & 0xFFFFu)));
+          x[2 * k + 1] = bf16_lo(*reinterpret_cast<const uint16_t*>(xb + (oo[k] >> 16)));
+        }
+        float v[8], rx[8];
+        e2m1_decode8(h ? p_hi : p_lo, v);
+        const float d = tab[p_s].x;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rx[k] = __builtin_fmaf(-v[k], d, x[k]);
+        const Half8 qr = quantize_half8<k46, kRule>(rx, ts.k6, ts.k4, tab);
+        __builtin_amdgcn_raw_buffer_store_b32(qr.w, r_packed, (nb + b) * 8u + 4u * h, 0,
+                                              kResCodeStore);
+        if (h == 0u)
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)qr.S, r_scales, nb + b, 0, kMergedStore);
+      }
+    } else if (batch) {
       each_block([&](const uint32_t(&w)[16], uint32_t j, const auto& mid) {
         residual_tail<k46, kRule>(w, j, nb, j < nrb, false, r_packed, r_scales, ts, tab,
-                                          stash + slot * nrb + j, stash_items, mid);
+                                  stash + slot * nrb + j, stash_items, mid);
       });
       // A full batch, or the wave's last row: quantize the stashed blocks
       // (LDS operations of one wave complete in order).
@@ -771,8 +862,8 @@ __global__ __launch_bounds__(wave_threads(kRms, kVpl)) void quantize_residual_wa
       }
     } else {
       each_block([&](const uint32_t(&w)[16], uint32_t j, const auto& mid) {
-        residual_tail<k46, kRule>(w, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts,
-                                          tab, nullptr, 0u, mid);
+        residual_tail<k46, kRule>(w, j, nb, j < nrb, dup != 0u, r_packed, r_scales, ts, tab,
+                                  nullptr, 0u, mid);
       });
     }
   }
@@ -870,8 +961,12 @@ static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t
   auto waves_with = [&](int64_t items) {
     return std::min<int64_t>(max_waves, (163840 - fixed) / (cols * 2 + items * 64));
   };
+  // Rows of at most 32 residual blocks take the two-lanes-per-block
+  // residual pass after each row (no stash) where the instantiation holds
+  // it; otherwise the stash or, failing that, the in-place second stage.
+  const bool pair_res = pair_res_fits(kRms, kVpl) && !dup && nrb > 0 && nrb <= 32;
   int64_t stash_items = 0;
-  if (!dup && nrb > 0) {
+  if (!dup && nrb > 0 && !pair_res) {
     const int64_t need = std::min<int64_t>(12, waves_with(0));
     for (int64_t cap : {32, 64})
       if (nrb <= cap && waves_with(cap) >= need) {
@@ -894,7 +989,7 @@ static hipError_t launch_residual_wave(const uint16_t* in, int64_t rows, int64_t
   quantize_residual_wave_kernel<V, kVpl, kRms>
       <<<(unsigned)groups, (unsigned)(waves * 64), lds, s>>>(
           in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, ra,
-          (uint32_t)dup, (uint32_t)stash_items);
+          (uint32_t)dup, (uint32_t)stash_items, (uint32_t)pair_res);
   return hipGetLastError();
 }
 
