@@ -375,24 +375,25 @@ def test_out_of_range_order_poisons_the_output(rows, cols, nres, rms):
     assert torch.isnan(nv.gemm(a, b)).all().item()
 
 
-# ------------------------------------------- stashed residual passes ----
+# ------------------------------------------ residual second-stage modes ----
 
 STASH_SHAPES = [
     # (rows, cols, nres): residual blocks per row nrb = nres / 16 and rows per
-    # wave chosen to cover every stash mode of the one-row-per-wave kernel --
-    # passes of 32 blocks over 16 rows (nrb = 2, full and partial batches),
-    # over 2 rows (nrb = 16: the 32768 x 5120 configuration's mode, several
-    # batches per wave), one row per pass (nrb = 17 and 32), the 64-block
-    # stash (nrb = 48), no stash (nrb = 80) -- and ragged per-wave row counts.
+    # wave chosen to cover every second-stage mode of the one-row-per-wave
+    # kernel, with ragged per-wave row counts and several rows per wave:
+    # the lane-pair pass after each row (nrb <= 32 at 4, 10 and 12 vectors
+    # per lane: nrb = 2, 16, 17, 32), the 32-block stash of the kernels at 8
+    # and 16 vectors per lane (passes over 2 and 4 rows, full and partial
+    # batches), the 64-block stash (nrb = 48) and no stash (nrb = 80).
     (70001, 80, 32), (9221, 80, 32), (15367, 5120, 256), (7000, 1040, 272), (6000, 512, 512),
-    (5000, 2048, 768), (4000, 2048, 1280),
+    (20000, 3072, 256), (9000, 8192, 128), (5000, 2048, 768), (4000, 2048, 1280),
 ]
 
 
 @pytest.mark.parametrize("rows,cols,nres", STASH_SHAPES)
 @pytest.mark.parametrize("mode,rule", [(F46, MSE), (F46, MAE)])
-def test_quantize_residual_stash_batches(rows, cols, nres, mode, rule):
-    banner(f"residual stash passes {rows}x{cols} nres={nres} rule={rule}")
+def test_quantize_residual_second_stage_modes(rows, cols, nres, mode, rule):
+    banner(f"residual second-stage modes {rows}x{cols} nres={nres} rule={rule}")
     x = outlier_tensor(5000 + cols + nres, rows, cols)
     perm = oracle.channel_order(oracle.channel_absmax(x))
     got = gpu_residual(x, perm, nres, mode, rule)
