@@ -116,6 +116,35 @@ def test_extreme_magnitudes():
     check_against_oracle(y, AXIS_COLS, F46, MAE, what="subnormal blocks")
 
 
+def random_finite_patterns(shape, e_lo, e_hi, seed):
+    """bf16 bit patterns with a random sign and mantissa and an exponent field
+    drawn uniformly from [e_lo, e_hi] (0 gives zeros and subnormals; 255,
+    infinity and NaN, is outside the contract and never drawn)."""
+    rng = np.random.default_rng(seed)
+    sign = rng.integers(0, 2, shape, dtype=np.uint16) << 15
+    exp = rng.integers(e_lo, e_hi + 1, shape, dtype=np.uint16) << 7
+    man = rng.integers(0, 128, shape, dtype=np.uint16)
+    return (sign | exp | man).astype(np.uint16)
+
+
+# Exponent windows: subnormal-heavy (amax near 1e-31), thirty binades
+# around 1 (blocks spanning wide ranges), and the top of the range (amax
+# near 3e38, squared errors overflowing to +inf).
+PATTERN_WINDOWS = [(0, 24), (112, 142), (224, 254)]
+
+
+@pytest.mark.parametrize("e_lo,e_hi", PATTERN_WINDOWS)
+@pytest.mark.parametrize("mode,rule", RULES)
+def test_random_finite_bit_patterns(e_lo, e_hi, mode, rule):
+    """Whole tensors of random finite bf16 patterns in one exponent window,
+    both block layouts, ragged shapes: every output bit-exact."""
+    banner(f"random patterns e=[{e_lo},{e_hi}] mode={mode} rule={rule}")
+    x = random_finite_patterns((96, 1040), e_lo, e_hi, 9000 + e_lo)
+    check_against_oracle(x, AXIS_COLS, mode, rule, what=f"patterns rows e>={e_lo}")
+    xc = random_finite_patterns((272, 48), e_lo, e_hi, 9100 + e_lo)
+    check_against_oracle(xc, AXIS_ROWS, mode, rule, what=f"patterns cols e>={e_lo}")
+
+
 def test_tiny_tensor_amax():
     banner("tiny amax")
     x = np.zeros((2, 32), np.uint16)

@@ -375,6 +375,53 @@ def test_out_of_range_order_poisons_the_output(rows, cols, nres, rms):
     assert torch.isnan(nv.gemm(a, b)).all().item()
 
 
+# ------------------------------------------- random finite bit patterns ----
+
+def random_finite_patterns(shape, e_lo, e_hi, seed):
+    """bf16 patterns with random sign and mantissa and an exponent field
+    uniform in [e_lo, e_hi] (never 255: infinity and NaN are outside the
+    contract)."""
+    rng = np.random.default_rng(seed)
+    sign = rng.integers(0, 2, shape, dtype=np.uint16) << 15
+    exp = rng.integers(e_lo, e_hi + 1, shape, dtype=np.uint16) << 7
+    man = rng.integers(0, 128, shape, dtype=np.uint16)
+    return (sign | exp | man).astype(np.uint16)
+
+
+@pytest.mark.parametrize("e_lo,e_hi", [(0, 24), (112, 142), (224, 254)])
+@pytest.mark.parametrize("rows,cols,nres", [(37, 1040, 112), (19, 5120, 256), (9, 4096, 128),
+                                            (5, 12288, 512)])
+def test_quantize_residual_random_bit_patterns(e_lo, e_hi, rows, cols, nres):
+    """Random finite patterns in one exponent window (subnormal-heavy, thirty
+    binades around 1, the top of the range) through both stages: the
+    lane-pair pass, the stash and the workgroup kernel, bit-exact."""
+    banner(f"residual random patterns e=[{e_lo},{e_hi}] {rows}x{cols} nres={nres}")
+    x = random_finite_patterns((rows, cols), e_lo, e_hi, 700 + e_lo + cols)
+    perm = oracle.channel_order(oracle.channel_absmax(x))
+    for mode, rule in ((F46, MSE), (F46, MAXE)):
+        got = gpu_residual(x, perm, nres, mode, rule)
+        ref = oracle.quantize_residual(x, perm, nres, mode, rule)
+        assert_residual_same(got, ref, f"patterns e>={e_lo} {rows}x{cols} rule={rule}")
+
+
+@pytest.mark.parametrize("e_lo,e_hi", [(0, 24), (112, 142), (224, 254)])
+def test_rmsnorm_residual_random_bit_patterns(e_lo, e_hi):
+    """The fused RMSNorm path on random finite patterns (squares that
+    underflow, and sums of squares that overflow to +inf), with the first
+    pass forming g: bit-exact, and the same max |y|."""
+    banner(f"rmsnorm+residual random patterns e=[{e_lo},{e_hi}]")
+    rows, cols, nres = 23, 5120, 256
+    x = random_finite_patterns((rows, cols), e_lo, e_hi, 800 + e_lo)
+    w = testkit.fill((cols,), testkit.NORMAL, 1.0, 81)
+    eps = 1e-6
+    y = oracle.rmsnorm(x, w, eps)
+    perm = oracle.channel_order(oracle.channel_absmax(y))
+    got = gpu_rms_residual(x, w, eps, perm, nres, F46, MSE, amax=True)
+    ref = oracle.quantize_residual(y, perm, nres, F46, MSE)
+    assert_residual_same(got, ref, f"patterns e>={e_lo}")
+    assert got["amax"].view(np.uint32) == oracle.amax(y).view(np.uint32)
+
+
 # ------------------------------------------ residual second-stage modes ----
 
 STASH_SHAPES = [
