@@ -140,9 +140,21 @@ def test_random_finite_bit_patterns(e_lo, e_hi, mode, rule):
     both block layouts, ragged shapes: every output bit-exact."""
     banner(f"random patterns e=[{e_lo},{e_hi}] mode={mode} rule={rule}")
     x = random_finite_patterns((96, 1040), e_lo, e_hi, 9000 + e_lo)
-    check_against_oracle(x, AXIS_COLS, mode, rule, what=f"patterns rows e>={e_lo}")
+    _, ref = check_against_oracle(x, AXIS_COLS, mode, rule, what=f"patterns rows e>={e_lo}")
     xc = random_finite_patterns((272, 48), e_lo, e_hi, 9100 + e_lo)
-    check_against_oracle(xc, AXIS_ROWS, mode, rule, what=f"patterns cols e>={e_lo}")
+    _, refc = check_against_oracle(xc, AXIS_ROWS, mode, rule, what=f"patterns cols e>={e_lo}")
+    # Dequantize the oracle's outputs on the GPU, in both layouts and both
+    # output types: decoded values range from subnormals to near 2^128.
+    for axis, q, (rows, cols) in ((AXIS_COLS, ref, x.shape), (AXIS_ROWS, refc, xc.shape)):
+        for dtype in (torch.float32, torch.bfloat16):
+            want = oracle.dequantize(q["packed"], q["scales"], q["gscale"], rows, cols, axis,
+                                     out_bf16=dtype == torch.bfloat16)
+            out = nv.dequantize(torch.from_numpy(q["packed"]).cuda(),
+                                torch.from_numpy(q["scales"]).cuda(),
+                                torch.tensor([q["gscale"]], dtype=torch.float32, device="cuda"),
+                                rows, cols, axis, dtype)
+            got = out.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+            np.testing.assert_array_equal(got, want.view(got.dtype))
 
 
 def test_tiny_tensor_amax():
