@@ -211,6 +211,22 @@ def secondary(nv, torch, testkit, xd, g, out, stream, rows, cols):
     res["rmsnorm_residual_given_g_gbps"] = round(res_bytes / t_f1 / 1e9, 1)
     res["rmsnorm_residual_given_g_frac_of_hbm_peak"] = round(res_bytes / t_f1 / 1e9 / HBM_PEAK_GBPS, 4)
     res["rmsnorm_residual_two_pass_us"] = round(t_f2 * 1e6, 2)
+    # The same fused path on wider rows (8192 tokens x 16384 channels, 512
+    # residual channels, given g): the workgroup-shared kernel.
+    wr, wc, wn = 8192, 16384, 512
+    xw = torch.from_numpy(testkit.fill((wr, wc), testkit.STUDENT_T3, 0.5, 97).view(np.int16)).to(
+        dev).view(torch.bfloat16)
+    ww = torch.from_numpy(testkit.fill((wc,), testkit.NORMAL, 1.0, 96).view(np.int16)).to(
+        dev).view(torch.bfloat16)
+    _, pw = nv.channel_order(xw)
+    fw = nv.rmsnorm_quantize_residual(xw, pw, wn, weight=ww, gscale=g)
+    t_fw = call_time(lambda: nv.rmsnorm_quantize_residual(xw, pw, wn, weight=ww, gscale=g, out=fw),
+                     torch, stream)
+    wide_bytes = wr * wc * 2 + wr * (wc + wn) * (0.5 + 1 / 16)
+    res["rmsnorm_residual_8192x16384_given_g_us"] = round(t_fw * 1e6, 2)
+    res["rmsnorm_residual_8192x16384_frac_of_hbm_peak"] = round(
+        wide_bytes / t_fw / 1e9 / HBM_PEAK_GBPS, 4)
+    del xw, ww, pw, fw
     # W4A4 product on the matrix cores: these activations (as quantized by
     # the step) times a 5120 x 5120 weight, and the augmented product over
     # K = 5120 + 256 (residual activations, duplicated weight channels).

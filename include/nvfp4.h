@@ -287,7 +287,8 @@ nvfp4_status nvfp4_quantize_residual(const uint16_t* in_bf16, int64_t rows, int6
  * (bf16 rounding to nearest even).
  *   weight_bf16: cols bf16 (16-byte aligned), or NULL.
  *   eps: finite and >= 0 (NVFP4_ERR_ENUM otherwise).
- *   cols: a positive multiple of 16, at most 8192 (one row per wave in LDS).
+ *   cols: a positive multiple of 16, at most 24576 (rows of up to 8192
+ *     channels are held one per wave in LDS, wider ones shared by a workgroup).
  *   flags: 0 -- a first pass over x computes g from max |y| (g = A/(6M) as
  *     nvfp4_quantize) and writes it to *gscale_inout; or
  *     NVFP4_FLAG_GSCALE_GIVEN -- read g from *gscale_inout (one pass).

@@ -412,7 +412,7 @@ nvfp4_status nvfp4_rmsnorm_quantize_residual(const uint16_t* in_bf16, int64_t ro
   if (!(eps >= 0.0f && eps <= 3.0e38f)) return NVFP4_ERR_ENUM;  // finite, non-negative
   const nvfp4_status shape = check_shape(rows, cols, NVFP4_AXIS_COLS);
   if (shape != NVFP4_OK) return shape;
-  if (cols > nvfp4::kRmsMaxCols || nres < 0 || nres > cols || nres % 16 != 0)
+  if (cols > nvfp4::kRmsWideMaxCols || nres < 0 || nres > cols || nres % 16 != 0)
     return NVFP4_ERR_SHAPE;
   if (!aligned(in_bf16, 16) || !aligned(weight_bf16, 16) || !aligned(perm, 4) ||
       !aligned(packed_out, 4) || !aligned(gscale_inout, 4) || !aligned(amax_out, 4))

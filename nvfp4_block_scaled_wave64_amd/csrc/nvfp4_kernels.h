@@ -137,7 +137,8 @@ struct RmsArgs {
   float eps;
   uint32_t* amax_out;
 };
-constexpr int64_t kRmsMaxCols = 8192;  // one row per wave in LDS
+constexpr int64_t kRmsMaxCols = 8192;       // one row per wave in LDS
+constexpr int64_t kRmsWideMaxCols = 24576;  // rows shared by a workgroup, wider ones
 hipError_t launch_rms_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,
                                         const int32_t* perm, int64_t nres, const float* gscale,
                                         uint32_t variant, uint8_t* packed, uint8_t* scales,

@@ -642,6 +642,159 @@ __global__ __launch_bounds__(rms_threads(kVpl)) void rms_amax_kernel(const uint1
   wave_max_to(acc, bf16_pair_max(ymax), six_m);
 }
 
+// Wide rows with RMSNorm in front (kRmsMaxCols < cols <= kRmsWideMaxCols):
+// a 1024-thread workgroup per compute unit stages R rows per step, as
+// quantize_residual_kernel does, and normalizes them in LDS before the
+// gathers.  The sum of squares keeps the order above: chunk v of a row (its
+// elements 8v .. 8v+7, one 16-byte LDS read) is summed by lane v % 64 of a
+// wave that holds the 64 chunks of an aligned group, wave_tree_sum adds them
+// (the first six levels of the zero-padded pairwise tree), and one wave per
+// row adds the group sums with the same tree, the groups past the row's
+// padded length being zeros, which leave the pairwise sums unchanged.
+//   kOnlyAmax: the first pass of the fused path: normalize, fold
+//   RN(max |y| / six_m) into *acc, quantize nothing.
+//   V & kVarAmax: also fold max |y| into ra.amax_out while quantizing.
+// LDS: scale table (1 KiB), channel order (cols 16-bit byte offsets), the
+// weights as bf16 (cols), 64 group sums and one rstd per staged row, then
+// the R staged rows.
+template <uint32_t V, bool kOnlyAmax>
+__global__ __launch_bounds__(kResThreads) void rms_residual_wide_kernel(
+    const uint16_t* __restrict__ in, int64_t rows, uint32_t cols, const int32_t* __restrict__ perm,
+    uint32_t nres, const float* __restrict__ gscale, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ scales, RmsArgs ra, uint32_t R, float six_m, uint32_t* __restrict__ acc) {
+  constexpr bool k46 = (V & kVarFourOverSix) != 0;
+  constexpr int kRule = !k46 ? kRuleMse
+                        : (V & kVarMax) ? kRuleMax
+                        : (V & kVarMae) ? kRuleMae
+                                        : kRuleMse;
+  constexpr bool kTrack = kOnlyAmax || (V & kVarAmax) != 0;
+  extern __shared__ __align__(16) uint8_t lds[];
+  float2* tab = reinterpret_cast<float2*>(lds);
+  uint16_t* pm = reinterpret_cast<uint16_t*>(lds + 1024);
+  uint16_t* wb = pm + cols;                                   // weights, bf16
+  float* gsum = reinterpret_cast<float*>(wb + cols);          // [R][64]
+  float* rstd_s = gsum + 64u * R;                             // [R], padded to 16 bytes
+  uint16_t* xs = reinterpret_cast<uint16_t*>(rstd_s + ((R + 3u) & ~3u));
+  u32x4* xs4 = reinterpret_cast<u32x4*>(xs);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr uint32_t kWaves = kResThreads / 64;
+
+  const TensorScales ts = tensor_scales(kOnlyAmax ? 1.0f : *gscale);
+  if constexpr (!kOnlyAmax) build_scale_table(tab, ts);
+  int bad = 0;
+  for (uint32_t c = threadIdx.x; c < cols; c += kResThreads) {
+    if constexpr (!kOnlyAmax) {
+      const uint32_t v = (uint32_t)perm[c];
+      bad |= v >= cols;
+      pm[c] = (uint16_t)(2u * std::min(v, cols - 1u));
+    }
+    wb[c] = ra.weight ? ra.weight[c] : (uint16_t)0x3F80u;  // 1.0 without a weight vector
+  }
+  const uint32_t nb = cols >> 4, nrb = nres >> 4, bout = nb + nrb;
+  const uint32_t vrow = cols >> 3;
+  // Groups of 64 chunks per row in the zero-padded tree: its padded length
+  // is a power of two of at least 64, and vrow > 1024 here.
+  uint32_t ngroups = 1u;
+  while (64u * ngroups < vrow) ngroups *= 2u;
+  const int64_t niter = (rows + R - 1) / R;
+  if (__syncthreads_or(bad)) {
+    for (int64_t it = blockIdx.x; it < niter; it += gridDim.x)
+      poison_rows(it * R, 1, std::min<int64_t>(rows, it * R + R), bout, threadIdx.x,
+                  kResThreads, packed, scales);
+    return;
+  }
+
+  auto rows_at = [&](int64_t it) -> uint32_t {
+    return (uint32_t)std::min<int64_t>((int64_t)R, rows - it * R);
+  };
+  auto load = [&](int64_t it, u32x4 (&buf)[kResVec]) {
+    const uint32_t nv = rows_at(it) * vrow;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(in + it * R * cols, nv * 16u);
+    __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+    for (int k = 0; k < kResVec; ++k)
+      buf[k] = __builtin_amdgcn_raw_buffer_load_b128(r, (threadIdx.x + k * kResThreads) * 16u, 0,
+                                                     kStreamLoad);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  uint32_t ymax = 0u;  // packed bf16 max |y| (kTrack)
+  u32x4 buf[kResVec];
+  if ((int64_t)blockIdx.x < niter) load(blockIdx.x, buf);
+  uint32_t rot = 0u;
+  for (int64_t it = blockIdx.x; it < niter; it += gridDim.x) {
+    const uint32_t nr = rows_at(it);
+    __syncthreads();  // the previous rows are consumed (and pm, wb, tab written)
+#pragma unroll
+    for (int k = 0; k < kResVec; ++k) {
+      const uint32_t v = threadIdx.x + k * kResThreads;
+      if (v < nr * vrow) xs4[v] = buf[k];
+    }
+    __syncthreads();
+    if (it + gridDim.x < niter) load(it + gridDim.x, buf);
+
+    // Sum of squares: group sums (every lane of a wave takes part in the
+    // tree; chunks past the row read as zeros).
+    for (uint32_t g = wave; g < nr * ngroups; g += kWaves) {
+      const uint32_t rr = g / ngroups, chunk = (g - rr * ngroups) * 64u + lane;
+      float t = 0.0f;
+      if (chunk < vrow) {
+        const u32x4 q = xs4[rr * vrow + chunk];
+        t = __builtin_fmaf(bf16_lo(q.x), bf16_lo(q.x), t);
+        t = __builtin_fmaf(bf16_hi(q.x), bf16_hi(q.x), t);
+        t = __builtin_fmaf(bf16_lo(q.y), bf16_lo(q.y), t);
+        t = __builtin_fmaf(bf16_hi(q.y), bf16_hi(q.y), t);
+        t = __builtin_fmaf(bf16_lo(q.z), bf16_lo(q.z), t);
+        t = __builtin_fmaf(bf16_hi(q.z), bf16_hi(q.z), t);
+        t = __builtin_fmaf(bf16_lo(q.w), bf16_lo(q.w), t);
+        t = __builtin_fmaf(bf16_hi(q.w), bf16_hi(q.w), t);
+      }
+      const float gs = wave_tree_sum(t);
+      if (lane == 0u) gsum[rr * 64u + (g - rr * ngroups)] = gs;
+    }
+    __syncthreads();
+    if (wave < nr) {
+      const float t = lane < ngroups ? gsum[wave * 64u + lane] : 0.0f;
+      const float rstd = rms_rstd(wave_tree_sum(t), cols, ra.eps);
+      if (lane == 0u) rstd_s[wave] = rstd;
+    }
+    __syncthreads();
+    // Normalize the staged rows in place (8 elements per 16-byte slot).
+    const u32x4* w4 = reinterpret_cast<const u32x4*>(wb);
+    for (uint32_t v = threadIdx.x; v < nr * vrow; v += kResThreads) {
+      const uint32_t rr = v / vrow, c8 = v - rr * vrow;
+      const float rstd = rstd_s[rr];
+      const u32x4 w = w4[c8];
+      u32x4 q = xs4[v];
+      q.x = rms_pair<kTrack>(q.x, bf16_lo(w.x), bf16_hi(w.x), rstd, ymax);
+      q.y = rms_pair<kTrack>(q.y, bf16_lo(w.y), bf16_hi(w.y), rstd, ymax);
+      q.z = rms_pair<kTrack>(q.z, bf16_lo(w.z), bf16_hi(w.z), rstd, ymax);
+      q.w = rms_pair<kTrack>(q.w, bf16_lo(w.w), bf16_hi(w.w), rstd, ymax);
+      if constexpr (!kOnlyAmax) xs4[v] = q;
+    }
+    if constexpr (!kOnlyAmax) {
+      __syncthreads();
+      const int64_t r0 = it * R;
+      const __amdgpu_buffer_rsrc_t r_packed = make_rsrc(packed + r0 * bout * 8, nr * bout * 8u);
+      const __amdgpu_buffer_rsrc_t r_scales = make_rsrc(scales + r0 * bout, nr * bout);
+      const uint32_t nitems = nr * nb;
+#pragma unroll 1
+      for (uint32_t item = (threadIdx.x + rot) & (kResThreads - 1u); item < nitems;
+           item += kResThreads) {
+        const uint32_t rr = item / nb, j = item - rr * nb;
+        residual_block<k46, kRule>(xs + rr * cols, pm, j, rr * bout + j, nb, j < nrb, false,
+                                   r_packed, r_scales, ts, tab);
+      }
+      rot = (rot + 64u) & (kResThreads - 1u);
+    }
+  }
+  if constexpr (kOnlyAmax)
+    wave_max_to(acc, bf16_pair_max(ymax), six_m);
+  else if constexpr (kTrack)
+    wave_max_to(ra.amax_out, bf16_pair_max(ymax), 0.0f);
+}
+
 // Workgroup size bound of the narrow-row kernel: 12 waves where the row (in
 // registers), the normalization and two blocks in flight need more than 128
 // VGPRs.  Rows of 12 or more vectors per lane fit at most 12 waves per
@@ -1018,6 +1171,34 @@ static hipError_t launch_residual_v(const uint16_t* in, int64_t rows, int64_t co
   return launch_residual_group<V>(in, rows, cols, perm, nres, gscale, packed, scales, dup, s);
 }
 
+template <uint32_t V, bool kOnlyAmax>
+static hipError_t launch_rms_wide(const uint16_t* in, int64_t rows, int64_t cols,
+                                  const int32_t* perm, int64_t nres, const float* gscale,
+                                  uint8_t* packed, uint8_t* scales, const RmsArgs& ra,
+                                  float six_m, uint32_t* acc, hipStream_t s) {
+  // Rows per step: at least kResItems output blocks per thread, within the
+  // staging capacity of kResThreads * kResVec 16-byte vectors and the
+  // compute unit's 160 KiB of LDS (rms_residual_wide_kernel's layout).
+  const int64_t nb = cols / 16;
+  auto lds_for = [&](int64_t r) {
+    return 1024 + 4 * cols + 256 * r + 4 * ((r + 3) & ~int64_t(3)) + 2 * cols * r;
+  };
+  int64_t R = ((int64_t)kResItems * kResThreads + nb - 1) / nb;
+  R = std::min<int64_t>(R, (int64_t)kResThreads * kResVec * 8 / cols);
+  while (R > 1 && lds_for(R) > 163840) --R;
+  if (R < 1 || lds_for(R) > 163840) return hipErrorInvalidValue;
+  const size_t lds = (size_t)lds_for(R);
+  const hipError_t e = allow_lds<&rms_residual_wide_kernel<V, kOnlyAmax>>(lds);
+  if (e != hipSuccess) return e;
+  // One workgroup per compute unit, persistent over steps.
+  const int64_t niter = (rows + R - 1) / R;
+  const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(niter, device_cu_count()));
+  rms_residual_wide_kernel<V, kOnlyAmax><<<(unsigned)groups, kResThreads, lds, s>>>(
+      in, rows, (uint32_t)cols, perm, (uint32_t)nres, gscale, packed, scales, ra, (uint32_t)R,
+      six_m, acc);
+  return hipGetLastError();
+}
+
 template <uint32_t V>
 static hipError_t launch_rms_residual_v(const uint16_t* in, int64_t rows, int64_t cols,
                                         const int32_t* perm, int64_t nres, const float* gscale,
@@ -1035,8 +1216,11 @@ static hipError_t launch_rms_residual_v(const uint16_t* in, int64_t rows, int64_
   if (cols <= 6144)
     return launch_residual_wave<V, 12, true>(in, rows, cols, perm, nres, gscale, packed, scales,
                                              ra, false, s);
-  return launch_residual_wave<V, 16, true>(in, rows, cols, perm, nres, gscale, packed, scales,
-                                           ra, false, s);
+  if (cols <= kRmsMaxCols)
+    return launch_residual_wave<V, 16, true>(in, rows, cols, perm, nres, gscale, packed, scales,
+                                             ra, false, s);
+  return launch_rms_wide<V, false>(in, rows, cols, perm, nres, gscale, packed, scales, ra, 0.0f,
+                                   nullptr, s);
 }
 
 hipError_t launch_rms_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,
@@ -1081,7 +1265,9 @@ hipError_t launch_rms_amax(const uint16_t* in, int64_t rows, int64_t cols, const
   if (cols <= 4096) return launch_rms_amax_v<8>(in, rows, cols, ra, six_m, acc, s);
   if (cols <= 5120) return launch_rms_amax_v<10>(in, rows, cols, ra, six_m, acc, s);
   if (cols <= 6144) return launch_rms_amax_v<12>(in, rows, cols, ra, six_m, acc, s);
-  return launch_rms_amax_v<16>(in, rows, cols, ra, six_m, acc, s);
+  if (cols <= kRmsMaxCols) return launch_rms_amax_v<16>(in, rows, cols, ra, six_m, acc, s);
+  return launch_rms_wide<0u, true>(in, rows, cols, nullptr, 0, nullptr, nullptr, nullptr, ra,
+                                   six_m, acc, s);
 }
 
 hipError_t launch_quantize_residual(const uint16_t* in, int64_t rows, int64_t cols,

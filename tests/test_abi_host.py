@@ -223,14 +223,14 @@ def rq(**kw):
     (dict(in_=None), 1), (dict(perm=None), 1), (dict(packed=None), 1), (dict(g=None), 1),
     (dict(mode=5), 2), (dict(rule=4), 2), (dict(flags=2), 2), (dict(eps=-1.0), 2),
     (dict(eps=float("inf")), 2), (dict(eps=float("nan")), 2),
-    (dict(cols=8208), 3), (dict(cols=40), 3), (dict(rows=0), 3), (dict(nres=24), 3),
+    (dict(cols=24592), 3), (dict(cols=40), 3), (dict(rows=0), 3), (dict(nres=24), 3),
     (dict(w=ctypes.c_void_p(0x60008)), 4), (dict(amax=ctypes.c_void_p(0x60002)), 4),
     (dict(in_=MIS), 4),
     (dict(amax=E), 6), (dict(w=ctypes.c_void_p(0x30000)), 6), (dict(g=ctypes.c_void_p(0x10010)), 6),
 ])
 def test_rmsnorm_quantize_residual_rejects(kw, status):
     """nvfp4_rmsnorm_quantize_residual: nulls, enums (eps finite and >= 0,
-    only GSCALE_GIVEN), shape (cols <= 8192), alignment (weight 16 bytes),
+    only GSCALE_GIVEN), shape (cols <= 24576), alignment (weight 16 bytes),
     outputs overlapping inputs or each other."""
     assert rq(**kw) == status
 

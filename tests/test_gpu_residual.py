@@ -225,10 +225,14 @@ def gpu_rms_residual(x, w, eps, perm, nres, mode, rule, gscale=None, amax=False)
 
 RMS_SHAPES = [
     # (rows, cols, nres): every row-buffer size class of the fused kernel,
-    # fewer rows than waves, ragged row counts, nres = 0 and nres = cols
+    # fewer rows than waves, ragged row counts, nres = 0 and nres = cols;
+    # past 8192 channels the workgroup-shared kernel with 3, 2 and 1 rows
+    # per step, a partial last step, and its padded sum-of-squares tree
+    # (8208 and 10240 channels: 1026 and 1280 chunks in a 2048-leaf tree)
     (1, 16, 16), (7, 48, 0), (100, 1040, 64), (33, 2048, 256), (65, 2064, 128), (40, 4096, 512),
     (11, 4112, 32), (19, 5120, 256), (5, 5136, 16), (25, 6144, 96), (13, 6160, 1024),
-    (9, 8192, 8192),
+    (9, 8192, 8192), (6, 8208, 64), (4, 10240, 10240), (7, 12288, 512), (5, 16384, 1024),
+    (33, 16384, 0), (3, 24576, 256),
 ]
 
 
@@ -248,9 +252,9 @@ def test_rmsnorm_residual_matches_oracle(rows, cols, nres, weighted):
 
 
 @pytest.mark.parametrize("mode,rule", RULES)
-def test_rmsnorm_residual_rules_and_given_scale(mode, rule):
-    banner(f"rmsnorm+residual rules mode={mode} rule={rule}")
-    rows, cols, nres = 64, 3072, 192
+@pytest.mark.parametrize("rows,cols,nres", [(64, 3072, 192), (10, 16384, 384)])
+def test_rmsnorm_residual_rules_and_given_scale(mode, rule, rows, cols, nres):
+    banner(f"rmsnorm+residual rules mode={mode} rule={rule} {rows}x{cols}")
     x = outlier_tensor(41, rows, cols)
     w = testkit.fill((cols,), testkit.NORMAL, 0.5, 42)
     for eps in (0.0, 1e-2):
@@ -324,7 +328,8 @@ def test_check_order_counts_what_breaks_a_permutation(cols):
 
 @pytest.mark.parametrize("rows,cols,nres,rms", [
     (37, 80, 16, False), (300, 5120, 256, False), (20, 9216, 512, False),  # both kernel shapes
-    (37, 80, 16, True), (300, 5120, 256, True),  # fused RMSNorm (rows of at most 8192)
+    (37, 80, 16, True), (300, 5120, 256, True),  # fused RMSNorm, one row per wave
+    (9, 16384, 512, True),  # fused RMSNorm, rows shared by a workgroup
 ])
 def test_out_of_range_order_poisons_the_output(rows, cols, nres, rms):
     """An order entry outside [0, cols) makes nvfp4_quantize_residual (and
@@ -405,13 +410,14 @@ def test_quantize_residual_random_bit_patterns(e_lo, e_hi, rows, cols, nres):
 
 
 @pytest.mark.parametrize("e_lo,e_hi", [(0, 24), (112, 142), (224, 254)])
-def test_rmsnorm_residual_random_bit_patterns(e_lo, e_hi):
+@pytest.mark.parametrize("cols", [5120, 16384])
+def test_rmsnorm_residual_random_bit_patterns(e_lo, e_hi, cols):
     """The fused RMSNorm path on random finite patterns (squares that
     underflow, and sums of squares that overflow to +inf), with the first
     pass forming g: bit-exact, and the same max |y|."""
     banner(f"rmsnorm+residual random patterns e=[{e_lo},{e_hi}]")
-    rows, cols, nres = 23, 5120, 256
-    x = random_finite_patterns((rows, cols), e_lo, e_hi, 800 + e_lo)
+    rows, nres = 23, 256
+    x = random_finite_patterns((rows, cols), e_lo, e_hi, 800 + e_lo + cols)
     w = testkit.fill((cols,), testkit.NORMAL, 1.0, 81)
     eps = 1e-6
     y = oracle.rmsnorm(x, w, eps)
