@@ -150,6 +150,36 @@ def test_large_residual_sampled_rows(big_res):
     del r
 
 
+WIDE_ROWS, WIDE_COLS, WIDE_NRES = 70000, 16384, 512  # 2.3 GB: rows start past 2^31 bytes
+
+
+def test_large_rmsnorm_residual_wide_sampled_rows():
+    """The fused RMSNorm path on rows of 16384 channels (the workgroup-shared
+    kernel) over 2.3 GB with a given g: rows on both sides of the 2^31-byte
+    seam and random rows against the oracle's RMSNorm and two-stage quantize."""
+    banner(f"rmsnorm+residual {WIDE_ROWS}x{WIDE_COLS}")
+    x = testkit.fill((WIDE_ROWS, WIDE_COLS), testkit.STUDENT_T3, 0.5, 0x71D)
+    w = testkit.fill((WIDE_COLS,), testkit.NORMAL, 1.0, 0x71E)
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    wd = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16)
+    rng = np.random.default_rng(0x71F)
+    perm = rng.permutation(WIDE_COLS).astype(np.int32)
+    g = np.float32(0.004)
+    gd = torch.tensor([float(g)], dtype=torch.float32, device="cuda")
+    r = nv.rmsnorm_quantize_residual(xd, torch.from_numpy(perm).cuda(), WIDE_NRES, weight=wd,
+                                     eps=1e-6, gscale=gd)
+    torch.cuda.synchronize()
+    seam = (1 << 31) // (WIDE_COLS * 2)  # first row starting at or past 2^31 bytes
+    pick = np.unique(np.concatenate([[0, seam - 1, seam, seam + 1, WIDE_ROWS - 1],
+                                     rng.integers(0, WIDE_ROWS, 27)]))
+    y = oracle.rmsnorm(x[pick], w, 1e-6)
+    ref = oracle.quantize_residual(y, perm, WIDE_NRES, nv.MODE_4OVER6, nv.RULE_MSE, gscale=g)
+    idx = torch.from_numpy(pick).cuda()
+    np.testing.assert_array_equal(r["packed"][idx].cpu().numpy(), ref["packed"])
+    np.testing.assert_array_equal(r["scales"][idx].cpu().numpy(), ref["scales"])
+    del r, xd
+
+
 def test_large_w4a4_product_sampled_rows():
     """An activation operand of 2.25 GB of codes: the tiles' base addresses
     pass 2^31 bytes (64-bit per-tile bases, 32-bit offsets within a tile);
